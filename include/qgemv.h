@@ -1,0 +1,231 @@
+/*
+ * qgemv.h -- C ABI of the weight-quantized decode GEMV / skinny GEMM library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Batch-one LLM decode streams every weight once per token
+ * with about one multiply-add per weight, so it is bound by memory bandwidth
+ * (Uzu on Apple M5, fange-kb.cn, section "Why batch-one decoding is
+ * memory-bound"; "MLX Runner: An Inference Engine You Can Read", section
+ * "Optimized against a known ceiling").  This library provides that product,
+ * y = W x, for weights kept in quantized form and dequantized in registers,
+ * plus its skinny form Y = X W^T for M <= 32 activation rows, which is how a
+ * draft of 16-32 speculative tokens is verified in one pass (Uzu page,
+ * section "Producing several tokens from one model pass").
+ *
+ * Weight formats (each matrix is stored [N, K]: N output rows, K inputs):
+ *  - QG_FMT_Q4_ASYM_G64: 4-bit unsigned codes, one fp16 scale and one fp16
+ *    bias per group of 64 consecutive k; weight = scale * code + bias
+ *    ("MLX Runner", section "Architecture: one command buffer per token";
+ *    asymmetric 4-bit per the Uzu page, section "How Uzu optimizes bytes and
+ *    tokens per pass").
+ *  - QG_FMT_Q8_SYM_G32: int8 codes in [-127, 127], one fp16 scale per group of
+ *    32, multiplied by int8 activations (Uzu page, same section: 8-bit
+ *    symmetric checkpoints; activations quantized to 8 bits on the fly after a
+ *    block-diagonal randomized Hadamard-32 rotation).
+ *  - QG_FMT_MXFP4_G32: E2M1 codes with one E8M0 scale per 32 values (Deltafin
+ *    / Kimi K3 page, aihot.virxact.com, sections "How it works" and the compute
+ *    list: fused MXFP4 dequant + GEMV for the routed experts).
+ *
+ * Canonical (unpacked) layouts accepted by qgemv_pack, all row-major device
+ * buffers:
+ *  - Q4:    codes uint32 [N][K/8] (element k in bits 4*(k%8).., low nibble
+ *           first); scales, biases fp16 [N][K/64].
+ *  - Q8:    codes int8 [N][K];  scales fp16 [N][K/32];  biases NULL.
+ *  - MXFP4: codes uint8 [N][K/2] (element 2i in the low nibble of byte i);
+ *           scales uint8 E8M0 [N][K/32];  biases NULL.
+ * The packed layout is opaque: a buffer produced by qgemv_pack for a given
+ * (fmt, rows, K) is consumed only by calls with the same (fmt, N, K).
+ *
+ * Conventions for every call:
+ *  - Every buffer is caller-owned device memory.  The library allocates no
+ *    memory, frees none and never synchronizes; it keeps only a per-device
+ *    cache of the compute-unit count.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  A call validates
+ *    its arguments on the host, enqueues its kernels on `stream` and returns.
+ *  - Validation happens before any HIP call, so an invalid call returns its
+ *    error without touching the device.  Device pointers marked "16-B" must be
+ *    16-byte aligned; others need their element's natural alignment.
+ *  - A dimension of 0 (N = 0, M = 0, top_k = 0) is a valid empty problem:
+ *    nothing is enqueued (moe_expert_gemv_run with top_k = 0 still writes
+ *    y = 0).
+ *  - Calls are re-entrant; calls on different streams may run concurrently
+ *    as long as they do not write the same buffers.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_EINVAL = -1,       /* NULL where a pointer is required; unknown enum value */
+    QG_ESHAPE = -2,       /* dimension out of range (K not a multiple of the
+                             format's block, M outside 0..32, top_k > E, ...) */
+    QG_EALIGN = -3,       /* a device pointer violates its alignment */
+    QG_ESIZE = -4,        /* packed_bytes / workspace_bytes is not the size the
+                             layout needs */
+    QG_EUNSUPPORTED = -5, /* format x output x entry point combination not provided */
+    QG_EHIP = -6,         /* the HIP runtime reported an error */
+    QG_EINTERNAL = -7     /* unexpected internal failure */
+} qg_status;
+
+typedef enum {
+    QG_FMT_Q4_ASYM_G64 = 1,
+    QG_FMT_Q8_SYM_G32 = 2,
+    QG_FMT_MXFP4_G32 = 3
+} qg_format;
+
+typedef enum {
+    QG_OUT_BF16 = 0,       /* bf16, round to nearest even */
+    QG_OUT_F32 = 1,        /* fp32, the accumulator as computed */
+    QG_OUT_I32_GROUPS = 2  /* Q8 only: exact int32 group partials [M][N][K/32] */
+} qg_out;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qg_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int qg_version(void);
+
+/*
+ * qgemv_pack -- convert canonical device tensors into the packed device
+ * layout that the run calls stream with 128-bit coalesced loads.  Weights are
+ * packed once at load time and never stored dequantized ("MLX Runner",
+ * section "Architecture: one command buffer per token").
+ *
+ *  fmt          one of qg_format.
+ *  rows         N, the number of output rows; a stack of E equally shaped
+ *               expert matrices is packed as rows = E * N_expert.
+ *  K            inputs per row: a multiple of 64 (Q4) or 32 (Q8, MXFP4),
+ *               1 <= K <= 2^20.
+ *  codes, scales, biases   canonical device buffers (layouts above); biases is
+ *               required for Q4 and must be NULL otherwise.  Read only.
+ *  packed       device buffer (16-B) receiving the packed layout, or NULL to
+ *               query the size only (no device access at all then).
+ *  packed_bytes in: capacity of `packed` (ignored when packed is NULL);
+ *               out: bytes the layout needs.  Capacity below that -> QG_ESIZE.
+ *  stream       hipStream_t.
+ * Errors: QG_EINVAL (NULL codes/scales/packed_bytes, bias presence wrong),
+ * QG_ESHAPE, QG_EALIGN, QG_ESIZE, QG_EHIP.
+ */
+int qgemv_pack(int fmt, int64_t rows, int64_t K, const void *codes,
+               const void *scales, const void *biases, void *packed,
+               size_t *packed_bytes, void *stream);
+
+/*
+ * qgemv_run -- decode GEMV, one activation row: y[n] = sum_k w[n][k] x[k]
+ * (the product batch-one decode spends its time in; Uzu page, "Why batch-one
+ * decoding is memory-bound").  Weights are dequantized in registers and
+ * accumulated in fp32.
+ *
+ *  fmt          QG_FMT_Q4_ASYM_G64 or QG_FMT_MXFP4_G32 (Q8 -> QG_EUNSUPPORTED;
+ *               use qgemm_skinny_run with M = 1).
+ *  packed, packed_bytes   from qgemv_pack with the same (fmt, N, K); 16-B.
+ *  N, K         output rows and inputs; K <= 24576 for this call.
+ *  x            device bf16 [K], 16-B.  Read only.
+ *  y            device [N] of the output type (bf16 or fp32), written.
+ *  out_dtype    QG_OUT_BF16 or QG_OUT_F32.
+ * Errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN, QG_ESIZE, QG_EUNSUPPORTED, QG_EHIP.
+ */
+int qgemv_run(int fmt, const void *packed, size_t packed_bytes, int64_t N,
+              int64_t K, const void *x, void *y, int out_dtype, void *stream);
+
+/*
+ * qgemm_skinny_run -- the skinny product Y[m][n] = sum_k w[n][k] X[m][k] for
+ * M = 1..32 activation rows against the same weights, streamed once per call
+ * (one verification pass over a 16- or 32-token draft; Uzu page, "Producing
+ * several tokens from one model pass").  Runs on the MFMA matrix cores.
+ *
+ *  fmt          QG_FMT_Q4_ASYM_G64: X is bf16 [M][K], x_scales must be NULL.
+ *               QG_FMT_Q8_SYM_G32: X is int8 [M][K] (from hadamard32_quant_run,
+ *               so the weights must already be in the rotated basis) and
+ *               x_scales fp32 [M] is the per-row activation scale.
+ *  packed, packed_bytes   from qgemv_pack with the same (fmt, N, K); 16-B.
+ *  M            0..32.
+ *  X            device [M][K], rows contiguous, 16-B.  Read only.
+ *  Y            device output: [M][N] bf16 or fp32; for QG_OUT_I32_GROUPS
+ *               (Q8 only) int32 [M][N][K/32], the exact group partials
+ *               sum_{k in g} qw[n][k] * qx[m][k].
+ * Errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN, QG_ESIZE, QG_EUNSUPPORTED, QG_EHIP.
+ */
+int qgemm_skinny_run(int fmt, const void *packed, size_t packed_bytes,
+                     int64_t M, int64_t N, int64_t K, const void *X,
+                     const float *x_scales, void *Y, int out_dtype,
+                     void *stream);
+
+/*
+ * hadamard32_quant_run -- on-the-fly int8 quantization of activations after a
+ * block-diagonal randomized Hadamard transform (Uzu page, "How Uzu optimizes
+ * bytes and tokens per pass"): for each row m and each block of 32
+ * consecutive k, z = H32 (d . x) with H32 the +-1 Sylvester Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j)) and d the sign flips, applied before the
+ * mixing.  Then per row: amax = max |z|, Xq = round-half-even(z * 127 / amax)
+ * (computed in fp64; the sums are exact) and x_scales[m] = amax /
+ * (127 * sqrt(32)) rounded to fp32, so that x_scales[m] * Xq approximates the
+ * orthonormal rotation z / sqrt(32).  A zero row gives Xq = 0, scale 0.
+ *
+ *  X            device bf16 [M][K], 16-B.  Read only.
+ *  signs        device int8 [K], each +1 or -1 (other values are used as
+ *               given).  Read only.
+ *  M, K         M >= 0, K a positive multiple of 32.
+ *  Xq           device int8 [M][K], 16-B, written.
+ *  x_scales     device fp32 [M], written.
+ * Errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN, QG_EHIP.
+ */
+int hadamard32_quant_run(const void *X, const int8_t *signs, int64_t M,
+                         int64_t K, int8_t *Xq, float *x_scales, void *stream);
+
+/*
+ * Bytes of workspace moe_expert_gemv_run needs for (top_k, H, F): the SwiGLU
+ * activations h (fp32 [top_k][F]), the per-expert partial outputs (fp32
+ * [top_k][H]) and a status word.  Pure host function.
+ */
+size_t qg_moe_workspace_bytes(int64_t top_k, int64_t H, int64_t F);
+
+/*
+ * moe_expert_gemv_run -- one token through the routed experts of one MoE
+ * layer in MXFP4 (Deltafin / Kimi K3 page: the router selects the top-k
+ * experts and only those are read; fused MXFP4 dequant + GEMV):
+ *     for s < top_k with e = expert_ids[s]:
+ *         g = Wgate[e] x,  u = Wup[e] x,  h = silu(g) * u,
+ *     y = sum_s expert_w[s] * (Wdown[e] h).
+ * g, u, h and the partial outputs are fp32; y is rounded once at the end.
+ * expert_ids and expert_w stay on the device (no host round trip).  The
+ * weighted sum is taken in slot order, so results are deterministic.
+ *
+ *  packed_gate, packed_up   qgemv_pack(MXFP4, rows = E * F, K = H), 16-B.
+ *  packed_down              qgemv_pack(MXFP4, rows = E * H, K = F), 16-B.
+ *  bytes_*      sizes from those qgemv_pack calls.
+ *  E, H, F      experts, hidden size, expert FFN size; H and F positive
+ *               multiples of 32; H <= 24576, F <= 12288.
+ *  x            device bf16 [H], 16-B.  Read only.
+ *  top_k        0..min(E, 64).
+ *  expert_ids   device int32 [top_k]; an id outside [0, E) contributes 0.
+ *               The call rewrites a status word (uint32 at byte offset
+ *               4 * top_k * (F + H) of the workspace): 1 if any id was out
+ *               of range, else 0.
+ *  expert_w     device fp32 [top_k] router weights.
+ *  workspace    device buffer (16-B) of at least qg_moe_workspace_bytes bytes;
+ *               its contents are scratch, overwritten by every call.
+ *  y            device [H] bf16 or fp32, written.
+ * Errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN, QG_ESIZE, QG_EUNSUPPORTED, QG_EHIP.
+ */
+int moe_expert_gemv_run(const void *packed_gate, const void *packed_up,
+                        const void *packed_down, size_t bytes_gate,
+                        size_t bytes_up, size_t bytes_down, int64_t E,
+                        int64_t H, int64_t F, const void *x, int top_k,
+                        const int32_t *expert_ids, const float *expert_w,
+                        void *workspace, size_t workspace_bytes, void *y,
+                        int out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,200 @@
+"""Thin Python binding of the C ABI in include/qgemv.h.
+
+Argument marshalling only: tensors are passed to the library as raw device
+pointers with the current HIP stream, every step of the computation runs in
+the library's kernels.  PyTorch supplies device memory and streams; output
+tensors the caller does not provide are allocated here with torch.
+
+The binding refuses to run without the compiled library: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+from .build import LIB_PATH
+
+FMT_Q4_ASYM_G64 = 1
+FMT_Q8_SYM_G32 = 2
+FMT_MXFP4_G32 = 3
+
+OUT_BF16 = 0
+OUT_F32 = 1
+OUT_I32_GROUPS = 2
+
+QG_OK = 0
+QG_EINVAL = -1
+QG_ESHAPE = -2
+QG_EALIGN = -3
+QG_ESIZE = -4
+QG_EUNSUPPORTED = -5
+QG_EHIP = -6
+QG_EINTERNAL = -7
+
+# every function include/qgemv.h declares
+EXPORTS = (
+    "qg_status_string",
+    "qg_version",
+    "qgemv_pack",
+    "qgemv_run",
+    "qgemm_skinny_run",
+    "hadamard32_quant_run",
+    "qg_moe_workspace_bytes",
+    "moe_expert_gemv_run",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+def raw():
+    """The loaded library with argument types set (loads on first use)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    "libqgemv.so is not built (%s); run __graft_entry__.build() or "
+                    "python -m quantized_weight_decode_dequant_amd.build" % LIB_PATH)
+            lib = C.CDLL(LIB_PATH)
+            i64, p, i, sz = C.c_int64, C.c_void_p, C.c_int, C.c_size_t
+            lib.qg_status_string.argtypes = [i]
+            lib.qg_status_string.restype = C.c_char_p
+            lib.qg_version.argtypes = []
+            lib.qg_version.restype = i
+            lib.qgemv_pack.argtypes = [i, i64, i64, p, p, p, p, C.POINTER(sz), p]
+            lib.qgemv_pack.restype = i
+            lib.qgemv_run.argtypes = [i, p, sz, i64, i64, p, p, i, p]
+            lib.qgemv_run.restype = i
+            lib.qgemm_skinny_run.argtypes = [i, p, sz, i64, i64, i64, p, p, p, i, p]
+            lib.qgemm_skinny_run.restype = i
+            lib.hadamard32_quant_run.argtypes = [p, p, i64, i64, p, p, p]
+            lib.hadamard32_quant_run.restype = i
+            lib.qg_moe_workspace_bytes.argtypes = [i64, i64, i64]
+            lib.qg_moe_workspace_bytes.restype = sz
+            lib.moe_expert_gemv_run.argtypes = [p, p, p, sz, sz, sz, i64, i64, i64, p, i, p, p,
+                                                p, sz, p, i, p]
+            lib.moe_expert_gemv_run.restype = i
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return raw().qg_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != QG_OK:
+        raise QGError(status, where)
+
+
+# ------------------------------------------------------------------ torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return C.c_void_p(t.data_ptr())
+
+
+def _out_torch_dtype(out_dtype):
+    torch = _torch()
+    return {OUT_BF16: torch.bfloat16, OUT_F32: torch.float32, OUT_I32_GROUPS: torch.int32}[out_dtype]
+
+
+# ------------------------------------------------------------------ API
+def packed_bytes(fmt: int, rows: int, K: int) -> int:
+    n = C.c_size_t(0)
+    _check(raw().qgemv_pack(fmt, rows, K, None, None, None, None, C.byref(n), None), "qgemv_pack")
+    return n.value
+
+
+def qgemv_pack(fmt: int, rows: int, K: int, codes, scales, biases=None, out=None, stream=None):
+    """Pack canonical device tensors; returns the packed uint8 device tensor."""
+    torch = _torch()
+    nbytes = packed_bytes(fmt, rows, K)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
+    cap = C.c_size_t(out.numel() * out.element_size())
+    _check(raw().qgemv_pack(fmt, rows, K, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(out),
+                            C.byref(cap), _stream(stream)), "qgemv_pack")
+    return out[:nbytes] if out.numel() != nbytes else out
+
+
+def qgemv_run(fmt: int, packed, N: int, K: int, x, y=None, out_dtype: int = OUT_BF16,
+              stream=None):
+    torch = _torch()
+    if y is None:
+        y = torch.empty(N, dtype=_out_torch_dtype(out_dtype), device=x.device)
+    _check(raw().qgemv_run(fmt, _ptr(packed), packed.numel(), N, K, _ptr(x), _ptr(y), out_dtype,
+                           _stream(stream)), "qgemv_run")
+    return y
+
+
+def qgemm_skinny_run(fmt: int, packed, M: int, N: int, K: int, X, x_scales=None, Y=None,
+                     out_dtype: int = OUT_BF16, stream=None):
+    torch = _torch()
+    if Y is None:
+        shape = (M, N, K // 32) if out_dtype == OUT_I32_GROUPS else (M, N)
+        Y = torch.empty(shape, dtype=_out_torch_dtype(out_dtype), device=X.device)
+    _check(raw().qgemm_skinny_run(fmt, _ptr(packed), packed.numel(), M, N, K, _ptr(X),
+                                  _ptr(x_scales), _ptr(Y), out_dtype, _stream(stream)),
+           "qgemm_skinny_run")
+    return Y
+
+
+def hadamard32_quant_run(X, signs, M: int, K: int, Xq=None, x_scales=None, stream=None):
+    torch = _torch()
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scales is None:
+        x_scales = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(raw().hadamard32_quant_run(_ptr(X), _ptr(signs), M, K, _ptr(Xq), _ptr(x_scales),
+                                      _stream(stream)), "hadamard32_quant_run")
+    return Xq, x_scales
+
+
+def moe_workspace_bytes(top_k: int, H: int, F: int) -> int:
+    return raw().qg_moe_workspace_bytes(top_k, H, F)
+
+
+def moe_expert_gemv_run(packed_gate, packed_up, packed_down, E: int, H: int, F: int, x,
+                        expert_ids, expert_w, workspace=None, y=None, out_dtype: int = OUT_BF16,
+                        stream=None):
+    torch = _torch()
+    top_k = int(expert_ids.numel())
+    if workspace is None:
+        workspace = torch.empty(moe_workspace_bytes(top_k, H, F), dtype=torch.uint8,
+                                device=x.device)
+    if y is None:
+        y = torch.empty(H, dtype=_out_torch_dtype(out_dtype), device=x.device)
+    _check(raw().moe_expert_gemv_run(_ptr(packed_gate), _ptr(packed_up), _ptr(packed_down),
+                                     packed_gate.numel(), packed_up.numel(), packed_down.numel(),
+                                     E, H, F, _ptr(x), top_k, _ptr(expert_ids), _ptr(expert_w),
+                                     _ptr(workspace), workspace.numel(), _ptr(y), out_dtype,
+                                     _stream(stream)), "moe_expert_gemv_run")
+    return y

@@ -1,0 +1,179 @@
+// Internal declarations shared by the HIP sources of the qgemv library.
+// gfx950 (CDNA4) only: 64-lane wavefronts, MFMA matrix cores, 160 KB LDS/CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace qg {
+
+// ---------------------------------------------------------------- packed layout
+//
+// Every packed format is a sequence of "tiles".  A tile covers 16 consecutive
+// output rows (a rowblock) and a run of consecutive k; tiles are stored
+// rowblock-major, so one rowblock's tiles are contiguous.  Inside a tile the
+// first 1 KB (or 2 KB) holds the codes in the order a 64-lane wavefront reads
+// them with one 128-bit load per lane: lane l serves row n = 16*rb + (l & 15)
+// and k-slice kg = l >> 4.  This is also the operand layout of the
+// 16x16x32 MFMA instructions (lane l holds 8 consecutive k of column l & 15,
+// k-slice l >> 4), so one packed buffer feeds both the M = 1 VALU kernels and
+// the M <= 32 MFMA kernels.  The scales follow the codes inside the tile.
+//
+// Q4 asymmetric group-64, tile = 128 k (2 groups), 1152 B:
+//   [0, 1024)     lane l: 4 words; word 2t+h = group t of the tile, elements
+//                 32h + 8kg .. +8.  Within a word element 2j sits in bits
+//                 [4j, 4j+4) and element 2j+1 in bits [16+4j, 20+4j), so
+//                 (w >> 4j) & 0x000F000F yields the pair (2j, 2j+1) as the
+//                 two 16-bit halves of a register.
+//   [1024, 1152)  16 rows x 2 groups x {fp16 scale, fp16 bias}: row r at
+//                 1024 + 8r: (s0, b0, s1, b1).
+// Q8 symmetric group-32, tile = 128 k (4 groups), 2176 B:
+//   [0, 2048)     half j (1 KB each): lane l: 16 bytes = groups 2j, 2j+1 of
+//                 the tile, 8 consecutive int8 each (k = 32g + 8kg .. +8).
+//   [2048, 2176)  16 rows x 4 groups fp16 scales: row r at 2048 + 8r.
+// MXFP4 group-32, tile = 256 k (8 blocks), 2176 B:
+//   [0, 2048)     half j (1 KB each): lane l: 16 bytes = 32 E2M1 codes of
+//                 block 4j + kg (k = 128j + 32kg .. +32), element 2i in the
+//                 low nibble of byte i.
+//   [2048, 2176)  E8M0 scale bytes: half j at 2048 + 64j + l.
+// Rows past N and k past K are zero-filled (zero codes and zero scales).
+
+constexpr int RB = 16;              // rows per rowblock
+constexpr int Q4_TILE_K = 128;
+constexpr int Q4_TILE_BYTES = 1152;
+constexpr int Q8_TILE_K = 128;
+constexpr int Q8_TILE_BYTES = 2176;
+constexpr int FP4_TILE_K = 256;
+constexpr int FP4_TILE_BYTES = 2176;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Arguments are validated by
+// the C ABI layer before these are called.
+hipError_t launch_pack_q4(const uint32_t *codes, const uint16_t *scales,
+                          const uint16_t *biases, int64_t N, int64_t K,
+                          uint8_t *packed, hipStream_t s);
+hipError_t launch_pack_q8(const int8_t *codes, const uint16_t *scales,
+                          int64_t N, int64_t K, uint8_t *packed, hipStream_t s);
+hipError_t launch_pack_fp4(const uint8_t *codes, const uint8_t *scales,
+                           int64_t N, int64_t K, uint8_t *packed, hipStream_t s);
+
+hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y,
+                          int64_t N, int64_t K, bool out_f32, int cus,
+                          hipStream_t s);
+hipError_t launch_fp4_gemv(const uint8_t *packed, const uint16_t *x, void *y,
+                           int64_t N, int64_t K, bool out_f32, int cus,
+                           hipStream_t s);
+hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y,
+                            int64_t M, int64_t N, int64_t K, bool out_f32,
+                            int cus, hipStream_t s);
+hipError_t launch_q8_skinny(const uint8_t *packed, const int8_t *X,
+                            const float *x_scales, void *Y, int64_t M,
+                            int64_t N, int64_t K, int out_mode, int cus,
+                            hipStream_t s);
+hipError_t launch_had32_quant(const uint16_t *X, const int8_t *signs,
+                              int64_t M, int64_t K, int8_t *Xq,
+                              float *x_scales, double denom,
+                              hipStream_t s);
+hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd,
+                      int64_t E, int64_t H, int64_t F, const uint16_t *x,
+                      int top_k, const int32_t *ids, const float *w,
+                      uint8_t *workspace, void *y, bool out_f32, int cus,
+                      hipStream_t s);
+
+size_t q4_packed_bytes(int64_t N, int64_t K);
+size_t q8_packed_bytes(int64_t N, int64_t K);
+size_t fp4_packed_bytes(int64_t N, int64_t K);
+
+}  // namespace qg
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIPCC__)
+namespace qg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    unsigned u = __builtin_bit_cast(unsigned, f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu))
+        return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned w) {
+    return __builtin_bit_cast(float, w << 16);
+}
+__device__ __forceinline__ float bf16_hi(unsigned w) {
+    return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float f16_lo(unsigned w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(unsigned w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Two 4-bit codes (w >> 4j) & 0xF and (w >> 16+4j) & 0xF as the bf16 pair
+// (128 + q0, 128 + q1): 0x4300 is bf16 128.0, whose 7 mantissa bits have
+// weight 1, so OR-ing a code 0..15 into them gives 128 + code exactly.
+template <int J>
+__device__ __forceinline__ unsigned q4_pair_bias128(unsigned w) {
+    return ((w >> (4 * J)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// fp32 accumulate += (a.lo * b.lo + a.hi * b.hi) for bf16 pairs (single
+// rounding; v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+// Eight 4-bit codes of a packed Q4 word as the bf16x8 MFMA operand
+// (128 + q_0, ..., 128 + q_7).
+__device__ __forceinline__ bf16x8_t q4_word_to_bf16x8(unsigned w) {
+    u32x4_t v;
+    v[0] = q4_pair_bias128<0>(w);
+    v[1] = q4_pair_bias128<1>(w);
+    v[2] = q4_pair_bias128<2>(w);
+    v[3] = q4_pair_bias128<3>(w);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// E8M0 byte e -> the fp32 whose exponent field is e (2^(e-127) for
+// 1 <= e <= 254); the gfx950 scaled FP4 converts use only the exponent of
+// their fp32 scale operand.
+__device__ __forceinline__ float e8m0_as_f32(unsigned e) {
+    return __builtin_bit_cast(float, (e & 0xFFu) << 23);
+}
+
+// Two E2M1 codes of byte SEL of w, times the scale, as a bf16 pair (exact for
+// the E8M0 range used here).
+template <int SEL>
+__device__ __forceinline__ unsigned fp4_pair_bf16(unsigned w, float scale) {
+    return __builtin_bit_cast(
+        unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4_pair_f32(unsigned w, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T *p) {
+    return __builtin_nontemporal_load(p);
+}
+
+}  // namespace qg
+#endif

@@ -1,0 +1,174 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load, export every function include/qgemv.h declares, and
+reject invalid calls with the documented status before any HIP call (every
+call below fails validation, or is an empty problem that enqueues nothing,
+so no pointer is ever dereferenced).
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+import quantized_weight_decode_dequant_amd as pkg
+from quantized_weight_decode_dequant_amd import _lib as L
+
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+A = 0x10000  # an aligned fake device address: only used in calls that fail validation
+SZ = C.c_size_t
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*([A-Za-z_]\w*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = pkg.raw()
+    declared = declared_functions()
+    assert set(declared) == set(L.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.qg_version() >= 100
+
+
+def test_status_strings():
+    for st in range(0, -8, -1):
+        s = pkg.status_string(st)
+        assert s.startswith("QG_")
+    assert pkg.status_string(-99) == "unknown qg_status"
+
+
+def size_query(fmt, rows, K):
+    n = SZ(123)
+    st = pkg.raw().qgemv_pack(fmt, rows, K, None, None, None, None, C.byref(n), None)
+    return st, n.value
+
+
+def test_pack_size_query():
+    assert size_query(L.FMT_Q4_ASYM_G64, 16, 128) == (0, 1152)
+    assert size_query(L.FMT_Q4_ASYM_G64, 17, 128) == (0, 2304)
+    assert size_query(L.FMT_Q4_ASYM_G64, 16, 192) == (0, 2304)
+    assert size_query(L.FMT_Q4_ASYM_G64, 4096, 4096) == (0, 4096 * 4096 * 9 // 16)
+    assert size_query(L.FMT_Q8_SYM_G32, 16, 128) == (0, 2176)
+    assert size_query(L.FMT_Q8_SYM_G32, 16, 32) == (0, 2176)
+    assert size_query(L.FMT_MXFP4_G32, 16, 256) == (0, 2176)
+    assert size_query(L.FMT_MXFP4_G32, 2048, 7168) == (0, 2048 * 7168 * 17 // 32)
+    assert size_query(L.FMT_Q4_ASYM_G64, 0, 64) == (0, 0)
+    assert size_query(L.FMT_Q4_ASYM_G64, 16, 96)[0] == L.QG_ESHAPE
+    assert size_query(L.FMT_Q8_SYM_G32, 16, 48)[0] == L.QG_ESHAPE
+    assert size_query(L.FMT_Q4_ASYM_G64, 16, 0)[0] == L.QG_ESHAPE
+    assert size_query(L.FMT_Q4_ASYM_G64, -1, 64)[0] == L.QG_ESHAPE
+    assert size_query(7, 16, 64)[0] == L.QG_EINVAL
+    assert pkg.raw().qgemv_pack(1, 16, 64, None, None, None, None, None, None) == L.QG_EINVAL
+
+
+def test_pack_argument_errors():
+    lib = pkg.raw()
+    n = SZ(1 << 20)
+    # Q4 needs biases, Q8 must not have them
+    assert lib.qgemv_pack(1, 16, 64, A, A, None, A, C.byref(n), None) == L.QG_EINVAL
+    assert lib.qgemv_pack(2, 16, 64, A, A, A, A, C.byref(n), None) == L.QG_EINVAL
+    assert lib.qgemv_pack(1, 16, 64, None, A, A, A, C.byref(n), None) == L.QG_EINVAL
+    small = SZ(100)
+    assert lib.qgemv_pack(1, 16, 64, A, A, A, A, C.byref(small), None) == L.QG_ESIZE
+    assert small.value == 1152
+    assert lib.qgemv_pack(1, 16, 64, A, A, A, A + 8, C.byref(n), None) == L.QG_EALIGN
+    assert lib.qgemv_pack(1, 16, 64, A + 4, A, A, A, C.byref(n), None) == L.QG_EALIGN
+    # empty problem: nothing to do
+    z = SZ(0)
+    assert lib.qgemv_pack(1, 0, 64, A, A, A, A, C.byref(z), None) == L.QG_OK
+
+
+def test_gemv_validation():
+    lib = pkg.raw()
+    q4 = L.FMT_Q4_ASYM_G64
+    nb = 1152 * 2  # N = 32, K = 128
+    assert lib.qgemv_run(q4, A, nb, 32, 128, A, A, 7, None) == L.QG_EINVAL
+    assert lib.qgemv_run(9, A, nb, 32, 128, A, A, 0, None) == L.QG_EINVAL
+    assert lib.qgemv_run(L.FMT_Q8_SYM_G32, A, nb, 32, 128, A, A, 0, None) == L.QG_EUNSUPPORTED
+    assert lib.qgemv_run(q4, A, nb, 32, 128, A, A, L.OUT_I32_GROUPS, None) == L.QG_EUNSUPPORTED
+    assert lib.qgemv_run(q4, A, nb, 32, 100, A, A, 0, None) == L.QG_ESHAPE
+    assert lib.qgemv_run(q4, A, nb + 1, 32, 128, A, A, 0, None) == L.QG_ESIZE
+    assert lib.qgemv_run(q4, None, nb, 32, 128, A, A, 0, None) == L.QG_EINVAL
+    assert lib.qgemv_run(q4, A, nb, 32, 128, None, A, 0, None) == L.QG_EINVAL
+    assert lib.qgemv_run(q4, A + 2, nb, 32, 128, A, A, 0, None) == L.QG_EALIGN
+    assert lib.qgemv_run(q4, A, nb, 32, 128, A + 8, A, 0, None) == L.QG_EALIGN
+    assert lib.qgemv_run(q4, A, nb, 32, 128, A, A + 1, 0, None) == L.QG_EALIGN
+    assert lib.qgemv_run(q4, A, nb, 32, 128, A, A + 2, L.OUT_F32, None) == L.QG_EALIGN
+    kbig = 24576 + 64
+    assert lib.qgemv_run(q4, A, pkg.packed_bytes(q4, 32, kbig), 32, kbig, A, A, 0, None) == L.QG_ESHAPE
+    # N = 0 is an empty problem: OK, nothing enqueued
+    assert lib.qgemv_run(q4, A, 0, 0, 128, A, A, 0, None) == L.QG_OK
+
+
+def test_skinny_validation():
+    lib = pkg.raw()
+    q4, q8 = L.FMT_Q4_ASYM_G64, L.FMT_Q8_SYM_G32
+    nb4 = pkg.packed_bytes(q4, 32, 128)
+    nb8 = pkg.packed_bytes(q8, 32, 128)
+    assert lib.qgemm_skinny_run(q4, A, nb4, 33, 32, 128, A, None, A, 0, None) == L.QG_ESHAPE
+    assert lib.qgemm_skinny_run(q4, A, nb4, -1, 32, 128, A, None, A, 0, None) == L.QG_ESHAPE
+    assert lib.qgemm_skinny_run(L.FMT_MXFP4_G32, A, nb4, 4, 32, 128, A, None, A, 0, None) == L.QG_EUNSUPPORTED
+    assert lib.qgemm_skinny_run(q4, A, nb4, 4, 32, 128, A, None, A, L.OUT_I32_GROUPS, None) == L.QG_EUNSUPPORTED
+    assert lib.qgemm_skinny_run(q4, A, nb4, 4, 32, 128, A, A, A, 0, None) == L.QG_EINVAL
+    assert lib.qgemm_skinny_run(q8, A, nb8, 4, 32, 128, A, None, A, 0, None) == L.QG_EINVAL
+    assert lib.qgemm_skinny_run(q8, A, nb8 - 16, 4, 32, 128, A, A, A, 0, None) == L.QG_ESIZE
+    assert lib.qgemm_skinny_run(q8, A, nb8, 4, 32, 128, A + 4, A, A, 0, None) == L.QG_EALIGN
+    assert lib.qgemm_skinny_run(q8, A, nb8, 4, 32, 128, A, A + 2, A, 0, None) == L.QG_EALIGN
+    assert lib.qgemm_skinny_run(q8, A, nb8, 4, 32, 128, A, A, A + 2, L.OUT_I32_GROUPS, None) == L.QG_EALIGN
+    assert lib.qgemm_skinny_run(q8, A, nb8, 0, 32, 128, A, A, A, 0, None) == L.QG_OK
+
+
+def test_hadamard_validation():
+    lib = pkg.raw()
+    assert lib.hadamard32_quant_run(A, A, 4, 48, A, A, None) == L.QG_ESHAPE
+    assert lib.hadamard32_quant_run(A, A, 4, 0, A, A, None) == L.QG_ESHAPE
+    assert lib.hadamard32_quant_run(None, A, 4, 64, A, A, None) == L.QG_EINVAL
+    assert lib.hadamard32_quant_run(A, None, 4, 64, A, A, None) == L.QG_EINVAL
+    assert lib.hadamard32_quant_run(A + 2, A, 4, 64, A, A, None) == L.QG_EALIGN
+    assert lib.hadamard32_quant_run(A, A, 4, 64, A + 1, A, None) == L.QG_EALIGN
+    assert lib.hadamard32_quant_run(A, A, 0, 64, A, A, None) == L.QG_OK
+
+
+def test_moe_validation():
+    lib = pkg.raw()
+    E, H, F, k = 8, 256, 512, 2
+    bg = pkg.packed_bytes(L.FMT_MXFP4_G32, E * F, H)
+    bd = pkg.packed_bytes(L.FMT_MXFP4_G32, E * H, F)
+    ws = pkg.moe_workspace_bytes(k, H, F)
+    assert ws == 4 * k * (H + F) + 16
+
+    def call(**kw):
+        a = dict(g=A, u=A, d=A, bg=bg, bu=bg, bd=bd, E=E, H=H, F=F, x=A, k=k, ids=A, w=A, ws=A,
+                 wsb=ws, y=A, out=0)
+        a.update(kw)
+        return lib.moe_expert_gemv_run(a["g"], a["u"], a["d"], a["bg"], a["bu"], a["bd"], a["E"],
+                                       a["H"], a["F"], a["x"], a["k"], a["ids"], a["w"], a["ws"],
+                                       a["wsb"], a["y"], a["out"], None)
+
+    assert call(out=5) == L.QG_EINVAL
+    assert call(out=L.OUT_I32_GROUPS) == L.QG_EUNSUPPORTED
+    assert call(k=E + 1) == L.QG_ESHAPE
+    assert call(k=65) == L.QG_ESHAPE
+    assert call(H=250) == L.QG_ESHAPE
+    assert call(F=12288 + 32) == L.QG_ESHAPE
+    assert call(E=0) == L.QG_ESHAPE
+    assert call(g=None) == L.QG_EINVAL
+    assert call(ids=None) == L.QG_EINVAL
+    assert call(bd=bd + 16) == L.QG_ESIZE
+    assert call(bg=bg - 16) == L.QG_ESIZE
+    assert call(wsb=ws - 1) == L.QG_ESIZE
+    assert call(ws=A + 8) == L.QG_EALIGN
+    assert call(ids=A + 2) == L.QG_EALIGN
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        pkg.qgemv_run(L.FMT_Q4_ASYM_G64, torch.zeros(1152, dtype=torch.uint8), 16, 128,
+                      torch.zeros(128, dtype=torch.bfloat16), y=torch.zeros(16))

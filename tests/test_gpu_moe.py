@@ -1,0 +1,162 @@
+"""GPU parity: MXFP4 decode GEMV and the routed-expert MoE layer for one
+token (gather by device-resident router ids, gate/up, SwiGLU, down, weighted
+combine), against the CPU oracle."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_weight_decode_dequant_amd as pkg
+from quantized_weight_decode_dequant_amd import synth, weights
+from helpers import assert_bf16_close, assert_f32_close, note, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FP4 = pkg.FMT_MXFP4_G32
+
+
+def gemv_fp4(m, x, out_dtype):
+    N, K = m.codes.shape[0], m.codes.shape[1] * 2
+    packed = weights.pack_mxfp4(m.codes, m.scales, DEV)
+    y = pkg.qgemv_run(FP4, packed, N, K, weights.to_device(x, DEV), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_np(y)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (40, 288), (100, 7168), (64, 2048), (17, 24576)])
+def test_mxfp4_gemv(N, K):
+    note("mxfp4 gemv N=%d K=%d" % (N, K))
+    m = synth.mxfp4_matrix(60, N, K)
+    x = synth.moe_token(61, K)
+    ref = oracle.mxfp4_gemv(m.codes, m.scales, x)
+    assert_f32_close(gemv_fp4(m, x, pkg.OUT_F32), ref, what="f32")
+    assert_bf16_close(gemv_fp4(m, x, pkg.OUT_BF16), ref, what="bf16")
+
+
+def test_mxfp4_gemv_onehot_is_exact():
+    """E2M1 * 2^(e-127) * 1.0 is exact in fp32, so a one-hot x returns the
+    dequantized column bit-exactly."""
+    m = synth.mxfp4_matrix(62, 48, 512)
+    for k in (0, 1, 255, 256, 511):
+        x = synth.f32_to_bf16_bits(np.eye(1, 512, k, dtype=np.float32)[0])
+        assert np.array_equal(gemv_fp4(m, x, pkg.OUT_F32), oracle.mxfp4_gemv(m.codes, m.scales, x))
+
+
+def _pool(seed, E, H, F):
+    ex = [synth.expert(seed, e, H, F) for e in range(E)]
+    st = lambda f: np.stack([f(e) for e in ex])  # noqa: E731
+    return (st(lambda e: e.gate.codes), st(lambda e: e.gate.scales), st(lambda e: e.up.codes),
+            st(lambda e: e.up.scales), st(lambda e: e.down.codes), st(lambda e: e.down.scales))
+
+
+def _pack_pool(pool, E, H, F):
+    gc, gs, uc, us, dc, ds = pool
+    pg = weights.pack_mxfp4(gc.reshape(E * F, H // 2), gs.reshape(E * F, H // 32), DEV)
+    pu = weights.pack_mxfp4(uc.reshape(E * F, H // 2), us.reshape(E * F, H // 32), DEV)
+    pd = weights.pack_mxfp4(dc.reshape(E * H, F // 2), ds.reshape(E * H, F // 32), DEV)
+    return pg, pu, pd
+
+
+def run_moe(packed, E, H, F, x, ids, w, out_dtype, workspace=None):
+    pg, pu, pd = packed
+    y = pkg.moe_expert_gemv_run(pg, pu, pd, E, H, F, weights.to_device(x, DEV),
+                                weights.to_device(ids, DEV), weights.to_device(w, DEV),
+                                workspace=workspace, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_np(y)
+
+
+@pytest.mark.parametrize("E,H,F,top_k", [(6, 256, 512, 3), (4, 96, 160, 4), (9, 1024, 256, 1)])
+def test_moe_small(E, H, F, top_k):
+    note("moe E=%d H=%d F=%d top_k=%d" % (E, H, F, top_k))
+    pool = _pool(70, E, H, F)
+    x = synth.moe_token(71, H)
+    ids, w = synth.router(72, E, top_k)
+    ref = oracle.moe(*pool, x, ids, w)
+    packed = _pack_pool(pool, E, H, F)
+    assert_f32_close(run_moe(packed, E, H, F, x, ids, w, pkg.OUT_F32), ref, what="f32")
+    assert_bf16_close(run_moe(packed, E, H, F, x, ids, w, pkg.OUT_BF16), ref, what="bf16")
+
+
+def test_moe_invalid_id_and_empty():
+    E, H, F = 5, 128, 96
+    pool = _pool(73, E, H, F)
+    packed = _pack_pool(pool, E, H, F)
+    x = synth.moe_token(74, H)
+    ids = np.array([2, 7, 0], dtype=np.int32)  # 7 is out of range: contributes nothing
+    w = np.array([0.5, 0.3, 0.2], dtype=np.float32)
+    ws = torch.empty(pkg.moe_workspace_bytes(3, H, F), dtype=torch.uint8, device=DEV)
+    got = run_moe(packed, E, H, F, x, ids, w, pkg.OUT_F32, workspace=ws)
+    status_off = 4 * 3 * (H + F)
+    assert int(ws[status_off:status_off + 4].view(torch.int32).item()) == 1
+    ref = oracle.moe(*pool, x, ids, w)
+    assert_f32_close(got, ref, what="invalid id")
+    # a valid call rewrites the status word to 0
+    run_moe(packed, E, H, F, x, ids[[0, 2]], w[[0, 2]], pkg.OUT_F32,
+            workspace=ws[:pkg.moe_workspace_bytes(2, H, F)])
+    status_off2 = 4 * 2 * (H + F)
+    assert int(ws[status_off2:status_off2 + 4].view(torch.int32).item()) == 0
+    # top_k = 0: y = 0
+    y0 = run_moe(packed, E, H, F, x, np.zeros(0, np.int32), np.zeros(0, np.float32), pkg.OUT_F32)
+    assert not np.any(y0)
+
+
+def test_moe_permutation_invariance():
+    E, H, F = 8, 256, 256
+    pool = _pool(75, E, H, F)
+    packed = _pack_pool(pool, E, H, F)
+    x = synth.moe_token(76, H)
+    ids, w = synth.router(77, E, 4)
+    p = np.array([3, 1, 0, 2])
+    a = run_moe(packed, E, H, F, x, ids, w, pkg.OUT_F32)
+    b = run_moe(packed, E, H, F, x, ids[p], w[p], pkg.OUT_F32)
+    ref = oracle.moe(*pool, x, ids, w)
+    assert_f32_close(a, ref)
+    assert_f32_close(b, ref)
+
+
+def test_moe_routed_expert_workload_full():
+    """The MoE workload at full size: 384 experts, hidden 7168, expert FFN
+    2048, top-16 by a seeded router.  The 16 selected experts hold the seeded
+    synthetic weights; every other expert of the 384 is filled with random
+    bytes (random codes and scale bytes, NaN scales included), so reading a
+    wrong expert changes the result."""
+    E, H, F, top_k = 384, 7168, 2048, 16
+    note("moe full E=%d H=%d F=%d top_k=%d" % (E, H, F, top_k))
+    ids, w = synth.router(80, E, top_k)
+    x = synth.moe_token(81, H)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(82)
+    bg = pkg.packed_bytes(FP4, E * F, H)
+    bd = pkg.packed_bytes(FP4, E * H, F)
+    pg = torch.randint(0, 256, (bg,), dtype=torch.uint8, device=DEV, generator=g)
+    pu = torch.randint(0, 256, (bg,), dtype=torch.uint8, device=DEV, generator=g)
+    pd = torch.randint(0, 256, (bd,), dtype=torch.uint8, device=DEV, generator=g)
+    eg, ed = bg // E, bd // E
+    sel = []
+    for e in ids.tolist():
+        ex = synth.expert(83, e, H, F)
+        pkg.qgemv_pack(FP4, F, H, weights.to_device(ex.gate.codes, DEV),
+                       weights.to_device(ex.gate.scales, DEV), out=pg[e * eg:(e + 1) * eg])
+        pkg.qgemv_pack(FP4, F, H, weights.to_device(ex.up.codes, DEV),
+                       weights.to_device(ex.up.scales, DEV), out=pu[e * eg:(e + 1) * eg])
+        pkg.qgemv_pack(FP4, H, F, weights.to_device(ex.down.codes, DEV),
+                       weights.to_device(ex.down.scales, DEV), out=pd[e * ed:(e + 1) * ed])
+        sel.append(ex)
+    got = run_moe((pg, pu, pd), E, H, F, x, ids, w, pkg.OUT_BF16)
+    note("  gpu done; oracle over the 16 selected experts")
+
+    def one(s):
+        ex = sel[s]
+        pool = tuple(a[None] for a in (ex.gate.codes, ex.gate.scales, ex.up.codes, ex.up.scales,
+                                       ex.down.codes, ex.down.scales))
+        return oracle.moe(*pool, x, np.array([0], np.int32), w[s:s + 1])
+
+    with ThreadPoolExecutor(max_workers=16) as pool:
+        parts = list(pool.map(one, range(top_k)))
+    ref = np.zeros(H)
+    for p in parts:  # slot order, as the definition sums
+        ref += p
+    assert_bf16_close(got, ref, what="moe full")
