@@ -1,0 +1,228 @@
+"""Benchmark: the synthetic dense decode step on one MI355X.
+
+A step is one decode token's worth of weight-quantized GEMVs: 36 layers x
+(q, k, v, o, gate, up, down) + lm_head, 4-bit asymmetric group-64 weights
+(4.257 GB packed), bf16 activations, M = 1.  Inputs are resident in HBM
+before timing starts.  Reported:
+  value          whole-step algorithmic bytes / step time (GB/s)
+  tok_per_s      equivalent decode tokens per second (1 / step time)
+  m16            the same weights in one verification pass with a 16-row
+                 activation tile per projection (skinny M = 16)
+  roofline       the GEMV kernel: algorithmic bytes per launch / mean launch
+                 duration (HIP events on the launch stream) vs 8 TB/s
+  cpu_baseline   the CPU oracle on a bounded sample of the same step
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("qgemv achieved HBM GB/s (% of MI355X peak) + equiv. decode tok/s, M=1 and M=16")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_weight_decode_dequant_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % kernel)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(step, budget_s: float):
+    """The oracle, as it stands, on the first GEMVs of the step until the time
+    budget is spent (one thread; input generation is not timed)."""
+    import oracle
+    from quantized_weight_decode_dequant_amd import roofline, synth
+    done_bytes, names, elapsed = 0.0, [], 0.0
+    for item, name, N, K in synth.decode_step_shapes():
+        m = synth.q4_matrix(step.seed, N, K, item=item)
+        x = synth.activations(step.seed, 1, K, item=item)
+        t = time.perf_counter()
+        oracle.q4_gemm(m.codes, m.scales, m.biases, x)
+        elapsed += time.perf_counter() - t
+        done_bytes += roofline.q4_gemm_bytes(1, N, K)
+        names.append(name)
+        if elapsed >= budget_s:
+            break
+    gbs = done_bytes / elapsed / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "tok_per_s": round(gbs * 1e9 / step.algorithmic_bytes(1), 6),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "first %d GEMVs of the decode step (%s .. %s), %.3f GB algorithmic, %.1f s" % (
+            len(names), names[0], names[-1], done_bytes / 1e9, elapsed),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-m16", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_weight_decode_dequant_amd as pkg
+    from quantized_weight_decode_dequant_amd import roofline, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkg.raw()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log("device:", props.name, getattr(props, "gcnArchName", ""))
+
+    t = time.time()
+    step = workloads.build_decode_step(args.seed, skinny_m=0 if args.no_m16 else 16, log=log)
+    log("workload ready in %.1f s: %d GEMVs, %.3f GB packed" % (
+        time.time() - t, len(step.gemvs), step.weight_bytes / 1e9))
+    step_bytes = step.algorithmic_bytes(1)
+
+    # ---- decode step, M = 1: every GEMV of the step in one grouped launch
+    Q4 = pkg.FMT_Q4_ASYM_G64
+    plan = pkg.qg_batch_plan_build(Q4, 1, [(g.packed, g.N, g.K, g.x, g.y) for g in step.gemvs])
+    torch.cuda.synchronize()
+    log("plan: grid %d workgroups" % plan.grid)
+    for _ in range(args.warmup):
+        pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        pkg.qg_batch_run(plan)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log("step: %.3f ms (wall %.3f ms)" % (ms_step, wall * 1e3 / args.steps))
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    # one launch per step: the kernel's mean launch duration is the step time
+    achieved = gbs
+    traffic = traffic_from_profiles("q4_gemv_step")
+
+    # ---- for comparison: the same step as one qgemv_run launch per GEMV (HIP graph)
+    graph = workloads.capture_graph(lambda: workloads.run_step_eager(step))
+    graph.replay()
+    torch.cuda.synchronize()
+    n_cmp = max(3, args.steps // 5)
+    e0.record()
+    for _ in range(n_cmp):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_launch_graph = e0.elapsed_time(e1) / n_cmp
+    log("step as %d launches in a graph: %.3f ms" % (len(step.gemvs), ms_per_launch_graph))
+    del graph
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "synthetic dense decode step, M=1: 36 layers x (q 4096x4096, k/v 4096x1024, "
+                        "o 4096x4096, gate/up 4096x12288, down 12288x4096) + lm_head 4096x151936, "
+                        "4-bit asymmetric group-64, bf16 activations",
+            "gemvs": len(step.gemvs),
+            "packed_weight_bytes": step.weight_bytes,
+            "algorithmic_bytes_per_step": int(step_bytes),
+            "seed": args.seed,
+            "launch": "one grouped kernel launch per step (qg_batch_run over a device work list "
+                      "of the %d GEMVs)" % len(step.gemvs),
+            "ms_per_step_one_launch_per_gemv": round(ms_per_launch_graph, 4),
+        },
+        "pct_of_peak": round(100 * gbs / roofline.HBM_PEAK_GBS, 2),
+        "tok_per_s": round(1e3 / ms_step, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "q4_gemv_kernel (work-list mode, one launch = one decode step)",
+            "achieved": round(achieved, 2),
+            "peak": roofline.HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / roofline.HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(step_bytes),
+            "mean_launch_ms": round(ms_step, 5),
+        },
+    }
+
+    # ---- verification pass, M = 16, same weights, one grouped launch
+    if not args.no_m16:
+        plan16 = pkg.qg_batch_plan_build(Q4, 16, [(g.packed, g.N, g.K, g.X, g.Y) for g in step.gemvs])
+        for _ in range(max(1, args.warmup)):
+            pkg.qg_batch_run(plan16)
+        torch.cuda.synchronize()
+        n16 = max(5, args.steps // 2)
+        e0.record()
+        for _ in range(n16):
+            pkg.qg_batch_run(plan16)
+        e1.record()
+        torch.cuda.synchronize()
+        ms16 = e0.elapsed_time(e1) / n16
+        b16 = step.algorithmic_bytes(16)
+        result["m16"] = {
+            "ms_per_pass": round(ms16, 4),
+            "value": round(b16 / (ms16 * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "pct_of_peak": round(100 * b16 / (ms16 * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2),
+            "passes_per_s": round(1e3 / ms16, 2),
+            "tflops": round(step.flops(16) / (ms16 * 1e-3) / 1e12, 2),
+            "launch": "one grouped kernel launch per pass (16-row activation tile per projection)",
+        }
+        log("m16 pass: %.3f ms" % ms16)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(step, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -224,6 +224,71 @@ int moe_expert_gemv_run(const void *packed_gate, const void *packed_up,
                         void *workspace, size_t workspace_bytes, void *y,
                         int out_dtype, void *stream);
 
+/*
+ * Grouped launches: many independent products in one kernel launch.
+ *
+ * A decode step runs every projection of the model once per token; issuing
+ * them as one piece of GPU work, rather than one launch each, is what the
+ * "one command buffer per token" design of "MLX Runner: An Inference Engine
+ * You Can Read" (section "Architecture: one command buffer per token") does
+ * on Apple GPUs.  Here the products are described once, on the host, by an
+ * array of qg_gemv_desc; qg_batch_plan_build validates them, balances the
+ * work across the GPU by bytes and writes a work list into caller-owned
+ * device memory; qg_batch_run then enqueues a single persistent kernel that
+ * computes every product of the list.  The products must be independent (no
+ * output of one is an input of another within the list).
+ */
+typedef struct qg_gemv_desc {
+    const void *packed;   /* from qgemv_pack(fmt, N, K); 16-B */
+    size_t packed_bytes;
+    int64_t N, K;
+    const void *x;        /* device bf16 [M][K], 16-B; read only */
+    void *y;              /* device [M][N] of the plan's output type; written */
+} qg_gemv_desc;
+
+/* Launch plan: plain host data, filled by qg_batch_plan_build and consumed
+ * by qg_batch_run.  The fields are not meant to be edited. */
+typedef struct qg_batch_plan {
+    int32_t fmt, M, count, out_dtype;
+    int32_t grid, kmax, reserved0, reserved1;
+    const void *worklist;
+    size_t worklist_bytes;
+} qg_batch_plan;
+
+/* Device bytes of the work list for `count` products (host function). */
+size_t qg_batch_worklist_bytes(int32_t count);
+
+/*
+ * qg_batch_plan_build -- validate `count` product descriptors and write their
+ * work list to `worklist`.
+ *
+ *  fmt          QG_FMT_Q4_ASYM_G64 (other formats -> QG_EUNSUPPORTED).
+ *  M            activation rows of every product: 1 (decode GEMVs, K <= 24576
+ *               each) or 2..32 (a verification pass).
+ *  count        1..65536 descriptors in `descs` (host array, read only; it
+ *               need not outlive the call).
+ *  out_dtype    QG_OUT_BF16 or QG_OUT_F32, for every product.
+ *  worklist     device buffer (16-B) of at least qg_batch_worklist_bytes(count)
+ *               bytes; written asynchronously on `stream`, then read by every
+ *               qg_batch_run of this plan, so it must stay allocated and
+ *               unmodified while the plan is in use.
+ *  plan         host struct receiving the plan.
+ * Errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN, QG_ESIZE (a descriptor's
+ * packed_bytes, or worklist_bytes), QG_EUNSUPPORTED, QG_EHIP.
+ */
+int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *descs,
+                        int out_dtype, void *worklist, size_t worklist_bytes,
+                        qg_batch_plan *plan, void *stream);
+
+/*
+ * qg_batch_run -- enqueue one kernel computing every product of the plan:
+ * Y_i = X_i W_i^T (y_i = W_i x_i for M = 1), with the arithmetic of
+ * qgemv_run (M = 1) or qgemm_skinny_run (M > 1).  The buffers named in the
+ * descriptors must still be valid.  Safe to capture in a HIP graph.
+ * Errors: QG_EINVAL (NULL or malformed plan), QG_EHIP.
+ */
+int qg_batch_run(const qg_batch_plan *plan, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,7 +43,24 @@ EXPORTS = (
     "hadamard32_quant_run",
     "qg_moe_workspace_bytes",
     "moe_expert_gemv_run",
+    "qg_batch_worklist_bytes",
+    "qg_batch_plan_build",
+    "qg_batch_run",
 )
+
+
+class GemvDesc(C.Structure):
+    """struct qg_gemv_desc"""
+    _fields_ = [("packed", C.c_void_p), ("packed_bytes", C.c_size_t), ("N", C.c_int64),
+                ("K", C.c_int64), ("x", C.c_void_p), ("y", C.c_void_p)]
+
+
+class BatchPlan(C.Structure):
+    """struct qg_batch_plan"""
+    _fields_ = [("fmt", C.c_int32), ("M", C.c_int32), ("count", C.c_int32),
+                ("out_dtype", C.c_int32), ("grid", C.c_int32), ("kmax", C.c_int32),
+                ("reserved0", C.c_int32), ("reserved1", C.c_int32), ("worklist", C.c_void_p),
+                ("worklist_bytes", C.c_size_t)]
 
 _lock = threading.Lock()
 _lib = None
@@ -83,6 +100,13 @@ def raw():
             lib.moe_expert_gemv_run.argtypes = [p, p, p, sz, sz, sz, i64, i64, i64, p, i, p, p,
                                                 p, sz, p, i, p]
             lib.moe_expert_gemv_run.restype = i
+            lib.qg_batch_worklist_bytes.argtypes = [C.c_int32]
+            lib.qg_batch_worklist_bytes.restype = sz
+            lib.qg_batch_plan_build.argtypes = [i, i64, C.c_int32, C.POINTER(GemvDesc), i, p, sz,
+                                                C.POINTER(BatchPlan), p]
+            lib.qg_batch_plan_build.restype = i
+            lib.qg_batch_run.argtypes = [C.POINTER(BatchPlan), p]
+            lib.qg_batch_run.restype = i
             _lib = lib
     return _lib
 
@@ -198,3 +222,52 @@ def moe_expert_gemv_run(packed_gate, packed_up, packed_down, E: int, H: int, F: 
                                      _ptr(workspace), workspace.numel(), _ptr(y), out_dtype,
                                      _stream(stream)), "moe_expert_gemv_run")
     return y
+
+
+# ------------------------------------------------------------------ grouped launches
+class Plan:
+    """A built qg_batch_plan plus the device work list and the tensors its
+    descriptors point at (kept alive as long as the plan)."""
+
+    def __init__(self, plan, worklist, keep):
+        self.plan = plan
+        self.worklist = worklist
+        self._keep = keep
+
+    @property
+    def grid(self) -> int:
+        return self.plan.grid
+
+
+def qg_batch_worklist_bytes(count: int) -> int:
+    return raw().qg_batch_worklist_bytes(count)
+
+
+def qg_batch_plan_build(fmt: int, M: int, entries, out_dtype: int = OUT_BF16, worklist=None,
+                        stream=None) -> Plan:
+    """entries: sequence of (packed, N, K, x, y) with device tensors; x is bf16
+    [M, K] ([K] for M = 1), y is [M, N] of the output type."""
+    torch = _torch()
+    entries = list(entries)
+    descs = (GemvDesc * len(entries))()
+    keep = []
+    for d, (packed, N, K, x, y) in zip(descs, entries):
+        d.packed = _ptr(packed)
+        d.packed_bytes = packed.numel()
+        d.N, d.K = N, K
+        d.x = _ptr(x)
+        d.y = _ptr(y)
+        keep.extend((packed, x, y))
+    nbytes = qg_batch_worklist_bytes(len(entries))
+    if worklist is None:
+        dev = entries[0][0].device if entries else None
+        worklist = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    plan = BatchPlan()
+    _check(raw().qg_batch_plan_build(fmt, M, len(entries), descs, out_dtype, _ptr(worklist),
+                                     worklist.numel(), C.byref(plan), _stream(stream)),
+           "qg_batch_plan_build")
+    return Plan(plan, worklist, keep)
+
+
+def qg_batch_run(plan: Plan, stream=None):
+    _check(raw().qg_batch_run(C.byref(plan.plan), _stream(stream)), "qg_batch_run")

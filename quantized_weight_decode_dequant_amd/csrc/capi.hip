@@ -6,6 +6,8 @@
 // output") -- then enqueues its kernels on the caller's stream and returns.
 #include <atomic>
 #include <cmath>
+#include <cstring>
+#include <vector>
 
 #include "../../include/qgemv.h"
 #include "qg_internal.h"
@@ -252,6 +254,145 @@ int moe_expert_gemv_run(const void *packed_gate, const void *packed_up, const vo
                                      expert_w, reinterpret_cast<uint8_t *>(workspace), y,
                                      out_dtype == QG_OUT_F32, cus,
                                      reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return QG_EINTERNAL;
+    }
+}
+
+
+size_t qg_batch_worklist_bytes(int32_t count) {
+    if (count < 0) return 0;
+    return (size_t)WL_HEADER_BYTES + sizeof(WorkItem) * (size_t)count +
+           sizeof(WorkStart) * (size_t)(WL_GRID_MAX + 1);
+}
+
+int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *descs,
+                        int out_dtype, void *worklist, size_t worklist_bytes,
+                        qg_batch_plan *plan, void *stream) {
+    try {
+        if (!descs || !worklist || !plan) return QG_EINVAL;
+        if (out_dtype != QG_OUT_BF16 && out_dtype != QG_OUT_F32) {
+            if (out_dtype == QG_OUT_I32_GROUPS) return QG_EUNSUPPORTED;
+            return QG_EINVAL;
+        }
+        if (format_group(fmt) == 0) return QG_EINVAL;
+        if (fmt != QG_FMT_Q4_ASYM_G64) return QG_EUNSUPPORTED;
+        if (M < 1 || M > M_MAX || count < 1 || count > 65536) return QG_ESHAPE;
+        if (worklist_bytes < qg_batch_worklist_bytes(count)) return QG_ESIZE;
+        if (!aligned(worklist, 16)) return QG_EALIGN;
+        const size_t yal = out_dtype == QG_OUT_F32 ? 4 : 2;
+        int64_t kmax = 0;
+        for (int32_t i = 0; i < count; ++i) {
+            const qg_gemv_desc &d = descs[i];
+            int st = check_matrix(fmt, d.N, d.K);
+            if (st != QG_OK) return st;
+            if (d.N < 1) return QG_ESHAPE;
+            if (M == 1 && d.K > GEMV_K_MAX) return QG_ESHAPE;
+            if (!d.packed || !d.x || !d.y) return QG_EINVAL;
+            if (d.packed_bytes != packed_bytes_for(fmt, d.N, d.K)) return QG_ESIZE;
+            if (!aligned(d.packed, 16) || !aligned(d.x, 16) || !aligned(d.y, yal)) return QG_EALIGN;
+            if (d.K > kmax) kmax = d.K;
+        }
+        int cus = 0;
+        int st = device_cus(&cus);
+        if (st != QG_OK) return st;
+
+        // units and their costs (in 128-k tiles, plus a fixed per-unit overhead
+        // for the reduction and the synchronization around it)
+        const int rpu = (M == 1) ? 1 : (M <= 16 ? SK_ROWBLOCKS_M16 : SK_ROWBLOCKS_M32);
+        std::vector<WorkItem> items((size_t)count);
+        int64_t total_units = 0, total_cost = 0;
+        for (int32_t i = 0; i < count; ++i) {
+            const qg_gemv_desc &d = descs[i];
+            WorkItem &w = items[(size_t)i];
+            w = WorkItem{};
+            w.packed = reinterpret_cast<const uint8_t *>(d.packed);
+            w.x = d.x;
+            w.y = d.y;
+            w.N = (int32_t)d.N;
+            w.K = (int32_t)d.K;
+            w.P = (int32_t)ceil_div(d.K, Q4_TILE_K);
+            w.units = (int32_t)ceil_div(ceil_div(d.N, RB), rpu);
+            w.out_f32 = out_dtype == QG_OUT_F32 ? 1 : 0;
+            total_units += w.units;
+            total_cost += (int64_t)w.units * ((int64_t)w.P * rpu + 2);
+        }
+        int per_cu = 4;
+        if (M == 1) {
+            const size_t lds = q4_gemv_lds_bytes(kmax);
+            per_cu = (int)((160 * 1024) / lds);
+            if (per_cu > 8) per_cu = 8;
+            if (per_cu < 1) per_cu = 1;
+        }
+        int64_t grid = (int64_t)cus * per_cu;
+        if (grid > WL_GRID_MAX) grid = WL_GRID_MAX;
+        if (grid > total_units) grid = total_units;
+
+        // contiguous, cost-balanced ranges: workgroup j starts at the first
+        // unit whose preceding cost reaches j * total / grid
+        std::vector<WorkStart> starts((size_t)grid + 1);
+        {
+            int64_t j = 0, before = 0;
+            for (int32_t i = 0; i < count && j < grid; ++i) {
+                const int64_t c = (int64_t)items[(size_t)i].P * rpu + 2;
+                for (int32_t u = 0; u < items[(size_t)i].units && j < grid; ++u) {
+                    while (j < grid && before >= (j * total_cost) / grid) {
+                        starts[(size_t)j] = WorkStart{i, u};
+                        ++j;
+                    }
+                    before += c;
+                }
+            }
+            for (; j <= grid; ++j) starts[(size_t)j] = WorkStart{count, 0};
+        }
+
+        // header + items + starts, uploaded through kernel arguments
+        std::vector<uint32_t> words(qg_batch_worklist_bytes(count) / 4, 0u);
+        uint32_t *hdr = words.data();
+        hdr[0] = WL_MAGIC;
+        hdr[1] = (uint32_t)count;
+        hdr[2] = (uint32_t)grid;
+        hdr[3] = (uint32_t)M;
+        std::memcpy(words.data() + WL_HEADER_BYTES / 4, items.data(), sizeof(WorkItem) * items.size());
+        const size_t starts_off = (WL_HEADER_BYTES + sizeof(WorkItem) * items.size()) / 4;
+        std::memcpy(words.data() + starts_off, starts.data(), sizeof(WorkStart) * starts.size());
+        const size_t nwords = starts_off + sizeof(WorkStart) * starts.size() / 4;
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        st = hip_status(launch_write_words(words.data(), nwords, reinterpret_cast<uint32_t *>(worklist), s));
+        if (st != QG_OK) return st;
+
+        plan->fmt = fmt;
+        plan->M = (int32_t)M;
+        plan->count = count;
+        plan->out_dtype = out_dtype;
+        plan->grid = (int32_t)grid;
+        plan->kmax = (int32_t)kmax;
+        plan->reserved0 = 0;
+        plan->reserved1 = 0;
+        plan->worklist = worklist;
+        plan->worklist_bytes = worklist_bytes;
+        return QG_OK;
+    } catch (...) {
+        return QG_EINTERNAL;
+    }
+}
+
+int qg_batch_run(const qg_batch_plan *plan, void *stream) {
+    try {
+        if (!plan || !plan->worklist || !aligned(plan->worklist, 16)) return QG_EINVAL;
+        if (plan->fmt != QG_FMT_Q4_ASYM_G64 || plan->M < 1 || plan->M > M_MAX ||
+            plan->count < 1 || plan->count > 65536 || plan->grid < 1 ||
+            plan->grid > WL_GRID_MAX || plan->kmax < 64 ||
+            (plan->M == 1 && plan->kmax > GEMV_K_MAX) ||
+            plan->worklist_bytes < qg_batch_worklist_bytes(plan->count))
+            return QG_EINVAL;
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(plan->worklist);
+        const WorkItem *items = reinterpret_cast<const WorkItem *>(base + WL_HEADER_BYTES);
+        const WorkStart *starts = reinterpret_cast<const WorkStart *>(items + plan->count);
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        if (plan->M == 1)
+            return hip_status(launch_q4_gemv_list(items, starts, plan->grid, plan->kmax, s));
+        return hip_status(launch_q4_skinny_list(items, starts, plan->grid, plan->M, s));
     } catch (...) {
         return QG_EINTERNAL;
     }

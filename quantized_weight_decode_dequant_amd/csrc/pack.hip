@@ -175,3 +175,32 @@ hipError_t launch_pack_fp4(const uint8_t *codes, const uint8_t *scales, int64_t 
 }
 
 }  // namespace qg
+
+namespace qg {
+
+// Device upload through kernel arguments: the words travel inside the kernel
+// argument block, so the host buffer need not outlive the call and no
+// host-side synchronization is needed.
+constexpr int WW_WORDS = 896;
+struct WordChunk {
+    uint32_t n;
+    uint32_t w[WW_WORDS];
+};
+
+__global__ void __launch_bounds__(256) write_words_kernel(WordChunk chunk, uint32_t *__restrict__ dst) {
+    for (uint32_t i = threadIdx.x; i < chunk.n; i += blockDim.x) dst[i] = chunk.w[i];
+}
+
+hipError_t launch_write_words(const uint32_t *src, size_t nwords, uint32_t *dst, hipStream_t s) {
+    for (size_t off = 0; off < nwords; off += WW_WORDS) {
+        WordChunk c;
+        c.n = (uint32_t)((nwords - off) < (size_t)WW_WORDS ? (nwords - off) : (size_t)WW_WORDS);
+        for (uint32_t i = 0; i < c.n; ++i) c.w[i] = src[off + i];
+        hipLaunchKernelGGL(write_words_kernel, dim3(1), dim3(256), 0, s, c, dst + off);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace qg

@@ -49,6 +49,33 @@ constexpr int FP4_TILE_BYTES = 2176;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ---------------------------------------------------------------- work lists
+// One entry per matrix of a grouped launch (device-resident, written by
+// qg_batch_plan_build), or passed by value for a single-matrix launch.
+// `units` is the number of scheduling units of the matrix: rowblocks for the
+// M = 1 kernel, groups of SK_ROWBLOCKS rowblocks for the skinny kernel.
+struct alignas(16) WorkItem {
+    const uint8_t *packed;
+    const void *x;   // bf16 [M][K]
+    void *y;         // [M][N]
+    int32_t N, K;
+    int32_t P;       // 128-k tiles per row
+    int32_t units;
+    int32_t out_f32;
+    int32_t pad;
+};
+static_assert(sizeof(WorkItem) == 48, "work item layout");
+
+// First unit of each workgroup, in (item, unit) order; entry [grid] is the
+// end sentinel.  Workgroup j processes [starts[j], starts[j+1]).
+struct WorkStart {
+    int32_t item, unit;
+};
+
+constexpr int WL_HEADER_BYTES = 64;
+constexpr int WL_GRID_MAX = 4096;
+constexpr uint32_t WL_MAGIC = 0x4C57'4751u;  // "QGWL"
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are validated by
 // the C ABI layer before these are called.
@@ -63,6 +90,16 @@ hipError_t launch_pack_fp4(const uint8_t *codes, const uint8_t *scales,
 hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y,
                           int64_t N, int64_t K, bool out_f32, int cus,
                           hipStream_t s);
+// grouped launches over a device work list
+size_t q4_gemv_lds_bytes(int64_t kmax);
+hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts,
+                               int grid, int64_t kmax, hipStream_t s);
+constexpr int SK_ROWBLOCKS_M16 = 4;   // rowblocks per skinny unit, M <= 16
+constexpr int SK_ROWBLOCKS_M32 = 8;   // rowblocks per skinny unit, M <= 32
+hipError_t launch_q4_skinny_list(const WorkItem *items, const WorkStart *starts,
+                                 int grid, int64_t M, hipStream_t s);
+hipError_t launch_write_words(const uint32_t *src, size_t nwords, uint32_t *dst,
+                              hipStream_t s);
 hipError_t launch_fp4_gemv(const uint8_t *packed, const uint16_t *x, void *y,
                            int64_t N, int64_t K, bool out_f32, int cus,
                            hipStream_t s);
@@ -124,31 +161,12 @@ __device__ __forceinline__ float f16_hi(unsigned w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// Two 4-bit codes (w >> 4j) & 0xF and (w >> 16+4j) & 0xF as the bf16 pair
-// (128 + q0, 128 + q1): 0x4300 is bf16 128.0, whose 7 mantissa bits have
-// weight 1, so OR-ing a code 0..15 into them gives 128 + code exactly.
-template <int J>
-__device__ __forceinline__ unsigned q4_pair_bias128(unsigned w) {
-    return ((w >> (4 * J)) & 0x000F000Fu) | 0x43004300u;
-}
-
 // fp32 accumulate += (a.lo * b.lo + a.hi * b.hi) for bf16 pairs (single
 // rounding; v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c,
                                            false);
-}
-
-// Eight 4-bit codes of a packed Q4 word as the bf16x8 MFMA operand
-// (128 + q_0, ..., 128 + q_7).
-__device__ __forceinline__ bf16x8_t q4_word_to_bf16x8(unsigned w) {
-    u32x4_t v;
-    v[0] = q4_pair_bias128<0>(w);
-    v[1] = q4_pair_bias128<1>(w);
-    v[2] = q4_pair_bias128<2>(w);
-    v[3] = q4_pair_bias128<3>(w);
-    return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // E8M0 byte e -> the fp32 whose exponent field is e (2^(e-127) for
@@ -173,6 +191,39 @@ __device__ __forceinline__ f32x2_t fp4_pair_f32(unsigned w, float scale) {
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T *p) {
     return __builtin_nontemporal_load(p);
+}
+
+// (a & mask) | orv in one v_and_or_b32.  gfx9 VOP3 reads at most one SGPR or
+// literal, so the mask rides in an SGPR and orv must be a VGPR.
+__device__ __forceinline__ unsigned and_or(unsigned a, unsigned mask, unsigned orv) {
+    unsigned d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(orv));
+    return d;
+}
+
+// bf16 128.0 twice, materialized once into a VGPR (opaque to the compiler so it
+// is not re-materialized at every use).
+__device__ __forceinline__ unsigned bf16_magic128x2() {
+    unsigned m;
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+    return m;
+}
+
+// The four bf16 pairs (128 + q_2j, 128 + q_2j+1), j = 0..3, of a packed Q4 word.
+__device__ __forceinline__ void q4_unpack(unsigned w, unsigned magic, unsigned out[4]) {
+    out[0] = and_or(w, 0x000F000Fu, magic);
+    out[1] = and_or(w >> 4, 0x000F000Fu, magic);
+    out[2] = and_or(w >> 8, 0x000F000Fu, magic);
+    out[3] = and_or(w >> 12, 0x000F000Fu, magic);
+}
+
+// Eight 4-bit codes of a packed Q4 word as the bf16x8 MFMA operand
+// (128 + q_0, ..., 128 + q_7).
+__device__ __forceinline__ bf16x8_t q4_word_to_bf16x8(unsigned w, unsigned magic) {
+    unsigned o[4];
+    q4_unpack(w, magic, o);
+    u32x4_t v = {o[0], o[1], o[2], o[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
 }
 
 }  // namespace qg

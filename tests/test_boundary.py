@@ -172,3 +172,62 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         pkg.qgemv_run(L.FMT_Q4_ASYM_G64, torch.zeros(1152, dtype=torch.uint8), 16, 128,
                       torch.zeros(128, dtype=torch.bfloat16), y=torch.zeros(16))
+
+
+def test_batch_validation():
+    """Every call fails validation before touching the device (no plan here is
+    ever well-formed enough to launch)."""
+    lib = pkg.raw()
+    q4 = L.FMT_Q4_ASYM_G64
+    n = 3
+    wl = pkg.qg_batch_worklist_bytes(n)
+    assert wl == 64 + 48 * n + 8 * 4097
+    good = dict(packed=A, packed_bytes=pkg.packed_bytes(q4, 64, 256), N=64, K=256, x=A, y=A)
+
+    def descs(**over):
+        arr = (L.GemvDesc * n)()
+        for i in range(n):
+            d = dict(good)
+            if i == 1:
+                d.update(over)
+            for k, v in d.items():
+                setattr(arr[i], k, v)
+        return arr
+
+    plan = L.BatchPlan()
+
+    def build(fmt=q4, M=1, count=n, arr=None, out=0, wl_ptr=A, wl_bytes=wl, plan_ptr=True):
+        arr = descs() if arr is None else arr
+        return lib.qg_batch_plan_build(fmt, M, count, arr, out, wl_ptr, wl_bytes,
+                                       C.byref(plan) if plan_ptr else None, None)
+
+    assert build(plan_ptr=False) == L.QG_EINVAL
+    assert build(wl_ptr=None) == L.QG_EINVAL
+    assert build(out=5) == L.QG_EINVAL
+    assert build(out=L.OUT_I32_GROUPS) == L.QG_EUNSUPPORTED
+    assert build(fmt=9) == L.QG_EINVAL
+    assert build(fmt=L.FMT_Q8_SYM_G32) == L.QG_EUNSUPPORTED
+    assert build(M=0) == L.QG_ESHAPE
+    assert build(M=33) == L.QG_ESHAPE
+    assert build(count=0) == L.QG_ESHAPE
+    assert build(wl_bytes=wl - 1) == L.QG_ESIZE
+    assert build(wl_ptr=A + 4) == L.QG_EALIGN
+    assert build(arr=descs(K=100)) == L.QG_ESHAPE
+    assert build(arr=descs(N=0, packed_bytes=0)) == L.QG_ESHAPE
+    assert build(arr=descs(K=24576 + 64, packed_bytes=pkg.packed_bytes(q4, 64, 24576 + 64))) == L.QG_ESHAPE
+    assert build(arr=descs(packed_bytes=123)) == L.QG_ESIZE
+    assert build(arr=descs(x=None)) == L.QG_EINVAL
+    assert build(arr=descs(x=A + 2)) == L.QG_EALIGN
+    assert build(arr=descs(y=A + 1)) == L.QG_EALIGN
+    assert build(arr=descs(y=A + 2), out=L.OUT_F32) == L.QG_EALIGN
+    # malformed plans are refused before any launch
+    assert lib.qg_batch_run(None, None) == L.QG_EINVAL
+    bad = L.BatchPlan()
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL
+    bad.fmt, bad.M, bad.count, bad.grid, bad.kmax = q4, 1, 3, 0, 256
+    bad.worklist, bad.worklist_bytes = A, wl
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # grid 0
+    bad.grid = 5000
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # grid > max
+    bad.grid, bad.worklist_bytes = 4, wl - 8
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # work list too small

@@ -1,0 +1,120 @@
+"""GPU parity of the grouped launch (qg_batch_plan_build + qg_batch_run):
+many independent 4-bit GEMVs / skinny products in one kernel, against the
+oracle, bitwise against the single-matrix entry points (same arithmetic in
+the same order), and under HIP-graph replay."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_weight_decode_dequant_amd as pkg
+from quantized_weight_decode_dequant_amd import synth, weights, workloads
+from helpers import assert_bf16_close, assert_f32_close, note, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+Q4 = pkg.FMT_Q4_ASYM_G64
+
+SHAPES = [(40, 192), (1, 64), (256, 4096), (33, 12288), (100, 1216), (1024, 4096), (17, 320)]
+
+
+def _mats(seed, shapes):
+    return [synth.q4_matrix(seed, N, K, item=i) for i, (N, K) in enumerate(shapes)]
+
+
+@pytest.mark.parametrize("out_dtype", [pkg.OUT_F32, pkg.OUT_BF16])
+def test_batch_m1_mixed_shapes(out_dtype):
+    note("batch M=1 mixed shapes out=%d" % out_dtype)
+    mats = _mats(90, SHAPES)
+    xs = [synth.activations(91, 1, m.K, item=i) for i, m in enumerate(mats)]
+    dt = torch.float32 if out_dtype == pkg.OUT_F32 else torch.bfloat16
+    entries, singles = [], []
+    for m, x in zip(mats, xs):
+        p = weights.pack_q4(m, DEV)
+        xd = weights.to_device(x[0], DEV)
+        y = torch.empty(m.N, dtype=dt, device=DEV)
+        entries.append((p, m.N, m.K, xd, y))
+        singles.append(pkg.qgemv_run(Q4, p, m.N, m.K, xd, out_dtype=out_dtype))
+    plan = pkg.qg_batch_plan_build(Q4, 1, entries, out_dtype)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    for (p, N, K, xd, y), s, m, x in zip(entries, singles, mats, xs):
+        ref = oracle.q4_gemm(m.codes, m.scales, m.biases, x)[0]
+        got = to_np(y)
+        if out_dtype == pkg.OUT_F32:
+            assert_f32_close(got, ref, what="N=%d K=%d" % (N, K))
+        else:
+            assert_bf16_close(got, ref, what="N=%d K=%d" % (N, K))
+        assert torch.equal(y, s), "batch differs from qgemv_run for N=%d K=%d" % (N, K)
+
+
+@pytest.mark.parametrize("M", [2, 5, 16, 17, 32])
+def test_batch_skinny_mixed_shapes(M):
+    note("batch skinny M=%d" % M)
+    shapes = [(40, 192), (256, 4096), (33, 1216), (130, 640)]
+    mats = _mats(92, shapes)
+    Xs = [synth.activations(93, M, m.K, item=i) for i, m in enumerate(mats)]
+    entries, singles = [], []
+    for m, X in zip(mats, Xs):
+        p = weights.pack_q4(m, DEV)
+        Xd = weights.to_device(X, DEV)
+        Y = torch.empty((M, m.N), dtype=torch.float32, device=DEV)
+        entries.append((p, m.N, m.K, Xd, Y))
+        singles.append(pkg.qgemm_skinny_run(Q4, p, M, m.N, m.K, Xd, out_dtype=pkg.OUT_F32))
+    plan = pkg.qg_batch_plan_build(Q4, M, entries, pkg.OUT_F32)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    for (p, N, K, Xd, Y), s, m, X in zip(entries, singles, mats, Xs):
+        assert_f32_close(to_np(Y), oracle.q4_gemm(m.codes, m.scales, m.biases, X), what="N=%d K=%d" % (N, K))
+        assert torch.equal(Y, s)
+
+
+def test_batch_graph_replay():
+    """The grouped launch captured in a HIP graph: several replays, with eager
+    work and synchronizations between them, each checked against the eager
+    result."""
+    note("batch graph replay")
+    mats = _mats(94, [(256, 4096), (1024, 4096), (64, 12288)])
+    entries = []
+    for i, m in enumerate(mats):
+        p = weights.pack_q4(m, DEV)
+        x = weights.to_device(synth.activations(95, 1, m.K, item=i)[0], DEV)
+        entries.append((p, m.N, m.K, x, torch.empty(m.N, dtype=torch.bfloat16, device=DEV)))
+    plan = pkg.qg_batch_plan_build(Q4, 1, entries)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    eager = [e[4].clone() for e in entries]
+    g = workloads.capture_graph(lambda: pkg.qg_batch_run(plan))
+    for rep in range(4):
+        for e in entries:
+            e[4].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, ref in zip(entries, eager):
+            assert torch.equal(e[4], ref), "replay %d differs" % rep
+        _ = torch.randn(1000, device=DEV).sum().item()  # unrelated eager work in between
+
+
+def test_batch_decode_step_full():
+    """The whole synthetic decode step (253 GEMVs, 4.26 GB) in one launch:
+    every output bitwise equal to qgemv_run's, and sampled rows of several
+    projections against the oracle."""
+    note("batch decode step full")
+    step = workloads.build_decode_step(0)
+    plan = pkg.qg_batch_plan_build(Q4, 1, [(g.packed, g.N, g.K, g.x, g.y) for g in step.gemvs])
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    got = [g.y.clone() for g in step.gemvs]
+    workloads.run_step_eager(step)
+    torch.cuda.synchronize()
+    for g, b in zip(step.gemvs, got):
+        assert torch.equal(g.y, b), g.name
+    rng = np.random.default_rng(96)
+    for idx in (0, 1, 4, 6, 250, 252):
+        item, name, N, K = synth.decode_step_shapes()[idx]
+        m = synth.q4_matrix(0, N, K, item=item)
+        x = synth.activations(0, 1, K, item=item)
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 64, replace=False)]))
+        ref = oracle.q4_gemm(m.codes[rows], m.scales[rows], m.biases[rows], x)[0]
+        assert_bf16_close(to_np(got[idx])[rows], ref, what=name)
