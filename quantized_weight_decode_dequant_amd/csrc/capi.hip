@@ -317,13 +317,7 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
             total_units += w.units;
             total_cost += (int64_t)w.units * ((int64_t)w.P * rpu + 2);
         }
-        int per_cu = 4;
-        if (M == 1) {
-            const size_t lds = q4_gemv_lds_bytes(kmax);
-            per_cu = (int)((160 * 1024) / lds);
-            if (per_cu > 8) per_cu = 8;
-            if (per_cu < 1) per_cu = 1;
-        }
+        const int per_cu = (M == 1) ? q4_gemv_wgs_per_cu() : 4;
         int64_t grid = (int64_t)cus * per_cu;
         if (grid > WL_GRID_MAX) grid = WL_GRID_MAX;
         if (grid > total_units) grid = total_units;

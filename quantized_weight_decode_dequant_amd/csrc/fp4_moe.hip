@@ -109,7 +109,7 @@ fp4_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restrict__
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint4 *xl = reinterpret_cast<uint4 *>(smem);
     float *red = reinterpret_cast<float *>(smem + (size_t)P * 512);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
     stage_x_bf16(xl, x, K, P, tid, WAVES * 64);
     __syncthreads();
     int par = 0;
@@ -171,7 +171,7 @@ moe_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__ p
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint4 *xl = reinterpret_cast<uint4 *>(smem);
     float *red = reinterpret_cast<float *>(smem + (size_t)P * 512);  // [2][2][WAVES][16]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
     stage_x_bf16(xl, x, H, P, tid, WAVES * 64);
     __syncthreads();
     const int per = (items + gridDim.x - 1) / gridDim.x;
@@ -238,7 +238,7 @@ moe_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws,
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float4 *hl = reinterpret_cast<float4 *>(smem);                       // [P*64] float4
     float *red = reinterpret_cast<float *>(smem + (size_t)P * 1024);    // [2][WAVES][16]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
     const int per = (items + gridDim.x - 1) / gridDim.x;
     const int i0 = blockIdx.x * per;
     const int i1 = min(items, i0 + per);

@@ -6,18 +6,22 @@
 // Uzu page, section "Why batch-one decoding is memory-bound": every weight is
 // streamed once with about one multiply-add).
 //
-// Work split.  A workgroup owns one rowblock (16 rows) at a time; its waves
-// split the rowblock's 128-k tiles.  Each lane reads one 16-byte slot per
-// tile (4 words = 32 codes of one row); one 64-lane load covers 16 rows x
-// 128 k = 1 KB contiguous.  x is staged in LDS together with per-(tile,
-// group, k-slice) partial sums of x, which carry the bias term.
+// Work split.  A workgroup owns a contiguous range of rowblocks (16 rows
+// each); for one rowblock its 4 waves split the 128-k tiles, 8 tiles per
+// wave.  Each lane reads one 16-byte slot per tile (4 words = 32 codes of one
+// row); one 64-lane load covers 16 rows x 128 k = 1 KB contiguous.  K is
+// processed in segments of 4096: the workgroup stages that slice of x in LDS
+// (with per-(tile, group, k-slice) partial sums of x, which carry the bias
+// term), sweeps up to 64 of its rowblocks, keeps their partial row sums in
+// LDS and moves to the next segment.  LDS use is therefore ~14 KB whatever
+// K is, which keeps 8 workgroups resident per CU.
 //
 // Two launch modes share the body:
-//  - single matrix (qgemv_run): rowblocks rb = blockIdx.x + i * gridDim.x;
+//  - single matrix (qgemv_run): workgroup j takes rowblocks
+//    [j*n/G, (j+1)*n/G);
 //  - work list (one launch for many independent GEMVs, e.g. every projection
 //    of a decode step): workgroup j walks the contiguous (matrix, rowblock)
-//    range [starts[j], starts[j+1]), balanced by bytes on the host, and
-//    re-stages x only when the matrix changes.
+//    range [starts[j], starts[j+1]), balanced by bytes on the host.
 //
 // Arithmetic per word: (w >> 4j) & 0x000F000F | 0x43004300 (one
 // v_and_or_b32) turns two codes into the bf16 pair (128 + q, 128 + q'),
@@ -31,58 +35,68 @@
 namespace qg {
 
 constexpr int GV_WAVES = 4;
-constexpr int GV_TPW = 8;  // tiles per wave per batch
+constexpr int GV_TPW = 8;                     // tiles per wave per (rowblock, segment)
 constexpr int GV_THREADS = GV_WAVES * 64;
+constexpr int GV_SEG_TILES = GV_WAVES * GV_TPW;  // 32 tiles = 4096 k per segment
+constexpr int GV_RMAX = 64;                   // rowblocks per block of partial sums
+constexpr int GV_WGS_PER_CU = 5;              // resident workgroups per CU (register bound)
+
+int q4_gemv_wgs_per_cu() { return GV_WGS_PER_CU; }
 
 size_t q4_gemv_lds_bytes(int64_t kmax) {
-    const int64_t P = ceil_div(kmax, Q4_TILE_K);
-    return (size_t)P * 256 + (size_t)P * 32 + 2 * GV_WAVES * 16 * 4;
+    (void)kmax;  // independent of K: x is staged one 4096-k segment at a time
+    return (size_t)GV_SEG_TILES * 256 + (size_t)GV_SEG_TILES * 32 + GV_RMAX * 16 * 4 +
+           2 * GV_WAVES * 16 * 4;
 }
 
 struct GemvLds {
-    unsigned *xl;  // bf16 pairs [P*64]
-    float *xsum;   // [P*8]
-    float *red;    // [2][WAVES][16]
+    unsigned *xl;   // bf16 pairs of the staged segment [32*64]
+    float *xsum;    // [32*8]
+    float *part;    // [GV_RMAX][16] partial row sums across segments
+    float *red;     // [2][WAVES][16]
 };
 
-// Stage x (zero past K) and its per-(tile, group, k-slice) sums.  Ends with a
-// barrier; the caller guarantees no wave still reads the previous x.
-__device__ __forceinline__ void gv_stage_x(const GemvLds &L, const uint16_t *x, int K, int P,
+// Stage x[seg*4096 .. +4096) (zero past K) and its per-(tile, group,
+// k-slice) sums.  Ends with a barrier; the caller guarantees no wave still
+// reads the previous segment.
+__device__ __forceinline__ void gv_stage_x(const GemvLds &L, const uint16_t *x, int K, int seg,
                                            int tid) {
-    constexpr int U = 8;
-    const int n4 = P * 16, nx4 = K / 8;
-    for (int b = tid; b < n4; b += GV_THREADS * U) {
-        uint4 v[U];
+    const int k0 = seg * GV_SEG_TILES * Q4_TILE_K;
+    const int n4 = GV_SEG_TILES * 16;          // uint4 of the segment
+    const int nx4 = (K - k0) / 8;              // valid uint4 (K is a multiple of 64)
+    constexpr int U = (GV_SEG_TILES * 16) / GV_THREADS;  // 2
+    u32x4_t v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = b + u * GV_THREADS;
-            v[u] = (i < nx4) ? reinterpret_cast<const uint4 *>(x)[i] : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = b + u * GV_THREADS;
-            if (i < n4) reinterpret_cast<uint4 *>(L.xl)[i] = v[u];
-        }
+    for (int u = 0; u < U; ++u) {
+        const int i = tid + u * GV_THREADS;
+        v[u] = (i < nx4) ? ld_global(reinterpret_cast<const u32x4_t *>(x + k0) + i)
+                         : u32x4_t{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) reinterpret_cast<u32x4_t *>(L.xl)[tid + u * GV_THREADS] = v[u];
+    (void)n4;
     __syncthreads();
-    for (int i = tid; i < P * 8; i += GV_THREADS) {
+    {
+        const int i = tid;  // 256 threads = 32 tiles x 2 groups x 4 k-slices
         const int p = i >> 3, t = (i >> 2) & 1, kg = i & 3;
         float s = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint4 v = reinterpret_cast<const uint4 *>(L.xl)[16 * p + 8 * t + 4 * h + kg];
-            s += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
-                 bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+            const uint4 w = reinterpret_cast<const uint4 *>(L.xl)[16 * p + 8 * t + 4 * h + kg];
+            s += bf16_lo(w.x) + bf16_hi(w.x) + bf16_lo(w.y) + bf16_hi(w.y) + bf16_lo(w.z) +
+                 bf16_hi(w.z) + bf16_lo(w.w) + bf16_hi(w.w);
         }
         L.xsum[i] = s;
     }
     __syncthreads();
 }
+static_assert(GV_SEG_TILES * 8 == GV_THREADS, "one x-sum per thread");
 
-// One tile's contribution of this lane (16 codes per group, 2 groups).
-__device__ __forceinline__ float gv_tile(u32x4_t c, u32x2_t sb, const GemvLds &L, int p, int kg,
-                                         unsigned magic, float acc) {
-    const uint4 *xp = reinterpret_cast<const uint4 *>(L.xl) + 16 * p + kg;
+// One tile's contribution of this lane (16 codes per group, 2 groups); `pl`
+// is the tile's index within the staged segment.
+__device__ __forceinline__ float gv_tile(u32x4_t c, u32x2_t sb, const GemvLds &L, int pl, int kg,
+                                         const Q4Consts &magic, float acc) {
+    const uint4 *xp = reinterpret_cast<const uint4 *>(L.xl) + 16 * pl + kg;
     const uint4 xa0 = xp[0], xb0 = xp[4], xa1 = xp[8], xb1 = xp[12];
     unsigned q[4];
     float d0 = 0.f, d1 = 0.f;
@@ -108,7 +122,7 @@ __device__ __forceinline__ float gv_tile(u32x4_t c, u32x2_t sb, const GemvLds &L
     d1 = dot2_bf16(q[3], xb1.w, d1);
     const float s0 = f16_lo(sb[0]), b0 = f16_hi(sb[0]);
     const float s1 = f16_lo(sb[1]), b1 = f16_hi(sb[1]);
-    const float xs0 = L.xsum[p * 8 + kg], xs1 = L.xsum[p * 8 + 4 + kg];
+    const float xs0 = L.xsum[pl * 8 + kg], xs1 = L.xsum[pl * 8 + 4 + kg];
     acc = fmaf(s0, d0, acc);
     acc = fmaf(fmaf(-128.f, s0, b0), xs0, acc);
     acc = fmaf(s1, d1, acc);
@@ -116,27 +130,38 @@ __device__ __forceinline__ float gv_tile(u32x4_t c, u32x2_t sb, const GemvLds &L
     return acc;
 }
 
-// Rowblock rb of the matrix: this wave's tiles, then the cross-wave sum.
-__device__ __forceinline__ void gv_rowblock(const WorkItem &it, int rb, const GemvLds &L,
-                                            int lane, int wave, unsigned magic, int &par) {
+// Segment `seg` of rowblock rb: this wave's tiles, the cross-lane and
+// cross-wave sums, added to the rowblock's partial sums in LDS (segments in
+// order, so the result is deterministic).
+__device__ __forceinline__ void gv_rowblock_seg(const WorkItem &it, int rb, int seg, int nseg,
+                                                int slot, const GemvLds &L, int lane, int wave,
+                                                const Q4Consts &magic, int &par) {
     const int P = it.P, kg = lane >> 4;
-    const uint8_t *base = it.packed + (size_t)rb * P * Q4_TILE_BYTES;
+    const int pbase = seg * GV_SEG_TILES;
+    const int pn = min(GV_SEG_TILES, P - pbase);  // tiles in this segment
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+        uniform_ptr(it.packed + ((size_t)rb * P + pbase) * Q4_TILE_BYTES), (unsigned)pn * Q4_TILE_BYTES);
+    u32x4_t c[GV_TPW];
+    u32x2_t sb[GV_TPW];
+    const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
+#pragma unroll
+    for (int j = 0; j < GV_TPW; ++j) {
+        const unsigned to = (unsigned)min(wave + j * GV_WAVES, pn - 1) * Q4_TILE_BYTES;  // tail: re-read
+        c[j] = buf_ld_x4(rs, lc, to);
+        sb[j] = buf_ld_x2(rs, ls, to);
+    }
+    // keep all of this wave's loads issued before any of the arithmetic: the
+    // scheduler would otherwise move them next to their uses
+    __builtin_amdgcn_sched_barrier(0);
+    // no branch around the tiles (a branch would let the compiler sink each
+    // load next to its use): tail tiles are computed from the clamped
+    // re-read and discarded with a select
     float acc = 0.f;
-    for (int p0 = wave; p0 < P; p0 += GV_WAVES * GV_TPW) {
-        u32x4_t c[GV_TPW];
-        u32x2_t sb[GV_TPW];
 #pragma unroll
-        for (int j = 0; j < GV_TPW; ++j) {
-            const int p = min(p0 + j * GV_WAVES, P - 1);  // tail: re-read the last tile
-            const uint8_t *tb = base + (size_t)p * Q4_TILE_BYTES;
-            c[j] = ld_nt(reinterpret_cast<const u32x4_t *>(tb) + lane);
-            sb[j] = ld_nt(reinterpret_cast<const u32x2_t *>(tb + 1024) + (lane & 15));
-        }
-#pragma unroll
-        for (int j = 0; j < GV_TPW; ++j) {
-            const int p = p0 + j * GV_WAVES;
-            if (p < P) acc = gv_tile(c[j], sb[j], L, p, kg, magic, acc);
-        }
+    for (int j = 0; j < GV_TPW; ++j) {
+        const int pl = wave + j * GV_WAVES;
+        const float a = gv_tile(c[j], sb[j], L, min(pl, pn - 1), kg, magic, acc);
+        acc = (pl < pn) ? a : acc;
     }
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
@@ -147,48 +172,69 @@ __device__ __forceinline__ void gv_rowblock(const WorkItem &it, int rb, const Ge
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < GV_WAVES; ++w) v += red[w * 16 + lane];
-        const int row = rb * RB + lane;
-        if (row < it.N) {
-            if (it.out_f32)
-                reinterpret_cast<float *>(it.y)[row] = v;
-            else
-                reinterpret_cast<uint16_t *>(it.y)[row] = f32_to_bf16(v);
-        }
+        float *pp = L.part + slot * 16 + lane;
+        *pp = (seg > 0) ? *pp + v : v;
     }
     par ^= 1;
 }
 
-__global__ void __launch_bounds__(GV_THREADS)
+// Rowblocks [u0, u1) of one matrix, in blocks of GV_RMAX: for every 4096-k
+// segment, stage that slice of x once and sweep the block's rowblocks.
+__device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, const GemvLds &L,
+                                         int tid, int lane, int wave, const Q4Consts &magic, int &par) {
+    const int nseg = (it.P + GV_SEG_TILES - 1) / GV_SEG_TILES;
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(it.x);
+#pragma unroll 1
+    for (int ub = u0; ub < u1; ub += GV_RMAX) {
+        const int ue = min(u1, ub + GV_RMAX);
+#pragma unroll 1
+        for (int seg = 0; seg < nseg; ++seg) {
+            __syncthreads();  // nobody still reads the previous segment or partials
+            gv_stage_x(L, x, it.K, seg, tid);
+#pragma unroll 1
+            for (int u = ub; u < ue; ++u)
+                gv_rowblock_seg(it, u, seg, nseg, u - ub, L, lane, wave, magic, par);
+        }
+        // the block's finished rows, written once by the whole workgroup (no
+        // global store between the loads of the sweep above)
+        __syncthreads();
+        const int r0 = ub * RB, nr = min(ue * RB, it.N) - r0;
+        for (int r = tid; r < nr; r += GV_THREADS) {
+            const float v = L.part[r];
+            if (it.out_f32)
+                reinterpret_cast<float *>(it.y)[r0 + r] = v;
+            else
+                reinterpret_cast<uint16_t *>(it.y)[r0 + r] = f32_to_bf16(v);
+        }
+    }
+}
+
+// at most 95 VGPRs: 5 waves per SIMD, 5 workgroups of 4 waves per CU
+__global__ void __launch_bounds__(GV_THREADS, GV_WGS_PER_CU)
 q4_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
-               WorkItem single, int pmax) {
+               WorkItem single) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     GemvLds L;
     L.xl = reinterpret_cast<unsigned *>(smem);
-    L.xsum = reinterpret_cast<float *>(smem + (size_t)pmax * 256);
-    L.red = L.xsum + pmax * 8;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const unsigned magic = bf16_magic128x2();
+    L.xsum = reinterpret_cast<float *>(smem + (size_t)GV_SEG_TILES * 256);
+    L.part = L.xsum + GV_SEG_TILES * 8;
+    L.red = L.part + GV_RMAX * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const Q4Consts magic = q4_consts();
     int par = 0;
     if (items == nullptr) {
-        gv_stage_x(L, reinterpret_cast<const uint16_t *>(single.x), single.K, single.P, tid);
-        for (int rb = blockIdx.x; rb < single.units; rb += gridDim.x)
-            gv_rowblock(single, rb, L, lane, wave, magic, par);
+        // single matrix: a contiguous share of the rowblocks per workgroup
+        const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
+        gv_range(single, (int)(j * n / g), (int)((j + 1) * n / g), L, tid, lane, wave, magic, par);
         return;
     }
     const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
-    int i = s.item, u = s.unit, staged = -1;
-    WorkItem it;
-    while (i < e.item || (i == e.item && u < e.unit)) {
-        if (i != staged) {
-            it = items[i];
-            gv_stage_x(L, reinterpret_cast<const uint16_t *>(it.x), it.K, it.P, tid);
-            staged = i;
-        }
-        gv_rowblock(it, u, L, lane, wave, magic, par);
-        if (++u == it.units) {
-            ++i;
-            u = 0;
-        }
+#pragma unroll 1
+    for (int i = s.item; i < e.item || (i == e.item && e.unit > 0); ++i) {
+        const WorkItem it = items[i];
+        const int u0 = (i == s.item) ? s.unit : 0;
+        const int u1 = (i == e.item) ? e.unit : it.units;
+        if (u0 < u1) gv_range(it, u0, u1, L, tid, lane, wave, magic, par);
     }
 }
 
@@ -203,18 +249,17 @@ hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int
     it.P = (int32_t)ceil_div(K, Q4_TILE_K);
     it.units = (int32_t)ceil_div(N, RB);
     it.out_f32 = out_f32 ? 1 : 0;
-    const int grid = (int)(it.units < (int64_t)cus * 8 ? it.units : (int64_t)cus * 8);
+    const int grid = (int)(it.units < (int64_t)cus * GV_WGS_PER_CU ? it.units : (int64_t)cus * GV_WGS_PER_CU);
     hipLaunchKernelGGL(q4_gemv_kernel, dim3(grid), dim3(GV_THREADS), q4_gemv_lds_bytes(K), s,
-                       (const WorkItem *)nullptr, (const WorkStart *)nullptr, it, it.P);
+                       (const WorkItem *)nullptr, (const WorkStart *)nullptr, it);
     return hipGetLastError();
 }
 
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts, int grid,
                                int64_t kmax, hipStream_t s) {
     WorkItem none{};
-    const int pmax = (int)ceil_div(kmax, Q4_TILE_K);
     hipLaunchKernelGGL(q4_gemv_kernel, dim3(grid), dim3(GV_THREADS), q4_gemv_lds_bytes(kmax), s,
-                       items, starts, none, pmax);
+                       items, starts, none);
     return hipGetLastError();
 }
 

@@ -92,6 +92,7 @@ hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y,
                           hipStream_t s);
 // grouped launches over a device work list
 size_t q4_gemv_lds_bytes(int64_t kmax);
+int q4_gemv_wgs_per_cu();
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts,
                                int grid, int64_t kmax, hipStream_t s);
 constexpr int SK_ROWBLOCKS_M16 = 4;   // rowblocks per skinny unit, M <= 16
@@ -188,40 +189,88 @@ __device__ __forceinline__ f32x2_t fp4_pair_f32(unsigned w, float scale) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
 }
 
+// Streaming (non-temporal) load through the global address space.  Pointers
+// read from memory (work lists) are otherwise generic, which makes the
+// compiler emit FLAT loads; those also count against the LDS counter, so every
+// LDS read would wait for the outstanding HBM loads.
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T *p) {
-    return __builtin_nontemporal_load(p);
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) T *)p);
 }
 
-// (a & mask) | orv in one v_and_or_b32.  gfx9 VOP3 reads at most one SGPR or
-// literal, so the mask rides in an SGPR and orv must be a VGPR.
-__device__ __forceinline__ unsigned and_or(unsigned a, unsigned mask, unsigned orv) {
-    unsigned d;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(orv));
-    return d;
+// A wave-uniform pointer made opaque to the optimizer (readfirstlane of both
+// halves), so address arithmetic on it stays scalar instead of being folded
+// into per-lane 64-bit vector offsets.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+    return reinterpret_cast<const uint8_t *>(((unsigned long long)hi << 32) | lo);
 }
 
-// bf16 128.0 twice, materialized once into a VGPR (opaque to the compiler so it
-// is not re-materialized at every use).
-__device__ __forceinline__ unsigned bf16_magic128x2() {
-    unsigned m;
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
-    return m;
+// Non-temporal load of the T at byte offset `off` from a wave-uniform base:
+// with an unsigned 32-bit offset the address selects the SGPR-base +
+// VGPR-offset form of global_load, no 64-bit address per load.
+template <typename T>
+__device__ __forceinline__ T ld_nt_off(const void *base, unsigned off) {
+    typedef const __attribute__((address_space(1))) char gchar;
+    typedef const __attribute__((address_space(1))) T gT;
+    gchar *b = (gchar *)base;
+    return __builtin_nontemporal_load((gT *)(b + off));
+}
+
+// Buffer resource over [base, base + bytes) for raw buffer loads (gfx9
+// descriptor word 3).  Loads through it take the wave-uniform part of the
+// address in an SGPR (soffset) and one 32-bit per-lane VGPR offset; any byte
+// at or past `bytes` reads as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Non-temporal (streaming) buffer loads: aux = slc.
+__device__ __forceinline__ u32x4_t buf_ld_x4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
+}
+__device__ __forceinline__ u32x2_t buf_ld_x2(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 2));
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_global(const T *p) {
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+
+// The two constants of the nibble unpack, held in VGPRs.  gfx9 VOP3
+// instructions read at most one SGPR or literal, so with both operands in
+// registers (a & mask) | magic selects to a single v_and_or_b32.  They are
+// materialized once through an opaque move so the compiler does not
+// re-materialize them at every use.
+struct Q4Consts {
+    unsigned mask;   // 0x000F000F
+    unsigned magic;  // bf16 128.0 twice
+};
+
+__device__ __forceinline__ Q4Consts q4_consts() {
+    Q4Consts k;
+    asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(k.mask));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.magic));
+    return k;
 }
 
 // The four bf16 pairs (128 + q_2j, 128 + q_2j+1), j = 0..3, of a packed Q4 word.
-__device__ __forceinline__ void q4_unpack(unsigned w, unsigned magic, unsigned out[4]) {
-    out[0] = and_or(w, 0x000F000Fu, magic);
-    out[1] = and_or(w >> 4, 0x000F000Fu, magic);
-    out[2] = and_or(w >> 8, 0x000F000Fu, magic);
-    out[3] = and_or(w >> 12, 0x000F000Fu, magic);
+__device__ __forceinline__ void q4_unpack(unsigned w, const Q4Consts &k, unsigned out[4]) {
+    out[0] = (w & k.mask) | k.magic;
+    out[1] = ((w >> 4) & k.mask) | k.magic;
+    out[2] = ((w >> 8) & k.mask) | k.magic;
+    out[3] = ((w >> 12) & k.mask) | k.magic;
 }
 
 // Eight 4-bit codes of a packed Q4 word as the bf16x8 MFMA operand
 // (128 + q_0, ..., 128 + q_7).
-__device__ __forceinline__ bf16x8_t q4_word_to_bf16x8(unsigned w, unsigned magic) {
+__device__ __forceinline__ bf16x8_t q4_word_to_bf16x8(unsigned w, const Q4Consts &k) {
     unsigned o[4];
-    q4_unpack(w, magic, o);
+    q4_unpack(w, k, o);
     u32x4_t v = {o[0], o[1], o[2], o[3]};
     return __builtin_bit_cast(bf16x8_t, v);
 }

@@ -28,10 +28,10 @@ constexpr int SK_THREADS = SK_WAVES * 64;
 
 template <int MT, int KC, int RPW>
 __device__ __forceinline__ void sk_q4_unit(const WorkItem &it, int unit, int M, uint16_t *xl,
-                                           float *xs, int tid, unsigned magic) {
+                                           float *xs, int tid, const Q4Consts &magic) {
     constexpr int MP = MT * 16;
     constexpr int RS = KC * 128 + 8;  // LDS row stride in bf16
-    const int lane = tid & 63, wave = tid >> 6, kg = lane >> 4;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
     const int P = it.P, K = it.K, N = it.N;
     const int nrb = (N + RB - 1) / RB;
     const int rb0 = unit * (SK_WAVES * RPW) + wave * RPW;
@@ -170,7 +170,7 @@ q4_skinny_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict
     __shared__ __attribute__((aligned(16))) uint16_t xl[MP * RS];
     __shared__ __attribute__((aligned(16))) float xs[2 * KC * MP];  // [group-in-chunk][m]
     const int tid = threadIdx.x;
-    const unsigned magic = bf16_magic128x2();
+    const Q4Consts magic = q4_consts();
     if (items == nullptr) {
         for (int u = blockIdx.x; u < single.units; u += gridDim.x)
             sk_q4_unit<MT, KC, RPW>(single, u, M, xl, xs, tid, magic);
@@ -201,7 +201,7 @@ q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ 
     constexpr int MP = MT * 16;
     constexpr int RS = KC * 128 + 16;  // LDS row stride in bytes
     __shared__ __attribute__((aligned(16))) int8_t xl[MP * RS];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
     const int G = K / 32;
     const int items = (nrb + SK_WAVES - 1) / SK_WAVES;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
