@@ -112,7 +112,7 @@ def main():
     log("device:", props.name, getattr(props, "gcnArchName", ""))
 
     t = time.time()
-    step = workloads.build_decode_step(args.seed, skinny_m=0 if args.no_m16 else 16, log=log)
+    step = workloads.build_decode_step(args.seed, log=log)
     log("workload ready in %.1f s: %d GEMVs, %.3f GB packed" % (
         time.time() - t, len(step.gemvs), step.weight_bytes / 1e9))
     step_bytes = step.algorithmic_bytes(1)
@@ -194,30 +194,36 @@ def main():
         },
     }
 
-    # ---- verification pass, M = 16, same weights, one grouped launch
+    # ---- verification passes, M = 16 and M = 32, same weights, one grouped launch each
     if not args.no_m16:
-        plan16 = pkg.qg_batch_plan_build(Q4, 16, [(g.packed, g.N, g.K, g.X, g.Y) for g in step.gemvs])
-        for _ in range(max(1, args.warmup)):
-            pkg.qg_batch_run(plan16)
-        torch.cuda.synchronize()
-        n16 = max(5, args.steps // 2)
-        e0.record()
-        for _ in range(n16):
-            pkg.qg_batch_run(plan16)
-        e1.record()
-        torch.cuda.synchronize()
-        ms16 = e0.elapsed_time(e1) / n16
-        b16 = step.algorithmic_bytes(16)
-        result["m16"] = {
-            "ms_per_pass": round(ms16, 4),
-            "value": round(b16 / (ms16 * 1e-3) / 1e9, 2),
-            "unit": "GB/s",
-            "pct_of_peak": round(100 * b16 / (ms16 * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2),
-            "passes_per_s": round(1e3 / ms16, 2),
-            "tflops": round(step.flops(16) / (ms16 * 1e-3) / 1e12, 2),
-            "launch": "one grouped kernel launch per pass (16-row activation tile per projection)",
-        }
-        log("m16 pass: %.3f ms" % ms16)
+        for M in (16, 32):
+            Xs = [workloads.verification_tile(args.seed, g, M) for g in step.gemvs]
+            Ys = [torch.empty((M, g.N), dtype=torch.bfloat16, device=dev) for g in step.gemvs]
+            planM = pkg.qg_batch_plan_build(
+                Q4, M, [(g.packed, g.N, g.K, X, Y) for g, X, Y in zip(step.gemvs, Xs, Ys)])
+            for _ in range(max(1, args.warmup)):
+                pkg.qg_batch_run(planM)
+            torch.cuda.synchronize()
+            nM = max(5, args.steps // 2)
+            e0.record()
+            for _ in range(nM):
+                pkg.qg_batch_run(planM)
+            e1.record()
+            torch.cuda.synchronize()
+            msM = e0.elapsed_time(e1) / nM
+            bM = step.algorithmic_bytes(M)
+            result["m%d" % M] = {
+                "ms_per_pass": round(msM, 4),
+                "value": round(bM / (msM * 1e-3) / 1e9, 2),
+                "unit": "GB/s",
+                "pct_of_peak": round(100 * bM / (msM * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2),
+                "passes_per_s": round(1e3 / msM, 2),
+                "tflops": round(step.flops(M) / (msM * 1e-3) / 1e12, 2),
+                "launch": "one grouped kernel launch per pass (%d-row activation tile per "
+                          "projection)" % M,
+            }
+            log("m%d pass: %.3f ms" % (M, msM))
+            del planM, Xs, Ys
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_budget)

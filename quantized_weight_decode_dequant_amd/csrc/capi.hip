@@ -299,7 +299,7 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
 
         // units and their costs (in 128-k tiles, plus a fixed per-unit overhead
         // for the reduction and the synchronization around it)
-        const int rpu = (M == 1) ? 1 : (M <= 16 ? SK_ROWBLOCKS_M16 : SK_ROWBLOCKS_M32);
+        const int rpu = 1;  // scheduling unit: one rowblock, for every M
         std::vector<WorkItem> items((size_t)count);
         int64_t total_units = 0, total_cost = 0;
         for (int32_t i = 0; i < count; ++i) {
@@ -317,7 +317,7 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
             total_units += w.units;
             total_cost += (int64_t)w.units * ((int64_t)w.P * rpu + 2);
         }
-        const int per_cu = (M == 1) ? q4_gemv_wgs_per_cu() : 4;
+        const int per_cu = (M == 1) ? q4_gemv_wgs_per_cu() : q4_skinny_wgs_per_cu(M);
         int64_t grid = (int64_t)cus * per_cu;
         if (grid > WL_GRID_MAX) grid = WL_GRID_MAX;
         if (grid > total_units) grid = total_units;

@@ -52,8 +52,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------- work lists
 // One entry per matrix of a grouped launch (device-resident, written by
 // qg_batch_plan_build), or passed by value for a single-matrix launch.
-// `units` is the number of scheduling units of the matrix: rowblocks for the
-// M = 1 kernel, groups of SK_ROWBLOCKS rowblocks for the skinny kernel.
+// `units` is the number of scheduling units of the matrix: its rowblocks.
 struct alignas(16) WorkItem {
     const uint8_t *packed;
     const void *x;   // bf16 [M][K]
@@ -95,8 +94,7 @@ size_t q4_gemv_lds_bytes(int64_t kmax);
 int q4_gemv_wgs_per_cu();
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts,
                                int grid, int64_t kmax, hipStream_t s);
-constexpr int SK_ROWBLOCKS_M16 = 4;   // rowblocks per skinny unit, M <= 16
-constexpr int SK_ROWBLOCKS_M32 = 8;   // rowblocks per skinny unit, M <= 32
+int q4_skinny_wgs_per_cu(int64_t M);
 hipError_t launch_q4_skinny_list(const WorkItem *items, const WorkStart *starts,
                                  int grid, int64_t M, hipStream_t s);
 hipError_t launch_write_words(const uint32_t *src, size_t nwords, uint32_t *dst,

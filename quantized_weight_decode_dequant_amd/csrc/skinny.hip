@@ -13,12 +13,10 @@
 // the exact int32 group partial; acc += sw * float(partial) (exact
 // conversion, |partial| <= 32 * 127^2), then y = sx[m] * acc.
 //
-// Work split: a workgroup of 4 waves owns a unit of 4 * RPW consecutive
-// rowblocks (each wave RPW rowblocks, sharing its A operands across them)
-// and walks K in chunks of KC tiles; each chunk of X is staged into LDS
-// (rows padded by 16 bytes so the 16 A-operand rows hit distinct banks) and
-// shared by the 4 waves.  The Q4 kernel also runs over a device work list of
-// independent matrices (one launch for a whole verification pass).
+// The X slices staged in LDS have rows padded by 16 bytes so the 16
+// A-operand rows of one MFMA hit distinct banks.  The Q4 kernel also runs
+// over a device work list of independent matrices (one launch for a whole
+// verification pass); see sk_q4_range for its work split.
 #include "qg_internal.h"
 
 namespace qg {
@@ -26,95 +24,123 @@ namespace qg {
 constexpr int SK_WAVES = 4;
 constexpr int SK_THREADS = SK_WAVES * 64;
 
-template <int MT, int KC, int RPW>
-__device__ __forceinline__ void sk_q4_unit(const WorkItem &it, int unit, int M, uint16_t *xl,
-                                           float *xs, int tid, const Q4Consts &magic) {
-    constexpr int MP = MT * 16;
-    constexpr int RS = KC * 128 + 8;  // LDS row stride in bf16
+// Q4 skinny, work split: a workgroup owns a contiguous range of rowblocks
+// and walks it in blocks of SK_BLOCK = 4 * RPI * NI rowblocks.  For each
+// K-segment of TPS tiles it stages that slice of X (all M rows) and its group
+// sums in LDS once, then each wave sweeps NI iterations of RPI rowblocks: it
+// loads their TPS tiles (8 slots per iteration), and accumulates the MFMA
+// results into per-rowblock registers.  X is re-staged once per block and
+// segment, not once per rowblock.  X is zero past K, so tiles past the end of
+// K (clamped re-reads) contribute exactly zero; rowblocks past the range are
+// computed from clamped re-reads and simply not stored.
+template <int MT, int TPS, int RPI, int NI>
+struct SkCfg {
+    static constexpr int MP = MT * 16;          // padded rows of X
+    static constexpr int RS = TPS * 128 + 8;    // LDS row stride in bf16 (16-byte pad)
+    static constexpr int BLOCK = SK_WAVES * RPI * NI;
+    static constexpr size_t LDS = (size_t)MP * RS * 2 + (size_t)2 * TPS * MP * 4;
+};
+
+template <int MT, int TPS, int RPI, int NI>
+__device__ __forceinline__ void sk_q4_range(const WorkItem &it, int u0, int u1, int M,
+                                            uint16_t *xl, float *xs, int tid,
+                                            const Q4Consts &kq) {
+    typedef SkCfg<MT, TPS, RPI, NI> C;
+    constexpr int MP = C::MP, RS = C::RS;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
     const int P = it.P, K = it.K, N = it.N;
-    const int nrb = (N + RB - 1) / RB;
-    const int rb0 = unit * (SK_WAVES * RPW) + wave * RPW;
+    const int nseg = (P + TPS - 1) / TPS;
     const uint16_t *X = reinterpret_cast<const uint16_t *>(it.x);
-    f32x4_t acc[RPW][MT];
+    const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
+#pragma unroll 1
+    for (int ub = u0; ub < u1; ub += C::BLOCK) {
+        f32x4_t acc[NI][RPI][MT];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[r][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int pc = 0; pc < P; pc += KC) {
-        const int nt = min(KC, P - pc);
-        // this chunk's weight slots (clamped indices: always in bounds)
-        u32x4_t c[KC][RPW];
-        u32x2_t sb[KC][RPW];
+            for (int r = 0; r < RPI; ++r)
 #pragma unroll
-        for (int j = 0; j < KC; ++j)
+                for (int mt = 0; mt < MT; ++mt) acc[i][r][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int seg = 0; seg < nseg; ++seg) {
+            const int p0 = seg * TPS, pn = min(TPS, P - p0);
+            __syncthreads();  // the previous segment's LDS reads are done
+            {
+                constexpr int TOT = MP * TPS * 16;  // uint4 of the segment
+                constexpr int U = (TOT + SK_THREADS - 1) / SK_THREADS;
+                const int k0 = p0 * 128;
+                u32x4_t v[U];
 #pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                const int rb = min(rb0 + r, nrb - 1);
-                const int p = min(pc + j, P - 1);
-                const uint8_t *tb = it.packed + ((size_t)rb * P + p) * Q4_TILE_BYTES;
-                c[j][r] = ld_nt(reinterpret_cast<const u32x4_t *>(tb) + lane);
-                sb[j][r] = ld_nt(reinterpret_cast<const u32x2_t *>(tb + 1024) + (lane & 15));
-            }
-        __syncthreads();  // the previous chunk's LDS reads are done
-        {
-            constexpr int TOT = MP * KC * 16;  // uint4 per chunk
-            constexpr int U = (TOT + SK_THREADS - 1) / SK_THREADS;
-            const int k0 = pc * 128;
-            uint4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = tid + u * SK_THREADS;
-                const int m = i / (KC * 16), c8 = i % (KC * 16);
-                const int k = k0 + c8 * 8;
-                v[u] = (i < TOT && m < M && k < K)
-                           ? *reinterpret_cast<const uint4 *>(X + (size_t)m * K + k)
-                           : make_uint4(0u, 0u, 0u, 0u);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = tid + u * SK_THREADS;
-                const int m = i / (KC * 16), c8 = i % (KC * 16);
-                if (i < TOT) *reinterpret_cast<uint4 *>(xl + m * RS + c8 * 8) = v[u];
-            }
-        }
-        __syncthreads();
-        for (int i = tid; i < 2 * KC * MP; i += SK_THREADS) {
-            const int g = i / MP, m = i % MP;
-            const uint4 *rr = reinterpret_cast<const uint4 *>(xl + m * RS + g * 64);
-            float sum = 0.f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint4 v = rr[q];
-                sum += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
-                       bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
-            }
-            xs[i] = sum;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < KC; ++j) {
-            if (j < nt) {
-                bf16x8_t A[MT][4];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const uint16_t *ar = xl + (16 * mt + (lane & 15)) * RS + j * 128 + 8 * kg;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) A[mt][q] = *reinterpret_cast<const bf16x8_t *>(ar + 32 * q);
-                }
-                f32x4_t xs0[MT], xs1[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    xs0[mt] = *reinterpret_cast<const f32x4_t *>(xs + (2 * j) * MP + 16 * mt + 4 * kg);
-                    xs1[mt] = *reinterpret_cast<const f32x4_t *>(xs + (2 * j + 1) * MP + 16 * mt + 4 * kg);
+                for (int u = 0; u < U; ++u) {
+                    const int i = tid + u * SK_THREADS;
+                    const int m = i / (TPS * 16), c8 = i % (TPS * 16);
+                    const int k = k0 + c8 * 8;
+                    v[u] = (i < TOT && m < M && k < K)
+                               ? ld_global(reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k))
+                               : u32x4_t{0u, 0u, 0u, 0u};
                 }
 #pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                    if (rb0 + r < nrb) {
+                for (int u = 0; u < U; ++u) {
+                    const int i = tid + u * SK_THREADS;
+                    const int m = i / (TPS * 16), c8 = i % (TPS * 16);
+                    if (i < TOT) *reinterpret_cast<u32x4_t *>(xl + m * RS + c8 * 8) = v[u];
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < 2 * TPS * MP; i += SK_THREADS) {
+                const int g = i / MP, m = i % MP;
+                const uint4 *rr = reinterpret_cast<const uint4 *>(xl + m * RS + g * 64);
+                float sum = 0.f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint4 w = rr[q];
+                    sum += bf16_lo(w.x) + bf16_hi(w.x) + bf16_lo(w.y) + bf16_hi(w.y) + bf16_lo(w.z) +
+                           bf16_hi(w.z) + bf16_lo(w.w) + bf16_hi(w.w);
+                }
+                xs[i] = sum;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                // this iteration's RPI rowblocks, TPS tiles each
+                u32x4_t c[TPS][RPI];
+                u32x2_t sb[TPS][RPI];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < RPI; ++r) {
+                    const int rb = min(ub + (i * SK_WAVES + wave) * RPI + r, u1 - 1);
+                    const __amdgpu_buffer_rsrc_t rs =
+                        make_rsrc(uniform_ptr(it.packed + ((size_t)rb * P + p0) * Q4_TILE_BYTES),
+                                  (unsigned)pn * Q4_TILE_BYTES);
+#pragma unroll
+                    for (int j = 0; j < TPS; ++j) {
+                        const unsigned to = (unsigned)min(j, pn - 1) * Q4_TILE_BYTES;
+                        c[j][r] = buf_ld_x4(rs, lc, to);
+                        sb[j][r] = buf_ld_x2(rs, ls, to);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < TPS; ++j) {
+                    // one tile's operands live at a time (the scheduler would
+                    // otherwise hoist every tile's LDS reads and spill)
+                    __builtin_amdgcn_sched_barrier(0);
+                    bf16x8_t A[MT][4];
+                    f32x4_t xs0[MT], xs1[MT];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint16_t *ar = xl + (16 * mt + (lane & 15)) * RS + j * 128 + 8 * kg;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            A[mt][q] = *reinterpret_cast<const bf16x8_t *>(ar + 32 * q);
+                        xs0[mt] = *reinterpret_cast<const f32x4_t *>(xs + (2 * j) * MP + 16 * mt + 4 * kg);
+                        xs1[mt] = *reinterpret_cast<const f32x4_t *>(xs + (2 * j + 1) * MP + 16 * mt + 4 * kg);
+                    }
+#pragma unroll
+                    for (int r = 0; r < RPI; ++r) {
                         bf16x8_t B[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) B[q] = q4_word_to_bf16x8(c[j][r][q], magic);
+                        for (int q = 0; q < 4; ++q) B[q] = q4_word_to_bf16x8(c[j][r][q], kq);
                         const float s0 = f16_lo(sb[j][r][0]), b0 = f16_hi(sb[j][r][0]);
                         const float s1 = f16_lo(sb[j][r][1]), b1 = f16_hi(sb[j][r][1]);
                         const float bb0 = fmaf(-128.f, s0, b0), bb1 = fmaf(-128.f, s1, b1);
@@ -126,69 +152,75 @@ __device__ __forceinline__ void sk_q4_unit(const WorkItem &it, int unit, int M, 
                             C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][2], B[2], C1, 0, 0, 0);
                             C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][3], B[3], C1, 0, 0, 0);
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                float a = acc[r][mt][i];
-                                a = fmaf(s0, C0[i], a);
-                                a = fmaf(bb0, xs0[mt][i], a);
-                                a = fmaf(s1, C1[i], a);
-                                a = fmaf(bb1, xs1[mt][i], a);
-                                acc[r][mt][i] = a;
+                            for (int e = 0; e < 4; ++e) {
+                                float a = acc[i][r][mt][e];
+                                a = fmaf(s0, C0[e], a);
+                                a = fmaf(bb0, xs0[mt][e], a);
+                                a = fmaf(s1, C1[e], a);
+                                a = fmaf(bb1, xs1[mt][e], a);
+                                acc[i][r][mt][e] = a;
                             }
                         }
                     }
                 }
             }
         }
-    }
+        // the block's outputs: each wave stores its own rowblocks
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const int n = (rb0 + r) * RB + (lane & 15);
-        if (rb0 + r < nrb && n < N) {
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int r = 0; r < RPI; ++r) {
+                const int rb = ub + (i * SK_WAVES + wave) * RPI + r;
+                const int n = rb * RB + (lane & 15);
+                if (rb < u1 && n < N) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = 16 * mt + 4 * kg + i;
-                    if (m < M) {
-                        if (it.out_f32)
-                            reinterpret_cast<float *>(it.y)[(size_t)m * N + n] = acc[r][mt][i];
-                        else
-                            reinterpret_cast<uint16_t *>(it.y)[(size_t)m * N + n] =
-                                f32_to_bf16(acc[r][mt][i]);
-                    }
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = 16 * mt + 4 * kg + e;
+                            if (m < M) {
+                                if (it.out_f32)
+                                    reinterpret_cast<float *>(it.y)[(size_t)m * N + n] = acc[i][r][mt][e];
+                                else
+                                    reinterpret_cast<uint16_t *>(it.y)[(size_t)m * N + n] =
+                                        f32_to_bf16(acc[i][r][mt][e]);
+                            }
+                        }
                 }
-        }
+            }
     }
 }
 
-template <int MT, int KC, int RPW>
-__global__ void __launch_bounds__(SK_THREADS)
+// <MT, TPS, RPI, NI, workgroups per CU>.  M <= 16: one 16-row tile, 8 tiles
+// (1024 k) per segment, blocks of 24 rowblocks, 166 VGPRs (3 workgroups per
+// CU); M <= 32: two 16-row tiles, 4 tiles per segment, blocks of 16
+// rowblocks, 2 workgroups per CU.  Both stage 33 KB of X per segment; the
+// register budgets are the largest that compile without spilling.
+#define SK_M16 1, 8, 1, 6, 3
+#define SK_M32 2, 4, 1, 4, 2
+
+template <int MT, int TPS, int RPI, int NI, int WPC>
+__global__ void __launch_bounds__(SK_THREADS, WPC)
 q4_skinny_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
                  WorkItem single, int M) {
-    constexpr int MP = MT * 16;
-    constexpr int RS = KC * 128 + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t xl[MP * RS];
-    __shared__ __attribute__((aligned(16))) float xs[2 * KC * MP];  // [group-in-chunk][m]
+    typedef SkCfg<MT, TPS, RPI, NI> C;
+    __shared__ __attribute__((aligned(16))) uint16_t xl[C::MP * C::RS];
+    __shared__ __attribute__((aligned(16))) float xs[2 * TPS * C::MP];  // [group-in-segment][m]
     const int tid = threadIdx.x;
-    const Q4Consts magic = q4_consts();
+    const Q4Consts kq = q4_consts();
     if (items == nullptr) {
-        for (int u = blockIdx.x; u < single.units; u += gridDim.x)
-            sk_q4_unit<MT, KC, RPW>(single, u, M, xl, xs, tid, magic);
+        const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
+        const int u0 = (int)(j * n / g), u1 = (int)((j + 1) * n / g);
+        if (u0 < u1) sk_q4_range<MT, TPS, RPI, NI>(single, u0, u1, M, xl, xs, tid, kq);
         return;
     }
     const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
-    int i = s.item, u = s.unit, loaded = -1;
-    WorkItem it;
-    while (i < e.item || (i == e.item && u < e.unit)) {
-        if (i != loaded) {
-            it = items[i];
-            loaded = i;
-        }
-        sk_q4_unit<MT, KC, RPW>(it, u, M, xl, xs, tid, magic);
-        if (++u == it.units) {
-            ++i;
-            u = 0;
-        }
+#pragma unroll 1
+    for (int i = s.item; i < e.item || (i == e.item && e.unit > 0); ++i) {
+        const WorkItem it = items[i];
+        const int u0 = (i == s.item) ? s.unit : 0;
+        const int u1 = (i == e.item) ? e.unit : it.units;
+        if (u0 < u1) sk_q4_range<MT, TPS, RPI, NI>(it, u0, u1, M, xl, xs, tid, kq);
     }
 }
 
@@ -301,11 +333,9 @@ q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ 
     }
 }
 
-static inline int sk_units(int64_t N, int rowblocks_per_unit) {
-    return (int)ceil_div(ceil_div(N, RB), rowblocks_per_unit);
-}
-
 static inline int min_grid(int units, int cap) { return units < cap ? units : cap; }
+
+int q4_skinny_wgs_per_cu(int64_t M) { return M <= 16 ? 3 : 2; }
 
 hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y, int64_t M,
                             int64_t N, int64_t K, bool out_f32, int cus, hipStream_t s) {
@@ -316,18 +346,16 @@ hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y, i
     it.N = (int32_t)N;
     it.K = (int32_t)K;
     it.P = (int32_t)ceil_div(K, Q4_TILE_K);
+    it.units = (int32_t)ceil_div(N, RB);
     it.out_f32 = out_f32 ? 1 : 0;
-    if (M <= 16) {
-        it.units = sk_units(N, SK_ROWBLOCKS_M16);
-        hipLaunchKernelGGL((q4_skinny_kernel<1, 8, SK_ROWBLOCKS_M16 / SK_WAVES>),
-                           dim3(min_grid(it.units, cus * 4)), dim3(SK_THREADS), 0, s,
+    // blocks of 32 rowblocks unless that leaves CUs idle
+    const int grid = min_grid((int)ceil_div(it.units, 8), cus * q4_skinny_wgs_per_cu(M));
+    if (M <= 16)
+        hipLaunchKernelGGL((q4_skinny_kernel<SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s,
                            (const WorkItem *)nullptr, (const WorkStart *)nullptr, it, (int)M);
-    } else {
-        it.units = sk_units(N, SK_ROWBLOCKS_M32);
-        hipLaunchKernelGGL((q4_skinny_kernel<2, 4, SK_ROWBLOCKS_M32 / SK_WAVES>),
-                           dim3(min_grid(it.units, cus * 4)), dim3(SK_THREADS), 0, s,
+    else
+        hipLaunchKernelGGL((q4_skinny_kernel<SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s,
                            (const WorkItem *)nullptr, (const WorkStart *)nullptr, it, (int)M);
-    }
     return hipGetLastError();
 }
 
@@ -335,11 +363,11 @@ hipError_t launch_q4_skinny_list(const WorkItem *items, const WorkStart *starts,
                                  int64_t M, hipStream_t s) {
     WorkItem none{};
     if (M <= 16)
-        hipLaunchKernelGGL((q4_skinny_kernel<1, 8, SK_ROWBLOCKS_M16 / SK_WAVES>), dim3(grid),
-                           dim3(SK_THREADS), 0, s, items, starts, none, (int)M);
+        hipLaunchKernelGGL((q4_skinny_kernel<SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s, items,
+                           starts, none, (int)M);
     else
-        hipLaunchKernelGGL((q4_skinny_kernel<2, 4, SK_ROWBLOCKS_M32 / SK_WAVES>), dim3(grid),
-                           dim3(SK_THREADS), 0, s, items, starts, none, (int)M);
+        hipLaunchKernelGGL((q4_skinny_kernel<SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s, items,
+                           starts, none, (int)M);
     return hipGetLastError();
 }
 

@@ -70,6 +70,13 @@ def build_decode_step(seed: int = 0, layers: int = synth.DECODE_LAYERS, device="
     return step
 
 
+def verification_tile(seed: int, g: Gemv, M: int, device="cuda"):
+    """The M-row bf16 activation tile of one projection for a verification
+    pass (seeded per projection, independent of the M = 1 vector)."""
+    import torch
+    return weights.to_device(synth.activations(seed + 1, M, g.K, item=g.item), device).view(torch.bfloat16)
+
+
 def run_step_eager(step: DecodeStep, stream=None):
     """One decode step: every GEMV of the step enqueued on the stream."""
     for g in step.gemvs:
