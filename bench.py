@@ -57,6 +57,86 @@ def traffic_from_profiles(kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+STEP_KERNEL = "q4_gemv_kernel<true>"
+COPY_BYTES = 1 << 30
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(names)
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, command: str):
+    """Turn two rocprofv3 --pmc CSVs (FETCH_SIZE, then WRITE_SIZE) of a
+    --traffic-pass run into HBM bytes per launch of the decode-step kernel,
+    each counter scaled by what it reads for the plain 1 GiB copy."""
+    def per_kernel(path, counter):
+        vals = {}
+        for r in _csv_rows(path):
+            if _col(r, "Counter_Name", "counter_name") != counter:
+                continue
+            name = _col(r, "Kernel_Name", "kernel_name")
+            vals.setdefault(name, []).append(float(_col(r, "Counter_Value", "counter_value")))
+        return vals
+
+    def pick(vals, pred):
+        keys = [k for k in vals if pred(k)]
+        if not keys:
+            raise SystemExit("kernel not found in counters: %s" % sorted(vals))
+        v = vals[keys[0]]
+        return sum(v) / len(v), keys[0]
+
+    def pick_copy(vals):
+        # the calibration copy is the largest copy dispatch of the pass (the
+        # input uploads also run small copy kernels)
+        best = None
+        for k, v in vals.items():
+            if "copy" in k.lower() or "elementwise" in k.lower():
+                m = max(v)
+                if best is None or m > best[0]:
+                    best = (m, k)
+        if best is None:
+            raise SystemExit("copy kernel not found in counters")
+        return best
+
+    out = {"command": command, "kernel_source_hash": kernel_source_hash()}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        step_kib, step_name = pick(vals, lambda k: STEP_KERNEL in k)
+        copy_kib, copy_name = pick_copy(vals)
+        factor = copy_kib * 1024 / COPY_BYTES
+        out[counter] = {"step_kernel": step_name, "step_kib_per_dispatch": step_kib,
+                        "copy_kernel": copy_name, "copy_kib_per_dispatch": copy_kib,
+                        "copy_factor": factor, "step_bytes_scaled": step_kib * 1024 / factor}
+    out["hbm_bytes_per_launch"] = int(out["FETCH_SIZE"]["step_bytes_scaled"] +
+                                      out["WRITE_SIZE"]["step_bytes_scaled"])
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def summarize_trace(stats_csv: str, command: str):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    rows = _csv_rows(stats_csv)
+    print("Command: `%s`\n" % command)
+    print("| kernel | calls | average (us) | min (us) | max (us) | share |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        name = _col(r, "Name", "KernelName", "Kernel_Name")
+        print("| `%s` | %s | %.2f | %.2f | %.2f | %.2f%% |" % (
+            name[:90], _col(r, "Calls"), float(_col(r, "AverageNs")) / 1e3,
+            float(_col(r, "MinNs")) / 1e3, float(_col(r, "MaxNs")) / 1e3,
+            float(_col(r, "Percentage"))))
+
+
 def cpu_baseline(step, budget_s: float):
     """The oracle, as it stands, on the first GEMVs of the step until the time
     budget is spent (one thread; input generation is not timed)."""
@@ -94,7 +174,18 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m16", action="store_true")
+    ap.add_argument("--traffic-pass", action="store_true",
+                    help="run one decode step and one plain 1 GiB copy, for counter collection")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV")
+    ap.add_argument("--command", default="", help="command line recorded in summaries")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, command=args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.command)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -122,6 +213,15 @@ def main():
     plan = pkg.qg_batch_plan_build(Q4, 1, [(g.packed, g.N, g.K, g.x, g.y) for g in step.gemvs])
     torch.cuda.synchronize()
     log("plan: grid %d workgroups" % plan.grid)
+    if args.traffic_pass:
+        pkg.qg_batch_run(plan)
+        torch.cuda.synchronize()
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("traffic pass: one decode step, one %d-byte copy" % COPY_BYTES)
+        return
     for _ in range(args.warmup):
         pkg.qg_batch_run(plan)
     torch.cuda.synchronize()

@@ -210,6 +210,9 @@ __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, con
 }
 
 // at most 95 VGPRs: 5 waves per SIMD, 5 workgroups of 4 waves per CU
+// LIST = false: one matrix (`single`); LIST = true: the work list.  Two
+// instantiations, so profiles tell a whole decode step from single GEMVs.
+template <bool LIST>
 __global__ void __launch_bounds__(GV_THREADS, GV_WGS_PER_CU)
 q4_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
                WorkItem single) {
@@ -222,7 +225,7 @@ q4_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Q4Consts magic = q4_consts();
     int par = 0;
-    if (items == nullptr) {
+    if (!LIST) {
         // single matrix: a contiguous share of the rowblocks per workgroup
         const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
         gv_range(single, (int)(j * n / g), (int)((j + 1) * n / g), L, tid, lane, wave, magic, par);
@@ -250,7 +253,7 @@ hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int
     it.units = (int32_t)ceil_div(N, RB);
     it.out_f32 = out_f32 ? 1 : 0;
     const int grid = (int)(it.units < (int64_t)cus * GV_WGS_PER_CU ? it.units : (int64_t)cus * GV_WGS_PER_CU);
-    hipLaunchKernelGGL(q4_gemv_kernel, dim3(grid), dim3(GV_THREADS), q4_gemv_lds_bytes(K), s,
+    hipLaunchKernelGGL(q4_gemv_kernel<false>, dim3(grid), dim3(GV_THREADS), q4_gemv_lds_bytes(K), s,
                        (const WorkItem *)nullptr, (const WorkStart *)nullptr, it);
     return hipGetLastError();
 }
@@ -258,7 +261,7 @@ hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts, int grid,
                                int64_t kmax, hipStream_t s) {
     WorkItem none{};
-    hipLaunchKernelGGL(q4_gemv_kernel, dim3(grid), dim3(GV_THREADS), q4_gemv_lds_bytes(kmax), s,
+    hipLaunchKernelGGL(q4_gemv_kernel<true>, dim3(grid), dim3(GV_THREADS), q4_gemv_lds_bytes(kmax), s,
                        items, starts, none);
     return hipGetLastError();
 }

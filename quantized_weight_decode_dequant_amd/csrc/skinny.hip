@@ -199,7 +199,7 @@ __device__ __forceinline__ void sk_q4_range(const WorkItem &it, int u0, int u1, 
 #define SK_M16 1, 8, 1, 6, 3
 #define SK_M32 2, 4, 1, 4, 2
 
-template <int MT, int TPS, int RPI, int NI, int WPC>
+template <bool LIST, int MT, int TPS, int RPI, int NI, int WPC>
 __global__ void __launch_bounds__(SK_THREADS, WPC)
 q4_skinny_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
                  WorkItem single, int M) {
@@ -208,7 +208,7 @@ q4_skinny_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict
     __shared__ __attribute__((aligned(16))) float xs[2 * TPS * C::MP];  // [group-in-segment][m]
     const int tid = threadIdx.x;
     const Q4Consts kq = q4_consts();
-    if (items == nullptr) {
+    if (!LIST) {
         const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
         const int u0 = (int)(j * n / g), u1 = (int)((j + 1) * n / g);
         if (u0 < u1) sk_q4_range<MT, TPS, RPI, NI>(single, u0, u1, M, xl, xs, tid, kq);
@@ -351,10 +351,10 @@ hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y, i
     // blocks of 32 rowblocks unless that leaves CUs idle
     const int grid = min_grid((int)ceil_div(it.units, 8), cus * q4_skinny_wgs_per_cu(M));
     if (M <= 16)
-        hipLaunchKernelGGL((q4_skinny_kernel<SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s,
+        hipLaunchKernelGGL((q4_skinny_kernel<false, SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s,
                            (const WorkItem *)nullptr, (const WorkStart *)nullptr, it, (int)M);
     else
-        hipLaunchKernelGGL((q4_skinny_kernel<SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s,
+        hipLaunchKernelGGL((q4_skinny_kernel<false, SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s,
                            (const WorkItem *)nullptr, (const WorkStart *)nullptr, it, (int)M);
     return hipGetLastError();
 }
@@ -363,10 +363,10 @@ hipError_t launch_q4_skinny_list(const WorkItem *items, const WorkStart *starts,
                                  int64_t M, hipStream_t s) {
     WorkItem none{};
     if (M <= 16)
-        hipLaunchKernelGGL((q4_skinny_kernel<SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s, items,
+        hipLaunchKernelGGL((q4_skinny_kernel<true, SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s, items,
                            starts, none, (int)M);
     else
-        hipLaunchKernelGGL((q4_skinny_kernel<SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s, items,
+        hipLaunchKernelGGL((q4_skinny_kernel<true, SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s, items,
                            starts, none, (int)M);
     return hipGetLastError();
 }
