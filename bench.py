@@ -174,6 +174,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m16", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the single-GEMV, int8 and MoE workloads")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="run one decode step and one plain 1 GiB copy, for counter collection")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
@@ -324,6 +326,61 @@ def main():
             }
             log("m%d pass: %.3f ms" % (M, msM))
             del planM, Xs, Ys
+
+    # ---- the other workloads of the hot path, each against its own bytes
+    if not args.no_extras:
+        # single 4096 x 4096 GEMV (qgemv_run), the 72 distinct q/o matrices of
+        # the step back to back (680 MB, larger than the last-level cache)
+        sq = [g for g in step.gemvs if g.N == 4096 and g.K == 4096]
+        it_sq = [0]
+
+        def one_gemv():
+            g = sq[it_sq[0] % len(sq)]
+            it_sq[0] += 1
+            pkg.qgemv_run(Q4, g.packed, g.N, g.K, g.x, g.y)
+
+        ms1 = workloads.time_ms(one_gemv, 4 * len(sq))
+        b1 = roofline.q4_gemm_bytes(1, 4096, 4096)
+        result["single_gemv"] = {
+            "workload": "4-bit g64 GEMV 4096x4096, M=1, one qgemv_run launch each, %d distinct "
+                        "matrices back to back" % len(sq),
+            "us_per_gemv": round(ms1 * 1e3, 3),
+            "value": round(b1 / (ms1 * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "pct_of_peak": round(100 * b1 / (ms1 * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2)}
+        log("single gemv: %.2f us" % (ms1 * 1e3))
+
+        # 8-bit symmetric group-32 verification, M = 16, both projection shapes
+        i8 = {}
+        for N, K in ((12288, 4096), (4096, 12288)):
+            wl = workloads.Int8Verify(args.seed, N, K)
+            msq = workloads.time_ms(wl.quantize, 50)
+            msg = workloads.time_ms(wl.gemm, 4 * len(wl.packed))
+            bq = roofline.hadamard_quant_bytes(16, K)
+            bg = roofline.q8_gemm_bytes(16, N, K)
+            i8["%dx%d" % (K, N)] = {
+                "hadamard_quant_us": round(msq * 1e3, 3),
+                "hadamard_quant_GBs": round(bq / (msq * 1e-3) / 1e9, 2),
+                "gemm_us": round(msg * 1e3, 3),
+                "gemm_GBs": round(bg / (msg * 1e-3) / 1e9, 2),
+                "gemm_pct_of_peak": round(100 * bg / (msg * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2)}
+            log("int8 %dx%d: hadamard %.2f us, gemm %.2f us" % (K, N, msq * 1e3, msg * 1e3))
+            del wl
+        result["int8_verify"] = dict(i8, workload="8-bit sym g32 weights, M=16 activations "
+                                     "(1 percent x20 outliers) rotated by randomized Hadamard-32 and "
+                                     "quantized to int8; %d copies of each matrix" % 40)
+
+        # MXFP4 routed experts, one token through one layer
+        moe = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16)
+        msm = workloads.time_ms(moe.run, 64)
+        bm = roofline.moe_token_bytes(16, 7168, 2048)
+        result["moe"] = {
+            "workload": "MXFP4 MoE layer, 384 experts, hidden 7168, expert FFN 2048, top-16 "
+                        "(a different seeded route per call), M=1",
+            "us_per_token_layer": round(msm * 1e3, 3),
+            "value": round(bm / (msm * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "pct_of_peak": round(100 * bm / (msm * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2)}
+        log("moe: %.2f us" % (msm * 1e3))
+        del moe
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_budget)

@@ -104,3 +104,91 @@ def capture_graph(fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def time_ms(fn, iters: int, warmup: int = 2) -> float:
+    """Mean milliseconds per call of fn() on the current stream (HIP events
+    around the whole loop, so back-to-back launch gaps are included)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+class Int8Verify:
+    """The 8-bit verification workload: a 16-row activation tile rotated and
+    quantized to int8, then multiplied with 8-bit symmetric group-32 weights.
+    The packed matrix is replicated `copies` times at distinct addresses so
+    consecutive calls stream from HBM, not from the 256 MB last-level cache."""
+
+    def __init__(self, seed: int, N: int, K: int, M: int = 16, copies: int = 40, device="cuda"):
+        import torch
+        self.N, self.K, self.M = N, K, M
+        w = synth.q8_matrix(seed, N, K)
+        base = weights.pack_q8(w, device)
+        self.packed = [base] + [base.clone() for _ in range(copies - 1)]
+        self.X = weights.to_device(synth.q8_activations(seed, M, K), device)
+        self.signs = weights.to_device(synth.rotation_signs(seed, K), device)
+        self.Xq = torch.empty((M, K), dtype=torch.int8, device=device)
+        self.sx = torch.empty(M, dtype=torch.float32, device=device)
+        self.Y = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+        self.i = 0
+
+    def quantize(self):
+        _lib.hadamard32_quant_run(self.X, self.signs, self.M, self.K, self.Xq, self.sx)
+
+    def gemm(self):
+        p = self.packed[self.i % len(self.packed)]
+        self.i += 1
+        _lib.qgemm_skinny_run(_lib.FMT_Q8_SYM_G32, p, self.M, self.N, self.K, self.Xq, self.sx,
+                              Y=self.Y)
+
+
+class MoeLayer:
+    """One routed-expert MoE layer in MXFP4 (E experts, hidden H, expert FFN
+    F): the whole pool packed on the device, codes uniform over the 16 E2M1
+    codes and E8M0 scales uniform in 118..128, drawn with a seeded device
+    generator; `routes` seeded router draws (top_k of E, softmax weights), a
+    different one per call so the selected experts change between calls."""
+
+    def __init__(self, seed: int, E: int, H: int, F: int, top_k: int, routes: int = 64,
+                 device="cuda"):
+        import numpy as np
+        import torch
+        self.E, self.H, self.F, self.top_k = E, H, F, top_k
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+
+        def stack(rows, K):
+            codes = torch.randint(0, 256, (E * rows, K // 2), dtype=torch.uint8, device=device,
+                                  generator=g)
+            scales = torch.randint(118, 129, (E * rows, K // 32), dtype=torch.uint8,
+                                   device=device, generator=g)
+            out = _lib.qgemv_pack(_lib.FMT_MXFP4_G32, E * rows, K, codes, scales)
+            del codes, scales
+            return out
+
+        self.gate = stack(F, H)
+        self.up = stack(F, H)
+        self.down = stack(H, F)
+        ids, ws = zip(*[synth.router(seed, E, top_k, item=r) for r in range(routes)])
+        self.ids = weights.to_device(np.stack(ids), device)
+        self.w = weights.to_device(np.stack(ws), device)
+        self.x = weights.to_device(synth.moe_token(seed, H), device)
+        self.workspace = torch.empty(_lib.moe_workspace_bytes(top_k, H, F), dtype=torch.uint8,
+                                     device=device)
+        self.y = torch.empty(H, dtype=torch.bfloat16, device=device)
+        self.i = 0
+
+    def run(self):
+        r = self.i % self.ids.shape[0]
+        self.i += 1
+        _lib.moe_expert_gemv_run(self.gate, self.up, self.down, self.E, self.H, self.F, self.x,
+                                 self.ids[r], self.w[r], workspace=self.workspace, y=self.y)
