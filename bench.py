@@ -339,11 +339,11 @@ def main():
             it_sq[0] += 1
             pkg.qgemv_run(Q4, g.packed, g.N, g.K, g.x, g.y)
 
-        ms1 = workloads.time_ms(one_gemv, 4 * len(sq))
+        ms1 = workloads.time_graph_ms(one_gemv, len(sq))
         b1 = roofline.q4_gemm_bytes(1, 4096, 4096)
         result["single_gemv"] = {
             "workload": "4-bit g64 GEMV 4096x4096, M=1, one qgemv_run launch each, %d distinct "
-                        "matrices back to back" % len(sq),
+                        "matrices back to back (captured in a HIP graph)" % len(sq),
             "us_per_gemv": round(ms1 * 1e3, 3),
             "value": round(b1 / (ms1 * 1e-3) / 1e9, 2), "unit": "GB/s",
             "pct_of_peak": round(100 * b1 / (ms1 * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2)}
@@ -353,8 +353,8 @@ def main():
         i8 = {}
         for N, K in ((12288, 4096), (4096, 12288)):
             wl = workloads.Int8Verify(args.seed, N, K)
-            msq = workloads.time_ms(wl.quantize, 50)
-            msg = workloads.time_ms(wl.gemm, 4 * len(wl.packed))
+            msq = workloads.time_graph_ms(wl.quantize, 40)
+            msg = workloads.time_graph_ms(wl.gemm, len(wl.packed))
             bq = roofline.hadamard_quant_bytes(16, K)
             bg = roofline.q8_gemm_bytes(16, N, K)
             i8["%dx%d" % (K, N)] = {
@@ -367,15 +367,15 @@ def main():
             del wl
         result["int8_verify"] = dict(i8, workload="8-bit sym g32 weights, M=16 activations "
                                      "(1 percent x20 outliers) rotated by randomized Hadamard-32 and "
-                                     "quantized to int8; %d copies of each matrix" % 40)
+                                     "quantized to int8; %d copies of each matrix; calls captured in a HIP graph" % 40)
 
         # MXFP4 routed experts, one token through one layer
         moe = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16)
-        msm = workloads.time_ms(moe.run, 64)
+        msm = workloads.time_graph_ms(moe.run, 64)
         bm = roofline.moe_token_bytes(16, 7168, 2048)
         result["moe"] = {
             "workload": "MXFP4 MoE layer, 384 experts, hidden 7168, expert FFN 2048, top-16 "
-                        "(a different seeded route per call), M=1",
+                        "(a different seeded route per call), M=1; calls captured in a HIP graph",
             "us_per_token_layer": round(msm * 1e3, 3),
             "value": round(bm / (msm * 1e-3) / 1e9, 2), "unit": "GB/s",
             "pct_of_peak": round(100 * bm / (msm * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2)}

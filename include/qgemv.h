@@ -171,8 +171,8 @@ int qgemm_skinny_run(int fmt, const void *packed, size_t packed_bytes,
  * orthonormal rotation z / sqrt(32).  A zero row gives Xq = 0, scale 0.
  *
  *  X            device bf16 [M][K], 16-B.  Read only.
- *  signs        device int8 [K], each +1 or -1 (other values are used as
- *               given).  Read only.
+ *  signs        device int8 [K], 16-B, each +1 or -1 (other values are used
+ *               as given).  Read only.
  *  M, K         M >= 0, K a positive multiple of 32.
  *  Xq           device int8 [M][K], 16-B, written.
  *  x_scales     device fp32 [M], written.

@@ -203,7 +203,8 @@ int hadamard32_quant_run(const void *X, const int8_t *signs, int64_t M, int64_t 
     try {
         if (!X || !signs || !Xq || !x_scales) return QG_EINVAL;
         if (M < 0 || M > N_MAX || K <= 0 || K > K_MAX || K % 32 != 0) return QG_ESHAPE;
-        if (!aligned(X, 16) || !aligned(Xq, 16) || !aligned(x_scales, 4)) return QG_EALIGN;
+        if (!aligned(X, 16) || !aligned(signs, 16) || !aligned(Xq, 16) || !aligned(x_scales, 4))
+            return QG_EALIGN;
         if (M == 0) return QG_OK;
         // 127 * sqrt(32): the Hadamard's global 1/sqrt(32) folded into the scale
         const double denom = 127.0 * std::sqrt(32.0);

@@ -1,22 +1,19 @@
-// Skinny products Y[M, N] = X[M, K] W^T for M = 1..32 activation rows against
-// weights streamed once per call: the verification pass of a 16-32 token
-// draft (Uzu page, fange-kb.cn, section "Producing several tokens from one
-// model pass": sixteen candidate rows give the matrix units sixteen rows of
-// work instead of one).  Both kernels run on the gfx950 MFMA units with the
-// 16x16x32 shapes, whose B operand (lane l: 8 consecutive k of column l & 15,
-// k-slice l >> 4) is exactly one packed weight slot (see qg_internal.h).
-//
-// Q4 (bf16 X): each packed word becomes the bf16x8 operand (128 + q); one
+// Skinny Q4 products Y[M, N] = X[M, K] W^T for M = 1..32 bf16 activation
+// rows against weights streamed once per call: the verification pass of a
+// 16-32 token draft (Uzu page, fange-kb.cn, section "Producing several tokens
+// from one model pass": sixteen candidate rows give the matrix units sixteen
+// rows of work instead of one).  The kernel runs on the gfx950 MFMA units
+// with the 16x16x32 bf16 shape, whose B operand (lane l: 8 consecutive k of
+// column l & 15, k-slice l >> 4) is exactly one packed weight slot (see
+// qg_internal.h): each packed word becomes the bf16x8 operand (128 + q); one
 // MFMA pair covers one group of 64, its fp32 result is scaled per (row n,
 // group) on the VALU: acc += s * C + (b - 128 s) * sum_{k in g} X[m, k].
-// Q8 (int8 X from the Hadamard quantizer): one i8 MFMA per group of 32 gives
-// the exact int32 group partial; acc += sw * float(partial) (exact
-// conversion, |partial| <= 32 * 127^2), then y = sx[m] * acc.
 //
 // The X slices staged in LDS have rows padded by 16 bytes so the 16
-// A-operand rows of one MFMA hit distinct banks.  The Q4 kernel also runs
-// over a device work list of independent matrices (one launch for a whole
-// verification pass); see sk_q4_range for its work split.
+// A-operand rows of one MFMA hit distinct banks.  The kernel also runs over
+// a device work list of independent matrices (one launch for a whole
+// verification pass); see sk_q4_range for its work split.  The int8 path
+// lives in q8_skinny.hip.
 #include "qg_internal.h"
 
 namespace qg {
@@ -224,115 +221,6 @@ q4_skinny_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict
     }
 }
 
-// out_mode: 0 = bf16, 1 = fp32, 2 = int32 group partials [M][N][K/32]
-template <int MT, int KC>
-__global__ void __launch_bounds__(SK_THREADS)
-q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ X,
-                 const float *__restrict__ x_scales, void *__restrict__ Y, int M, int N, int K,
-                 int P, int nrb, int out_mode) {
-    constexpr int MP = MT * 16;
-    constexpr int RS = KC * 128 + 16;  // LDS row stride in bytes
-    __shared__ __attribute__((aligned(16))) int8_t xl[MP * RS];
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
-    const int G = K / 32;
-    const int items = (nrb + SK_WAVES - 1) / SK_WAVES;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int rb = item * SK_WAVES + wave;
-        const bool active = rb < nrb;
-        const uint8_t *base = packed + (size_t)(active ? rb : nrb - 1) * P * Q8_TILE_BYTES;
-        const int n = rb * RB + (lane & 15);
-        f32x4_t acc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int pc = 0; pc < P; pc += KC) {
-            const int nt = min(KC, P - pc);
-            u32x4_t c0[KC], c1[KC];
-            u32x2_t sc[KC];
-#pragma unroll
-            for (int j = 0; j < KC; ++j) {
-                const uint8_t *tb = base + (size_t)min(pc + j, P - 1) * Q8_TILE_BYTES;
-                c0[j] = ld_nt(reinterpret_cast<const u32x4_t *>(tb) + lane);
-                c1[j] = ld_nt(reinterpret_cast<const u32x4_t *>(tb + 1024) + lane);
-                sc[j] = ld_nt(reinterpret_cast<const u32x2_t *>(tb + 2048) + (lane & 15));
-            }
-            __syncthreads();
-            {
-                constexpr int TOT = MP * KC * 8;  // uint4 per chunk
-                constexpr int U = (TOT + SK_THREADS - 1) / SK_THREADS;
-                const int k0 = pc * 128;
-                uint4 v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = tid + u * SK_THREADS;
-                    const int m = i / (KC * 8), c16 = i % (KC * 8);
-                    const int k = k0 + c16 * 16;
-                    v[u] = (i < TOT && m < M && k < K)
-                               ? *reinterpret_cast<const uint4 *>(X + (size_t)m * K + k)
-                               : make_uint4(0u, 0u, 0u, 0u);
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = tid + u * SK_THREADS;
-                    const int m = i / (KC * 8), c16 = i % (KC * 8);
-                    if (i < TOT) *reinterpret_cast<uint4 *>(xl + m * RS + c16 * 16) = v[u];
-                }
-            }
-            __syncthreads();
-            if (active) {
-#pragma unroll
-                for (int j = 0; j < KC; ++j) {
-                    if (j < nt) {
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4) {
-                            const u32x4_t ch = (g4 < 2) ? c0[j] : c1[j];
-                            const int gg = g4 & 1;
-                            const long bop = (long)(((unsigned long)ch[2 * gg + 1] << 32) | ch[2 * gg]);
-                            const unsigned swbits = (g4 < 2) ? sc[j][0] : sc[j][1];
-                            const float sw = (g4 & 1) ? f16_hi(swbits) : f16_lo(swbits);
-                            const int g = (pc + j) * 4 + g4;
-#pragma unroll
-                            for (int mt = 0; mt < MT; ++mt) {
-                                const int8_t *ar = xl + (16 * mt + (lane & 15)) * RS + j * 128 + 32 * g4 + 8 * kg;
-                                const long aop = *reinterpret_cast<const long *>(ar);
-                                i32x4_t C = {0, 0, 0, 0};
-                                C = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, C, 0, 0, 0);
-                                if (out_mode == 2) {
-                                    if (g < G) {
-#pragma unroll
-                                        for (int i = 0; i < 4; ++i) {
-                                            const int m = 16 * mt + 4 * kg + i;
-                                            if (m < M && n < N)
-                                                reinterpret_cast<int32_t *>(Y)[((size_t)m * N + n) * G + g] = C[i];
-                                        }
-                                    }
-                                } else {
-#pragma unroll
-                                    for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sw, (float)C[i], acc[mt][i]);
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-        }
-        if (active && out_mode != 2) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = 16 * mt + 4 * kg + i;
-                    if (m < M && n < N) {
-                        const float v = x_scales[m] * acc[mt][i];
-                        if (out_mode == 1)
-                            reinterpret_cast<float *>(Y)[(size_t)m * N + n] = v;
-                        else
-                            reinterpret_cast<uint16_t *>(Y)[(size_t)m * N + n] = f32_to_bf16(v);
-                    }
-                }
-        }
-    }
-}
-
 static inline int min_grid(int units, int cap) { return units < cap ? units : cap; }
 
 int q4_skinny_wgs_per_cu(int64_t M) { return M <= 16 ? 3 : 2; }
@@ -368,22 +256,6 @@ hipError_t launch_q4_skinny_list(const WorkItem *items, const WorkStart *starts,
     else
         hipLaunchKernelGGL((q4_skinny_kernel<true, SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s, items,
                            starts, none, (int)M);
-    return hipGetLastError();
-}
-
-hipError_t launch_q8_skinny(const uint8_t *packed, const int8_t *X, const float *x_scales,
-                            void *Y, int64_t M, int64_t N, int64_t K, int out_mode, int cus,
-                            hipStream_t s) {
-    const int P = (int)ceil_div(K, Q8_TILE_K);
-    const int nrb = (int)ceil_div(N, RB);
-    const int units = (nrb + SK_WAVES - 1) / SK_WAVES;
-    if (M <= 16) {
-        hipLaunchKernelGGL((q8_skinny_kernel<1, 8>), dim3(min_grid(units, cus * 4)), dim3(SK_THREADS),
-                           0, s, packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, out_mode);
-    } else {
-        hipLaunchKernelGGL((q8_skinny_kernel<2, 4>), dim3(min_grid(units, cus * 4)), dim3(SK_THREADS),
-                           0, s, packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, out_mode);
-    }
     return hipGetLastError();
 }
 

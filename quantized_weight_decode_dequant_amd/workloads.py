@@ -122,6 +122,26 @@ def time_ms(fn, iters: int, warmup: int = 2) -> float:
     return e0.elapsed_time(e1) / iters
 
 
+def time_graph_ms(fn, calls: int, reps: int = 5) -> float:
+    """Mean milliseconds per call of fn() measured on the GPU: `calls`
+    invocations captured into one HIP graph, the graph replayed `reps` times
+    between HIP events.  For kernels shorter than the host's launch path this
+    times the device, not the Python binding."""
+    import torch
+    graph = capture_graph(lambda: [fn() for _ in range(calls)])
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * calls)
+    del graph
+    return ms
+
+
 class Int8Verify:
     """The 8-bit verification workload: a 16-row activation tile rotated and
     quantized to int8, then multiplied with 8-bit symmetric group-32 weights.

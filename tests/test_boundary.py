@@ -132,6 +132,7 @@ def test_hadamard_validation():
     assert lib.hadamard32_quant_run(A, None, 4, 64, A, A, None) == L.QG_EINVAL
     assert lib.hadamard32_quant_run(A + 2, A, 4, 64, A, A, None) == L.QG_EALIGN
     assert lib.hadamard32_quant_run(A, A, 4, 64, A + 1, A, None) == L.QG_EALIGN
+    assert lib.hadamard32_quant_run(A, A + 1, 4, 64, A, A, None) == L.QG_EALIGN
     assert lib.hadamard32_quant_run(A, A, 0, 64, A, A, None) == L.QG_OK
 
 

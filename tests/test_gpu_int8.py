@@ -23,7 +23,8 @@ def gpu_had32(X, signs):
     return Xq.cpu().numpy(), sx.cpu().numpy()
 
 
-@pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (2, 4128), (16, 4096), (16, 12288), (33, 640)])
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (2, 160), (2, 4128), (16, 4096), (16, 12288),
+                                 (33, 640), (2, 24576), (2, 24672), (1, 49216)])
 def test_hadamard_quant_bit_exact(M, K):
     note("hadamard quant M=%d K=%d" % (M, K))
     X = synth.q8_activations(40, M, K)
@@ -87,7 +88,8 @@ def test_q8_group_partials_bit_exact(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 32), (3, 40, 96), (16, 100, 384), (17, 33, 160),
-                                   (32, 64, 4128)])
+                                   (32, 64, 4128), (16, 40, 4256), (5, 24, 8288), (32, 20, 8288),
+                                   (16, 17, 32800)])
 def test_q8_skinny_outputs(M, N, K):
     note("q8 outputs M=%d N=%d K=%d" % (M, N, K))
     w = synth.q8_matrix(46, N, K)
