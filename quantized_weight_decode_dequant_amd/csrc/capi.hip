@@ -187,9 +187,13 @@ int qgemm_skinny_run(int fmt, const void *packed, size_t packed_bytes, int64_t M
         if ((st = device_cus(&cus)) != QG_OK) return st;
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
         const uint8_t *p = reinterpret_cast<const uint8_t *>(packed);
-        if (fmt == QG_FMT_Q4_ASYM_G64)
-            return hip_status(launch_q4_skinny(p, reinterpret_cast<const uint16_t *>(X), Y, M, N,
-                                               K, out_dtype == QG_OUT_F32, cus, s));
+        if (fmt == QG_FMT_Q4_ASYM_G64) {
+            const uint16_t *xx = reinterpret_cast<const uint16_t *>(X);
+            const bool f32 = out_dtype == QG_OUT_F32;
+            if (M > 1 && q4_skinny_stream_fits(N, cus))
+                return hip_status(launch_q4_skinny_stream(p, xx, Y, M, N, K, f32, cus, s));
+            return hip_status(launch_q4_skinny(p, xx, Y, M, N, K, f32, cus, s));
+        }
         const int mode = out_dtype == QG_OUT_BF16 ? 0 : (out_dtype == QG_OUT_F32 ? 1 : 2);
         return hip_status(launch_q8_skinny(p, reinterpret_cast<const int8_t *>(X), x_scales, Y, M,
                                            N, K, mode, cus, s));
@@ -318,7 +322,7 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
             total_units += w.units;
             total_cost += (int64_t)w.units * ((int64_t)w.P * rpu + 2);
         }
-        const int per_cu = (M == 1) ? q4_gemv_wgs_per_cu() : q4_skinny_wgs_per_cu(M);
+        const int per_cu = (M == 1) ? q4_gemv_wgs_per_cu() : q4_skinny_stream_wgs_per_cu();
         int64_t grid = (int64_t)cus * per_cu;
         if (grid > WL_GRID_MAX) grid = WL_GRID_MAX;
         if (grid > total_units) grid = total_units;
@@ -387,7 +391,7 @@ int qg_batch_run(const qg_batch_plan *plan, void *stream) {
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
         if (plan->M == 1)
             return hip_status(launch_q4_gemv_list(items, starts, plan->grid, plan->kmax, s));
-        return hip_status(launch_q4_skinny_list(items, starts, plan->grid, plan->M, s));
+        return hip_status(launch_q4_skinny_stream_list(items, starts, plan->grid, plan->M, s));
     } catch (...) {
         return QG_EINTERNAL;
     }

@@ -1,0 +1,395 @@
+// Streaming skinny Q4 product Y[M, N] = X[M, K] W^T, M = 2..32 bf16
+// activation rows, for passes that stream many rowblocks per workgroup: the
+// grouped verification pass over every projection of a decode step and
+// single matrices with thousands of rowblocks (Uzu page, fange-kb.cn, section
+// "Producing several tokens from one model pass": one weight read serves all
+// the candidate rows).  Arithmetic per tile as in skinny.hip: each packed word
+// becomes the bf16x8 MFMA operand (128 + q); one v_mfma_f32_16x16x32_bf16
+// pair covers one group of 64 and acc += s * C + (b - 128 s) * sum_g X.
+//
+// Work split.  One workgroup per CU (16 waves; 12 for 32 rows) holds a
+// whole 4096-k slice of X (16 rows; 2048 k for 32 rows) in LDS, 128 KB, with
+// the per-(group, row) sums of X, so X is staged once per matrix and
+// segment.  Each wave owns every 16th (12th) rowblock of the workgroup's
+// range and streams its batches (4 consecutive 128-k tiles of one rowblock)
+// double-buffered: the load of each tile of the next batch is issued just
+// before the arithmetic of the same tile of the current batch.  The
+// rowblock's 16 x M results stay in the wave's registers until its last
+// batch.  When K spans several segments the wave works on blocks of up to 4
+// rowblocks whose sums it keeps in registers across the segments.  Every
+// rowblock accumulates its tiles in K order, as the kernel of skinny.hip
+// does, so both give identical results.  Tiles past the end of K re-read the
+// last tile; X and its sums are staged as zero there, so they add exactly
+// zero.
+#include "qg_internal.h"
+
+namespace qg {
+
+constexpr int SS_TPB = 4;  // tiles per batch
+constexpr int SS_R = 4;    // rowblocks a wave carries across segments
+
+template <int MT>
+struct SsCfg {
+    // waves per workgroup: the most whose registers fit without real spills
+    static constexpr int WAVES = MT == 1 ? 16 : 12;
+    static constexpr int THREADS = WAVES * 64;
+    static constexpr int MP = 16 * MT;               // padded activation rows
+    static constexpr int SEGK = 32 / MT;             // tiles per staged segment
+    static constexpr int RS = SEGK * 128 + 8;        // LDS row stride in bf16 (16-byte pad)
+    static constexpr size_t LDS_X = (size_t)MP * RS * 2;
+    static constexpr size_t LDS = LDS_X + (size_t)2 * SEGK * MP * 4;
+};
+static_assert(SsCfg<1>::LDS <= 160 * 1024 && SsCfg<2>::LDS <= 160 * 1024, "LDS budget");
+
+struct SsBatch {
+    u32x4_t c[SS_TPB];
+    u32x2_t sb[SS_TPB];
+};
+
+// Stage tiles [0, nt) of segment `seg` of X (rows past M and k past K are
+// zero) and the sums of each row over each group of 64: xs[g * MP + m].
+template <int MT>
+__device__ __forceinline__ void ss_stage(const uint16_t *X, int M, int K, int seg, int nt,
+                                         uint16_t *xl, float *xs, int tid) {
+    typedef SsCfg<MT> C;
+    const int k0 = seg * C::SEGK * Q4_TILE_K;
+    const int per_row = nt * 16;  // 16-byte chunks per row
+    const int total = C::MP * per_row;
+    constexpr int U = 4;
+#pragma unroll 1
+    for (int i0 = tid; i0 < total; i0 += U * C::THREADS) {
+        u32x4_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * C::THREADS;
+            const int m = i / per_row, c8 = i - m * per_row;
+            const int k = k0 + 8 * c8;
+            v[u] = (i < total && m < M && k < K)
+                       ? ld_global(reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k))
+                       : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * C::THREADS;
+            const int m = i / per_row, c8 = i - m * per_row;
+            if (i < total) *reinterpret_cast<u32x4_t *>(xl + m * C::RS + 8 * c8) = v[u];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * nt * C::MP; i += C::THREADS) {
+        const int g = i / C::MP, m = i - g * C::MP;
+        const uint4 *rr = reinterpret_cast<const uint4 *>(xl + m * C::RS + g * 64);
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint4 w = rr[q];
+            sum += bf16_lo(w.x) + bf16_hi(w.x) + bf16_lo(w.y) + bf16_hi(w.y) + bf16_lo(w.z) +
+                   bf16_hi(w.z) + bf16_lo(w.w) + bf16_hi(w.w);
+        }
+        xs[i] = sum;
+    }
+    __syncthreads();
+}
+
+// One tile (index pl within the staged segment) into acc.
+template <int MT>
+__device__ __forceinline__ void ss_tile(u32x4_t c, u32x2_t sb, const uint16_t *xl,
+                                        const float *xs, int pl, int lane, const Q4Consts &kq,
+                                        f32x4_t acc[MT]) {
+    typedef SsCfg<MT> C;
+    const int kg = lane >> 4, r16 = lane & 15;
+    bf16x8_t B[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) B[q] = q4_word_to_bf16x8(c[q], kq);
+    const float s0 = f16_lo(sb[0]), b0 = f16_hi(sb[0]);
+    const float s1 = f16_lo(sb[1]), b1 = f16_hi(sb[1]);
+    const float bb0 = fmaf(-128.f, s0, b0), bb1 = fmaf(-128.f, s1, b1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const uint16_t *ar = xl + (16 * mt + r16) * C::RS + pl * 128 + 8 * kg;
+        bf16x8_t A[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) A[q] = *reinterpret_cast<const bf16x8_t *>(ar + 32 * q);
+        const f32x4_t xs0 = *reinterpret_cast<const f32x4_t *>(xs + (2 * pl) * C::MP + 16 * mt + 4 * kg);
+        const f32x4_t xs1 = *reinterpret_cast<const f32x4_t *>(xs + (2 * pl + 1) * C::MP + 16 * mt + 4 * kg);
+        f32x4_t C0 = {0.f, 0.f, 0.f, 0.f}, C1 = {0.f, 0.f, 0.f, 0.f};
+        C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], C0, 0, 0, 0);
+        C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[1], C0, 0, 0, 0);
+        C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], B[2], C1, 0, 0, 0);
+        C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], B[3], C1, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float a = acc[mt][e];
+            a = fmaf(s0, C0[e], a);
+            a = fmaf(bb0, xs0[e], a);
+            a = fmaf(s1, C1[e], a);
+            a = fmaf(bb1, xs1[e], a);
+            acc[mt][e] = a;
+        }
+    }
+}
+
+// Issue tile j's loads of batch N (tiles nb0 .. nb0 + 3 of the buffer rs,
+// clamped to the last of pn tiles), then tile j's arithmetic of batch B
+// (tiles pl0 ..), for j = 0..3.
+template <int MT>
+__device__ __forceinline__ void ss_step(SsBatch &N, __amdgpu_buffer_rsrc_t rs, int nb0, int pn,
+                                        const SsBatch &B, int pl0, const uint16_t *xl,
+                                        const float *xs, int lane, const Q4Consts &kq,
+                                        f32x4_t cur[MT]) {
+    const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
+#pragma unroll
+    for (int j = 0; j < SS_TPB; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned to = (unsigned)min(nb0 + j, pn - 1) * Q4_TILE_BYTES;
+        N.c[j] = buf_ld_x4(rs, lc, to);
+        N.sb[j] = buf_ld_x2(rs, ls, to);
+        __builtin_amdgcn_sched_barrier(0);
+        ss_tile<MT>(B.c[j], B.sb[j], xl, xs, pl0 + j, lane, kq, cur);
+    }
+}
+
+// Buffer over the segment's tiles of rowblock rb (empty when !valid: loads
+// read zero without touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ss_rsrc(const WorkItem &it, int rb, int pbase,
+                                                          int pn, bool valid) {
+    const uint8_t *base = it.packed + ((size_t)rb * it.P + pbase) * Q4_TILE_BYTES;
+    return make_rsrc(uniform_ptr(base), valid ? (unsigned)pn * Q4_TILE_BYTES : 0u);
+}
+
+template <int MT>
+__device__ __forceinline__ void ss_store(const WorkItem &it, int rb, int M, const f32x4_t acc[MT],
+                                         int lane) {
+    const int n = rb * RB + (lane & 15), kg = lane >> 4;
+    if (n >= it.N) return;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 16 * mt + 4 * kg + e;
+            if (m < M) {
+                if (it.out_f32)
+                    reinterpret_cast<float *>(it.y)[(size_t)m * it.N + n] = acc[mt][e];
+                else
+                    reinterpret_cast<uint16_t *>(it.y)[(size_t)m * it.N + n] = f32_to_bf16(acc[mt][e]);
+            }
+        }
+}
+
+template <int MT>
+__device__ __forceinline__ void ss_zero(f32x4_t a[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// The running sums of the wave's i-th rowblock of the block (i uniform) in
+// and out of the working registers, so each rowblock accumulates its tiles
+// in K order across the segments.
+template <int MT>
+__device__ __forceinline__ void ss_pick(const f32x4_t acc[SS_R][MT], int i, f32x4_t cur[MT]) {
+#pragma unroll
+    for (int r = 0; r < SS_R; ++r)
+        if (r == i)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) cur[mt] = acc[r][mt];
+}
+template <int MT>
+__device__ __forceinline__ void ss_put(f32x4_t acc[SS_R][MT], int i, const f32x4_t cur[MT]) {
+#pragma unroll
+    for (int r = 0; r < SS_R; ++r)
+        if (r == i)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[r][mt] = cur[mt];
+}
+
+// Position in a wave's batch stream: its i-th rowblock, batch b.
+struct SsCursor {
+    int i, b;
+};
+__device__ __forceinline__ SsCursor ss_next(SsCursor c, int nb) {
+    if (++c.b == nb) {
+        c.b = 0;
+        ++c.i;
+    }
+    return c;
+}
+
+// Rowblocks [u0, u1) of one matrix.
+template <int MT>
+__device__ __forceinline__ void ss_range(const WorkItem &it, int u0, int u1, int M, uint16_t *xl,
+                                         float *xs, int tid, int lane, int wave,
+                                         const Q4Consts &kq) {
+    typedef SsCfg<MT> C;
+    const uint16_t *X = reinterpret_cast<const uint16_t *>(it.x);
+    const int nseg = (it.P + C::SEGK - 1) / C::SEGK;
+    if (nseg == 1) {
+        // the whole K is one segment: X is staged once, each wave streams all
+        // of its rowblocks and stores each one's results after its last batch
+        const int pn = it.P, nb = (pn + SS_TPB - 1) / SS_TPB;
+        const int mine = (u1 - u0 > wave) ? (u1 - u0 - wave + C::WAVES - 1) / C::WAVES : 0;
+        const int T = mine * nb;
+        SsBatch A, B;
+        f32x4_t cur[MT];
+        ss_zero<MT>(cur);
+        SsCursor ca = {0, 0};
+        {
+            const __amdgpu_buffer_rsrc_t rs = ss_rsrc(it, u0 + wave, 0, pn, T > 0);
+            const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
+#pragma unroll
+            for (int j = 0; j < SS_TPB; ++j) {
+                const unsigned to = (unsigned)min(j, pn - 1) * Q4_TILE_BYTES;
+                A.c[j] = buf_ld_x4(rs, lc, to);
+                A.sb[j] = buf_ld_x2(rs, ls, to);
+            }
+        }
+        __syncthreads();  // nobody still reads the previous range's X
+        ss_stage<MT>(X, M, it.K, 0, nb * SS_TPB, xl, xs, tid);
+        int t = 0;
+#pragma unroll 1
+        for (;;) {
+            if (t >= T) break;
+            const SsCursor cb = ss_next(ca, nb);
+            ss_step<MT>(B, ss_rsrc(it, u0 + wave + C::WAVES * cb.i, 0, pn, t + 1 < T), cb.b * SS_TPB,
+                        pn, A, ca.b * SS_TPB, xl, xs, lane, kq, cur);
+            if (ca.b == nb - 1) {
+                ss_store<MT>(it, u0 + wave + C::WAVES * ca.i, M, cur, lane);
+                ss_zero<MT>(cur);
+            }
+            if (t + 1 >= T) break;
+            const SsCursor cc = ss_next(cb, nb);
+            ss_step<MT>(A, ss_rsrc(it, u0 + wave + C::WAVES * cc.i, 0, pn, t + 2 < T), cc.b * SS_TPB,
+                        pn, B, cb.b * SS_TPB, xl, xs, lane, kq, cur);
+            if (cb.b == nb - 1) {
+                ss_store<MT>(it, u0 + wave + C::WAVES * cb.i, M, cur, lane);
+                ss_zero<MT>(cur);
+            }
+            t += 2;
+            ca = cc;
+        }
+        return;
+    }
+    // K spans several segments: blocks of C::WAVES * SS_R rowblocks, each
+    // wave's (up to SS_R) sums kept in registers across the segments
+#pragma unroll 1
+    for (int ub = u0; ub < u1; ub += C::WAVES * SS_R) {
+        const int left = u1 - ub;
+        int mine = (left > wave) ? (left - wave + C::WAVES - 1) / C::WAVES : 0;
+        mine = min(mine, SS_R);
+        f32x4_t acc[SS_R][MT];
+#pragma unroll
+        for (int r = 0; r < SS_R; ++r) ss_zero<MT>(acc[r]);
+#pragma unroll 1
+        for (int seg = 0; seg < nseg; ++seg) {
+            const int pbase = seg * C::SEGK;
+            const int pn = min(C::SEGK, it.P - pbase), nb = (pn + SS_TPB - 1) / SS_TPB;
+            const int T = mine * nb;
+            SsBatch A, B;
+            f32x4_t cur[MT];
+            SsCursor ca = {0, 0};
+            {
+                const __amdgpu_buffer_rsrc_t rs = ss_rsrc(it, ub + wave, pbase, pn, T > 0);
+                const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
+#pragma unroll
+                for (int j = 0; j < SS_TPB; ++j) {
+                    const unsigned to = (unsigned)min(j, pn - 1) * Q4_TILE_BYTES;
+                    A.c[j] = buf_ld_x4(rs, lc, to);
+                    A.sb[j] = buf_ld_x2(rs, ls, to);
+                }
+            }
+            __syncthreads();  // nobody still reads the previous segment of X
+            ss_stage<MT>(X, M, it.K, seg, nb * SS_TPB, xl, xs, tid);
+            int t = 0;
+#pragma unroll 1
+            for (;;) {
+                if (t >= T) break;
+                const SsCursor cb = ss_next(ca, nb);
+                if (ca.b == 0) ss_pick<MT>(acc, ca.i, cur);
+                ss_step<MT>(B, ss_rsrc(it, ub + wave + C::WAVES * cb.i, pbase, pn, t + 1 < T),
+                            cb.b * SS_TPB, pn, A, ca.b * SS_TPB, xl, xs, lane, kq, cur);
+                if (ca.b == nb - 1) ss_put<MT>(acc, ca.i, cur);
+                if (t + 1 >= T) break;
+                const SsCursor cc = ss_next(cb, nb);
+                if (cb.b == 0) ss_pick<MT>(acc, cb.i, cur);
+                ss_step<MT>(A, ss_rsrc(it, ub + wave + C::WAVES * cc.i, pbase, pn, t + 2 < T),
+                            cc.b * SS_TPB, pn, B, cb.b * SS_TPB, xl, xs, lane, kq, cur);
+                if (cb.b == nb - 1) ss_put<MT>(acc, cb.i, cur);
+                t += 2;
+                ca = cc;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < SS_R; ++r)
+            if (r < mine) ss_store<MT>(it, ub + wave + C::WAVES * r, M, acc[r], lane);
+    }
+}
+
+template <bool LIST, int MT>
+__global__ void __launch_bounds__(SsCfg<MT>::THREADS, 1)
+q4_skinny_stream_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
+                        WorkItem single, int M) {
+    typedef SsCfg<MT> C;
+    __shared__ __attribute__((aligned(16))) uint16_t xl[C::MP * C::RS];
+    __shared__ __attribute__((aligned(16))) float xs[2 * C::SEGK * C::MP];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const Q4Consts kq = q4_consts();
+    if (!LIST) {
+        const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
+        const int u0 = (int)(j * n / g), u1 = (int)((j + 1) * n / g);
+        if (u0 < u1) ss_range<MT>(single, u0, u1, M, xl, xs, tid, lane, wave, kq);
+        return;
+    }
+    const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
+#pragma unroll 1
+    for (int i = s.item; i < e.item || (i == e.item && e.unit > 0); ++i) {
+        const WorkItem it = items[i];
+        const int u0 = (i == s.item) ? s.unit : 0;
+        const int u1 = (i == e.item) ? e.unit : it.units;
+        if (u0 < u1) ss_range<MT>(it, u0, u1, M, xl, xs, tid, lane, wave, kq);
+    }
+}
+
+int q4_skinny_stream_wgs_per_cu() { return 1; }
+
+// A single matrix goes to the streaming kernel when every wave of a
+// one-per-CU grid gets at least two rowblocks.
+bool q4_skinny_stream_fits(int64_t N, int cus) {
+    return ceil_div(N, RB) >= (int64_t)2 * SsCfg<1>::WAVES * cus;
+}
+
+hipError_t launch_q4_skinny_stream(const uint8_t *packed, const uint16_t *X, void *Y, int64_t M,
+                                   int64_t N, int64_t K, bool out_f32, int cus, hipStream_t s) {
+    WorkItem it{};
+    it.packed = packed;
+    it.x = X;
+    it.y = Y;
+    it.N = (int32_t)N;
+    it.K = (int32_t)K;
+    it.P = (int32_t)ceil_div(K, Q4_TILE_K);
+    it.units = (int32_t)ceil_div(N, RB);
+    it.out_f32 = out_f32 ? 1 : 0;
+    const int grid = (int)(it.units < cus ? it.units : cus);
+    if (M <= 16)
+        hipLaunchKernelGGL((q4_skinny_stream_kernel<false, 1>), dim3(grid), dim3(SsCfg<1>::THREADS),
+                           0, s, (const WorkItem *)nullptr, (const WorkStart *)nullptr,
+                           it, (int)M);
+    else
+        hipLaunchKernelGGL((q4_skinny_stream_kernel<false, 2>), dim3(grid), dim3(SsCfg<2>::THREADS),
+                           0, s, (const WorkItem *)nullptr, (const WorkStart *)nullptr,
+                           it, (int)M);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_skinny_stream_list(const WorkItem *items, const WorkStart *starts, int grid,
+                                        int64_t M, hipStream_t s) {
+    WorkItem none{};
+    if (M <= 16)
+        hipLaunchKernelGGL((q4_skinny_stream_kernel<true, 1>), dim3(grid), dim3(SsCfg<1>::THREADS),
+                           0, s, items, starts, none, (int)M);
+    else
+        hipLaunchKernelGGL((q4_skinny_stream_kernel<true, 2>), dim3(grid), dim3(SsCfg<2>::THREADS),
+                           0, s, items, starts, none, (int)M);
+    return hipGetLastError();
+}
+
+}  // namespace qg

@@ -95,8 +95,14 @@ int q4_gemv_wgs_per_cu();
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts,
                                int grid, int64_t kmax, hipStream_t s);
 int q4_skinny_wgs_per_cu(int64_t M);
-hipError_t launch_q4_skinny_list(const WorkItem *items, const WorkStart *starts,
-                                 int grid, int64_t M, hipStream_t s);
+// streaming skinny kernel (one 8-wave workgroup per CU, X staged whole)
+int q4_skinny_stream_wgs_per_cu();
+bool q4_skinny_stream_fits(int64_t N, int cus);
+hipError_t launch_q4_skinny_stream(const uint8_t *packed, const uint16_t *X, void *Y,
+                                   int64_t M, int64_t N, int64_t K, bool out_f32,
+                                   int cus, hipStream_t s);
+hipError_t launch_q4_skinny_stream_list(const WorkItem *items, const WorkStart *starts,
+                                        int grid, int64_t M, hipStream_t s);
 hipError_t launch_write_words(const uint32_t *src, size_t nwords, uint32_t *dst,
                               hipStream_t s);
 hipError_t launch_fp4_gemv(const uint8_t *packed, const uint16_t *x, void *y,

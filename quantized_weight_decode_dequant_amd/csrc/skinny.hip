@@ -247,16 +247,4 @@ hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y, i
     return hipGetLastError();
 }
 
-hipError_t launch_q4_skinny_list(const WorkItem *items, const WorkStart *starts, int grid,
-                                 int64_t M, hipStream_t s) {
-    WorkItem none{};
-    if (M <= 16)
-        hipLaunchKernelGGL((q4_skinny_kernel<true, SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s, items,
-                           starts, none, (int)M);
-    else
-        hipLaunchKernelGGL((q4_skinny_kernel<true, SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s, items,
-                           starts, none, (int)M);
-    return hipGetLastError();
-}
-
 }  // namespace qg

@@ -51,7 +51,7 @@ def test_batch_m1_mixed_shapes(out_dtype):
 @pytest.mark.parametrize("M", [2, 5, 16, 17, 32])
 def test_batch_skinny_mixed_shapes(M):
     note("batch skinny M=%d" % M)
-    shapes = [(40, 192), (256, 4096), (33, 1216), (130, 640)]
+    shapes = [(40, 192), (256, 4096), (33, 1216), (130, 640), (48, 12288), (300, 8256)]
     mats = _mats(92, shapes)
     Xs = [synth.activations(93, M, m.K, item=i) for i, m in enumerate(mats)]
     entries, singles = [], []
@@ -118,3 +118,28 @@ def test_batch_decode_step_full():
         rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 64, replace=False)]))
         ref = oracle.q4_gemm(m.codes[rows], m.scales[rows], m.biases[rows], x)[0]
         assert_bf16_close(to_np(got[idx])[rows], ref, what=name)
+
+
+@pytest.mark.parametrize("M", [16, 32])
+def test_batch_verification_pass_full(M):
+    """The whole verification pass (every projection of the decode step against
+    its own M-row activation tile) in one launch: sampled output columns of
+    several projections against the oracle, and the lm_head output bitwise
+    equal to a single-matrix qgemm_skinny_run."""
+    note("batch verification pass M=%d" % M)
+    step = workloads.build_decode_step(0, skinny_m=M)
+    plan = pkg.qg_batch_plan_build(Q4, M, [(g.packed, g.N, g.K, g.X, g.Y) for g in step.gemvs])
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(97)
+    for idx in (0, 1, 4, 6, 251, 252):
+        item, name, N, K = synth.decode_step_shapes()[idx]
+        m = synth.q4_matrix(0, N, K, item=item)
+        X = synth.activations(1, M, K, item=item)
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 48, replace=False)]))
+        ref = oracle.q4_gemm(m.codes[rows], m.scales[rows], m.biases[rows], X)
+        assert_bf16_close(to_np(step.gemvs[idx].Y)[:, rows], ref, what="%s M=%d" % (name, M))
+    g = step.gemvs[-1]
+    single = pkg.qgemm_skinny_run(Q4, g.packed, M, g.N, g.K, g.X)
+    torch.cuda.synchronize()
+    assert torch.equal(single, g.Y)
