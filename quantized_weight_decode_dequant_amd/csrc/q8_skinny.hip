@@ -11,184 +11,295 @@
 // x 16 weight rows; its B operand (lane l: 8 consecutive k of row l & 15,
 // k-slice l >> 4) is half of one 16-byte packed slot (see qg_internal.h).
 //
-// Work split.  A call streams every weight byte once, and a single matrix of
-// this pass is only tens of MB, so the launch must put the whole chip's load
-// queue to work at once rather than stream a few rowblocks per CU.  A
-// workgroup owns one rowblock (16 weight rows) at a time and its W waves
-// split that rowblock's K: wave w takes chunks w, w + W, ... of T tiles (128
-// k each), issues all of a chunk's weight loads and the matching Xq loads
-// (the MFMA A operand, read straight from the L2-resident activation tile)
-// before any arithmetic, then folds the group partials into fp32.  The W
-// per-wave partial sums are reduced in LDS in wave order (deterministic) and
-// the first MT waves write Y.  Loads go through buffer resources: Xq rows
-// past M read as zero; chunk slots past the rowblock's last tile re-read
-// that tile and are given a zero scale (their int32 partials are finite, so
-// the fp32 sums are unchanged) and never write group partials.
+// Work split.  A single matrix of this pass is only tens of MB and its
+// activation tile is 64-384 KB, so the launch gives every CU one workgroup
+// of 16 waves, which holds a K-segment of Xq (up to 96 KB) in LDS and walks
+// rowblocks (16 weight rows) in a grid-strided loop.  Within a rowblock the
+// 16 waves split K: wave w takes T consecutive 128-k tiles of each segment.
+// The weight loads of a rowblock are all issued at once; when K is one
+// segment those of the next rowblock go out before the arithmetic of the
+// current one, and every segment's go out before its Xq is staged.  Xq is
+// staged with coalesced 16-byte loads and read back by each MFMA as its
+// 8-byte A operand.  The 16 per-wave partial sums of a rowblock are reduced
+// in LDS in wave order (deterministic).  Weight tiles past the end of K read
+// as zero (their offsets sit in the range-checked part of the buffer
+// address), and so does Xq past K and past row M, so ragged shapes need no
+// branches.
 #include "qg_internal.h"
 
 namespace qg {
 
-constexpr int Q8_WMAX = 16;  // waves per workgroup
+constexpr int Q8_WAVES = 16;
+constexpr int Q8_THREADS = Q8_WAVES * 64;
 
-template <int MT, int T, bool GROUPS>
-__global__ void __launch_bounds__(Q8_WMAX * 64)
-q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ X,
-                 const float *__restrict__ x_scales, void *__restrict__ Y, int M, int N, int K,
-                 int P, int nrb, int out_f32) {
-    __shared__ f32x4_t red[GROUPS ? 1 : Q8_WMAX][MT][64];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int W = blockDim.x >> 6;
-    const int kg = lane >> 4, r16 = lane & 15;
-    const int G = K / 32;
-    const int nch = (P + T - 1) / T;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (unsigned)(M * K));
-    // Xq row of this lane in each 16-row activation tile; rows >= M start
-    // at or past M * K and read as zero
-    unsigned xo[MT];
+template <int MT, int T>
+struct Q8Cfg {
+    static constexpr int MP = 16 * MT;                // padded activation rows
+    static constexpr int SEGT = Q8_WAVES * T;         // tiles per staged segment
+    static constexpr int RS = SEGT * Q8_TILE_K + 8;   // LDS row stride in bytes (8 mod 128)
+    static constexpr size_t LDS_X = (size_t)MP * RS;
+};
+
+template <int T>
+struct Q8W {
+    u32x4_t c0[T], c1[T];
+    u32x2_t sc[T];
+};
+
+// The loads of tiles [p0, p0 + T) of one rowblock (buffer rw over its P
+// tiles; an empty buffer, or tiles past P, read as zero).
+template <int T>
+__device__ __forceinline__ void q8_load(Q8W<T> &B, __amdgpu_buffer_rsrc_t rw, int p0, int lane) {
+    const unsigned lc = 16u * lane, ls = 2048u + 8u * (lane & 15);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xo[mt] = (unsigned)((16 * mt + r16) * K + 8 * kg);
+    for (int j = 0; j < T; ++j) {
+        const unsigned tw = (unsigned)(p0 + j) * Q8_TILE_BYTES;
+        B.c0[j] = buf_ld_x4(rw, tw + lc, 0);
+        B.c1[j] = buf_ld_x4(rw, tw + lc + 1024u, 0);
+        B.sc[j] = buf_ld_x2(rw, tw + ls, 0);
+    }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t q8_rsrc(const uint8_t *packed, int rb, int P,
+                                                          bool valid) {
     const unsigned wbytes = (unsigned)P * Q8_TILE_BYTES;
+    return make_rsrc(uniform_ptr(packed + (size_t)rb * wbytes), valid ? wbytes : 0u);
+}
 
+// Stage segment `seg` of Xq (SEGT tiles; zero past K and past row M).
+template <int MT, int T>
+__device__ __forceinline__ void q8_stage(const int8_t *X, int M, int K, int seg, int8_t *xl,
+                                         int tid) {
+    typedef Q8Cfg<MT, T> C;
+    const int k0 = seg * C::SEGT * Q8_TILE_K;
+    constexpr int PER_ROW = C::SEGT * Q8_TILE_K / 16;  // 16-byte chunks per row
+    constexpr int TOTAL = C::MP * PER_ROW;
+    constexpr int U = 4;
 #pragma unroll 1
-    for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
-        const __amdgpu_buffer_rsrc_t rw =
-            make_rsrc(uniform_ptr(packed + (size_t)rb * wbytes), wbytes);
-        const int n = rb * RB + r16;
-        f32x4_t acc[MT];
+    for (int i0 = tid; i0 < TOTAL; i0 += U * Q8_THREADS) {
+        u32x4_t v[U];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-        for (int c = wave; c < nch; c += W) {
-            const int p0 = c * T;
-            u32x4_t c0[T], c1[T];
-            u32x2_t sc[T], a[T][4][MT];
-            __builtin_amdgcn_sched_barrier(0);
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * Q8_THREADS;
+            const int m = i / PER_ROW, c = i - m * PER_ROW;
+            const int k = k0 + 16 * c;
+            v[u] = (i < TOTAL && m < M && k < K)
+                       ? ld_global(reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k))
+                       : u32x4_t{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-            for (int j = 0; j < T; ++j) {
-                // tiles past the end re-read the last tile (their scales
-                // are zeroed below); the uniform tile offset rides in soffset
-                const unsigned tw = (unsigned)min(p0 + j, P - 1) * Q8_TILE_BYTES;
-                c0[j] = buf_ld_x4(rw, 16u * lane, tw);
-                c1[j] = buf_ld_x4(rw, 16u * lane + 1024u, tw);
-                sc[j] = buf_ld_x2(rw, 8u * r16 + 2048u, tw);
-            }
-#pragma unroll
-            for (int j = 0; j < T; ++j) {
-                // the whole Xq offset in the range-checked VGPR offset
-                const unsigned tx = (unsigned)min(p0 + j, P - 1) * 128u;
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        a[j][g][mt] = buf_ld_x2(rx, xo[mt] + tx + 32u * g, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < T; ++j) {
-                // one tile's partials live at a time
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x4_t &ch = (g < 2) ? c0[j] : c1[j];
-                    const u32x2_t bw = {ch[2 * (g & 1)], ch[2 * (g & 1) + 1]};
-                    const long bop = __builtin_bit_cast(long, bw);
-                    const unsigned swbits = sc[j][g >> 1];
-                    const float sw = (p0 + j < P) ? ((g & 1) ? f16_hi(swbits) : f16_lo(swbits)) : 0.f;
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const long aop = __builtin_bit_cast(long, a[j][g][mt]);
-                        const i32x4_t C = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                            aop, bop, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
-                        if constexpr (GROUPS) {
-                            const int gg = (p0 + j) * 4 + g;
-                            if (gg < G && n < N) {
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    const int m = 16 * mt + 4 * kg + e;
-                                    if (m < M)
-                                        reinterpret_cast<int32_t *>(Y)[((size_t)m * N + n) * G + gg] = C[e];
-                                }
-                            }
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[mt][e] = fmaf(sw, (float)C[e], acc[mt][e]);
-                        }
-                    }
-                }
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * Q8_THREADS;
+            const int m = i / PER_ROW, c = i - m * PER_ROW;
+            if (i < TOTAL) {
+                // rows are 8-byte aligned: two 8-byte stores
+                u32x2_t *d = reinterpret_cast<u32x2_t *>(xl + m * C::RS + 16 * c);
+                d[0] = u32x2_t{v[u][0], v[u][1]};
+                d[1] = u32x2_t{v[u][2], v[u][3]};
             }
         }
-        if constexpr (!GROUPS) {
-            // K-split reduction over the waves, in wave order
+    }
+    __syncthreads();
+}
+
+// The MFMAs of this wave's tiles (segment-relative index ps of its first
+// tile, absolute index p0); group partials are either folded into acc with
+// the weight scales or, for GROUPS, written out as they are.
+template <int MT, int T, bool GROUPS>
+__device__ __forceinline__ void q8_compute(const Q8W<T> &B, const int8_t *xl, int ps, int p0,
+                                           int lane, f32x4_t acc[MT], void *Y, int M, int N,
+                                           int G, int n) {
+    typedef Q8Cfg<MT, T> C;
+    const int kg = lane >> 4, r16 = lane & 15;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
-            __syncthreads();
-#pragma unroll 1
-            for (int mt = wave; mt < MT; mt += W) {
-                f32x4_t s = red[0][mt][lane];
-#pragma unroll 1
-                for (int w = 1; w < W; ++w) s += red[w][mt][lane];
-                if (n < N) {
+    for (int j = 0; j < T; ++j) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int m = 16 * mt + 4 * kg + e;
-                        if (m < M) {
-                            const float v = x_scales[m] * s[e];
-                            if (out_f32)
-                                reinterpret_cast<float *>(Y)[(size_t)m * N + n] = v;
-                            else
-                                reinterpret_cast<uint16_t *>(Y)[(size_t)m * N + n] = f32_to_bf16(v);
+        for (int g = 0; g < 4; ++g) {
+            const u32x4_t &ch = (g < 2) ? B.c0[j] : B.c1[j];
+            const u32x2_t bw = {ch[2 * (g & 1)], ch[2 * (g & 1) + 1]};
+            const long bop = __builtin_bit_cast(long, bw);
+            const unsigned swbits = B.sc[j][g >> 1];
+            const float sw = (g & 1) ? f16_hi(swbits) : f16_lo(swbits);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const long aop = *reinterpret_cast<const long *>(
+                    xl + (16 * mt + r16) * C::RS + (ps + j) * Q8_TILE_K + 32 * g + 8 * kg);
+                const i32x4_t P4 = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, i32x4_t{0, 0, 0, 0},
+                                                                        0, 0, 0);
+                if constexpr (GROUPS) {
+                    const int gg = (p0 + j) * 4 + g;
+                    if (gg < G && n < N) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = 16 * mt + 4 * kg + e;
+                            if (m < M) reinterpret_cast<int32_t *>(Y)[((size_t)m * N + n) * G + gg] = P4[e];
                         }
                     }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[mt][e] = fmaf(sw, (float)P4[e], acc[mt][e]);
                 }
             }
-            __syncthreads();  // red is reused by the next rowblock
         }
     }
 }
 
-// Tiles per wave chunk: the smallest compiled size with which 16 waves cover
-// the rowblock's K in one chunk each, so every weight byte of a rowblock is
-// requested at the start; longer K loops.  The register budget (1024-thread
-// workgroups leave 128 VGPRs per lane) caps T at 6 for one 16-row activation
-// tile and 4 for two (T = 6 spills a few registers that are only reloaded by
-// the epilogue).
+// Sum the 16 waves' partials of rowblock rb in wave order and write Y.
+template <int MT>
+__device__ __forceinline__ void q8_finish(const f32x4_t acc[MT], f32x4_t (*red)[64], int wave,
+                                          int lane, const float *x_scales, void *Y, int M, int N,
+                                          int n, int out_f32) {
+    const int kg = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        red[wave][lane] = acc[mt];
+        __syncthreads();
+        if (wave == 0) {
+            f32x4_t s = red[0][lane];
+#pragma unroll
+            for (int w = 1; w < Q8_WAVES; ++w) s += red[w][lane];
+            if (n < N) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 16 * mt + 4 * kg + e;
+                    if (m < M) {
+                        const float v = x_scales[m] * s[e];
+                        if (out_f32)
+                            reinterpret_cast<float *>(Y)[(size_t)m * N + n] = v;
+                        else
+                            reinterpret_cast<uint16_t *>(Y)[(size_t)m * N + n] = f32_to_bf16(v);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void q8_zero(f32x4_t a[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int MT, int T, bool GROUPS>
+__global__ void __launch_bounds__(Q8_THREADS, 1)
+q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ X,
+                 const float *__restrict__ x_scales, void *__restrict__ Y, int M, int N, int K,
+                 int P, int nrb, int out_f32) {
+    typedef Q8Cfg<MT, T> C;
+    __shared__ __attribute__((aligned(16))) int8_t xl[C::LDS_X];
+    __shared__ f32x4_t red[GROUPS ? 1 : Q8_WAVES][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = K / 32;
+    const int nseg = (P + C::SEGT - 1) / C::SEGT;
+    int rb = blockIdx.x;
+    if (rb >= nrb) return;
+    f32x4_t acc[MT];
+    Q8W<T> A, B;
+    if (nseg == 1) {
+        // Xq staged once; the next rowblock's weights load during this one's
+        // arithmetic
+        const int p0 = wave * T;
+        q8_load<T>(A, q8_rsrc(packed, rb, P, true), p0, lane);
+        q8_stage<MT, T>(X, M, K, 0, xl, tid);
+#pragma unroll 1
+        for (;;) {
+            int nx = rb + gridDim.x;
+            q8_load<T>(B, q8_rsrc(packed, nx, P, nx < nrb), p0, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            q8_zero<MT>(acc);
+            const int n = rb * RB + (lane & 15);
+            q8_compute<MT, T, GROUPS>(A, xl, p0, p0, lane, acc, Y, M, N, G, n);
+            if constexpr (!GROUPS) q8_finish<MT>(acc, red, wave, lane, x_scales, Y, M, N, n, out_f32);
+            if (nx >= nrb) break;
+            rb = nx;
+            nx = rb + gridDim.x;
+            q8_load<T>(A, q8_rsrc(packed, nx, P, nx < nrb), p0, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            q8_zero<MT>(acc);
+            const int n2 = rb * RB + (lane & 15);
+            q8_compute<MT, T, GROUPS>(B, xl, p0, p0, lane, acc, Y, M, N, G, n2);
+            if constexpr (!GROUPS) q8_finish<MT>(acc, red, wave, lane, x_scales, Y, M, N, n2, out_f32);
+            if (nx >= nrb) break;
+            rb = nx;
+        }
+        return;
+    }
+    // several segments per rowblock: Xq re-staged per segment, each
+    // segment's weight loads issued before its staging
+#pragma unroll 1
+    for (; rb < nrb; rb += gridDim.x) {
+        const int n = rb * RB + (lane & 15);
+        q8_zero<MT>(acc);
+#pragma unroll 1
+        for (int seg = 0; seg < nseg; ++seg) {
+            const int p0 = seg * C::SEGT + wave * T;
+            q8_load<T>(A, q8_rsrc(packed, rb, P, true), p0, lane);
+            __syncthreads();  // nobody still reads the previous segment
+            q8_stage<MT, T>(X, M, K, seg, xl, tid);
+            q8_compute<MT, T, GROUPS>(A, xl, wave * T, p0, lane, acc, Y, M, N, G, n);
+        }
+        if constexpr (!GROUPS) q8_finish<MT>(acc, red, wave, lane, x_scales, Y, M, N, n, out_f32);
+    }
+    (void)B;
+}
+
+// Tiles per wave and segment: fewest segments first, then least padding.
+template <int MT>
+static int q8_pick_t(int P) {
+    const int cands1[2] = {2, 3}, cands2[2] = {1, 2};
+    const int *c = MT == 1 ? cands1 : cands2;
+    const int nc = 2;
+    int best = c[0], bseg = 1 << 30, bwaste = 1 << 30;
+    for (int i = 0; i < nc; ++i) {
+        const int segt = Q8_WAVES * c[i];
+        const int nseg = (P + segt - 1) / segt, waste = nseg * segt - P;
+        if (nseg < bseg || (nseg == bseg && waste < bwaste)) {
+            best = c[i];
+            bseg = nseg;
+            bwaste = waste;
+        }
+    }
+    return best;
+}
+
+template <int MT, int T, bool GROUPS>
+static void q8_launch(int grid, hipStream_t s, const uint8_t *packed, const int8_t *X,
+                      const float *x_scales, void *Y, int M, int N, int K, int P, int nrb,
+                      int out_f32) {
+    hipLaunchKernelGGL((q8_skinny_kernel<MT, T, GROUPS>), dim3(grid), dim3(Q8_THREADS), 0, s,
+                       packed, X, x_scales, Y, M, N, K, P, nrb, out_f32);
+}
+
 template <int MT, bool GROUPS>
 static hipError_t launch_q8_mt(const uint8_t *packed, const int8_t *X, const float *x_scales,
-                               void *Y, int M, int N, int K, int P, int nrb, int out_f32,
+                               void *Y, int M, int N, int K, int P, int nrb, int out_f32, int cus,
                                hipStream_t s) {
-    const int need = (P + Q8_WMAX - 1) / Q8_WMAX;
-    int T = MT == 1 ? 6 : 4;
-    if (need <= 2 || GROUPS) T = 2;  // the group-partial mode is for testing
-    else if (need <= 4) T = 4;
-    const int nch = (P + T - 1) / T;
-    const int W = nch < Q8_WMAX ? nch : Q8_WMAX;
-    const int grid = nrb < 65536 ? nrb : 65536;
-    const dim3 g(grid), b(W * 64);
-    if (GROUPS || T == 2)
-        hipLaunchKernelGGL((q8_skinny_kernel<MT, 2, GROUPS>), g, b, 0, s, packed, X, x_scales, Y, M,
-                           N, K, P, nrb, out_f32);
-    else if (T == 4)
-        hipLaunchKernelGGL((q8_skinny_kernel<MT, 4, false>), g, b, 0, s, packed, X, x_scales, Y, M,
-                           N, K, P, nrb, out_f32);
-    else
-        hipLaunchKernelGGL((q8_skinny_kernel<MT, (MT == 1 ? 6 : 4), false>), g, b, 0, s, packed, X,
-                           x_scales, Y, M, N, K, P, nrb, out_f32);
+    const int grid = nrb < cus ? nrb : cus;
+    const int T = q8_pick_t<MT>(P);
+    if (MT == 1) {
+        if (T == 2) q8_launch<1, 2, GROUPS>(grid, s, packed, X, x_scales, Y, M, N, K, P, nrb, out_f32);
+        else q8_launch<1, 3, GROUPS>(grid, s, packed, X, x_scales, Y, M, N, K, P, nrb, out_f32);
+    } else {
+        if (T == 1) q8_launch<2, 1, GROUPS>(grid, s, packed, X, x_scales, Y, M, N, K, P, nrb, out_f32);
+        else q8_launch<2, 2, GROUPS>(grid, s, packed, X, x_scales, Y, M, N, K, P, nrb, out_f32);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_q8_skinny(const uint8_t *packed, const int8_t *X, const float *x_scales,
                             void *Y, int64_t M, int64_t N, int64_t K, int out_mode, int cus,
                             hipStream_t s) {
-    (void)cus;
     const int P = (int)ceil_div(K, Q8_TILE_K);
     const int nrb = (int)ceil_div(N, RB);
     const int f32 = out_mode == 1 ? 1 : 0;
     if (out_mode == 2)
-        return M <= 16 ? launch_q8_mt<1, true>(packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, 0, s)
-                       : launch_q8_mt<2, true>(packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, 0, s);
-    return M <= 16 ? launch_q8_mt<1, false>(packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, f32, s)
-                   : launch_q8_mt<2, false>(packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, f32, s);
+        return M <= 16 ? launch_q8_mt<1, true>(packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, 0, cus, s)
+                       : launch_q8_mt<2, true>(packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, 0, cus, s);
+    return M <= 16 ? launch_q8_mt<1, false>(packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, f32, cus, s)
+                   : launch_q8_mt<2, false>(packed, X, x_scales, Y, (int)M, (int)N, (int)K, P, nrb, f32, cus, s);
 }
 
 }  // namespace qg
