@@ -6,62 +6,100 @@
 // quantized to 8 bits on the fly so verification runs on the int8 matrix
 // path).
 //
-// One workgroup of 1024 threads per activation row.  Each 16-lane quarter
-// of a wavefront owns one block of 32: lane p holds elements 2p and 2p + 1,
-// so the first butterfly stage (index bit 0) is a register add/subtract and
-// the other four (bits 1..4) exchange across lanes p ^ 1, 2, 4, 8.  After
-// the five stages the lane holds z_i = sum_j (-1)^popcount(i & j) d_j x_j
-// (Sylvester order) for its two i.  The sums are carried in fp64, where a
-// signed sum of 32 bf16 values is exact for activations of ordinary range,
-// so the quantization decision sees the exact z.  A row of up to 24576
-// elements is loaded once with every load issued up front and its z kept in
-// registers; the row maximum amax = max |z| is reduced through LDS and the
-// same registers are quantized to round-half-even(z * 127 / amax) (fp64
-// division, correctly rounded).  Longer rows are processed in rounds of
-// 24576 and recomputed from x for the second pass.
+// One workgroup of 1024 threads per activation row.  Four lanes own one
+// block of 32: lane part p holds elements 8p .. 8p + 7, so the first three
+// butterfly stages (index bits 0, 1, 2) are register adds and subtracts and
+// the last two (bits 3, 4) exchange with the lanes p ^ 1 and p ^ 2 of the
+// same quad through DPP moves.  Stages run in index-bit order and the lower
+// index of each pair takes a + c, the upper a - c, so after the five stages
+// the lane holds z_i = sum_j (-1)^popcount(i & j) d_j x_j (Sylvester
+// order).  The sums are carried in fp64, where a signed sum of 32 bf16 values
+// is exact for activations of ordinary range, so the quantization decision
+// sees the exact z.  A row of up to 24576 elements is loaded once, with every
+// load issued up front, and its z kept in registers; the row maximum amax =
+// max |z| is reduced through LDS.  Each code is round-half-even(z * 127 /
+// amax) of the correctly rounded fp64 quotient: it is taken from the product
+// with 1 / amax unless that product lies within 1e-9 of a rounding boundary
+// (its error is below 1e-13), in which case the quotient is computed by a
+// true division.  Longer rows are processed in rounds of 24576 and
+// recomputed from x for the second pass.
 #include "qg_internal.h"
 
 namespace qg {
 
 constexpr int HQ_THREADS = 1024;
 constexpr int HQ_WAVES = HQ_THREADS / 64;
-constexpr int HQ_R = 12;  // 4-block units per wave per round (24576 k per round)
+constexpr int HQ_R = 3;  // 16-block units per wave per round (24576 k per round)
 
-// z of this lane's two elements of a block: v0 = d_2p x_2p, v1 = d_2p+1 x_2p+1.
-__device__ __forceinline__ void fwht32_pair(double &v0, double &v1, int p) {
-    const double s0 = v0 + v1, s1 = v0 - v1;
-    v0 = s0;
-    v1 = s1;
+// Exchange with the lane p ^ S of the quad (S = 1 or 2), by DPP quad_perm.
+template <int S>
+__device__ __forceinline__ double quad_xor(double v) {
+    constexpr int ctrl = S == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] / [2,3,0,1]
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, ctrl, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), ctrl, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// The five butterfly stages over this lane's 8 elements (part p of the block).
+__device__ __forceinline__ void fwht32_oct(double z[8], int p) {
 #pragma unroll
-    for (int s = 1; s < 16; s <<= 1) {
-        const double o0 = __shfl_xor(v0, s), o1 = __shfl_xor(v1, s);
-        v0 = (p & s) ? (o0 - v0) : (v0 + o0);
-        v1 = (p & s) ? (o1 - v1) : (v1 + o1);
+    for (int s = 1; s < 8; s <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (!(e & s)) {
+                const double a = z[e], c = z[e + s];
+                z[e] = a + c;
+                z[e + s] = a - c;
+            }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double o = quad_xor<1>(z[e]);
+        z[e] = (p & 1) ? (o - z[e]) : (z[e] + o);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double o = quad_xor<2>(z[e]);
+        z[e] = (p & 2) ? (o - z[e]) : (z[e] + o);
     }
 }
 
-// Load and transform one round: unit u = round * HQ_WAVES * HQ_R + wave +
-// HQ_WAVES * i covers blocks 4u .. 4u + 3; lane l takes block 4u + (l >> 4).
-__device__ __forceinline__ void hq_round(const uint16_t *xr, const int8_t *signs, int nblk,
-                                         int round, int wave, int lane, double z[HQ_R][2],
-                                         bool ok[HQ_R]) {
-    const int p = lane & 15;
-    unsigned xv[HQ_R];
-    unsigned short sv[HQ_R];
+// Load and transform this wave's units of one round.  Unit u covers blocks
+// 16u .. 16u + 15, lane l takes block 16u + (l >> 2), part l & 3.  Buffer
+// loads past the row read as zero.
+__device__ __forceinline__ void hq_round(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsg,
+                                         int nunit, int round, int wave, int lane,
+                                         double z[HQ_R][8]) {
+    const int p = lane & 3;
+    u32x4_t xv[HQ_R];
+    u32x2_t sv[HQ_R];
 #pragma unroll
     for (int i = 0; i < HQ_R; ++i) {
-        const int b = 4 * ((round * HQ_R + i) * HQ_WAVES + wave) + (lane >> 4);
-        ok[i] = b < nblk;
-        const int k = 32 * b + 2 * p;
-        xv[i] = ok[i] ? *reinterpret_cast<const unsigned *>(xr + k) : 0u;
-        sv[i] = ok[i] ? *reinterpret_cast<const unsigned short *>(signs + k) : (unsigned short)0;
+        const int u = (round * HQ_R + i) * HQ_WAVES + wave;
+        const unsigned k = 32u * (16u * (unsigned)u + (lane >> 2)) + 8u * p;
+        if (u < nunit) {  // uniform
+            xv[i] = buf_ld_x4(rx, 2u * k, 0);
+            sv[i] = buf_ld_x2(rsg, k, 0);
+        } else {
+            xv[i] = u32x4_t{0u, 0u, 0u, 0u};
+            sv[i] = u32x2_t{0u, 0u};
+        }
     }
 #pragma unroll
     for (int i = 0; i < HQ_R; ++i) {
-        const double d0 = (double)(int8_t)(sv[i] & 0xFF), d1 = (double)(int8_t)(sv[i] >> 8);
-        z[i][0] = d0 * (double)bf16_lo(xv[i]);
-        z[i][1] = d1 * (double)bf16_hi(xv[i]);
-        fwht32_pair(z[i][0], z[i][1], p);
+        if ((round * HQ_R + i) * HQ_WAVES + wave >= nunit) {  // uniform
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[i][e] = 0.0;
+            continue;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const unsigned w = xv[i][e >> 1];
+            const float x = (e & 1) ? bf16_hi(w) : bf16_lo(w);
+            const int d = (int)(int8_t)((sv[i][e >> 2] >> (8 * (e & 3))) & 0xFFu);
+            z[i][e] = (double)d * (double)x;
+        }
+        fwht32_oct(z[i], p);
     }
 }
 
@@ -72,19 +110,20 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
     const int m = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int p = lane & 15;
     const int nblk = K / 32;
-    const int nround = (nblk + 4 * HQ_WAVES * HQ_R - 1) / (4 * HQ_WAVES * HQ_R);
-    const uint16_t *xr = X + (size_t)m * K;
-    double z[HQ_R][2];
-    bool ok[HQ_R];
+    const int nunit = (nblk + 15) / 16;
+    const int nround = (nunit + HQ_WAVES * HQ_R - 1) / (HQ_WAVES * HQ_R);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (size_t)m * K, 2u * (unsigned)K);
+    const __amdgpu_buffer_rsrc_t rsg = make_rsrc(signs, (unsigned)K);
+    double z[HQ_R][8];
     double amax = 0.0;
 #pragma unroll 1
     for (int r = 0; r < nround; ++r) {
-        hq_round(xr, signs, nblk, r, wave, lane, z, ok);
+        hq_round(rx, rsg, nunit, r, wave, lane, z);
 #pragma unroll
         for (int i = 0; i < HQ_R; ++i)
-            if (ok[i]) amax = fmax(amax, fmax(fabs(z[i][0]), fabs(z[i][1])));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmax(amax, fabs(z[i][e]));
     }
     // row maximum: wave, then across waves
 #pragma unroll
@@ -94,24 +133,30 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
     amax = 0.0;
 #pragma unroll
     for (int w = 0; w < HQ_WAVES; ++w) amax = fmax(amax, wmax[w]);
+    const double rinv = amax > 0.0 ? 1.0 / amax : 0.0;
 
     int8_t *qr = Xq + (size_t)m * K;
 #pragma unroll 1
     for (int r = nround - 1; r >= 0; --r) {
         // the last round is still in registers
-        if (r != nround - 1) hq_round(xr, signs, nblk, r, wave, lane, z, ok);
+        if (r != nround - 1) hq_round(rx, rsg, nunit, r, wave, lane, z);
 #pragma unroll
         for (int i = 0; i < HQ_R; ++i) {
-            if (!ok[i]) continue;
-            double q0 = 0.0, q1 = 0.0;
-            if (amax > 0.0) {
-                q0 = fmin(fmax(rint(z[i][0] * 127.0 / amax), -127.0), 127.0);
-                q1 = fmin(fmax(rint(z[i][1] * 127.0 / amax), -127.0), 127.0);
+            const int u = (r * HQ_R + i) * HQ_WAVES + wave;
+            const int b = 16 * u + (lane >> 2);
+            if (u >= nunit) break;  // uniform
+            unsigned packed[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double t = z[i][e] * 127.0;
+                double q = rint(t * rinv);
+                if (fabs(fabs(t * rinv - q) - 0.5) < 1e-9) q = rint(t / amax);
+                q = fmin(fmax(q, -127.0), 127.0);
+                packed[e >> 2] |= ((unsigned)(int)q & 0xFFu) << (8 * (e & 3));
             }
-            const int b = 4 * ((r * HQ_R + i) * HQ_WAVES + wave) + (lane >> 4);
-            const unsigned short v =
-                (unsigned short)(((unsigned)(int)q0 & 0xFFu) | (((unsigned)(int)q1 & 0xFFu) << 8));
-            *reinterpret_cast<unsigned short *>(qr + 32 * b + 2 * p) = v;
+            if (b < nblk)
+                *reinterpret_cast<u32x2_t *>(qr + 32 * b + 8 * (lane & 3)) =
+                    u32x2_t{packed[0], packed[1]};
         }
     }
     if (tid == 0) x_scales[m] = amax > 0.0 ? (float)(amax / denom) : 0.f;
