@@ -10,12 +10,19 @@
 // significant bits, so the scaled value is exact in bf16 and in fp32.
 //
 // MoE, three launches on one stream, the expert ids never leave the device:
-//   A  item = (slot s, rowblock of F): g and u rows of expert ids[s] against
-//      x (bf16 in LDS), h = silu(g) * u in fp32 -> workspace h[s][F].
-//   B  item = (slot s, rowblock of H): Wdown[ids[s]] rows against h[s]
+//   A  unit = (slot s, rowblock of F): the g and u rows of expert ids[s]
+//      against x (bf16 in LDS), h = silu(g) * u in fp32 -> workspace h[s][F].
+//   B  unit = (slot s, rowblock of H): Wdown[ids[s]] rows against h[s]
 //      (fp32 in LDS) -> workspace part[s][H].
 //   C  y[n] = sum_s w[s] * part[s][n] in slot order (deterministic, no
 //      atomics), rounded once; also writes the status word.
+// A and B give each workgroup a contiguous range of units and stream them
+// like the Q4 decode GEMV: a unit's tiles are cut into batches of 4, every
+// fourth batch goes to the same wave, and each wave streams its batches
+// double-buffered with the load of each tile of its next batch issued just
+// before the arithmetic of the same tile of the current one.  A wave folds
+// its sums of a unit into its own LDS slot; the workgroup adds the wave slots
+// in wave order when a block of up to 32 units ends.
 #include "qg_internal.h"
 
 namespace qg {
@@ -162,129 +169,225 @@ hipError_t launch_fp4_gemv(const uint8_t *packed, const uint16_t *x, void *y, in
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ MoE streaming
+constexpr int MS_WAVES = 4;
+constexpr int MS_THREADS = MS_WAVES * 64;
+constexpr int MS_TPB = 4;     // tiles per batch
+constexpr int MS_RMAX = 32;   // units per output block
+
+struct Fp4Batch {
+    u32x4_t c0[MS_TPB], c1[MS_TPB];
+    unsigned e0[MS_TPB], e1[MS_TPB];
+};
+
+__device__ __forceinline__ unsigned buf_ld_u8(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                              unsigned soff) {
+    return (unsigned)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 2);
+}
+
+// One tile's slot loads (tile tp of the buffer, clamped to its last of pn).
+__device__ __forceinline__ void fp4_tile_load(Fp4Batch &B, int j, __amdgpu_buffer_rsrc_t rs,
+                                              int tp, int pn, int lane) {
+    const unsigned to = (unsigned)min(tp, pn - 1) * FP4_TILE_BYTES;
+    B.c0[j] = buf_ld_x4(rs, 16u * lane, to);
+    B.c1[j] = buf_ld_x4(rs, 1024u + 16u * lane, to);
+    B.e0[j] = buf_ld_u8(rs, 2048u + lane, to);
+    B.e1[j] = buf_ld_u8(rs, 2112u + lane, to);
+}
+
+// Position in a wave's batch stream: unit i (relative to the block), batch b.
+struct MsCursor {
+    int i, b;
+};
+__device__ __forceinline__ MsCursor ms_advance(MsCursor c, int nbu) {
+    c.b += MS_WAVES;
+    while (c.b >= nbu) {  // uniform
+        c.b -= nbu;
+        ++c.i;
+    }
+    return c;
+}
+
 // ------------------------------------------------------------ MoE phase A
-template <int WAVES, int TPW>
-__global__ void __launch_bounds__(WAVES * 64)
+// Units u = s * nrbF + rb; a unit has 2 * nb batches: nb of the gate rows,
+// then nb of the up rows (nb = batches of PH tiles).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t moe_a_rsrc(
+    const uint8_t *pg, const uint8_t *pu, const int32_t *ids, int E, int nrbF, int PH, int nb,
+    int unit, int b, bool valid) {
+    // past the wave's last batch the unit may lie past the last slot: no
+    // id is read for it
+    const int s = valid ? unit / nrbF : 0, rb = valid ? unit - s * nrbF : 0;
+    const int e = valid ? ids[s] : -1;
+    const bool ok = valid && e >= 0 && e < E;
+    const uint8_t *mat = (b < nb) ? pg : pu;
+    const uint8_t *base = mat + ((size_t)(ok ? e : 0) * nrbF + rb) * (size_t)PH * FP4_TILE_BYTES;
+    return make_rsrc(uniform_ptr(base), ok ? (unsigned)PH * FP4_TILE_BYTES : 0u);
+}
+
+__global__ void __launch_bounds__(MS_THREADS, 4)
 moe_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__ pu,
                    const uint16_t *__restrict__ x, const int32_t *__restrict__ ids, int E,
-                   int H, int F, int P, int nrbF, int items, float *__restrict__ h_ws) {
+                   int H, int F, int PH, int nrbF, int units, float *__restrict__ h_ws) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint4 *xl = reinterpret_cast<uint4 *>(smem);
-    float *red = reinterpret_cast<float *>(smem + (size_t)P * 512);  // [2][2][WAVES][16]
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
-    stage_x_bf16(xl, x, H, P, tid, WAVES * 64);
-    __syncthreads();
-    const int per = (items + gridDim.x - 1) / gridDim.x;
-    const int i0 = blockIdx.x * per;
-    const int i1 = min(items, i0 + per);
-    int par = 0;
-    for (int it = i0; it < i1; ++it) {
-        const int s = it / nrbF, rb = it % nrbF;
-        const int e = ids[s];
-        if (e < 0 || e >= E) {  // uniform over the workgroup
-            if (wave == 0 && lane < 16) h_ws[(size_t)s * F + rb * RB + lane] = 0.f;
-            continue;
-        }
-        const size_t off = ((size_t)e * nrbF + rb) * (size_t)P * FP4_TILE_BYTES;
-        const uint8_t *gb = pg + off, *ub = pu + off;
-        float ag = 0.f, au = 0.f;
-        for (int p0 = wave; p0 < P; p0 += WAVES * TPW) {
-            Fp4Slot sg[TPW], su[TPW];
+    const int nb = (PH + MS_TPB - 1) / MS_TPB, nbu = 2 * nb;
+    uint4 *xl = reinterpret_cast<uint4 *>(smem);                               // [nb*4 tiles][32]
+    float *part = reinterpret_cast<float *>(smem + (size_t)nb * MS_TPB * 512);  // [RMAX][WAVES][2][16]
+    const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t G = gridDim.x, j = blockIdx.x;
+    const int u0 = (int)(j * units / G), u1 = (int)((j + 1) * units / G);
+    if (u0 >= u1) return;
+#pragma unroll 1
+    for (int ub = u0; ub < u1; ub += MS_RMAX) {
+        const int nr = min(u1 - ub, MS_RMAX);
+        const int T = nr * nbu;
+        int t = (wave - (ub & 3) * (nbu & 3)) & 3;  // absolute batch index = wave mod 4
+        MsCursor ca = {t / nbu, t % nbu};
+        Fp4Batch A, B;
+        float acc = 0.f;
+        {
+            // the first batch loads while x is staged and the sums cleared
+            const __amdgpu_buffer_rsrc_t rs =
+                moe_a_rsrc(pg, pu, ids, E, nrbF, PH, nb, ub + ca.i, ca.b, t < T);
+            const int tb = (ca.b % nb) * MS_TPB;
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                const int p = p0 + j * WAVES;
-                if (p < P) {
-                    sg[j] = fp4_load(gb + (size_t)p * FP4_TILE_BYTES, lane);
-                    su[j] = fp4_load(ub + (size_t)p * FP4_TILE_BYTES, lane);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                const int p = p0 + j * WAVES;
-                if (p < P) {
-                    const uint4 *xp = xl + 32 * p + 4 * kg;
-                    ag = fp4_tile_dot_bf16(sg[j].c0, sg[j].c1, sg[j].e0, sg[j].e1, xp, ag);
-                    au = fp4_tile_dot_bf16(su[j].c0, su[j].c1, su[j].e0, su[j].e1, xp, au);
-                }
-            }
+            for (int q = 0; q < MS_TPB; ++q) fp4_tile_load(A, q, rs, tb + q, PH, lane);
         }
-        ag = reduce_kslices(ag);
-        au = reduce_kslices(au);
-        float *rp = red + par * 2 * WAVES * 16;
-        if (lane < 16) {
-            rp[wave * 16 + lane] = ag;
-            rp[WAVES * 16 + wave * 16 + lane] = au;
+        if (ub == u0) stage_x_bf16(xl, x, H, nb * MS_TPB, tid, MS_THREADS);
+        for (int i = tid; i < nr * MS_WAVES * 32; i += MS_THREADS) part[i] = 0.f;
+        __syncthreads();  // x staged, partial sums cleared
+#pragma unroll 1
+        for (;;) {
+            if (t >= T) break;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                Fp4Batch &Cur = half ? B : A;
+                Fp4Batch &Nxt = half ? A : B;
+                const MsCursor cn = ms_advance(ca, nbu);
+                const bool nvalid = t + MS_WAVES < T;
+                const __amdgpu_buffer_rsrc_t rs =
+                    moe_a_rsrc(pg, pu, ids, E, nrbF, PH, nb, ub + cn.i, cn.b, nvalid);
+                const int tbn = (cn.b % nb) * MS_TPB, tbc = (ca.b % nb) * MS_TPB;
+#pragma unroll
+                for (int q = 0; q < MS_TPB; ++q) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    fp4_tile_load(Nxt, q, rs, tbn + q, PH, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc = fp4_tile_dot_bf16(Cur.c0[q], Cur.c1[q], Cur.e0[q], Cur.e1[q],
+                                            xl + 32 * (tbc + q) + 4 * kg, acc);
+                }
+                // flush at the wave's last batch of this unit's gate or up rows
+                const bool gate = ca.b < nb;
+                const bool last = !nvalid || cn.i != ca.i || (gate && cn.b >= nb);
+                if (last) {
+                    acc = reduce_kslices(acc);
+                    if (lane < 16)
+                        part[((ca.i * MS_WAVES + wave) * 2 + (gate ? 0 : 1)) * 16 + lane] += acc;
+                    acc = 0.f;
+                }
+                t += MS_WAVES;
+                ca = cn;
+                if (t >= T) break;
+            }
         }
         __syncthreads();
-        if (wave == 0 && lane < 16) {
+        for (int r = tid; r < nr * 16; r += MS_THREADS) {
+            const int i = r >> 4, row = r & 15;
             float g = 0.f, u = 0.f;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
-                g += rp[w * 16 + lane];
-                u += rp[WAVES * 16 + w * 16 + lane];
+            for (int w = 0; w < MS_WAVES; ++w) {
+                g += part[((i * MS_WAVES + w) * 2 + 0) * 16 + row];
+                u += part[((i * MS_WAVES + w) * 2 + 1) * 16 + row];
             }
-            h_ws[(size_t)s * F + rb * RB + lane] = g / (1.f + expf(-g)) * u;
+            const int unit = ub + i, s = unit / nrbF, rb = unit - s * nrbF;
+            h_ws[(size_t)s * F + rb * RB + row] = g / (1.f + expf(-g)) * u;
         }
-        par ^= 1;
+        __syncthreads();  // part is reused by the next block
     }
 }
 
 // ------------------------------------------------------------ MoE phase B
-template <int WAVES, int TPW>
-__global__ void __launch_bounds__(WAVES * 64)
+// Units u = s * nrbH + rb; h[s] is staged per run of units of one slot.
+__global__ void __launch_bounds__(MS_THREADS, 4)
 moe_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws,
-                const int32_t *__restrict__ ids, int E, int H, int F, int P, int nrbH,
-                int items, float *__restrict__ part) {
+                const int32_t *__restrict__ ids, int E, int H, int F, int PF, int nrbH,
+                int units, float *__restrict__ part_ws) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float4 *hl = reinterpret_cast<float4 *>(smem);                       // [P*64] float4
-    float *red = reinterpret_cast<float *>(smem + (size_t)P * 1024);    // [2][WAVES][16]
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), kg = lane >> 4;
-    const int per = (items + gridDim.x - 1) / gridDim.x;
-    const int i0 = blockIdx.x * per;
-    const int i1 = min(items, i0 + per);
-    int cur = -1, par = 0;
-    for (int it = i0; it < i1; ++it) {
-        const int s = it / nrbH, rb = it % nrbH;
-        if (s != cur) {  // uniform: stage h[s] (zero past F)
-            __syncthreads();
-            const float4 *src = reinterpret_cast<const float4 *>(h_ws + (size_t)s * F);
-            for (int i = tid; i < P * 64; i += WAVES * 64)
-                hl[i] = (i < F / 4) ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-            __syncthreads();
-            cur = s;
-        }
+    const int nb = (PF + MS_TPB - 1) / MS_TPB;
+    float4 *hl = reinterpret_cast<float4 *>(smem);                               // [nb*4 tiles][64]
+    float *part = reinterpret_cast<float *>(smem + (size_t)nb * MS_TPB * 1024);  // [RMAX][WAVES][16]
+    const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t G = gridDim.x, j = blockIdx.x;
+    const int u0 = (int)(j * units / G), u1 = (int)((j + 1) * units / G);
+#pragma unroll 1
+    for (int ub = u0; ub < u1;) {
+        const int s = ub / nrbH;
         const int e = ids[s];
-        if (e < 0 || e >= E) {
-            if (wave == 0 && lane < 16) part[(size_t)s * H + rb * RB + lane] = 0.f;
-            continue;
-        }
-        const uint8_t *db = pd + ((size_t)e * nrbH + rb) * (size_t)P * FP4_TILE_BYTES;
+        const bool ok = e >= 0 && e < E;
+        const int nr = min(min(u1, (s + 1) * nrbH) - ub, MS_RMAX);  // one slot per block
+        const int rb0 = ub - s * nrbH;
+        const int T = nr * nb;
+        int t = (wave - (ub & 3) * (nb & 3)) & 3;
+        MsCursor ca = {t / nb, t % nb};
+        const uint8_t *ebase = pd + (size_t)(ok ? e : 0) * nrbH * (size_t)PF * FP4_TILE_BYTES;
+        Fp4Batch A, B;
         float acc = 0.f;
-        for (int p0 = wave; p0 < P; p0 += WAVES * TPW) {
-            Fp4Slot sl[TPW];
+        {
+            // the first batch loads while h[s] is staged
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+                uniform_ptr(ebase + (size_t)(rb0 + ca.i) * PF * FP4_TILE_BYTES),
+                (ok && t < T) ? (unsigned)PF * FP4_TILE_BYTES : 0u);
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                const int p = p0 + j * WAVES;
-                if (p < P) sl[j] = fp4_load(db + (size_t)p * FP4_TILE_BYTES, lane);
-            }
+            for (int q = 0; q < MS_TPB; ++q) fp4_tile_load(A, q, rs, ca.b * MS_TPB + q, PF, lane);
+        }
+        __syncthreads();  // the previous block is written out
+        {
+            const float4 *src = reinterpret_cast<const float4 *>(h_ws + (size_t)s * F);
+            for (int i = tid; i < nb * MS_TPB * 64; i += MS_THREADS)
+                hl[i] = (i < F / 4) ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int i = tid; i < nr * MS_WAVES * 16; i += MS_THREADS) part[i] = 0.f;
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (;;) {
+            if (t >= T) break;
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                const int p = p0 + j * WAVES;
-                if (p < P)
-                    acc = fp4_tile_dot_f32(sl[j].c0, sl[j].c1, sl[j].e0, sl[j].e1,
-                                           hl + 64 * p + 8 * kg, acc);
+            for (int half = 0; half < 2; ++half) {
+                Fp4Batch &Cur = half ? B : A;
+                Fp4Batch &Nxt = half ? A : B;
+                const MsCursor cn = ms_advance(ca, nb);
+                const bool nvalid = t + MS_WAVES < T;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+                    uniform_ptr(ebase + (size_t)(rb0 + cn.i) * PF * FP4_TILE_BYTES),
+                    (ok && nvalid) ? (unsigned)PF * FP4_TILE_BYTES : 0u);
+#pragma unroll
+                for (int q = 0; q < MS_TPB; ++q) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    fp4_tile_load(Nxt, q, rs, cn.b * MS_TPB + q, PF, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc = fp4_tile_dot_f32(Cur.c0[q], Cur.c1[q], Cur.e0[q], Cur.e1[q],
+                                           hl + 64 * (ca.b * MS_TPB + q) + 8 * kg, acc);
+                }
+                if (!nvalid || cn.i != ca.i) {
+                    acc = reduce_kslices(acc);
+                    if (lane < 16) part[(ca.i * MS_WAVES + wave) * 16 + lane] += acc;
+                    acc = 0.f;
+                }
+                t += MS_WAVES;
+                ca = cn;
+                if (t >= T) break;
             }
         }
-        acc = reduce_kslices(acc);
-        if (lane < 16) red[par * WAVES * 16 + wave * 16 + lane] = acc;
         __syncthreads();
-        if (wave == 0 && lane < 16) {
+        for (int r = tid; r < nr * 16; r += MS_THREADS) {
+            const int i = r >> 4, row = r & 15;
             float v = 0.f;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) v += red[par * WAVES * 16 + w * 16 + lane];
-            part[(size_t)s * H + rb * RB + lane] = v;
+            for (int w = 0; w < MS_WAVES; ++w) v += part[(i * MS_WAVES + w) * 16 + row];
+            part_ws[(size_t)s * H + (rb0 + i) * RB + row] = v;
         }
-        par ^= 1;
+        ub += nr;
     }
 }
 
@@ -294,52 +397,63 @@ moe_combine_kernel(const float *__restrict__ part, const int32_t *__restrict__ i
                    const float *__restrict__ w, int E, int H, int top_k, void *__restrict__ y,
                    int out_f32, unsigned *__restrict__ status) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
-    if (n < H) {
-        float v = 0.f;
-        for (int s = 0; s < top_k; ++s) {
-            const int e = ids[s];
-            if (e >= 0 && e < E) v = fmaf(w[s], part[(size_t)s * H + n], v);
+    constexpr int C = 16;  // slots whose loads are issued together
+    float v = 0.f;
+    unsigned bad = 0;
+#pragma unroll 1
+    for (int s0 = 0; s0 < top_k; s0 += C) {
+        float pv[C], wv[C];
+        int ev[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int s = s0 + c;
+            ev[c] = s < top_k ? ids[s] : 0;
+            wv[c] = s < top_k ? w[s] : 0.f;
+            pv[c] = (s < top_k && n < H) ? part[(size_t)s * H + n] : 0.f;
         }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if (s0 + c < top_k) {
+                if (ev[c] >= 0 && ev[c] < E) v = fmaf(wv[c], pv[c], v);
+                else bad = 1;
+            }
+        }
+    }
+    if (n < H) {
         if (out_f32)
             reinterpret_cast<float *>(y)[n] = v;
         else
             reinterpret_cast<uint16_t *>(y)[n] = f32_to_bf16(v);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        unsigned bad = 0;
-        for (int s = 0; s < top_k; ++s) {
-            const int e = ids[s];
-            if (e < 0 || e >= E) bad = 1;
-        }
-        status[0] = bad;
-    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) status[0] = bad;
 }
 
 hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd, int64_t E,
                       int64_t H, int64_t F, const uint16_t *x, int top_k, const int32_t *ids,
                       const float *w, uint8_t *workspace, void *y, bool out_f32, int cus,
                       hipStream_t s) {
-    constexpr int WAVES = 4, TPW = 4;
     float *h_ws = reinterpret_cast<float *>(workspace);
     float *part = h_ws + (size_t)top_k * F;
     unsigned *status = reinterpret_cast<unsigned *>(part + (size_t)top_k * H);
     if (top_k > 0) {
         const int PH = (int)ceil_div(H, FP4_TILE_K);  // tiles along H (gate/up rows)
         const int nrbF = (int)(F / RB);
-        const int itemsA = top_k * nrbF;
-        const int gridA = itemsA < cus * 4 ? itemsA : cus * 4;
-        const size_t ldsA = (size_t)PH * 512 + 2 * 2 * WAVES * 16 * 4;
-        hipLaunchKernelGGL((moe_gate_up_kernel<WAVES, TPW>), dim3(gridA), dim3(WAVES * 64), ldsA,
-                           s, pg, pu, x, ids, (int)E, (int)H, (int)F, PH, nrbF, itemsA, h_ws);
+        const int unitsA = top_k * nrbF;
+        const int gridA = unitsA < cus * 4 ? unitsA : cus * 4;
+        const size_t ldsA = (size_t)ceil_div(PH, MS_TPB) * MS_TPB * 512 +
+                            (size_t)MS_RMAX * MS_WAVES * 2 * 16 * 4;
+        hipLaunchKernelGGL(moe_gate_up_kernel, dim3(gridA), dim3(MS_THREADS), ldsA, s, pg, pu, x,
+                           ids, (int)E, (int)H, (int)F, PH, nrbF, unitsA, h_ws);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         const int PF = (int)ceil_div(F, FP4_TILE_K);  // tiles along F (down rows)
         const int nrbH = (int)(H / RB);
-        const int itemsB = top_k * nrbH;
-        const int gridB = itemsB < cus * 4 ? itemsB : cus * 4;
-        const size_t ldsB = (size_t)PF * 1024 + 2 * WAVES * 16 * 4;
-        hipLaunchKernelGGL((moe_down_kernel<WAVES, TPW>), dim3(gridB), dim3(WAVES * 64), ldsB, s,
-                           pd, h_ws, ids, (int)E, (int)H, (int)F, PF, nrbH, itemsB, part);
+        const int unitsB = top_k * nrbH;
+        const int gridB = unitsB < cus * 4 ? unitsB : cus * 4;
+        const size_t ldsB = (size_t)ceil_div(PF, MS_TPB) * MS_TPB * 1024 +
+                            (size_t)MS_RMAX * MS_WAVES * 16 * 4;
+        hipLaunchKernelGGL(moe_down_kernel, dim3(gridB), dim3(MS_THREADS), ldsB, s, pd, h_ws, ids,
+                           (int)E, (int)H, (int)F, PF, nrbH, unitsB, part);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
