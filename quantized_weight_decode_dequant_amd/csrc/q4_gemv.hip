@@ -232,11 +232,11 @@ __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, con
             const int nb = (pn + GV_TPW - 1) / GV_TPW;
             const int T = nr * nb;  // batches of the block in this segment
             // wave w takes the batches whose absolute index (rowblock * nb +
-            // batch) is w mod 4, so how a rowblock's batches are split over
+            // batch) is w mod GV_WAVES, so how a rowblock's batches are split over
             // the waves, and hence its rounding, does not depend on where the
             // workgroup's range starts (single and grouped launches agree
             // bit for bit)
-            int t = (wave - (ub & 3) * (nb & 3)) & 3;
+            int t = (wave - (int)(((int64_t)ub * nb) % GV_WAVES) + GV_WAVES) % GV_WAVES;
             GvCursor ca = {t / nb, t % nb};
             GvBatch A, B;
             float acc = 0.f;
