@@ -16,6 +16,8 @@
 //      (fp32 in LDS) -> workspace part[s][H].
 //   C  y[n] = sum_s w[s] * part[s][n] in slot order (deterministic, no
 //      atomics), rounded once; also writes the status word.
+// When h of all slots fits in LDS (128 KB: e.g. top-16 of F = 2048), B and C
+// are one launch that computes whole rowblocks of y (see below).
 // A and B give each workgroup a contiguous range of units and stream them
 // like the Q4 decode GEMV: a unit's tiles are cut into batches of 4, every
 // fourth batch goes to the same wave, and each wave streams its batches
@@ -391,6 +393,128 @@ moe_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws,
     }
 }
 
+// ------------------------------------------------------------ MoE phase B+C fused
+// When h of every slot fits in LDS (top_k * F <= MF_HMAX floats), one
+// workgroup of 16 waves per CU stages all of them once and computes whole
+// output rowblocks of y: unit = rowblock rb of H, its batches (slot s, 4 tiles
+// of F) go to the waves in turn, each wave sums w_s * (its batches' dot
+// products), and the 16 wave sums are added in wave order (deterministic).
+// This replaces the per-slot partials and the combine launch.
+constexpr int MF_WAVES = 16;
+constexpr int MF_THREADS = MF_WAVES * 64;
+constexpr int MF_HMAX = 32768;  // fp32 values of h staged (128 KB)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mf_rsrc(const uint8_t *pd, const int32_t *ids,
+                                                          int E, int nrbH, int PF, int rb, int s,
+                                                          bool valid) {
+    const int e = valid ? ids[s] : -1;
+    const bool ok = valid && e >= 0 && e < E;
+    const uint8_t *base = pd + ((size_t)(ok ? e : 0) * nrbH + rb) * (size_t)PF * FP4_TILE_BYTES;
+    return make_rsrc(uniform_ptr(base), ok ? (unsigned)PF * FP4_TILE_BYTES : 0u);
+}
+
+__global__ void __launch_bounds__(MF_THREADS, 1)
+moe_down_fused_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws,
+                      const int32_t *__restrict__ ids, const float *__restrict__ w, int E, int H,
+                      int F, int PF, int nrbH, int top_k, void *__restrict__ y, int out_f32,
+                      unsigned *__restrict__ status) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int nb = (PF + MS_TPB - 1) / MS_TPB;       // batches per slot
+    const int hstride = nb * MS_TPB * 64;             // float4 per staged slot
+    float4 *hl = reinterpret_cast<float4 *>(smem);
+    float *red = reinterpret_cast<float *>(smem + (size_t)top_k * hstride * 16);  // [WAVES][16]
+    float *wl = red + MF_WAVES * 16;                                                // [top_k]
+    const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (blockIdx.x == 0 && tid == 0) {
+        unsigned bad = 0;
+        for (int s = 0; s < top_k; ++s)
+            if (ids[s] < 0 || ids[s] >= E) bad = 1;
+        status[0] = bad;
+    }
+    const int T = top_k * nb;  // batches per unit
+    const int G = gridDim.x;
+    const MsCursor first = {wave / nb, wave % nb};  // a wave's first batch of every unit
+    Fp4Batch A, B;
+    int rb = blockIdx.x;
+    {
+        const __amdgpu_buffer_rsrc_t rs = mf_rsrc(pd, ids, E, nrbH, PF, rb, first.i, wave < T);
+#pragma unroll
+        for (int q = 0; q < MS_TPB; ++q) fp4_tile_load(A, q, rs, first.b * MS_TPB + q, PF, lane);
+    }
+    // while the first batch loads: stage every slot's h and weight
+    for (int i = tid; i < top_k; i += MF_THREADS) {
+        const int e = ids[i];
+        wl[i] = (e >= 0 && e < E) ? w[i] : 0.f;  // an invalid id contributes nothing
+    }
+    for (int i = tid; i < top_k * hstride; i += MF_THREADS) {
+        const int s = i / hstride, c = i - s * hstride;
+        hl[i] = (c < F / 4) ? reinterpret_cast<const float4 *>(h_ws + (size_t)s * F)[c]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (;;) {
+        // this unit's first batch is in A; the last step of the unit already
+        // loads the next unit's first batch
+        int t = wave, steps = 0;
+        MsCursor ca = first;
+        float acc = 0.f;
+#pragma unroll 1
+        for (;;) {
+            if (t >= T) break;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                Fp4Batch &Cur = half ? B : A;
+                Fp4Batch &Nxt = half ? A : B;
+                MsCursor cn = ca;
+                cn.b += MF_WAVES;
+                while (cn.b >= nb) {  // uniform
+                    cn.b -= nb;
+                    ++cn.i;
+                }
+                const bool more = t + MF_WAVES < T;
+                const int nrb = more ? rb : rb + G;
+                if (!more) cn = first;
+                const bool nvalid = more || (nrb < nrbH && wave < T);
+                const __amdgpu_buffer_rsrc_t rs = mf_rsrc(pd, ids, E, nrbH, PF, nrb, cn.i, nvalid);
+                const float4 *hs = hl + ca.i * hstride;
+                float bs = 0.f;
+#pragma unroll
+                for (int q = 0; q < MS_TPB; ++q) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    fp4_tile_load(Nxt, q, rs, cn.b * MS_TPB + q, PF, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    bs = fp4_tile_dot_f32(Cur.c0[q], Cur.c1[q], Cur.e0[q], Cur.e1[q],
+                                          hs + 64 * (ca.b * MS_TPB + q) + 8 * kg, bs);
+                }
+                acc = fmaf(wl[ca.i], bs, acc);
+                ++steps;
+                t += MF_WAVES;
+                ca = cn;
+                if (t >= T) break;
+            }
+        }
+        acc = reduce_kslices(acc);
+        if (lane < 16) red[wave * 16 + lane] = acc;
+        __syncthreads();
+        if (tid < 16) {
+            float v = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < MF_WAVES; ++wv) v += red[wv * 16 + tid];
+            const int n = rb * RB + tid;
+            if (out_f32)
+                reinterpret_cast<float *>(y)[n] = v;
+            else
+                reinterpret_cast<uint16_t *>(y)[n] = f32_to_bf16(v);
+        }
+        __syncthreads();  // red is reused by the next unit
+        rb += G;
+        if (rb >= nrbH) break;
+        if (steps & 1) A = B;  // the next unit's first batch went to B
+    }
+}
+
 // ------------------------------------------------------------ MoE phase C
 __global__ void __launch_bounds__(256)
 moe_combine_kernel(const float *__restrict__ part, const int32_t *__restrict__ ids,
@@ -448,6 +572,16 @@ hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd, i
         if (err != hipSuccess) return err;
         const int PF = (int)ceil_div(F, FP4_TILE_K);  // tiles along F (down rows)
         const int nrbH = (int)(H / RB);
+        const int64_t hstaged = (int64_t)top_k * ceil_div(PF, MS_TPB) * MS_TPB * 256;
+        if (hstaged <= MF_HMAX) {
+            // down projection and the weighted sum over slots in one launch
+            const int gridF = nrbH < cus ? nrbH : cus;
+            const size_t ldsF = (size_t)hstaged * 4 + (size_t)MF_WAVES * 16 * 4 + (size_t)top_k * 4;
+            hipLaunchKernelGGL(moe_down_fused_kernel, dim3(gridF), dim3(MF_THREADS), ldsF, s, pd,
+                               h_ws, ids, w, (int)E, (int)H, (int)F, PF, nrbH, top_k, y,
+                               out_f32 ? 1 : 0, status);
+            return hipGetLastError();
+        }
         const int unitsB = top_k * nrbH;
         const int gridB = unitsB < cus * 4 ? unitsB : cus * 4;
         const size_t ldsB = (size_t)ceil_div(PF, MS_TPB) * MS_TPB * 1024 +
