@@ -265,9 +265,9 @@ __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, con
 #pragma unroll
             for (int w = 1; w < GV_WAVES; ++w) v += pp[16 * w];
             if (it.out_f32)
-                reinterpret_cast<float *>(it.y)[r0 + r] = v;
+                st_global<float>(it.y, (size_t)r0 + r, v);
             else
-                reinterpret_cast<uint16_t *>(it.y)[r0 + r] = f32_to_bf16(v);
+                st_global<uint16_t>(it.y, (size_t)r0 + r, f32_to_bf16(v));
         }
     }
 }

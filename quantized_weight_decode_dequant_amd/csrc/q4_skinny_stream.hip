@@ -26,13 +26,14 @@
 namespace qg {
 
 constexpr int SS_TPB = 4;  // tiles per batch
-constexpr int SS_R = 4;    // rowblocks a wave carries across segments
 
 template <int MT>
 struct SsCfg {
     // waves per workgroup: the most whose registers fit without real spills
     static constexpr int WAVES = MT == 1 ? 16 : 12;
     static constexpr int THREADS = WAVES * 64;
+    // rowblocks whose results a wave keeps in registers (stored together)
+    static constexpr int R = MT == 1 ? 4 : 2;
     static constexpr int MP = 16 * MT;               // padded activation rows
     static constexpr int SEGK = 32 / MT;             // tiles per staged segment
     static constexpr int RS = SEGK * 128 + 8;        // LDS row stride in bf16 (16-byte pad)
@@ -40,6 +41,7 @@ struct SsCfg {
     static constexpr size_t LDS = LDS_X + (size_t)2 * SEGK * MP * 4;
 };
 static_assert(SsCfg<1>::LDS <= 160 * 1024 && SsCfg<2>::LDS <= 160 * 1024, "LDS budget");
+static_assert(SsCfg<1>::SEGK % 8 == 0 && SsCfg<2>::SEGK % 8 == 0, "segments hold an even number of batches");
 
 struct SsBatch {
     u32x4_t c[SS_TPB];
@@ -157,6 +159,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ss_rsrc(const WorkItem &it, in
     return make_rsrc(uniform_ptr(base), valid ? (unsigned)pn * Q4_TILE_BYTES : 0u);
 }
 
+// Store a rowblock's 16 x M results.
 template <int MT>
 __device__ __forceinline__ void ss_store(const WorkItem &it, int rb, int M, const f32x4_t acc[MT],
                                          int lane) {
@@ -169,9 +172,9 @@ __device__ __forceinline__ void ss_store(const WorkItem &it, int rb, int M, cons
             const int m = 16 * mt + 4 * kg + e;
             if (m < M) {
                 if (it.out_f32)
-                    reinterpret_cast<float *>(it.y)[(size_t)m * it.N + n] = acc[mt][e];
+                    st_global<float>(it.y, (size_t)m * it.N + n, acc[mt][e]);
                 else
-                    reinterpret_cast<uint16_t *>(it.y)[(size_t)m * it.N + n] = f32_to_bf16(acc[mt][e]);
+                    st_global<uint16_t>(it.y, (size_t)m * it.N + n, f32_to_bf16(acc[mt][e]));
             }
         }
 }
@@ -182,144 +185,121 @@ __device__ __forceinline__ void ss_zero(f32x4_t a[MT]) {
     for (int mt = 0; mt < MT; ++mt) a[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// The running sums of the wave's i-th rowblock of the block (i uniform) in
-// and out of the working registers, so each rowblock accumulates its tiles
-// in K order across the segments.
-template <int MT>
-__device__ __forceinline__ void ss_pick(const f32x4_t acc[SS_R][MT], int i, f32x4_t cur[MT]) {
+// The first batch (tiles 0..3 of the segment) of rowblock rb.
+__device__ __forceinline__ void ss_first(SsBatch &A, const WorkItem &it, int rb, int pbase, int pn,
+                                         bool valid, int lane) {
+    const __amdgpu_buffer_rsrc_t rs = ss_rsrc(it, rb, pbase, pn, valid);
+    const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
 #pragma unroll
-    for (int r = 0; r < SS_R; ++r)
-        if (r == i)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) cur[mt] = acc[r][mt];
-}
-template <int MT>
-__device__ __forceinline__ void ss_put(f32x4_t acc[SS_R][MT], int i, const f32x4_t cur[MT]) {
-#pragma unroll
-    for (int r = 0; r < SS_R; ++r)
-        if (r == i)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[r][mt] = cur[mt];
-}
-
-// Position in a wave's batch stream: its i-th rowblock, batch b.
-struct SsCursor {
-    int i, b;
-};
-__device__ __forceinline__ SsCursor ss_next(SsCursor c, int nb) {
-    if (++c.b == nb) {
-        c.b = 0;
-        ++c.i;
+    for (int j = 0; j < SS_TPB; ++j) {
+        const unsigned to = (unsigned)min(j, pn - 1) * Q4_TILE_BYTES;
+        A.c[j] = buf_ld_x4(rs, lc, to);
+        A.sb[j] = buf_ld_x2(rs, ls, to);
     }
-    return c;
 }
 
-// Rowblocks [u0, u1) of one matrix.
+// Batches of one rowblock and segment: nb real ones (4 tiles each, the last
+// possibly ragged), rounded up to an even count so that the double buffer
+// alternates A, B, A, ... identically for every rowblock (the padding batch
+// reads through an empty buffer and meets zero X, adding exactly zero).
+__device__ __forceinline__ int ss_batches_even(int pn) {
+    const int nb = (pn + SS_TPB - 1) / SS_TPB;
+    return nb + (nb & 1);
+}
+
+// This wave's rowblocks i0 .. i0 + n - 1 (n <= R; rowblock of index i is
+// first + WAVES * i) over one segment, each into acc[r] (r = i - i0, a
+// compile-time index).  A holds the first batch of rowblock i0 on entry; on
+// exit A holds the first batch of rowblock i0 + n, which is loaded (if
+// nextvalid) during the last step, so the stream never drains.
+template <int MT, int R>
+__device__ __forceinline__ void ss_block(SsBatch &A, SsBatch &B, const WorkItem &it, int first,
+                                         int i0, int n, bool nextvalid, int pbase, int pn,
+                                         const uint16_t *xl, const float *xs, int lane,
+                                         const Q4Consts &kq, f32x4_t acc[R][MT]) {
+    typedef SsCfg<MT> C;
+    const int nb = (pn + SS_TPB - 1) / SS_TPB, nbe = ss_batches_even(pn);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r >= n) break;  // uniform
+        const int rb = first + C::WAVES * (i0 + r);
+        const int rbn = rb + C::WAVES;  // the next rowblock's first batch follows this one's last
+        const bool vnext = (r + 1 < n) || nextvalid;
+#pragma unroll 1
+        for (int b = 0; b < nbe; b += 2) {
+            // batch b (in A) computed while b + 1 loads into B
+            ss_step<MT>(B, ss_rsrc(it, rb, pbase, pn, b + 1 < nb), (b + 1) * SS_TPB, pn, A,
+                        b * SS_TPB, xl, xs, lane, kq, acc[r]);
+            // batch b + 1 (in B) computed while b + 2, or the next rowblock's
+            // first batch, loads into A
+            const bool more = b + 2 < nbe;
+            ss_step<MT>(A, ss_rsrc(it, more ? rb : rbn, pbase, pn, more ? (b + 2 < nb) : vnext),
+                        more ? (b + 2) * SS_TPB : 0, pn, B, (b + 1) * SS_TPB, xl, xs, lane, kq,
+                        acc[r]);
+        }
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void ss_zero_block(f32x4_t acc[SsCfg<MT>::R][MT]) {
+#pragma unroll
+    for (int r = 0; r < SsCfg<MT>::R; ++r) ss_zero<MT>(acc[r]);
+}
+
+// Rowblocks [u0, u1) of one matrix; wave w owns rowblocks u0 + w + WAVES * i.
+// Results are kept in registers for R rowblocks and stored together (a store
+// in the middle of the load stream makes the wave wait for loads issued
+// before it).
 template <int MT>
 __device__ __forceinline__ void ss_range(const WorkItem &it, int u0, int u1, int M, uint16_t *xl,
                                          float *xs, int tid, int lane, int wave,
                                          const Q4Consts &kq) {
     typedef SsCfg<MT> C;
+    constexpr int R = C::R;
     const uint16_t *X = reinterpret_cast<const uint16_t *>(it.x);
     const int nseg = (it.P + C::SEGK - 1) / C::SEGK;
+    const int first = u0 + wave;
+    SsBatch A, B;
+    f32x4_t acc[R][MT];
     if (nseg == 1) {
-        // the whole K is one segment: X is staged once, each wave streams all
-        // of its rowblocks and stores each one's results after its last batch
-        const int pn = it.P, nb = (pn + SS_TPB - 1) / SS_TPB;
+        // the whole K is one segment: X is staged once and every wave streams
+        // all of its rowblocks without a barrier
+        const int pn = it.P, nbe = ss_batches_even(pn);
         const int mine = (u1 - u0 > wave) ? (u1 - u0 - wave + C::WAVES - 1) / C::WAVES : 0;
-        const int T = mine * nb;
-        SsBatch A, B;
-        f32x4_t cur[MT];
-        ss_zero<MT>(cur);
-        SsCursor ca = {0, 0};
-        {
-            const __amdgpu_buffer_rsrc_t rs = ss_rsrc(it, u0 + wave, 0, pn, T > 0);
-            const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
-#pragma unroll
-            for (int j = 0; j < SS_TPB; ++j) {
-                const unsigned to = (unsigned)min(j, pn - 1) * Q4_TILE_BYTES;
-                A.c[j] = buf_ld_x4(rs, lc, to);
-                A.sb[j] = buf_ld_x2(rs, ls, to);
-            }
-        }
+        ss_first(A, it, first, 0, pn, mine > 0, lane);
         __syncthreads();  // nobody still reads the previous range's X
-        ss_stage<MT>(X, M, it.K, 0, nb * SS_TPB, xl, xs, tid);
-        int t = 0;
+        ss_stage<MT>(X, M, it.K, 0, nbe * SS_TPB, xl, xs, tid);
 #pragma unroll 1
-        for (;;) {
-            if (t >= T) break;
-            const SsCursor cb = ss_next(ca, nb);
-            ss_step<MT>(B, ss_rsrc(it, u0 + wave + C::WAVES * cb.i, 0, pn, t + 1 < T), cb.b * SS_TPB,
-                        pn, A, ca.b * SS_TPB, xl, xs, lane, kq, cur);
-            if (ca.b == nb - 1) {
-                ss_store<MT>(it, u0 + wave + C::WAVES * ca.i, M, cur, lane);
-                ss_zero<MT>(cur);
-            }
-            if (t + 1 >= T) break;
-            const SsCursor cc = ss_next(cb, nb);
-            ss_step<MT>(A, ss_rsrc(it, u0 + wave + C::WAVES * cc.i, 0, pn, t + 2 < T), cc.b * SS_TPB,
-                        pn, B, cb.b * SS_TPB, xl, xs, lane, kq, cur);
-            if (cb.b == nb - 1) {
-                ss_store<MT>(it, u0 + wave + C::WAVES * cb.i, M, cur, lane);
-                ss_zero<MT>(cur);
-            }
-            t += 2;
-            ca = cc;
+        for (int i0 = 0; i0 < mine; i0 += R) {
+            const int n = min(R, mine - i0);
+            ss_zero_block<MT>(acc);
+            ss_block<MT, R>(A, B, it, first, i0, n, i0 + n < mine, 0, pn, xl, xs, lane, kq, acc);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (r < n) ss_store<MT>(it, first + C::WAVES * (i0 + r), M, acc[r], lane);
         }
         return;
     }
-    // K spans several segments: blocks of C::WAVES * SS_R rowblocks, each
-    // wave's (up to SS_R) sums kept in registers across the segments
+    // K spans several segments: blocks of WAVES * R rowblocks whose sums stay
+    // in registers across the segments; X is staged once per block and segment
 #pragma unroll 1
-    for (int ub = u0; ub < u1; ub += C::WAVES * SS_R) {
+    for (int ub = u0; ub < u1; ub += C::WAVES * R) {
         const int left = u1 - ub;
-        int mine = (left > wave) ? (left - wave + C::WAVES - 1) / C::WAVES : 0;
-        mine = min(mine, SS_R);
-        f32x4_t acc[SS_R][MT];
-#pragma unroll
-        for (int r = 0; r < SS_R; ++r) ss_zero<MT>(acc[r]);
+        const int n = min(R, (left > wave) ? (left - wave + C::WAVES - 1) / C::WAVES : 0);
+        const int i0 = (ub - u0) / C::WAVES;
+        ss_zero_block<MT>(acc);
 #pragma unroll 1
         for (int seg = 0; seg < nseg; ++seg) {
             const int pbase = seg * C::SEGK;
-            const int pn = min(C::SEGK, it.P - pbase), nb = (pn + SS_TPB - 1) / SS_TPB;
-            const int T = mine * nb;
-            SsBatch A, B;
-            f32x4_t cur[MT];
-            SsCursor ca = {0, 0};
-            {
-                const __amdgpu_buffer_rsrc_t rs = ss_rsrc(it, ub + wave, pbase, pn, T > 0);
-                const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
-#pragma unroll
-                for (int j = 0; j < SS_TPB; ++j) {
-                    const unsigned to = (unsigned)min(j, pn - 1) * Q4_TILE_BYTES;
-                    A.c[j] = buf_ld_x4(rs, lc, to);
-                    A.sb[j] = buf_ld_x2(rs, ls, to);
-                }
-            }
+            const int pn = min(C::SEGK, it.P - pbase), nbe = ss_batches_even(pn);
+            ss_first(A, it, first + C::WAVES * i0, pbase, pn, n > 0, lane);
             __syncthreads();  // nobody still reads the previous segment of X
-            ss_stage<MT>(X, M, it.K, seg, nb * SS_TPB, xl, xs, tid);
-            int t = 0;
-#pragma unroll 1
-            for (;;) {
-                if (t >= T) break;
-                const SsCursor cb = ss_next(ca, nb);
-                if (ca.b == 0) ss_pick<MT>(acc, ca.i, cur);
-                ss_step<MT>(B, ss_rsrc(it, ub + wave + C::WAVES * cb.i, pbase, pn, t + 1 < T),
-                            cb.b * SS_TPB, pn, A, ca.b * SS_TPB, xl, xs, lane, kq, cur);
-                if (ca.b == nb - 1) ss_put<MT>(acc, ca.i, cur);
-                if (t + 1 >= T) break;
-                const SsCursor cc = ss_next(cb, nb);
-                if (cb.b == 0) ss_pick<MT>(acc, cb.i, cur);
-                ss_step<MT>(A, ss_rsrc(it, ub + wave + C::WAVES * cc.i, pbase, pn, t + 2 < T),
-                            cc.b * SS_TPB, pn, B, cb.b * SS_TPB, xl, xs, lane, kq, cur);
-                if (cb.b == nb - 1) ss_put<MT>(acc, cb.i, cur);
-                t += 2;
-                ca = cc;
-            }
+            ss_stage<MT>(X, M, it.K, seg, nbe * SS_TPB, xl, xs, tid);
+            ss_block<MT, R>(A, B, it, first, i0, n, false, pbase, pn, xl, xs, lane, kq, acc);
         }
 #pragma unroll
-        for (int r = 0; r < SS_R; ++r)
-            if (r < mine) ss_store<MT>(it, ub + wave + C::WAVES * r, M, acc[r], lane);
+        for (int r = 0; r < R; ++r)
+            if (r < n) ss_store<MT>(it, first + C::WAVES * (i0 + r), M, acc[r], lane);
     }
 }
 

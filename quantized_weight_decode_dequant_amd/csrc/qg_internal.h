@@ -245,6 +245,14 @@ __device__ __forceinline__ T ld_global(const T *p) {
     return *(const __attribute__((address_space(1))) T *)p;
 }
 
+// Store through the global address space.  Output pointers read from a work
+// list are generic, and a FLAT store also counts against the LDS counter, so
+// every later LDS read of the wave would wait for the store to complete.
+template <typename T>
+__device__ __forceinline__ void st_global(void *base, size_t i, T v) {
+    ((__attribute__((address_space(1))) T *)base)[i] = v;
+}
+
 // The two constants of the nibble unpack, held in VGPRs.  gfx9 VOP3
 // instructions read at most one SGPR or literal, so with both operands in
 // registers (a & mask) | magic selects to a single v_and_or_b32.  They are

@@ -177,10 +177,10 @@ __device__ __forceinline__ void sk_q4_range(const WorkItem &it, int u0, int u1, 
                             const int m = 16 * mt + 4 * kg + e;
                             if (m < M) {
                                 if (it.out_f32)
-                                    reinterpret_cast<float *>(it.y)[(size_t)m * N + n] = acc[i][r][mt][e];
+                                    st_global<float>(it.y, (size_t)m * N + n, acc[i][r][mt][e]);
                                 else
-                                    reinterpret_cast<uint16_t *>(it.y)[(size_t)m * N + n] =
-                                        f32_to_bf16(acc[i][r][mt][e]);
+                                    st_global<uint16_t>(it.y, (size_t)m * N + n,
+                                                        f32_to_bf16(acc[i][r][mt][e]));
                             }
                         }
                 }

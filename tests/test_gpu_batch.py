@@ -143,3 +143,31 @@ def test_batch_verification_pass_full(M):
     single = pkg.qgemm_skinny_run(Q4, g.packed, M, g.N, g.K, g.X)
     torch.cuda.synchronize()
     assert torch.equal(single, g.Y)
+
+
+@pytest.mark.parametrize("M", [2, 5, 17])
+@pytest.mark.parametrize("out_dtype", [pkg.OUT_F32, pkg.OUT_BF16])
+def test_batch_skinny_writes_stay_inside_y(M, out_dtype):
+    """Every output tile lives inside a larger buffer filled with a sentinel:
+    after the grouped launch the bytes past each Y (ragged N, M not a multiple
+    of 16) are unchanged and Y matches the single-matrix call."""
+    note("batch skinny bounds M=%d out=%d" % (M, out_dtype))
+    shapes = [(40, 192), (33, 1216), (130, 640)]
+    mats = _mats(98, shapes)
+    dt = torch.float32 if out_dtype == pkg.OUT_F32 else torch.bfloat16
+    pad = 4096
+    entries, bufs, singles = [], [], []
+    for i, m in enumerate(mats):
+        p = weights.pack_q4(m, DEV)
+        Xd = weights.to_device(synth.activations(99, M, m.K, item=i), DEV)
+        buf = torch.full((M * m.N + pad,), 7.0, dtype=dt, device=DEV)
+        Y = buf[:M * m.N].view(M, m.N)
+        entries.append((p, m.N, m.K, Xd, Y))
+        bufs.append(buf)
+        singles.append(pkg.qgemm_skinny_run(Q4, p, M, m.N, m.K, Xd, out_dtype=out_dtype))
+    plan = pkg.qg_batch_plan_build(Q4, M, entries, out_dtype)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    for (p, N, K, Xd, Y), buf, s in zip(entries, bufs, singles):
+        assert torch.all(buf[M * N:] == 7.0), "write past Y for N=%d K=%d" % (N, K)
+        assert torch.equal(Y, s)
