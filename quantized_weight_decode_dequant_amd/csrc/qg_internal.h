@@ -94,8 +94,8 @@ size_t q4_gemv_lds_bytes(int64_t kmax);
 int q4_gemv_wgs_per_cu();
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts,
                                int grid, int64_t kmax, hipStream_t s);
-int q4_skinny_wgs_per_cu(int64_t M);
-// streaming skinny kernel (one 8-wave workgroup per CU, X staged whole)
+// streaming skinny kernel (one workgroup of 16 waves for M <= 16, 12 waves
+// for M <= 32, per CU; the X slice of a segment staged whole in LDS)
 int q4_skinny_stream_wgs_per_cu();
 bool q4_skinny_stream_fits(int64_t N, int cus);
 hipError_t launch_q4_skinny_stream(const uint8_t *packed, const uint16_t *X, void *Y,
@@ -212,21 +212,13 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
     return reinterpret_cast<const uint8_t *>(((unsigned long long)hi << 32) | lo);
 }
 
-// Non-temporal load of the T at byte offset `off` from a wave-uniform base:
-// with an unsigned 32-bit offset the address selects the SGPR-base +
-// VGPR-offset form of global_load, no 64-bit address per load.
-template <typename T>
-__device__ __forceinline__ T ld_nt_off(const void *base, unsigned off) {
-    typedef const __attribute__((address_space(1))) char gchar;
-    typedef const __attribute__((address_space(1))) T gT;
-    gchar *b = (gchar *)base;
-    return __builtin_nontemporal_load((gT *)(b + off));
-}
-
 // Buffer resource over [base, base + bytes) for raw buffer loads (gfx9
 // descriptor word 3).  Loads through it take the wave-uniform part of the
-// address in an SGPR (soffset) and one 32-bit per-lane VGPR offset; any byte
-// at or past `bytes` reads as zero.
+// address in an SGPR (soffset) and one 32-bit per-lane VGPR offset.  The
+// range check applies to the VGPR offset: a load whose VGPR offset is at or
+// past `bytes` reads zero without touching memory (so does every load through
+// a resource of 0 bytes), but the SGPR offset is added unchecked, so callers
+// keep SGPR offsets inside the buffer.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              0x00020000);

@@ -10,10 +10,10 @@
 // group) on the VALU: acc += s * C + (b - 128 s) * sum_{k in g} X[m, k].
 //
 // The X slices staged in LDS have rows padded by 16 bytes so the 16
-// A-operand rows of one MFMA hit distinct banks.  The kernel also runs over
-// a device work list of independent matrices (one launch for a whole
-// verification pass); see sk_q4_range for its work split.  The int8 path
-// lives in q8_skinny.hip.
+// A-operand rows of one MFMA hit distinct banks; see sk_q4_range for the work
+// split.  This kernel serves single matrices too small to fill the chip with
+// the streaming kernel of q4_skinny_stream.hip; the int8 path lives in
+// q8_skinny.hip.
 #include "qg_internal.h"
 
 namespace qg {
@@ -196,34 +196,21 @@ __device__ __forceinline__ void sk_q4_range(const WorkItem &it, int u0, int u1, 
 #define SK_M16 1, 8, 1, 6, 3
 #define SK_M32 2, 4, 1, 4, 2
 
-template <bool LIST, int MT, int TPS, int RPI, int NI, int WPC>
+template <int MT, int TPS, int RPI, int NI, int WPC>
 __global__ void __launch_bounds__(SK_THREADS, WPC)
-q4_skinny_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
-                 WorkItem single, int M) {
+q4_skinny_kernel(WorkItem it, int M) {
     typedef SkCfg<MT, TPS, RPI, NI> C;
     __shared__ __attribute__((aligned(16))) uint16_t xl[C::MP * C::RS];
     __shared__ __attribute__((aligned(16))) float xs[2 * TPS * C::MP];  // [group-in-segment][m]
-    const int tid = threadIdx.x;
     const Q4Consts kq = q4_consts();
-    if (!LIST) {
-        const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
-        const int u0 = (int)(j * n / g), u1 = (int)((j + 1) * n / g);
-        if (u0 < u1) sk_q4_range<MT, TPS, RPI, NI>(single, u0, u1, M, xl, xs, tid, kq);
-        return;
-    }
-    const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
-#pragma unroll 1
-    for (int i = s.item; i < e.item || (i == e.item && e.unit > 0); ++i) {
-        const WorkItem it = items[i];
-        const int u0 = (i == s.item) ? s.unit : 0;
-        const int u1 = (i == e.item) ? e.unit : it.units;
-        if (u0 < u1) sk_q4_range<MT, TPS, RPI, NI>(it, u0, u1, M, xl, xs, tid, kq);
-    }
+    const int64_t n = it.units, g = gridDim.x, j = blockIdx.x;
+    const int u0 = (int)(j * n / g), u1 = (int)((j + 1) * n / g);
+    if (u0 < u1) sk_q4_range<MT, TPS, RPI, NI>(it, u0, u1, M, xl, xs, (int)threadIdx.x, kq);
 }
 
 static inline int min_grid(int units, int cap) { return units < cap ? units : cap; }
 
-int q4_skinny_wgs_per_cu(int64_t M) { return M <= 16 ? 3 : 2; }
+static int q4_skinny_wgs_per_cu(int64_t M) { return M <= 16 ? 3 : 2; }
 
 hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y, int64_t M,
                             int64_t N, int64_t K, bool out_f32, int cus, hipStream_t s) {
@@ -239,11 +226,11 @@ hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y, i
     // blocks of 32 rowblocks unless that leaves CUs idle
     const int grid = min_grid((int)ceil_div(it.units, 8), cus * q4_skinny_wgs_per_cu(M));
     if (M <= 16)
-        hipLaunchKernelGGL((q4_skinny_kernel<false, SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s,
-                           (const WorkItem *)nullptr, (const WorkStart *)nullptr, it, (int)M);
+        hipLaunchKernelGGL((q4_skinny_kernel<SK_M16>), dim3(grid), dim3(SK_THREADS), 0, s, it,
+                           (int)M);
     else
-        hipLaunchKernelGGL((q4_skinny_kernel<false, SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s,
-                           (const WorkItem *)nullptr, (const WorkStart *)nullptr, it, (int)M);
+        hipLaunchKernelGGL((q4_skinny_kernel<SK_M32>), dim3(grid), dim3(SK_THREADS), 0, s, it,
+                           (int)M);
     return hipGetLastError();
 }
 
