@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -59,6 +61,7 @@ def traffic_from_profiles(kernel: str):
 
 STEP_KERNEL = "q4_gemv_kernel<true>"
 COPY_BYTES = 1 << 30
+PLAIN_READ_BYTES = 4 << 30   # larger than every cache level
 
 
 def _csv_rows(path):
@@ -173,7 +176,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-m16", action="store_true")
+    ap.add_argument("--no-m16", action="store_true", help="skip the verification passes")
+    ap.add_argument("--verify-m", default="16,32",
+                    help="activation rows of the timed verification passes (comma separated)")
+    ap.add_argument("--no-kernel-compare", action="store_true",
+                    help="skip timing both Q4 kernel families at M = 1, 2, 4")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the single-GEMV, int8 and MoE workloads")
     ap.add_argument("--traffic-pass", action="store_true",
@@ -242,6 +249,43 @@ def main():
     achieved = gbs
     traffic = traffic_from_profiles("q4_gemv_step")
 
+    # ---- spread: 200 more steps in 20 groups of 10, an event pair around
+    # each group (an event pair around every single launch reads about 3%
+    # below the kernel's duration in the kernel trace, so it is not used)
+    n_grp, per_grp = 20, 10
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_grp + 1)]
+    ev[0].record()
+    for k in range(n_grp):
+        for _ in range(per_grp):
+            pkg.qg_batch_run(plan)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    grp = np.array([ev[k].elapsed_time(ev[k + 1]) / per_grp for k in range(n_grp)])
+    p10, p50, p90 = (float(np.percentile(grp, q)) for q in (10, 50, 90))
+    log("step spread (%d groups of %d): p10 %.4f, median %.4f, p90 %.4f ms" % (
+        n_grp, per_grp, p10, p50, p90))
+    del ev
+
+    # ---- the plain-read ceiling on this GPU, same run: best of a few grids
+    rd = torch.empty(PLAIN_READ_BYTES, dtype=torch.uint8, device=dev)
+    rd.fill_(1)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    plain_best, plain_grid = 0.0, 0
+    for per_cu in (2, 4, 8):
+        grid = props.multi_processor_count * per_cu
+        pkg.qg_plain_read(rd, sink, grid)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            pkg.qg_plain_read(rd, sink, grid)
+        e1.record()
+        torch.cuda.synchronize()
+        r = PLAIN_READ_BYTES / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+        if r > plain_best:
+            plain_best, plain_grid = r, grid
+    log("plain read: %.1f GB/s (grid %d)" % (plain_best, plain_grid))
+    del rd, sink
+
     # ---- for comparison: the same step as one qgemv_run launch per GEMV (HIP graph)
     graph = workloads.capture_graph(lambda: workloads.run_step_eager(step))
     graph.replay()
@@ -282,6 +326,13 @@ def main():
             "ms_per_step_one_launch_per_gemv": round(ms_per_launch_graph, 4),
         },
         "pct_of_peak": round(100 * gbs / roofline.HBM_PEAK_GBS, 2),
+        "pct_of_plain_read": round(100 * gbs / plain_best, 2),
+        "plain_read": {"value": round(plain_best, 1), "unit": "GB/s", "bytes": PLAIN_READ_BYTES,
+                       "grid": plain_grid,
+                       "kernel": "qg_plain_read: one contiguous share per workgroup, "
+                                 "non-temporal 16-byte loads"},
+        "ms_per_step_spread": {"steps": n_grp * per_grp, "groups_of": per_grp,
+                               "p10": round(p10, 4), "median": round(p50, 4), "p90": round(p90, 4)},
         "tok_per_s": round(1e3 / ms_step, 2),
         "roofline": {
             "bound": "hbm",
@@ -296,36 +347,65 @@ def main():
         },
     }
 
-    # ---- verification passes, M = 16 and M = 32, same weights, one grouped launch each
+    # ---- verification passes: M-row activation tiles against the same
+    # weights, one grouped launch per pass
+    def time_pass(M, kernel=pkg.KERNEL_AUTO):
+        Xs = [workloads.verification_tile(args.seed, g, M) for g in step.gemvs]
+        Ys = [torch.empty((M, g.N), dtype=torch.bfloat16, device=dev) for g in step.gemvs]
+        planM = pkg.qg_batch_plan_build(
+            Q4, M, [(g.packed, g.N, g.K, X, Y) for g, X, Y in zip(step.gemvs, Xs, Ys)],
+            kernel=kernel)
+        for _ in range(max(1, args.warmup)):
+            pkg.qg_batch_run(planM)
+        torch.cuda.synchronize()
+        nM = max(5, args.steps // 2)
+        e0.record()
+        for _ in range(nM):
+            pkg.qg_batch_run(planM)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / nM, planM.plan.kernel
+
     if not args.no_m16:
-        for M in (16, 32):
-            Xs = [workloads.verification_tile(args.seed, g, M) for g in step.gemvs]
-            Ys = [torch.empty((M, g.N), dtype=torch.bfloat16, device=dev) for g in step.gemvs]
-            planM = pkg.qg_batch_plan_build(
-                Q4, M, [(g.packed, g.N, g.K, X, Y) for g, X, Y in zip(step.gemvs, Xs, Ys)])
-            for _ in range(max(1, args.warmup)):
-                pkg.qg_batch_run(planM)
-            torch.cuda.synchronize()
-            nM = max(5, args.steps // 2)
-            e0.record()
-            for _ in range(nM):
-                pkg.qg_batch_run(planM)
-            e1.record()
-            torch.cuda.synchronize()
-            msM = e0.elapsed_time(e1) / nM
+        for M in [int(v) for v in args.verify_m.split(",") if v]:
+            msM, _ = time_pass(M)
             bM = step.algorithmic_bytes(M)
+            passes = 1e3 / msM
             result["m%d" % M] = {
                 "ms_per_pass": round(msM, 4),
                 "value": round(bM / (msM * 1e-3) / 1e9, 2),
                 "unit": "GB/s",
                 "pct_of_peak": round(100 * bM / (msM * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2),
-                "passes_per_s": round(1e3 / msM, 2),
+                "passes_per_s": round(passes, 2),
+                # tokens per pass: 1 (no draft accepted), the pages' mean
+                # accepted draft length, and M (every row accepted: the bound)
+                "tok_per_s_equiv": {"tau_1": round(passes, 1),
+                                    "tau_%s" % roofline.MEAN_ACCEPTED_TOKENS: round(
+                                        passes * roofline.MEAN_ACCEPTED_TOKENS, 1),
+                                    "tau_%d" % M: round(passes * M, 1)},
                 "tflops": round(step.flops(M) / (msM * 1e-3) / 1e12, 2),
                 "launch": "one grouped kernel launch per pass (%d-row activation tile per "
                           "projection)" % M,
             }
             log("m%d pass: %.3f ms" % (M, msM))
-            del planM, Xs, Ys
+
+    # ---- the two Q4 kernel families on the same pass, for the rows where
+    # both apply: the default choice follows these figures
+    if not args.no_kernel_compare:
+        cmp = {}
+        for M in (1, 2, 4):
+            valu, _ = time_pass(M, pkg.KERNEL_VALU)
+            mfma, _ = time_pass(M, pkg.KERNEL_MFMA)
+            g0 = step.gemvs[0]
+            auto = pkg.qg_batch_plan_build(
+                Q4, M, [(g0.packed, g0.N, g0.K, workloads.verification_tile(args.seed, g0, M),
+                         torch.empty((M, g0.N), dtype=torch.bfloat16, device=dev))]).plan.kernel
+            cmp["m%d" % M] = {"valu_ms": round(valu, 4), "mfma_ms": round(mfma, 4),
+                              "default": "valu" if auto == pkg.KERNEL_VALU else "mfma"}
+            log("kernels m%d: valu %.3f ms, mfma %.3f ms" % (M, valu, mfma))
+        result["kernel_choice"] = dict(
+            cmp, workload="the verification pass over every projection of the decode step, "
+                          "forced onto each kernel family (bf16 output)")
 
     # ---- the other workloads of the hot path, each against its own bytes
     if not args.no_extras:

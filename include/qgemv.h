@@ -246,11 +246,26 @@ typedef struct qg_gemv_desc {
     void *y;              /* device [M][N] of the plan's output type; written */
 } qg_gemv_desc;
 
+/* Kernel family of a grouped launch.  Q4 products have two: the VALU GEMV
+ * kernel (codes unpacked in registers, one v_dot2 chain per activation row;
+ * 1..4 rows) and the bf16 MFMA kernel (16x16x32 tiles of 16 or 32 rows,
+ * whatever M is).  QG_KERNEL_AUTO takes the one measured faster on MI355X:
+ * VALU for M = 1, MFMA for M >= 2 (at M = 2 the MFMA pass over a decode
+ * step's weights already takes 0.74 ms against 0.86 ms on the VALU).  The
+ * others force a family, e.g. to measure both; results differ between the
+ * families only by fp32 rounding order. */
+typedef enum {
+    QG_KERNEL_AUTO = 0,
+    QG_KERNEL_VALU = 1,   /* M <= 4, else QG_EUNSUPPORTED */
+    QG_KERNEL_MFMA = 2
+} qg_kernel;
+
 /* Launch plan: plain host data, filled by qg_batch_plan_build and consumed
- * by qg_batch_run.  The fields are not meant to be edited. */
+ * by qg_batch_run.  The fields are not meant to be edited; `kernel` holds
+ * the family chosen (never QG_KERNEL_AUTO). */
 typedef struct qg_batch_plan {
     int32_t fmt, M, count, out_dtype;
-    int32_t grid, kmax, reserved0, reserved1;
+    int32_t grid, kmax, kernel, reserved1;
     const void *worklist;
     size_t worklist_bytes;
 } qg_batch_plan;
@@ -268,16 +283,18 @@ size_t qg_batch_worklist_bytes(int32_t count);
  *  count        1..65536 descriptors in `descs` (host array, read only; it
  *               need not outlive the call).
  *  out_dtype    QG_OUT_BF16 or QG_OUT_F32, for every product.
+ *  kernel       a qg_kernel: QG_KERNEL_AUTO, or a family to force.
  *  worklist     device buffer (16-B) of at least qg_batch_worklist_bytes(count)
  *               bytes; written asynchronously on `stream`, then read by every
  *               qg_batch_run of this plan, so it must stay allocated and
  *               unmodified while the plan is in use.
  *  plan         host struct receiving the plan.
- * Errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN, QG_ESIZE (a descriptor's
- * packed_bytes, or worklist_bytes), QG_EUNSUPPORTED, QG_EHIP.
+ * Errors: QG_EINVAL (also an unknown kernel), QG_ESHAPE, QG_EALIGN, QG_ESIZE
+ * (a descriptor's packed_bytes, or worklist_bytes), QG_EUNSUPPORTED (also
+ * QG_KERNEL_VALU with M > 4), QG_EHIP.
  */
 int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *descs,
-                        int out_dtype, void *worklist, size_t worklist_bytes,
+                        int out_dtype, int kernel, void *worklist, size_t worklist_bytes,
                         qg_batch_plan *plan, void *stream);
 
 /*
@@ -288,6 +305,24 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
  * Errors: QG_EINVAL (NULL or malformed plan), QG_EHIP.
  */
 int qg_batch_run(const qg_batch_plan *plan, void *stream);
+
+/*
+ * qg_plain_read -- measurement utility: read `bytes` of the device buffer
+ * `buf` once with plain streaming loads (workgroup j of `grid` takes the
+ * j-th contiguous share, non-temporal 16-byte loads) and write the XOR of
+ * the words each workgroup read to sink[j].  Its rate is the practical read
+ * ceiling of this GPU, against which the kernels above are also rated (both
+ * "MLX Runner: An Inference Engine You Can Read", section "Optimized against
+ * a known ceiling", and the Uzu page, section "Why batch-one decoding is
+ * memory-bound", rate decode by bandwidth over bytes).
+ *
+ *  buf      device, 16-B aligned; read only.  bytes: a multiple of 16 (0: no-op).
+ *  sink     device uint32 [grid], 4-B aligned; written.
+ *  grid     workgroups, 1..65536.
+ * Errors: QG_EINVAL (NULL pointer), QG_ESHAPE (bytes % 16, grid), QG_EALIGN,
+ * QG_EHIP.
+ */
+int qg_plain_read(const void *buf, size_t bytes, uint32_t *sink, int grid, void *stream);
 
 #ifdef __cplusplus
 }

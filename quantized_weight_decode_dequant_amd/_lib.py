@@ -24,6 +24,10 @@ OUT_BF16 = 0
 OUT_F32 = 1
 OUT_I32_GROUPS = 2
 
+KERNEL_AUTO = 0
+KERNEL_VALU = 1
+KERNEL_MFMA = 2
+
 QG_OK = 0
 QG_EINVAL = -1
 QG_ESHAPE = -2
@@ -46,6 +50,7 @@ EXPORTS = (
     "qg_batch_worklist_bytes",
     "qg_batch_plan_build",
     "qg_batch_run",
+    "qg_plain_read",
 )
 
 
@@ -59,7 +64,7 @@ class BatchPlan(C.Structure):
     """struct qg_batch_plan"""
     _fields_ = [("fmt", C.c_int32), ("M", C.c_int32), ("count", C.c_int32),
                 ("out_dtype", C.c_int32), ("grid", C.c_int32), ("kmax", C.c_int32),
-                ("reserved0", C.c_int32), ("reserved1", C.c_int32), ("worklist", C.c_void_p),
+                ("kernel", C.c_int32), ("reserved1", C.c_int32), ("worklist", C.c_void_p),
                 ("worklist_bytes", C.c_size_t)]
 
 _lock = threading.Lock()
@@ -102,11 +107,13 @@ def raw():
             lib.moe_expert_gemv_run.restype = i
             lib.qg_batch_worklist_bytes.argtypes = [C.c_int32]
             lib.qg_batch_worklist_bytes.restype = sz
-            lib.qg_batch_plan_build.argtypes = [i, i64, C.c_int32, C.POINTER(GemvDesc), i, p, sz,
+            lib.qg_batch_plan_build.argtypes = [i, i64, C.c_int32, C.POINTER(GemvDesc), i, i, p, sz,
                                                 C.POINTER(BatchPlan), p]
             lib.qg_batch_plan_build.restype = i
             lib.qg_batch_run.argtypes = [C.POINTER(BatchPlan), p]
             lib.qg_batch_run.restype = i
+            lib.qg_plain_read.argtypes = [p, sz, p, i, p]
+            lib.qg_plain_read.restype = i
             _lib = lib
     return _lib
 
@@ -244,9 +251,10 @@ def qg_batch_worklist_bytes(count: int) -> int:
 
 
 def qg_batch_plan_build(fmt: int, M: int, entries, out_dtype: int = OUT_BF16, worklist=None,
-                        stream=None) -> Plan:
+                        stream=None, kernel: int = KERNEL_AUTO) -> Plan:
     """entries: sequence of (packed, N, K, x, y) with device tensors; x is bf16
-    [M, K] ([K] for M = 1), y is [M, N] of the output type."""
+    [M, K] ([K] for M = 1), y is [M, N] of the output type.  kernel: one of
+    KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA."""
     torch = _torch()
     entries = list(entries)
     descs = (GemvDesc * len(entries))()
@@ -263,10 +271,21 @@ def qg_batch_plan_build(fmt: int, M: int, entries, out_dtype: int = OUT_BF16, wo
         dev = entries[0][0].device if entries else None
         worklist = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     plan = BatchPlan()
-    _check(raw().qg_batch_plan_build(fmt, M, len(entries), descs, out_dtype, _ptr(worklist),
+    _check(raw().qg_batch_plan_build(fmt, M, len(entries), descs, out_dtype, kernel, _ptr(worklist),
                                      worklist.numel(), C.byref(plan), _stream(stream)),
            "qg_batch_plan_build")
     return Plan(plan, worklist, keep)
+
+
+def qg_plain_read(buf, sink, grid: int, stream=None):
+    """Read the whole device tensor `buf` once (plain streaming loads); the
+    XOR of each workgroup's words lands in sink[j] (int32 device tensor of at
+    least `grid` elements)."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < grid:
+        raise ValueError("sink holds %d words, grid is %d" % (sink.numel(), grid))
+    _check(raw().qg_plain_read(_ptr(buf), nbytes, _ptr(sink), grid, _stream(stream)),
+           "qg_plain_read")
 
 
 def qg_batch_run(plan: Plan, stream=None):

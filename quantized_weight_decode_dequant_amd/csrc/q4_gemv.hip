@@ -1,4 +1,4 @@
-// Decode GEMV, one activation row, 4-bit asymmetric group-64 weights:
+// Decode GEMV, 4-bit asymmetric group-64 weights, on the VALU:
 //     y[n] = sum_g ( s[n,g] * sum_{k in g} q[n,k] x[k]  +  b[n,g] * sum_{k in g} x[k] )
 // which is sum_k (s*q + b) x with the weight dequantized in registers and
 // never stored ("MLX Runner: An Inference Engine You Can Read", section
@@ -7,7 +7,7 @@
 // streamed once with about one multiply-add).
 //
 // Work split.  A workgroup owns a contiguous range of rowblocks (16 rows
-// each) and walks it in blocks of up to 64 rowblocks.  A block's work is a
+// each) and walks it in blocks of up to 16 rowblocks.  A block's work is a
 // sequence of batches, one batch = 4 consecutive 128-k tiles of one rowblock
 // (4.5 KB; each lane reads one 16-byte slot per tile = 32 codes of one row,
 // one 64-lane load covers 16 rows x 128 k = 1 KB contiguous).  Every fourth
@@ -16,14 +16,21 @@
 // arithmetic of the same tile of the current batch, so each wave keeps one
 // to two batches in flight, and a load that the memory pipeline cannot yet
 // accept stalls one tile of arithmetic, not a batch.  The first batch is
-// issued before x is staged.  x is staged in LDS in segments of 12288 k
-// (every projection of a decode step is one segment) together with
-// per-(tile, group, k-slice) partial sums of x, which carry the bias term.
+// issued before x is staged.  x is staged in LDS in segments of 6144 k
+// together with per-(tile, group, k-slice) partial sums of x, which carry
+// the bias term; with 16-rowblock blocks that keeps a workgroup at 21.5 KB
+// of LDS, so LDS does not limit how many workgroups a CU holds.
 // A wave sums its batches of one rowblock in registers, folds the four
 // k-slices with two xor shuffles and adds the 16 row sums into its own LDS
 // slot of the rowblock; no barrier is needed until the block ends, when the
 // workgroup adds the four wave slots in wave order (deterministic) and
 // writes the block's rows with coalesced stores.
+//
+// The same kernel serves a few activation rows at once (M = 2..4, staged
+// side by side; 3 runs as 4 with a zero row): the codes of a tile are
+// unpacked once and feed one v_dot2 chain per row, so each weight is still
+// read once per call.  Past 4 rows the VALU work per byte outgrows the
+// bf16 MFMA kernels, whose cost does not depend on M up to 16.
 //
 // Two launch modes share the body:
 //  - single matrix (qgemv_run): workgroup j takes rowblocks
@@ -46,100 +53,127 @@ namespace qg {
 constexpr int GV_WAVES = 4;
 constexpr int GV_TPW = 4;                     // tiles per batch
 constexpr int GV_THREADS = GV_WAVES * 64;
-constexpr int GV_SEG_TILES = 96;              // 12288 k per staged segment
-constexpr int GV_RMAX = 64;                   // rowblocks per output block
-constexpr int GV_WGS_PER_CU = 5;              // resident workgroups per CU (register bound)
+constexpr int GV_RMAX = 16;                   // rowblocks per output block
+constexpr int GV_MR_MAX = 4;                  // most activation rows per launch
 
-int q4_gemv_wgs_per_cu() { return GV_WGS_PER_CU; }
+int q4_gemv_rows_max() { return GV_MR_MAX; }
 
-constexpr size_t GV_LDS_X = (size_t)GV_SEG_TILES * 256;      // bf16 x of a segment
-constexpr size_t GV_LDS_XSUM = (size_t)GV_SEG_TILES * 32;    // [tile][group][k-slice]
-constexpr size_t GV_LDS_PART = (size_t)GV_RMAX * GV_WAVES * 16 * 4;
+// Per row count MR (1, 2 or 4 staged activation rows): tiles per staged
+// segment (6144 k for one row; fewer for more rows, so that the staged x of
+// all rows stays at 12 KB) and the LDS of one workgroup.
+template <int MR>
+struct GvCfg {
+    static constexpr int SEG = 48 / MR;
+    static constexpr int ROW4 = SEG * 16;     // uint4 of staged x per row
+    static constexpr int ROWS = SEG * 8;      // x sums per row
+    static constexpr size_t LDS_X = (size_t)ROW4 * 16 * MR;
+    static constexpr size_t LDS_XSUM = (size_t)ROWS * 4 * MR;
+    static constexpr size_t LDS_PART = (size_t)GV_RMAX * GV_WAVES * MR * 16 * 4;
+    static constexpr size_t LDS = LDS_X + LDS_XSUM + LDS_PART;
+    // resident workgroups per CU, set by registers: at most 102 VGPRs for 5
+    // (1 or 2 rows), 128 for 4 (4 rows); LDS allows more
+    static constexpr int WPC = MR <= 2 ? 5 : 4;
+    static_assert(SEG % GV_TPW == 0, "segments hold whole batches");
+    static_assert((ROW4 * MR) % GV_THREADS == 0, "staging covers the segment evenly");
+    static_assert(LDS * WPC <= 160 * 1024, "LDS must not limit residency");
+};
 
-size_t q4_gemv_lds_bytes(int64_t kmax) {
-    (void)kmax;  // independent of K: x is staged one segment at a time
-    return GV_LDS_X + GV_LDS_XSUM + GV_LDS_PART;
+static int gv_rows(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : 4); }
+
+int q4_gemv_wgs_per_cu(int64_t M) { return gv_rows(M) <= 2 ? GvCfg<1>::WPC : GvCfg<4>::WPC; }
+
+size_t q4_gemv_lds_bytes(int64_t M) {
+    const int mr = gv_rows(M);
+    return mr == 1 ? GvCfg<1>::LDS : (mr == 2 ? GvCfg<2>::LDS : GvCfg<4>::LDS);
 }
 
 struct GemvLds {
-    unsigned *xl;   // bf16 pairs of the staged segment [96*64]
-    float *xsum;    // [96*8]
-    float *part;    // [GV_RMAX][GV_WAVES][16] per-wave row sums of the block
+    unsigned *xl;   // bf16 pairs of the staged segment, [MR][SEG*64]
+    float *xsum;    // [MR][SEG*8]: per (tile, group, k-slice)
+    float *part;    // [GV_RMAX][GV_WAVES][MR][16] per-wave row sums of the block
 };
 
-// Stage tiles [0, nt) of segment `seg` of x (zero past K; nt covers the
-// segment's tiles rounded up to whole batches) and their per-(tile, group,
-// k-slice) sums.  Ends with a barrier; the caller guarantees no wave still
-// reads the previous segment.
-__device__ __forceinline__ void gv_stage_x(const GemvLds &L, const uint16_t *x, int K, int seg,
-                                           int nt, int tid) {
-    const int k0 = seg * GV_SEG_TILES * Q4_TILE_K;
-    const int n4 = nt * 16;                    // uint4 to stage
-    const int nx4 = (K - k0) / 8;              // valid uint4 (K is a multiple of 64)
-    constexpr int U = (GV_SEG_TILES * 16) / GV_THREADS;  // 6
+// Stage tiles [0, nt) of segment `seg` of the M activation rows (rows past
+// M and k past K read as zero; nt covers the segment's tiles rounded up to
+// whole batches) and their per-(tile, group, k-slice) sums.  Ends with a
+// barrier; the caller guarantees no wave still reads the previous segment.
+template <int MR>
+__device__ __forceinline__ void gv_stage_x(const GemvLds &L, const uint16_t *x, int M, int K,
+                                           int seg, int nt, int tid) {
+    typedef GvCfg<MR> C;
+    const int k0 = seg * C::SEG * Q4_TILE_K;
+    const int n4 = nt * 16;                    // uint4 to stage per row
+    const int nx4 = (K - k0) / 8;              // valid uint4 per row (K is a multiple of 64)
+    constexpr int U = (C::ROW4 * MR) / GV_THREADS;
     u32x4_t v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int i = tid + u * GV_THREADS;
-        v[u] = (i < nx4 && i < n4) ? ld_global(reinterpret_cast<const u32x4_t *>(x + k0) + i)
-                                   : u32x4_t{0u, 0u, 0u, 0u};
+        const int i = tid + u * GV_THREADS, m = i / C::ROW4, j = i - m * C::ROW4;
+        v[u] = (m < M && j < nx4 && j < n4)
+                   ? ld_global(reinterpret_cast<const u32x4_t *>(x + (size_t)m * K + k0) + j)
+                   : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int i = tid + u * GV_THREADS;
-        if (i < n4) reinterpret_cast<u32x4_t *>(L.xl)[i] = v[u];
+        const int i = tid + u * GV_THREADS, m = i / C::ROW4, j = i - m * C::ROW4;
+        if (j < n4) reinterpret_cast<u32x4_t *>(L.xl)[i] = v[u];
     }
     __syncthreads();
-    for (int i = tid; i < nt * 8; i += GV_THREADS) {
-        const int p = i >> 3, t = (i >> 2) & 1, kg = i & 3;
-        float s = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint4 w = reinterpret_cast<const uint4 *>(L.xl)[16 * p + 8 * t + 4 * h + kg];
-            s += bf16_lo(w.x) + bf16_hi(w.x) + bf16_lo(w.y) + bf16_hi(w.y) + bf16_lo(w.z) +
-                 bf16_hi(w.z) + bf16_lo(w.w) + bf16_hi(w.w);
+    for (int m = 0; m < MR; ++m) {
+        const uint4 *xr = reinterpret_cast<const uint4 *>(L.xl) + m * C::ROW4;
+        for (int i = tid; i < nt * 8; i += GV_THREADS) {
+            const int p = i >> 3, t = (i >> 2) & 1, kg = i & 3;
+            float s = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint4 w = xr[16 * p + 8 * t + 4 * h + kg];
+                s += bf16_lo(w.x) + bf16_hi(w.x) + bf16_lo(w.y) + bf16_hi(w.y) + bf16_lo(w.z) +
+                     bf16_hi(w.z) + bf16_lo(w.w) + bf16_hi(w.w);
+            }
+            L.xsum[m * C::ROWS + i] = s;
         }
-        L.xsum[i] = s;
     }
     __syncthreads();
 }
-static_assert(GV_SEG_TILES % GV_TPW == 0, "segments hold whole batches");
 
-// One tile's contribution of this lane (16 codes per group, 2 groups).  xp
-// points at the tile's staged x for this lane's k-slice, xs at its x sums.
-// d starts at -128 * sum x so that the dot products of (128 + q) with x
-// leave sum q x; then acc += s * d + b * sum x per group.
-__device__ __forceinline__ float gv_tile(u32x4_t c, u32x2_t sb, const uint4 *xp, const float *xs,
-                                         const Q4Consts &magic, float acc) {
-    const uint4 xa0 = xp[0], xb0 = xp[4], xa1 = xp[8], xb1 = xp[12];
-    const float xs0 = xs[0], xs1 = xs[4];
-    unsigned q[4];
-    float d0 = -128.f * xs0, d1 = -128.f * xs1;
-    q4_unpack(c[0], magic, q);
-    d0 = dot2_bf16(q[0], xa0.x, d0);
-    d0 = dot2_bf16(q[1], xa0.y, d0);
-    d0 = dot2_bf16(q[2], xa0.z, d0);
-    d0 = dot2_bf16(q[3], xa0.w, d0);
-    q4_unpack(c[1], magic, q);
-    d0 = dot2_bf16(q[0], xb0.x, d0);
-    d0 = dot2_bf16(q[1], xb0.y, d0);
-    d0 = dot2_bf16(q[2], xb0.z, d0);
-    d0 = dot2_bf16(q[3], xb0.w, d0);
-    q4_unpack(c[2], magic, q);
-    d1 = dot2_bf16(q[0], xa1.x, d1);
-    d1 = dot2_bf16(q[1], xa1.y, d1);
-    d1 = dot2_bf16(q[2], xa1.z, d1);
-    d1 = dot2_bf16(q[3], xa1.w, d1);
-    q4_unpack(c[3], magic, q);
-    d1 = dot2_bf16(q[0], xb1.x, d1);
-    d1 = dot2_bf16(q[1], xb1.y, d1);
-    d1 = dot2_bf16(q[2], xb1.z, d1);
-    d1 = dot2_bf16(q[3], xb1.w, d1);
-    acc = fmaf(f16_lo(sb[0]), d0, acc);
-    acc = fmaf(f16_hi(sb[0]), xs0, acc);
-    acc = fmaf(f16_lo(sb[1]), d1, acc);
-    acc = fmaf(f16_hi(sb[1]), xs1, acc);
-    return acc;
+// One tile's contribution of this lane (16 codes per group, 2 groups) to
+// each of the MR rows.  The codes are unpacked once and serve every row.
+// xp points at the tile's staged x of row 0 for this lane's k-slice, xs at
+// its x sums.  d starts at -128 * sum x so that the dot products of
+// (128 + q) with x leave sum q x; then acc += s * d + b * sum x per group.
+template <int MR>
+__device__ __forceinline__ void gv_tile(u32x4_t c, u32x2_t sb, const uint4 *xp, const float *xs,
+                                        const Q4Consts &magic, float (&acc)[MR]) {
+    typedef GvCfg<MR> C;
+    float d[MR][2];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        d[m][0] = -128.f * xs[m * C::ROWS];
+        d[m][1] = -128.f * xs[m * C::ROWS + 4];
+    }
+    // word w holds 8 codes of group w >> 1; its x is uint4 4 * w of the tile
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        unsigned q[4];
+        q4_unpack(c[w], magic, q);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const uint4 xv = xp[m * C::ROW4 + 4 * w];
+            float &dd = d[m][w >> 1];
+            dd = dot2_bf16(q[0], xv.x, dd);
+            dd = dot2_bf16(q[1], xv.y, dd);
+            dd = dot2_bf16(q[2], xv.z, dd);
+            dd = dot2_bf16(q[3], xv.w, dd);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        acc[m] = fmaf(f16_lo(sb[0]), d[m][0], acc[m]);
+        acc[m] = fmaf(f16_hi(sb[0]), xs[m * C::ROWS], acc[m]);
+        acc[m] = fmaf(f16_lo(sb[1]), d[m][1], acc[m]);
+        acc[m] = fmaf(f16_hi(sb[1]), xs[m * C::ROWS + 4], acc[m]);
+    }
 }
 
 // Position of a wave's batch within the block: rowblock r (relative to the
@@ -186,10 +220,11 @@ __device__ __forceinline__ void gv_load(GvBatch &B, const WorkItem &it, int ub, 
 // rowblock the row sums go to the wave's LDS slot of that rowblock.  Tiles
 // past the segment's end re-read its last tile; their staged x and x sums
 // are zero, so they add exactly zero.
+template <int MR>
 __device__ __forceinline__ void gv_step(GvBatch &N, const WorkItem &it, int ub, int pbase, int pn,
                                         GvCursor cn, bool valid, const GvBatch &B, GvCursor c,
                                         int nb, const GemvLds &L, int lane, int wave,
-                                        const Q4Consts &magic, float &acc) {
+                                        const Q4Consts &magic, float (&acc)[MR]) {
     const uint8_t *base = it.packed + ((size_t)(ub + cn.r) * it.P + pbase) * Q4_TILE_BYTES;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(uniform_ptr(base), valid ? (unsigned)pn * Q4_TILE_BYTES : 0u);
@@ -204,31 +239,39 @@ __device__ __forceinline__ void gv_step(GvBatch &N, const WorkItem &it, int ub, 
         N.c[j] = buf_ld_x4(rs, lc, to);
         N.sb[j] = buf_ld_x2(rs, ls, to);
         __builtin_amdgcn_sched_barrier(0);
-        acc = gv_tile(B.c[j], B.sb[j], xp + 16 * j, xs + 8 * j, magic, acc);
+        gv_tile<MR>(B.c[j], B.sb[j], xp + 16 * j, xs + 8 * j, magic, acc);
     }
     if (c.b + GV_WAVES >= nb) {
-        acc += __shfl_xor(acc, 16);
-        acc += __shfl_xor(acc, 32);
-        if (lane < 16) L.part[(c.r * GV_WAVES + wave) * 16 + lane] += acc;
-        acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float a = acc[m];
+            a += __shfl_xor(a, 16);
+            a += __shfl_xor(a, 32);
+            if (lane < 16) L.part[((c.r * GV_WAVES + wave) * MR + m) * 16 + lane] += a;
+            acc[m] = 0.f;
+        }
     }
 }
 
 // Rowblocks [u0, u1) of one matrix, in blocks of GV_RMAX: for every segment
-// of K, stage that slice of x once and stream the block's batches.
-__device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, const GemvLds &L,
-                                         int tid, int lane, int wave, const Q4Consts &magic) {
-    const int nseg = (it.P + GV_SEG_TILES - 1) / GV_SEG_TILES;
+// of K, stage that slice of the M activation rows once and stream the
+// block's batches.
+template <int MR>
+__device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, int M,
+                                         const GemvLds &L, int tid, int lane, int wave,
+                                         const Q4Consts &magic) {
+    typedef GvCfg<MR> C;
+    const int nseg = (it.P + C::SEG - 1) / C::SEG;
     const uint16_t *x = reinterpret_cast<const uint16_t *>(it.x);
 #pragma unroll 1
     for (int ub = u0; ub < u1; ub += GV_RMAX) {
         const int nr = min(u1 - ub, GV_RMAX);
         __syncthreads();  // the previous block's partial sums have been written out
-        for (int i = tid; i < nr * GV_WAVES * 16; i += GV_THREADS) L.part[i] = 0.f;
+        for (int i = tid; i < nr * GV_WAVES * MR * 16; i += GV_THREADS) L.part[i] = 0.f;
 #pragma unroll 1
         for (int seg = 0; seg < nseg; ++seg) {
-            const int pbase = seg * GV_SEG_TILES;
-            const int pn = min(GV_SEG_TILES, it.P - pbase);
+            const int pbase = seg * C::SEG;
+            const int pn = min(C::SEG, it.P - pbase);
             const int nb = (pn + GV_TPW - 1) / GV_TPW;
             const int T = nr * nb;  // batches of the block in this segment
             // wave w takes the batches whose absolute index (rowblock * nb +
@@ -239,18 +282,22 @@ __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, con
             int t = (wave - (int)(((int64_t)ub * nb) % GV_WAVES) + GV_WAVES) % GV_WAVES;
             GvCursor ca = {t / nb, t % nb};
             GvBatch A, B;
-            float acc = 0.f;
+            float acc[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) acc[m] = 0.f;
             gv_load(A, it, ub, pbase, pn, ca, t < T, lane);
             __syncthreads();  // nobody still reads the previous segment
-            gv_stage_x(L, x, it.K, seg, nb * GV_TPW, tid);
+            gv_stage_x<MR>(L, x, M, it.K, seg, nb * GV_TPW, tid);
 #pragma unroll 1
             for (;;) {
                 if (t >= T) break;
                 const GvCursor cb = gv_advance(ca, nb);
-                gv_step(B, it, ub, pbase, pn, cb, t + GV_WAVES < T, A, ca, nb, L, lane, wave, magic, acc);
+                gv_step<MR>(B, it, ub, pbase, pn, cb, t + GV_WAVES < T, A, ca, nb, L, lane, wave,
+                            magic, acc);
                 if (t + GV_WAVES >= T) break;
                 const GvCursor cc = gv_advance(cb, nb);
-                gv_step(A, it, ub, pbase, pn, cc, t + 2 * GV_WAVES < T, B, cb, nb, L, lane, wave, magic, acc);
+                gv_step<MR>(A, it, ub, pbase, pn, cc, t + 2 * GV_WAVES < T, B, cb, nb, L, lane,
+                            wave, magic, acc);
                 t += 2 * GV_WAVES;
                 ca = cc;
             }
@@ -259,37 +306,40 @@ __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, con
         // global store between the loads of the sweep above)
         __syncthreads();
         const int r0 = ub * RB, nrow = min((ub + nr) * RB, it.N) - r0;
-        for (int r = tid; r < nrow; r += GV_THREADS) {
-            const float *pp = L.part + ((r >> 4) * GV_WAVES) * 16 + (r & 15);
+        for (int i = tid; i < M * nrow; i += GV_THREADS) {
+            const int m = i / nrow, r = i - m * nrow;
+            const float *pp = L.part + (((r >> 4) * GV_WAVES) * MR + m) * 16 + (r & 15);
             float v = pp[0];
 #pragma unroll
-            for (int w = 1; w < GV_WAVES; ++w) v += pp[16 * w];
+            for (int w = 1; w < GV_WAVES; ++w) v += pp[16 * MR * w];
+            const size_t o = (size_t)m * it.N + r0 + r;
             if (it.out_f32)
-                st_global<float>(it.y, (size_t)r0 + r, v);
+                st_global<float>(it.y, o, v);
             else
-                st_global<uint16_t>(it.y, (size_t)r0 + r, f32_to_bf16(v));
+                st_global<uint16_t>(it.y, o, f32_to_bf16(v));
         }
     }
 }
 
-// at most 168 VGPRs: 3 waves per SIMD, 3 workgroups of 4 waves per CU
-// LIST = false: one matrix (`single`); LIST = true: the work list.  Two
+// LIST = false: one matrix (`single`); LIST = true: the work list.  Separate
 // instantiations, so profiles tell a whole decode step from single GEMVs.
-template <bool LIST>
-__global__ void __launch_bounds__(GV_THREADS, GV_WGS_PER_CU)
+template <bool LIST, int MR>
+__global__ void __launch_bounds__(GV_THREADS, GvCfg<MR>::WPC)
 q4_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
-               WorkItem single) {
+               WorkItem single, int M) {
+    typedef GvCfg<MR> C;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     GemvLds L;
     L.xl = reinterpret_cast<unsigned *>(smem);
-    L.xsum = reinterpret_cast<float *>(smem + GV_LDS_X);
-    L.part = reinterpret_cast<float *>(smem + GV_LDS_X + GV_LDS_XSUM);
+    L.xsum = reinterpret_cast<float *>(smem + C::LDS_X);
+    L.part = reinterpret_cast<float *>(smem + C::LDS_X + C::LDS_XSUM);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Q4Consts magic = q4_consts();
     if (!LIST) {
         // single matrix: a contiguous share of the rowblocks per workgroup
         const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
-        gv_range(single, (int)(j * n / g), (int)((j + 1) * n / g), L, tid, lane, wave, magic);
+        gv_range<MR>(single, (int)(j * n / g), (int)((j + 1) * n / g), M, L, tid, lane, wave,
+                     magic);
         return;
     }
     const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
@@ -298,12 +348,30 @@ q4_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__
         const WorkItem it = items[i];
         const int u0 = (i == s.item) ? s.unit : 0;
         const int u1 = (i == e.item) ? e.unit : it.units;
-        if (u0 < u1) gv_range(it, u0, u1, L, tid, lane, wave, magic);
+        if (u0 < u1) gv_range<MR>(it, u0, u1, M, L, tid, lane, wave, magic);
     }
 }
 
-hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int64_t N,
+template <bool LIST>
+static hipError_t gv_launch(const WorkItem *items, const WorkStart *starts, const WorkItem &it,
+                            int grid, int64_t M, hipStream_t s) {
+    const int mr = gv_rows(M);
+    const size_t lds = q4_gemv_lds_bytes(M);
+    if (mr == 1)
+        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 1>), dim3(grid), dim3(GV_THREADS), lds, s, items,
+                           starts, it, (int)M);
+    else if (mr == 2)
+        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 2>), dim3(grid), dim3(GV_THREADS), lds, s, items,
+                           starts, it, (int)M);
+    else
+        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 4>), dim3(grid), dim3(GV_THREADS), lds, s, items,
+                           starts, it, (int)M);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int64_t M, int64_t N,
                           int64_t K, bool out_f32, int cus, hipStream_t s) {
+    if (M < 1 || M > GV_MR_MAX) return hipErrorInvalidValue;
     WorkItem it{};
     it.packed = packed;
     it.x = x;
@@ -313,18 +381,16 @@ hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int
     it.P = (int32_t)ceil_div(K, Q4_TILE_K);
     it.units = (int32_t)ceil_div(N, RB);
     it.out_f32 = out_f32 ? 1 : 0;
-    const int grid = (int)(it.units < (int64_t)cus * GV_WGS_PER_CU ? it.units : (int64_t)cus * GV_WGS_PER_CU);
-    hipLaunchKernelGGL(q4_gemv_kernel<false>, dim3(grid), dim3(GV_THREADS), q4_gemv_lds_bytes(K), s,
-                       (const WorkItem *)nullptr, (const WorkStart *)nullptr, it);
-    return hipGetLastError();
+    const int64_t cap = (int64_t)cus * q4_gemv_wgs_per_cu(M);
+    const int grid = (int)(it.units < cap ? it.units : cap);
+    return gv_launch<false>(nullptr, nullptr, it, grid, M, s);
 }
 
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts, int grid,
-                               int64_t kmax, hipStream_t s) {
+                               int64_t M, hipStream_t s) {
+    if (M < 1 || M > GV_MR_MAX) return hipErrorInvalidValue;
     WorkItem none{};
-    hipLaunchKernelGGL(q4_gemv_kernel<true>, dim3(grid), dim3(GV_THREADS), q4_gemv_lds_bytes(kmax), s,
-                       items, starts, none);
-    return hipGetLastError();
+    return gv_launch<true>(items, starts, none, grid, M, s);
 }
 
 }  // namespace qg

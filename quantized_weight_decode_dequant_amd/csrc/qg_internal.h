@@ -86,14 +86,15 @@ hipError_t launch_pack_q8(const int8_t *codes, const uint16_t *scales,
 hipError_t launch_pack_fp4(const uint8_t *codes, const uint8_t *scales,
                            int64_t N, int64_t K, uint8_t *packed, hipStream_t s);
 
-hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y,
-                          int64_t N, int64_t K, bool out_f32, int cus,
-                          hipStream_t s);
-// grouped launches over a device work list
-size_t q4_gemv_lds_bytes(int64_t kmax);
-int q4_gemv_wgs_per_cu();
+// Q4 GEMV on the VALU for 1..q4_gemv_rows_max() activation rows (x is
+// bf16 [M][K], y [M][N]); single matrix or a device work list
+hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int64_t M,
+                          int64_t N, int64_t K, bool out_f32, int cus, hipStream_t s);
+size_t q4_gemv_lds_bytes(int64_t M);
+int q4_gemv_wgs_per_cu(int64_t M);
+int q4_gemv_rows_max();
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts,
-                               int grid, int64_t kmax, hipStream_t s);
+                               int grid, int64_t M, hipStream_t s);
 // streaming skinny kernel (one workgroup of 16 waves for M <= 16, 12 waves
 // for M <= 32, per CU; the X slice of a segment staged whole in LDS)
 int q4_skinny_stream_wgs_per_cu();
@@ -103,6 +104,8 @@ hipError_t launch_q4_skinny_stream(const uint8_t *packed, const uint16_t *X, voi
                                    int cus, hipStream_t s);
 hipError_t launch_q4_skinny_stream_list(const WorkItem *items, const WorkStart *starts,
                                         int grid, int64_t M, hipStream_t s);
+hipError_t launch_plain_read(const void *buf, size_t bytes, uint32_t *sink, int grid,
+                             hipStream_t s);
 hipError_t launch_write_words(const uint32_t *src, size_t nwords, uint32_t *dst,
                               hipStream_t s);
 hipError_t launch_fp4_gemv(const uint8_t *packed, const uint16_t *x, void *y,

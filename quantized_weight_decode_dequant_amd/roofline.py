@@ -23,6 +23,12 @@ BF16_DENSE_TFLOPS = 2500.0
 I8_DENSE_TOPS = 5000.0
 FP32_VECTOR_TFLOPS = 157.3
 
+# Mean tokens produced per forward pass with speculative drafts, as the Uzu
+# CLI reports it for a 9B model on a base M5 (Uzu page, fange-kb.cn, section
+# "Run a model locally and inspect the runtime"): used only to express a
+# verification pass rate as an equivalent decode rate.
+MEAN_ACCEPTED_TOKENS = 8.39
+
 
 def q4_gemm_bytes(M: int, N: int, K: int, out_bytes: int = 2) -> float:
     """Q4 weights once + bf16 activations in + outputs out."""

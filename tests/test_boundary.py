@@ -136,6 +136,18 @@ def test_hadamard_validation():
     assert lib.hadamard32_quant_run(A, A, 0, 64, A, A, None) == L.QG_OK
 
 
+def test_plain_read_validation():
+    lib = pkg.raw()
+    assert lib.qg_plain_read(None, 64, A, 4, None) == L.QG_EINVAL
+    assert lib.qg_plain_read(A, 64, None, 4, None) == L.QG_EINVAL
+    assert lib.qg_plain_read(A, 65, A, 4, None) == L.QG_ESHAPE
+    assert lib.qg_plain_read(A, 64, A, 0, None) == L.QG_ESHAPE
+    assert lib.qg_plain_read(A, 64, A, 65537, None) == L.QG_ESHAPE
+    assert lib.qg_plain_read(A + 8, 64, A, 4, None) == L.QG_EALIGN
+    assert lib.qg_plain_read(A, 64, A + 2, 4, None) == L.QG_EALIGN
+    assert lib.qg_plain_read(A, 0, A, 4, None) == L.QG_OK
+
+
 def test_moe_validation():
     lib = pkg.raw()
     E, H, F, k = 8, 256, 512, 2
@@ -197,9 +209,10 @@ def test_batch_validation():
 
     plan = L.BatchPlan()
 
-    def build(fmt=q4, M=1, count=n, arr=None, out=0, wl_ptr=A, wl_bytes=wl, plan_ptr=True):
+    def build(fmt=q4, M=1, count=n, arr=None, out=0, kernel=0, wl_ptr=A, wl_bytes=wl,
+              plan_ptr=True):
         arr = descs() if arr is None else arr
-        return lib.qg_batch_plan_build(fmt, M, count, arr, out, wl_ptr, wl_bytes,
+        return lib.qg_batch_plan_build(fmt, M, count, arr, out, kernel, wl_ptr, wl_bytes,
                                        C.byref(plan) if plan_ptr else None, None)
 
     assert build(plan_ptr=False) == L.QG_EINVAL
@@ -210,6 +223,9 @@ def test_batch_validation():
     assert build(fmt=L.FMT_Q8_SYM_G32) == L.QG_EUNSUPPORTED
     assert build(M=0) == L.QG_ESHAPE
     assert build(M=33) == L.QG_ESHAPE
+    assert build(kernel=3) == L.QG_EINVAL
+    assert build(kernel=-1) == L.QG_EINVAL
+    assert build(M=5, kernel=L.KERNEL_VALU) == L.QG_EUNSUPPORTED
     assert build(count=0) == L.QG_ESHAPE
     assert build(wl_bytes=wl - 1) == L.QG_ESIZE
     assert build(wl_ptr=A + 4) == L.QG_EALIGN
@@ -225,8 +241,13 @@ def test_batch_validation():
     assert lib.qg_batch_run(None, None) == L.QG_EINVAL
     bad = L.BatchPlan()
     assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL
-    bad.fmt, bad.M, bad.count, bad.grid, bad.kmax = q4, 1, 3, 0, 256
+    bad.fmt, bad.M, bad.count, bad.grid, bad.kmax = q4, 1, 3, 4, 256
     bad.worklist, bad.worklist_bytes = A, wl
+    bad.kernel = L.KERNEL_AUTO
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # kernel not chosen
+    bad.kernel, bad.M = L.KERNEL_VALU, 5
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # VALU kernel past 4 rows
+    bad.kernel, bad.M, bad.grid = L.KERNEL_VALU, 1, 0
     assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # grid 0
     bad.grid = 5000
     assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # grid > max

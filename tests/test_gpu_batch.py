@@ -48,7 +48,7 @@ def test_batch_m1_mixed_shapes(out_dtype):
         assert torch.equal(y, s), "batch differs from qgemv_run for N=%d K=%d" % (N, K)
 
 
-@pytest.mark.parametrize("M", [2, 5, 16, 17, 32])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 16, 17, 32])
 def test_batch_skinny_mixed_shapes(M):
     note("batch skinny M=%d" % M)
     shapes = [(40, 192), (256, 4096), (33, 1216), (130, 640), (48, 12288), (300, 8256)]
@@ -120,15 +120,17 @@ def test_batch_decode_step_full():
         assert_bf16_close(to_np(got[idx])[rows], ref, what=name)
 
 
-@pytest.mark.parametrize("M", [16, 32])
-def test_batch_verification_pass_full(M):
+@pytest.mark.parametrize("M,kernel", [(4, pkg.KERNEL_VALU), (4, pkg.KERNEL_AUTO),
+                                      (16, pkg.KERNEL_AUTO), (32, pkg.KERNEL_AUTO)])
+def test_batch_verification_pass_full(M, kernel):
     """The whole verification pass (every projection of the decode step against
     its own M-row activation tile) in one launch: sampled output columns of
-    several projections against the oracle, and the lm_head output bitwise
-    equal to a single-matrix qgemm_skinny_run."""
-    note("batch verification pass M=%d" % M)
+    several projections against the oracle, and (default kernel) the lm_head
+    output bitwise equal to a single-matrix qgemm_skinny_run."""
+    note("batch verification pass M=%d kernel=%d" % (M, kernel))
     step = workloads.build_decode_step(0, skinny_m=M)
-    plan = pkg.qg_batch_plan_build(Q4, M, [(g.packed, g.N, g.K, g.X, g.Y) for g in step.gemvs])
+    plan = pkg.qg_batch_plan_build(Q4, M, [(g.packed, g.N, g.K, g.X, g.Y) for g in step.gemvs],
+                                   kernel=kernel)
     pkg.qg_batch_run(plan)
     torch.cuda.synchronize()
     rng = np.random.default_rng(97)
@@ -139,19 +141,23 @@ def test_batch_verification_pass_full(M):
         rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 48, replace=False)]))
         ref = oracle.q4_gemm(m.codes[rows], m.scales[rows], m.biases[rows], X)
         assert_bf16_close(to_np(step.gemvs[idx].Y)[:, rows], ref, what="%s M=%d" % (name, M))
-    g = step.gemvs[-1]
-    single = pkg.qgemm_skinny_run(Q4, g.packed, M, g.N, g.K, g.X)
-    torch.cuda.synchronize()
-    assert torch.equal(single, g.Y)
+    if kernel == pkg.KERNEL_AUTO:
+        g = step.gemvs[-1]
+        single = pkg.qgemm_skinny_run(Q4, g.packed, M, g.N, g.K, g.X)
+        torch.cuda.synchronize()
+        assert torch.equal(single, g.Y)
 
 
-@pytest.mark.parametrize("M", [2, 5, 17])
+@pytest.mark.parametrize("M,kernel", [(2, pkg.KERNEL_AUTO), (3, pkg.KERNEL_AUTO),
+                                      (5, pkg.KERNEL_AUTO), (17, pkg.KERNEL_AUTO),
+                                      (3, pkg.KERNEL_VALU), (1, pkg.KERNEL_MFMA)])
 @pytest.mark.parametrize("out_dtype", [pkg.OUT_F32, pkg.OUT_BF16])
-def test_batch_skinny_writes_stay_inside_y(M, out_dtype):
+def test_batch_skinny_writes_stay_inside_y(M, kernel, out_dtype):
     """Every output tile lives inside a larger buffer filled with a sentinel:
     after the grouped launch the bytes past each Y (ragged N, M not a multiple
-    of 16) are unchanged and Y matches the single-matrix call."""
-    note("batch skinny bounds M=%d out=%d" % (M, out_dtype))
+    of 16) are unchanged and Y matches the single-matrix call (default
+    kernel) or the oracle (a forced kernel)."""
+    note("batch skinny bounds M=%d kernel=%d out=%d" % (M, kernel, out_dtype))
     shapes = [(40, 192), (33, 1216), (130, 640)]
     mats = _mats(98, shapes)
     dt = torch.float32 if out_dtype == pkg.OUT_F32 else torch.bfloat16
@@ -165,9 +171,47 @@ def test_batch_skinny_writes_stay_inside_y(M, out_dtype):
         entries.append((p, m.N, m.K, Xd, Y))
         bufs.append(buf)
         singles.append(pkg.qgemm_skinny_run(Q4, p, M, m.N, m.K, Xd, out_dtype=out_dtype))
-    plan = pkg.qg_batch_plan_build(Q4, M, entries, out_dtype)
+    plan = pkg.qg_batch_plan_build(Q4, M, entries, out_dtype, kernel=kernel)
     pkg.qg_batch_run(plan)
     torch.cuda.synchronize()
-    for (p, N, K, Xd, Y), buf, s in zip(entries, bufs, singles):
+    for i, ((p, N, K, Xd, Y), buf, s, m) in enumerate(zip(entries, bufs, singles, mats)):
         assert torch.all(buf[M * N:] == 7.0), "write past Y for N=%d K=%d" % (N, K)
-        assert torch.equal(Y, s)
+        if kernel == pkg.KERNEL_AUTO:
+            assert torch.equal(Y, s)
+        else:
+            ref = oracle.q4_gemm(m.codes, m.scales, m.biases, synth.activations(99, M, m.K, item=i))
+            check = assert_f32_close if out_dtype == pkg.OUT_F32 else assert_bf16_close
+            check(to_np(Y), ref, what="N=%d K=%d" % (N, K))
+
+
+@pytest.mark.parametrize("M,kernel", [(1, pkg.KERNEL_VALU), (2, pkg.KERNEL_VALU),
+                                      (3, pkg.KERNEL_VALU), (4, pkg.KERNEL_VALU),
+                                      (1, pkg.KERNEL_MFMA), (2, pkg.KERNEL_MFMA)])
+def test_batch_forced_kernel(M, kernel):
+    """Either kernel family forced on a mixed list (ragged N, K spanning
+    several staged segments of both kernels) agrees with the oracle; the VALU
+    family at M = 1 is the default kernel, bit for bit."""
+    note("batch forced kernel M=%d kernel=%d" % (M, kernel))
+    shapes = [(40, 192), (256, 4096), (33, 1216), (130, 640), (48, 12288), (70, 3136)]
+    mats = _mats(100, shapes)
+    Xs = [synth.activations(101, M, m.K, item=i) for i, m in enumerate(mats)]
+    entries = []
+    for m, X in zip(mats, Xs):
+        Xd = weights.to_device(X, DEV)
+        entries.append((weights.pack_q4(m, DEV), m.N, m.K, Xd,
+                        torch.empty((M, m.N), dtype=torch.float32, device=DEV)))
+    plan = pkg.qg_batch_plan_build(Q4, M, entries, pkg.OUT_F32, kernel=kernel)
+    assert plan.plan.kernel == kernel
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    for (p, N, K, Xd, Y), m, X in zip(entries, mats, Xs):
+        assert_f32_close(to_np(Y), oracle.q4_gemm(m.codes, m.scales, m.biases, X),
+                         what="N=%d K=%d" % (N, K))
+    if M == 1 and kernel == pkg.KERNEL_VALU:
+        auto = [(p, N, K, Xd, torch.empty_like(Y)) for p, N, K, Xd, Y in entries]
+        plan_a = pkg.qg_batch_plan_build(Q4, 1, auto, pkg.OUT_F32)
+        assert plan_a.plan.kernel == pkg.KERNEL_VALU
+        pkg.qg_batch_run(plan_a)
+        torch.cuda.synchronize()
+        for e, a in zip(entries, auto):
+            assert torch.equal(e[4], a[4])
