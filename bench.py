@@ -140,6 +140,16 @@ def summarize_trace(stats_csv: str, command: str):
             float(_col(r, "Percentage"))))
 
 
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return "%s, %d logical CPUs" % (line.split(":", 1)[1].strip(), os.cpu_count() or 0)
+    except OSError:
+        pass
+    return "unknown, %d logical CPUs" % (os.cpu_count() or 0)
+
+
 def cpu_baseline(step, budget_s: float):
     """The oracle, as it stands, on the first GEMVs of the step until the time
     budget is spent (one thread; input generation is not timed)."""
@@ -168,17 +178,54 @@ def cpu_baseline(step, budget_s: float):
     }
 
 
+def cpu_baseline_all_cores(step, budget_s: float, threads: int):
+    """The oracle, as it stands, on every host core the box gives this job:
+    each GEMV's output rows are split into `threads` slices computed by
+    concurrent oracle calls (the oracle releases the interpreter while it
+    runs).  Same GEMVs as the one-thread figure, until the budget is spent."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    from quantized_weight_decode_dequant_amd import roofline, synth
+    done_bytes, n, elapsed = 0.0, 0, 0.0
+    with ThreadPoolExecutor(threads) as pool:
+        for item, name, N, K in synth.decode_step_shapes():
+            m = synth.q4_matrix(step.seed, N, K, item=item)
+            x = synth.activations(step.seed, 1, K, item=item)
+            cuts = [N * i // threads for i in range(threads + 1)]
+            t = time.perf_counter()
+            list(pool.map(lambda j: oracle.q4_gemm(m.codes[cuts[j]:cuts[j + 1]],
+                                                   m.scales[cuts[j]:cuts[j + 1]],
+                                                   m.biases[cuts[j]:cuts[j + 1]], x),
+                          range(threads)))
+            elapsed += time.perf_counter() - t
+            done_bytes += roofline.q4_gemm_bytes(1, N, K)
+            n += 1
+            if elapsed >= budget_s:
+                break
+    gbs = done_bytes / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s",
+            "tok_per_s": round(gbs * 1e9 / step.algorithmic_bytes(1), 6),
+            "cores": threads, "kind": "oracle",
+            "sample": "first %d GEMVs of the decode step, output rows split over %d threads, "
+                      "%.3f GB algorithmic, %.1f s" % (n, threads, done_bytes / 1e9, elapsed)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed work before each measurement's warmup, so the "
+                         "GPU clocks reach their sustained state")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m16", action="store_true", help="skip the verification passes")
     ap.add_argument("--verify-m", default="16,32",
                     help="activation rows of the timed verification passes (comma separated)")
+    ap.add_argument("--no-per-shape", action="store_true",
+                    help="skip timing each projection shape on its own")
     ap.add_argument("--no-kernel-compare", action="store_true",
                     help="skip timing both Q4 kernel families at M = 1, 2, 4")
     ap.add_argument("--no-extras", action="store_true",
@@ -231,6 +278,9 @@ def main():
         torch.cuda.synchronize()
         log("traffic pass: one decode step, one %d-byte copy" % COPY_BYTES)
         return
+    # clocks settle first (the GPU runs a fresh workload below its sustained
+    # clock for roughly the first 0.2 s), then the W warmup steps
+    workloads.settle(lambda: pkg.qg_batch_run(plan), args.settle)
     for _ in range(args.warmup):
         pkg.qg_batch_run(plan)
     torch.cuda.synchronize()
@@ -355,6 +405,7 @@ def main():
         planM = pkg.qg_batch_plan_build(
             Q4, M, [(g.packed, g.N, g.K, X, Y) for g, X, Y in zip(step.gemvs, Xs, Ys)],
             kernel=kernel)
+        workloads.settle(lambda: pkg.qg_batch_run(planM), args.settle)
         for _ in range(max(1, args.warmup)):
             pkg.qg_batch_run(planM)
         torch.cuda.synchronize()
@@ -388,6 +439,42 @@ def main():
                           "projection)" % M,
             }
             log("m%d pass: %.3f ms" % (M, msM))
+
+    # ---- each distinct projection shape on its own, one call per matrix
+    # (the step's copies of that shape back to back, so the weights stream
+    # from HBM; the single lm_head repeats, and 350 MB of it exceeds the
+    # 256 MB last-level cache), at M = 1 (qgemv_run) and in verification
+    # tiles (qgemm_skinny_run)
+    if not args.no_per_shape:
+        shapes = {}
+        for g in step.gemvs:
+            shapes.setdefault((g.name.split(".")[-1], g.N, g.K), []).append(g)
+        per_shape = {}
+        for (name, N, K), gs in shapes.items():
+            row = {"N": N, "K": K, "matrices": len(gs)}
+            for M in [1] + [int(v) for v in args.verify_m.split(",") if v]:
+                X = workloads.verification_tile(args.seed, gs[0], M)
+                Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                it = [0]
+
+                def call():
+                    g = gs[it[0] % len(gs)]
+                    it[0] += 1
+                    if M == 1:
+                        pkg.qgemv_run(Q4, g.packed, N, K, X[0], Y[0])
+                    else:
+                        pkg.qgemm_skinny_run(Q4, g.packed, M, N, K, X, Y=Y)
+
+                ms = workloads.time_graph_ms(call, max(len(gs), 8))
+                b = roofline.q4_gemm_bytes(M, N, K)
+                row["m%d" % M] = {"us": round(ms * 1e3, 2),
+                                  "GBs": round(b / (ms * 1e-3) / 1e9, 1),
+                                  "pct_of_peak": round(100 * b / (ms * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1)}
+            per_shape[name] = row
+            log("shape %s %dx%d: %s" % (name, N, K, ", ".join(
+                "m%s %.1f us" % (k[1:], v["us"]) for k, v in row.items() if k.startswith("m") and k != "matrices")))
+        result["per_shape"] = dict(per_shape, workload="one qgemv_run (M=1) or qgemm_skinny_run "
+                                   "(M rows) per call, captured in a HIP graph, bf16 output")
 
     # ---- the two Q4 kernel families on the same pass, for the rows where
     # both apply: the default choice follows these figures
@@ -464,6 +551,10 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_budget)
+        threads = max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")), 16))
+        result["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(step, args.cpu_budget / 2,
+                                                                     threads)
+        result["cpu_baseline"]["host"] = host_cpu_model()
     print(json.dumps(result), flush=True)
 
 

@@ -122,15 +122,30 @@ def time_ms(fn, iters: int, warmup: int = 2) -> float:
     return e0.elapsed_time(e1) / iters
 
 
-def time_graph_ms(fn, calls: int, reps: int = 5) -> float:
+def settle(fn, seconds: float, chunk: int = 20):
+    """Run fn() untimed, `chunk` calls between synchronizations, until at least
+    `seconds` of wall time have passed: a GPU coming out of a lighter load
+    runs below its sustained clock for a fraction of a second."""
+    import time
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(chunk):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_graph_ms(fn, calls: int, reps: int = 5, settle_s: float = 0.2) -> float:
     """Mean milliseconds per call of fn() measured on the GPU: `calls`
     invocations captured into one HIP graph, the graph replayed `reps` times
-    between HIP events.  For kernels shorter than the host's launch path this
-    times the device, not the Python binding."""
+    between HIP events (after `settle_s` seconds of untimed replays).  For
+    kernels shorter than the host's launch path this times the device, not
+    the Python binding."""
     import torch
     graph = capture_graph(lambda: [fn() for _ in range(calls)])
     graph.replay()
     torch.cuda.synchronize()
+    settle(graph.replay, settle_s, chunk=4)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):

@@ -102,7 +102,8 @@ def run_skinny(m, X, out_dtype):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 17, 31, 32])
-@pytest.mark.parametrize("N,K", [(40, 192), (100, 1216), (70, 3136)])
+@pytest.mark.parametrize("N,K", [(40, 192), (100, 1216), (70, 3136), (300, 2048), (20, 4224),
+                                 (700, 8320)])
 def test_q4_skinny_ragged(M, N, K):
     note("q4 skinny M=%d N=%d K=%d" % (M, N, K))
     m = synth.q4_matrix(20, N, K)
