@@ -59,7 +59,7 @@ def traffic_from_profiles(kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-STEP_KERNEL = "q4_gemv_kernel<true>"
+STEP_KERNEL = "q4_gemv_kernel<true, 1>"
 COPY_BYTES = 1 << 30
 PLAIN_READ_BYTES = 4 << 30   # larger than every cache level
 
@@ -126,10 +126,23 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, command: str):
     print(json.dumps(out, indent=1))
 
 
-def summarize_trace(stats_csv: str, command: str):
-    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+def summarize_trace(stats_csv: str, command: str, trace_csv: str = None, timed=None):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv;
+    with the dispatch trace and the (first, count) of the timed launches that
+    bench.py reports, also the mean duration of exactly those launches of the
+    decode-step kernel."""
     rows = _csv_rows(stats_csv)
     print("Command: `%s`\n" % command)
+    if trace_csv and timed:
+        first, count = timed
+        step = sorted((int(_col(r, "Dispatch_Id")), int(_col(r, "Start_Timestamp")),
+                       int(_col(r, "End_Timestamp")))
+                      for r in _csv_rows(trace_csv) if STEP_KERNEL in _col(r, "Kernel_Name"))
+        win = step[first:first + count]
+        mean_us = sum(e - b for _, b, e in win) / len(win) / 1e3
+        print("Decode-step kernel `%s`: %d dispatches in the trace; the %d timed ones "
+              "(dispatches %d..%d of the kernel) average %.2f us.\n" % (
+                  STEP_KERNEL, len(step), len(win), first, first + len(win) - 1, mean_us))
     print("| kernel | calls | average (us) | min (us) | max (us) | share |")
     print("|---|---|---|---|---|---|")
     for r in rows:
@@ -234,13 +247,18 @@ def main():
                     help="run one decode step and one plain 1 GiB copy, for counter collection")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV")
+    ap.add_argument("--trace-csv", metavar="KERNEL_TRACE_CSV",
+                    help="with --summarize-trace: the dispatch trace of the same run")
+    ap.add_argument("--timed", nargs=2, type=int, metavar=("FIRST", "COUNT"),
+                    help="with --trace-csv: the timed step launches, as bench.py reported them")
     ap.add_argument("--command", default="", help="command line recorded in summaries")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, command=args.command)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.command)
+        summarize_trace(args.summarize_trace, args.command, args.trace_csv,
+                        tuple(args.timed) if args.timed else None)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -280,10 +298,12 @@ def main():
         return
     # clocks settle first (the GPU runs a fresh workload below its sustained
     # clock for roughly the first 0.2 s), then the W warmup steps
-    workloads.settle(lambda: pkg.qg_batch_run(plan), args.settle)
+    n_settle = workloads.settle(lambda: pkg.qg_batch_run(plan), args.settle)
     for _ in range(args.warmup):
         pkg.qg_batch_run(plan)
     torch.cuda.synchronize()
+    # step-kernel launches so far: the graph check below adds none
+    timed_first = n_settle + args.warmup
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
@@ -374,6 +394,7 @@ def main():
             "launch": "one grouped kernel launch per step (qg_batch_run over a device work list "
                       "of the %d GEMVs)" % len(step.gemvs),
             "ms_per_step_one_launch_per_gemv": round(ms_per_launch_graph, 4),
+            "timed_launches": [timed_first, args.steps],
         },
         "pct_of_peak": round(100 * gbs / roofline.HBM_PEAK_GBS, 2),
         "pct_of_plain_read": round(100 * gbs / plain_best, 2),

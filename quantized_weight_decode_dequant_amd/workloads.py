@@ -122,17 +122,20 @@ def time_ms(fn, iters: int, warmup: int = 2) -> float:
     return e0.elapsed_time(e1) / iters
 
 
-def settle(fn, seconds: float, chunk: int = 20):
+def settle(fn, seconds: float, chunk: int = 20) -> int:
     """Run fn() untimed, `chunk` calls between synchronizations, until at least
-    `seconds` of wall time have passed: a GPU coming out of a lighter load
-    runs below its sustained clock for a fraction of a second."""
+    `seconds` of wall time have passed (a GPU coming out of a lighter load
+    runs below its sustained clock for a fraction of a second); returns the
+    number of calls."""
     import time
     import torch
-    t0 = time.perf_counter()
+    t0, n = time.perf_counter(), 0
     while time.perf_counter() - t0 < seconds:
         for _ in range(chunk):
             fn()
+        n += chunk
         torch.cuda.synchronize()
+    return n
 
 
 def time_graph_ms(fn, calls: int, reps: int = 5, settle_s: float = 0.2) -> float:
