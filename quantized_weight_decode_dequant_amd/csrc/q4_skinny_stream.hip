@@ -13,12 +13,12 @@
 // segment.  Each wave owns every 16th (12th) rowblock of the workgroup's
 // range and streams its batches (4 consecutive 128-k tiles of one rowblock)
 // double-buffered: the load of each tile of the next batch is issued just
-// before the arithmetic of the same tile of the current batch.  The
-// rowblock's 16 x M results stay in the wave's registers until its last
-// batch.  When K spans several segments the wave works on blocks of up to 4
-// rowblocks whose sums it keeps in registers across the segments.  Every
-// rowblock accumulates its tiles in K order, as the kernel of skinny.hip
-// does, so both give identical results.  Tiles past the end of K re-read the
+// before the arithmetic of the same tile of the current batch.  The 16 x M
+// results of 6 (2) rowblocks stay in the wave's registers and are stored
+// together; when K spans several segments those are the rowblocks whose
+// sums the wave keeps across the segments.  Every rowblock accumulates its
+// tiles in K order within one wave, so single and grouped launches give
+// identical results.  Tiles past the end of K re-read the
 // last tile; X and its sums are staged as zero there, so they add exactly
 // zero.
 #include "qg_internal.h"
@@ -33,7 +33,7 @@ struct SsCfg {
     static constexpr int WAVES = MT == 1 ? 16 : 12;
     static constexpr int THREADS = WAVES * 64;
     // rowblocks whose results a wave keeps in registers (stored together)
-    static constexpr int R = MT == 1 ? 4 : 2;
+    static constexpr int R = MT == 1 ? 6 : 2;
     static constexpr int MP = 16 * MT;               // padded activation rows
     static constexpr int SEGK = 32 / MT;             // tiles per staged segment
     static constexpr int RS = SEGK * 128 + 8;        // LDS row stride in bf16 (16-byte pad)
