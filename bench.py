@@ -36,10 +36,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the sources that decide what the decode-step kernel reads and writes: the
+# kernel, the shared helpers, and the C ABI that builds its work list
+STEP_SOURCES = ("capi.hip", "q4_gemv.hip", "qg_internal.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_weight_decode_dequant_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in STEP_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
