@@ -471,13 +471,41 @@ def main():
     # from HBM; the single lm_head repeats, and 350 MB of it exceeds the
     # 256 MB last-level cache), at M = 1 (qgemv_run) and in verification
     # tiles (qgemm_skinny_run)
+    def plain_read_us(nbytes: int) -> float:
+        """Time of qg_plain_read over nbytes, distinct copies back to back (at
+        least 1 GB of them, beyond the last-level cache), best of 1, 2 and 4
+        workgroups per CU: the floor for one call that reads that much."""
+        nbytes = nbytes // 16 * 16
+        copies = max(2, min(256, (1 << 30) // nbytes + 1))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        for buf in bufs:
+            buf.fill_(1)
+        sink = torch.empty(65536, dtype=torch.int32, device=dev)
+        best = None
+        for per_cu in (1, 2, 4):
+            grid = props.multi_processor_count * per_cu
+            it = [0]
+
+            def call():
+                pkg.qg_plain_read(bufs[it[0] % copies], sink, grid)
+                it[0] += 1
+
+            us = workloads.time_graph_ms(call, min(copies, 64)) * 1e3
+            best = us if best is None else min(best, us)
+        del bufs
+        return best
+
     if not args.no_per_shape:
         shapes = {}
         for g in step.gemvs:
             shapes.setdefault((g.name.split(".")[-1], g.N, g.K), []).append(g)
-        per_shape = {}
+        per_shape, floors = {}, {}
         for (name, N, K), gs in shapes.items():
-            row = {"N": N, "K": K, "matrices": len(gs)}
+            wbytes = int(roofline.q4_gemm_bytes(1, N, K))
+            if wbytes not in floors:
+                floors[wbytes] = plain_read_us(wbytes)
+            row = {"N": N, "K": K, "matrices": len(gs),
+                   "plain_read_us": round(floors[wbytes], 2)}
             for M in [1] + [int(v) for v in args.verify_m.split(",") if v]:
                 X = workloads.verification_tile(args.seed, gs[0], M)
                 Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -495,12 +523,15 @@ def main():
                 b = roofline.q4_gemm_bytes(M, N, K)
                 row["m%d" % M] = {"us": round(ms * 1e3, 2),
                                   "GBs": round(b / (ms * 1e-3) / 1e9, 1),
-                                  "pct_of_peak": round(100 * b / (ms * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1)}
+                                  "pct_of_peak": round(100 * b / (ms * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1),
+                                  "pct_of_plain_read": round(100 * floors[wbytes] / (ms * 1e3), 1)}
             per_shape[name] = row
-            log("shape %s %dx%d: %s" % (name, N, K, ", ".join(
+            log("shape %s %dx%d: plain read %.1f us; %s" % (name, N, K, floors[wbytes], ", ".join(
                 "m%s %.1f us" % (k[1:], v["us"]) for k, v in row.items() if k.startswith("m") and k != "matrices")))
         result["per_shape"] = dict(per_shape, workload="one qgemv_run (M=1) or qgemm_skinny_run "
-                                   "(M rows) per call, captured in a HIP graph, bf16 output")
+                                   "(M rows) per call, captured in a HIP graph, bf16 output; "
+                                   "plain_read_us: qg_plain_read of the same weight bytes, one call, "
+                                   "the floor for a call that size (launch and ramp included)")
 
     # ---- the two Q4 kernel families on the same pass, for the rows where
     # both apply: the default choice follows these figures
@@ -534,7 +565,9 @@ def main():
 
         ms1 = workloads.time_graph_ms(one_gemv, len(sq))
         b1 = roofline.q4_gemm_bytes(1, 4096, 4096)
+        fl1 = plain_read_us(int(b1))
         result["single_gemv"] = {
+            "plain_read_us": round(fl1, 2), "pct_of_plain_read": round(100 * fl1 / (ms1 * 1e3), 1),
             "workload": "4-bit g64 GEMV 4096x4096, M=1, one qgemv_run launch each, %d distinct "
                         "matrices back to back (captured in a HIP graph)" % len(sq),
             "us_per_gemv": round(ms1 * 1e3, 3),
@@ -550,7 +583,10 @@ def main():
             msg = workloads.time_graph_ms(wl.gemm, len(wl.packed))
             bq = roofline.hadamard_quant_bytes(16, K)
             bg = roofline.q8_gemm_bytes(16, N, K)
+            flg = plain_read_us(int(bg))
             i8["%dx%d" % (K, N)] = {
+                "gemm_plain_read_us": round(flg, 2),
+                "gemm_pct_of_plain_read": round(100 * flg / (msg * 1e3), 1),
                 "hadamard_quant_us": round(msq * 1e3, 3),
                 "hadamard_quant_GBs": round(bq / (msq * 1e-3) / 1e9, 2),
                 "gemm_us": round(msg * 1e3, 3),
@@ -566,7 +602,9 @@ def main():
         moe = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16)
         msm = workloads.time_graph_ms(moe.run, 64)
         bm = roofline.moe_token_bytes(16, 7168, 2048)
+        flm = plain_read_us(int(bm))
         result["moe"] = {
+            "plain_read_us": round(flm, 2), "pct_of_plain_read": round(100 * flm / (msm * 1e3), 1),
             "workload": "MXFP4 MoE layer, 384 experts, hidden 7168, expert FFN 2048, top-16 "
                         "(a different seeded route per call), M=1; calls captured in a HIP graph",
             "us_per_token_layer": round(msm * 1e3, 3),
