@@ -68,9 +68,12 @@ def run_moe(packed, E, H, F, x, ids, w, out_dtype, workspace=None):
     return to_np(y)
 
 
-# the last case stages more h than fits in LDS, so it takes the two-launch
-# down projection plus combine instead of the fused one
+# two cases have more rowblocks of H than a GPU has CUs (the fused down
+# projection's workgroups then take two rowblocks each in turn); the last
+# case stages more h than fits in LDS, so it takes the two-launch down
+# projection plus combine instead of the fused one
 @pytest.mark.parametrize("E,H,F,top_k", [(6, 256, 512, 3), (4, 96, 160, 4), (9, 1024, 256, 1),
+                                         (5, 5120, 256, 3), (9, 4160, 512, 7),
                                          (5, 64, 12288, 4)])
 def test_moe_small(E, H, F, top_k):
     note("moe E=%d H=%d F=%d top_k=%d" % (E, H, F, top_k))
