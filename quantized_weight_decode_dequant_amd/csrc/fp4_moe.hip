@@ -150,9 +150,9 @@ fp4_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restrict__
             const int row = rb * RB + lane;
             if (row < N) {
                 if (out_f32)
-                    reinterpret_cast<float *>(y)[row] = v;
+                    st_global<float>(y, row, v);
                 else
-                    reinterpret_cast<uint16_t *>(y)[row] = f32_to_bf16(v);
+                    st_global<uint16_t>(y, row, f32_to_bf16(v));
             }
         }
         par ^= 1;
@@ -504,9 +504,9 @@ moe_down_fused_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ 
             for (int wv = 0; wv < MF_WAVES; ++wv) v += red[wv * 16 + tid];
             const int n = rb * RB + tid;
             if (out_f32)
-                reinterpret_cast<float *>(y)[n] = v;
+                st_global<float>(y, n, v);
             else
-                reinterpret_cast<uint16_t *>(y)[n] = f32_to_bf16(v);
+                st_global<uint16_t>(y, n, f32_to_bf16(v));
         }
         __syncthreads();  // red is reused by the next unit
         rb += G;
@@ -545,9 +545,9 @@ moe_combine_kernel(const float *__restrict__ part, const int32_t *__restrict__ i
     }
     if (n < H) {
         if (out_f32)
-            reinterpret_cast<float *>(y)[n] = v;
+            st_global<float>(y, n, v);
         else
-            reinterpret_cast<uint16_t *>(y)[n] = f32_to_bf16(v);
+            st_global<uint16_t>(y, n, f32_to_bf16(v));
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) status[0] = bad;
 }

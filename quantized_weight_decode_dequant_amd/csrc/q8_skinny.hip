@@ -132,7 +132,7 @@ __device__ __forceinline__ void q8_compute(const Q8W<T> &B, const int8_t *xl, in
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int m = 16 * mt + 4 * kg + e;
-                            if (m < M) reinterpret_cast<int32_t *>(Y)[((size_t)m * N + n) * G + gg] = P4[e];
+                            if (m < M) st_global<int32_t>(Y, ((size_t)m * N + n) * G + gg, P4[e]);
                         }
                     }
                 } else {
@@ -144,35 +144,64 @@ __device__ __forceinline__ void q8_compute(const Q8W<T> &B, const int8_t *xl, in
     }
 }
 
-// Sum the 16 waves' partials of rowblock rb in wave order and write Y.
-template <int MT>
-__device__ __forceinline__ void q8_finish(const f32x4_t acc[MT], f32x4_t (*red)[64], int wave,
-                                          int lane, const float *x_scales, void *Y, int M, int N,
-                                          int n, int out_f32) {
+// Sum the 16 waves' partials of rowblock rb in wave order and write Y.  xsc
+// holds the row scales of this lane's output rows (m = 16 mt + 4 kg + e),
+// read once at the start: a global load here would complete only after the
+// weight loads issued before it (loads complete in issue order), so the
+// reduction, and every wave waiting on it, would wait for the next
+// rowblock's weights.  With DB (two reduction buffers fit in LDS) the
+// partials of consecutive rowblocks alternate between the buffers, so one
+// barrier per 16-row tile suffices (a buffer is written again only after
+// the barrier of the next tile, which its readers pass after reading), and
+// waves 0..3 each add one of a lane's four values and store it; without,
+// wave 0 adds and stores all four between two barriers.  Either way every
+// value is the same sum in the same order.
+template <int MT, bool DB>
+__device__ __forceinline__ void q8_finish(const f32x4_t acc[MT], f32x4_t (*red)[Q8_WAVES][64],
+                                          int &par, int wave, int lane, const f32x4_t xsc[MT],
+                                          void *Y, int M, int N, int n, int out_f32) {
     const int kg = lane >> 4;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        red[wave][lane] = acc[mt];
+        f32x4_t(*rb)[64] = red[DB ? par : 0];
+        rb[wave][lane] = acc[mt];
         __syncthreads();
-        if (wave == 0) {
-            f32x4_t s = red[0][lane];
+        if (DB) {
+            if (wave < 4) {
+                const int e = wave, m = 16 * mt + 4 * kg + e;
+                float v = rb[0][lane][e];
 #pragma unroll
-            for (int w = 1; w < Q8_WAVES; ++w) s += red[w][lane];
-            if (n < N) {
+                for (int w = 1; w < Q8_WAVES; ++w) v += rb[w][lane][e];
+                const float sc = e == 0 ? xsc[mt][0] : e == 1 ? xsc[mt][1] : e == 2 ? xsc[mt][2] : xsc[mt][3];
+                if (n < N && m < M) {
+                    if (out_f32)
+                        st_global<float>(Y, (size_t)m * N + n, sc * v);
+                    else
+                        st_global<uint16_t>(Y, (size_t)m * N + n, f32_to_bf16(sc * v));
+                }
+            }
+            par ^= 1;
+        } else {
+            if (wave == 0) {
+                f32x4_t sum = rb[0][lane];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = 16 * mt + 4 * kg + e;
-                    if (m < M) {
-                        const float v = x_scales[m] * s[e];
-                        if (out_f32)
-                            reinterpret_cast<float *>(Y)[(size_t)m * N + n] = v;
-                        else
-                            reinterpret_cast<uint16_t *>(Y)[(size_t)m * N + n] = f32_to_bf16(v);
+                for (int w = 1; w < Q8_WAVES; ++w) sum += rb[w][lane];
+                if (n < N) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = 16 * mt + 4 * kg + e;
+                        if (m < M) {
+                            const float v = xsc[mt][e] * sum[e];
+                            if (out_f32)
+                                st_global<float>(Y, (size_t)m * N + n, v);
+                            else
+                                st_global<uint16_t>(Y, (size_t)m * N + n, f32_to_bf16(v));
+                        }
                     }
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -188,14 +217,26 @@ q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ 
                  const float *__restrict__ x_scales, void *__restrict__ Y, int M, int N, int K,
                  int P, int nrb, int out_f32) {
     typedef Q8Cfg<MT, T> C;
+    // two reduction buffers when they fit beside Xq
+    constexpr bool DB = C::LDS_X + 2 * sizeof(f32x4_t) * Q8_WAVES * 64 <= 160 * 1024;
     __shared__ __attribute__((aligned(16))) int8_t xl[C::LDS_X];
-    __shared__ f32x4_t red[GROUPS ? 1 : Q8_WAVES][64];
+    __shared__ f32x4_t red[GROUPS ? 1 : (DB ? 2 : 1)][GROUPS ? 1 : Q8_WAVES][64];
+    int par = 0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = K / 32;
     const int nseg = (P + C::SEGT - 1) / C::SEGT;
     int rb = blockIdx.x;
     if (rb >= nrb) return;
+    // the scales of this lane's output rows, before any weight load
+    f32x4_t xsc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 16 * mt + 4 * (lane >> 4) + e;
+            xsc[mt][e] = (!GROUPS && m < M) ? x_scales[m] : 0.f;
+        }
     f32x4_t acc[MT];
     Q8W<T> A, B;
     if (nseg == 1) {
@@ -212,7 +253,7 @@ q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ 
             q8_zero<MT>(acc);
             const int n = rb * RB + (lane & 15);
             q8_compute<MT, T, GROUPS>(A, xl, p0, p0, lane, acc, Y, M, N, G, n);
-            if constexpr (!GROUPS) q8_finish<MT>(acc, red, wave, lane, x_scales, Y, M, N, n, out_f32);
+            if constexpr (!GROUPS) q8_finish<MT, DB>(acc, red, par, wave, lane, xsc, Y, M, N, n, out_f32);
             if (nx >= nrb) break;
             rb = nx;
             nx = rb + gridDim.x;
@@ -221,7 +262,7 @@ q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ 
             q8_zero<MT>(acc);
             const int n2 = rb * RB + (lane & 15);
             q8_compute<MT, T, GROUPS>(B, xl, p0, p0, lane, acc, Y, M, N, G, n2);
-            if constexpr (!GROUPS) q8_finish<MT>(acc, red, wave, lane, x_scales, Y, M, N, n2, out_f32);
+            if constexpr (!GROUPS) q8_finish<MT, DB>(acc, red, par, wave, lane, xsc, Y, M, N, n2, out_f32);
             if (nx >= nrb) break;
             rb = nx;
         }
@@ -241,7 +282,7 @@ q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ 
             q8_stage<MT, T>(X, M, K, seg, xl, tid);
             q8_compute<MT, T, GROUPS>(A, xl, wave * T, p0, lane, acc, Y, M, N, G, n);
         }
-        if constexpr (!GROUPS) q8_finish<MT>(acc, red, wave, lane, x_scales, Y, M, N, n, out_f32);
+        if constexpr (!GROUPS) q8_finish<MT, DB>(acc, red, par, wave, lane, xsc, Y, M, N, n, out_f32);
     }
     (void)B;
 }
