@@ -93,30 +93,45 @@ struct GemvLds {
     float *part;    // [GV_RMAX][GV_WAVES][MR][16] per-wave row sums of the block
 };
 
-// Stage tiles [0, nt) of segment `seg` of the M activation rows (rows past
-// M and k past K read as zero; nt covers the segment's tiles rounded up to
-// whole batches) and their per-(tile, group, k-slice) sums.  Ends with a
-// barrier; the caller guarantees no wave still reads the previous segment.
+// Staging of tiles [0, nt) of segment `seg` of the M activation rows (rows
+// past M and k past K read as zero; nt covers the segment's tiles rounded up
+// to whole batches) with their per-(tile, group, k-slice) sums, in two
+// halves: gv_stage_load brings the x chunks into registers, gv_stage_store
+// writes them to LDS (the caller guarantees no wave still reads the previous
+// segment), sums them and ends with a barrier.  The x loads go out before
+// the segment's first weight loads: a wave's loads complete in issue order,
+// so x issued after the weights would wait for them.
 template <int MR>
-__device__ __forceinline__ void gv_stage_x(const GemvLds &L, const uint16_t *x, int M, int K,
-                                           int seg, int nt, int tid) {
+struct GvStage {
+    static constexpr int U = (GvCfg<MR>::ROW4 * MR) / GV_THREADS;
+    u32x4_t v[U];
+};
+
+template <int MR>
+__device__ __forceinline__ void gv_stage_load(GvStage<MR> &st, const uint16_t *x, int M, int K,
+                                              int seg, int nt, int tid) {
     typedef GvCfg<MR> C;
     const int k0 = seg * C::SEG * Q4_TILE_K;
     const int n4 = nt * 16;                    // uint4 to stage per row
     const int nx4 = (K - k0) / 8;              // valid uint4 per row (K is a multiple of 64)
-    constexpr int U = (C::ROW4 * MR) / GV_THREADS;
-    u32x4_t v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < GvStage<MR>::U; ++u) {
         const int i = tid + u * GV_THREADS, m = i / C::ROW4, j = i - m * C::ROW4;
-        v[u] = (m < M && j < nx4 && j < n4)
-                   ? ld_global(reinterpret_cast<const u32x4_t *>(x + (size_t)m * K + k0) + j)
-                   : u32x4_t{0u, 0u, 0u, 0u};
+        st.v[u] = (m < M && j < nx4 && j < n4)
+                      ? ld_global(reinterpret_cast<const u32x4_t *>(x + (size_t)m * K + k0) + j)
+                      : u32x4_t{0u, 0u, 0u, 0u};
     }
+}
+
+template <int MR>
+__device__ __forceinline__ void gv_stage_store(const GvStage<MR> &st, const GemvLds &L, int nt,
+                                               int tid) {
+    typedef GvCfg<MR> C;
+    const int n4 = nt * 16;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < GvStage<MR>::U; ++u) {
         const int i = tid + u * GV_THREADS, m = i / C::ROW4, j = i - m * C::ROW4;
-        if (j < n4) reinterpret_cast<u32x4_t *>(L.xl)[i] = v[u];
+        if (j < n4) reinterpret_cast<u32x4_t *>(L.xl)[i] = st.v[u];
     }
     __syncthreads();
 #pragma unroll
@@ -285,9 +300,11 @@ __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, int
             float acc[MR];
 #pragma unroll
             for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+            GvStage<MR> st;
+            gv_stage_load<MR>(st, x, M, it.K, seg, nb * GV_TPW, tid);
             gv_load(A, it, ub, pbase, pn, ca, t < T, lane);
             __syncthreads();  // nobody still reads the previous segment
-            gv_stage_x<MR>(L, x, M, it.K, seg, nb * GV_TPW, tid);
+            gv_stage_store<MR>(st, L, nb * GV_TPW, tid);
 #pragma unroll 1
             for (;;) {
                 if (t >= T) break;
