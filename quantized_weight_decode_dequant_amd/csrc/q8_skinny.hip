@@ -16,12 +16,12 @@
 // of 16 waves, which holds a K-segment of Xq (up to 96 KB) in LDS and walks
 // rowblocks (16 weight rows) in a grid-strided loop.  Within a rowblock the
 // 16 waves split K: wave w takes T consecutive 128-k tiles of each segment.
-// The weight loads of a rowblock are all issued at once; when K is one
-// segment those of the next rowblock go out before the arithmetic of the
-// current one, and every segment's go out before its Xq is staged.  Xq is
-// staged with coalesced 16-byte loads and read back by each MFMA as its
-// 8-byte A operand.  The 16 per-wave partial sums of a rowblock are reduced
-// in LDS in wave order (deterministic).  Weight tiles past the end of K read
+// The weight loads of a rowblock are all issued at once, right after the
+// first Xq loads of the segment (see q8_stage_pre); when K is one segment
+// those of the next rowblock go out before the arithmetic of the current
+// one.  Xq is staged with coalesced 16-byte loads and read back by each MFMA
+// as its 8-byte A operand.  The 16 per-wave partial sums of a rowblock are
+// reduced in LDS in wave order (deterministic).  Weight tiles past the end of K read
 // as zero (their offsets sit in the range-checked part of the buffer
 // address), and so does Xq past K and past row M, so ragged shapes need no
 // branches.
@@ -66,38 +66,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t q8_rsrc(const uint8_t *packed,
     return make_rsrc(uniform_ptr(packed + (size_t)rb * wbytes), valid ? wbytes : 0u);
 }
 
-// Stage segment `seg` of Xq (SEGT tiles; zero past K and past row M).
+// Staging of segment `seg` of Xq (SEGT tiles; zero past K and past row M).
+// The first Q8_PRE 16-byte chunks per thread are loaded into registers by
+// q8_stage_pre, which callers issue before the segment's weight loads (a
+// wave's loads complete in issue order, so Xq loaded after the weights would
+// wait for them); q8_stage_rest stores them, stages the remaining chunks, if
+// any, and ends with a barrier.
+constexpr int Q8_PRE = 4;
+
 template <int MT, int T>
-__device__ __forceinline__ void q8_stage(const int8_t *X, int M, int K, int seg, int8_t *xl,
-                                         int tid) {
-    typedef Q8Cfg<MT, T> C;
-    const int k0 = seg * C::SEGT * Q8_TILE_K;
-    constexpr int PER_ROW = C::SEGT * Q8_TILE_K / 16;  // 16-byte chunks per row
-    constexpr int TOTAL = C::MP * PER_ROW;
+struct Q8Stage {
+    static constexpr int PER_ROW = Q8Cfg<MT, T>::SEGT * Q8_TILE_K / 16;  // 16-byte chunks per row
+    static constexpr int TOTAL = Q8Cfg<MT, T>::MP * PER_ROW;
+    u32x4_t v[Q8_PRE];
+};
+
+template <int MT, int T>
+__device__ __forceinline__ u32x4_t q8_chunk(const int8_t *X, int M, int K, int seg, int i) {
+    typedef Q8Stage<MT, T> S;
+    const int m = i / S::PER_ROW, c = i - m * S::PER_ROW;
+    const int k = seg * Q8Cfg<MT, T>::SEGT * Q8_TILE_K + 16 * c;
+    return (i < S::TOTAL && m < M && k < K)
+               ? ld_global(reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k))
+               : u32x4_t{0u, 0u, 0u, 0u};
+}
+
+template <int MT, int T>
+__device__ __forceinline__ void q8_chunk_store(int8_t *xl, int i, u32x4_t v) {
+    typedef Q8Stage<MT, T> S;
+    const int m = i / S::PER_ROW, c = i - m * S::PER_ROW;
+    if (i < S::TOTAL) {
+        // rows are 8-byte aligned: two 8-byte stores
+        u32x2_t *d = reinterpret_cast<u32x2_t *>(xl + m * Q8Cfg<MT, T>::RS + 16 * c);
+        d[0] = u32x2_t{v[0], v[1]};
+        d[1] = u32x2_t{v[2], v[3]};
+    }
+}
+
+template <int MT, int T>
+__device__ __forceinline__ void q8_stage_pre(Q8Stage<MT, T> &st, const int8_t *X, int M, int K,
+                                             int seg, int tid) {
+#pragma unroll
+    for (int u = 0; u < Q8_PRE; ++u) st.v[u] = q8_chunk<MT, T>(X, M, K, seg, tid + u * Q8_THREADS);
+}
+
+template <int MT, int T>
+__device__ __forceinline__ void q8_stage_rest(const Q8Stage<MT, T> &st, const int8_t *X, int M,
+                                              int K, int seg, int8_t *xl, int tid) {
+    typedef Q8Stage<MT, T> S;
+#pragma unroll
+    for (int u = 0; u < Q8_PRE; ++u) q8_chunk_store<MT, T>(xl, tid + u * Q8_THREADS, st.v[u]);
     constexpr int U = 4;
 #pragma unroll 1
-    for (int i0 = tid; i0 < TOTAL; i0 += U * Q8_THREADS) {
+    for (int i0 = tid + Q8_PRE * Q8_THREADS; i0 < S::TOTAL; i0 += U * Q8_THREADS) {
         u32x4_t v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = i0 + u * Q8_THREADS;
-            const int m = i / PER_ROW, c = i - m * PER_ROW;
-            const int k = k0 + 16 * c;
-            v[u] = (i < TOTAL && m < M && k < K)
-                       ? ld_global(reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k))
-                       : u32x4_t{0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < U; ++u) v[u] = q8_chunk<MT, T>(X, M, K, seg, i0 + u * Q8_THREADS);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = i0 + u * Q8_THREADS;
-            const int m = i / PER_ROW, c = i - m * PER_ROW;
-            if (i < TOTAL) {
-                // rows are 8-byte aligned: two 8-byte stores
-                u32x2_t *d = reinterpret_cast<u32x2_t *>(xl + m * C::RS + 16 * c);
-                d[0] = u32x2_t{v[u][0], v[u][1]};
-                d[1] = u32x2_t{v[u][2], v[u][3]};
-            }
-        }
+        for (int u = 0; u < U; ++u) q8_chunk_store<MT, T>(xl, i0 + u * Q8_THREADS, v[u]);
     }
     __syncthreads();
 }
@@ -243,8 +269,10 @@ q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ 
         // Xq staged once; the next rowblock's weights load during this one's
         // arithmetic
         const int p0 = wave * T;
+        Q8Stage<MT, T> st;
+        q8_stage_pre<MT, T>(st, X, M, K, 0, tid);
         q8_load<T>(A, q8_rsrc(packed, rb, P, true), p0, lane);
-        q8_stage<MT, T>(X, M, K, 0, xl, tid);
+        q8_stage_rest<MT, T>(st, X, M, K, 0, xl, tid);
 #pragma unroll 1
         for (;;) {
             int nx = rb + gridDim.x;
@@ -277,9 +305,11 @@ q8_skinny_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ 
 #pragma unroll 1
         for (int seg = 0; seg < nseg; ++seg) {
             const int p0 = seg * C::SEGT + wave * T;
+            Q8Stage<MT, T> st;
+            q8_stage_pre<MT, T>(st, X, M, K, seg, tid);
             q8_load<T>(A, q8_rsrc(packed, rb, P, true), p0, lane);
             __syncthreads();  // nobody still reads the previous segment
-            q8_stage<MT, T>(X, M, K, seg, xl, tid);
+            q8_stage_rest<MT, T>(st, X, M, K, seg, xl, tid);
             q8_compute<MT, T, GROUPS>(A, xl, wave * T, p0, lane, acc, Y, M, N, G, n);
         }
         if constexpr (!GROUPS) q8_finish<MT, DB>(acc, red, par, wave, lane, xsc, Y, M, N, n, out_f32);
