@@ -225,6 +225,55 @@ int moe_expert_gemv_run(const void *packed_gate, const void *packed_up,
                         int out_dtype, void *stream);
 
 /*
+ * Bytes of workspace moe_expert_skinny_run needs for (T, top_k, H, F), with
+ * P = T * top_k (position, slot) pairs: h (fp32 [P][F]), the per-pair partial
+ * outputs (fp32 [P][H]), a 16-byte header (status word first) and the
+ * expert groups (32 bytes per pair).  Pure host function.
+ */
+size_t qg_moe_skinny_workspace_bytes(int64_t T, int64_t top_k, int64_t H,
+                                     int64_t F);
+
+/*
+ * moe_expert_skinny_run -- T positions (a verification tile of draft tokens)
+ * through the routed experts of one MoE layer in MXFP4, each position with
+ * its own router output (Deltafin / Kimi K3 page, "How it works": only the
+ * selected experts are read):
+ *     for t < T, s < top_k with e = expert_ids[t][s]:
+ *         g = Wgate[e] X[t],  u = Wup[e] X[t],  h = silu(g) * u,
+ *     Y[t] = sum_s expert_w[t][s] * (Wdown[e] h).
+ * Each row of Y is what moe_expert_gemv_run returns for X[t], ids[t], w[t],
+ * up to rounding.  The weights of an expert chosen by several positions are
+ * read once for up to four of them, so a pass reads about the union of the
+ * positions' experts.  g, u, h and the partial outputs are fp32 (h enters
+ * the down projection as a bf16 pair hi + lo, relative error <= 2^-16); Y is
+ * rounded once at the end; every sum is taken in a fixed order, so results
+ * are deterministic.  The ids stay on the device.
+ *
+ *  packed_gate, packed_up, packed_down, bytes_*, E, H, F
+ *               as for moe_expert_gemv_run.
+ *  T            positions, 1..32, with T * top_k <= 2048.
+ *  X            device bf16 [T][H], 16-B.  Read only.
+ *  top_k        0..min(E, 64).
+ *  expert_ids   device int32 [T][top_k]; an id outside [0, E) contributes 0.
+ *               The call rewrites a status word (uint32 at byte offset
+ *               4 * T * top_k * (F + H) of the workspace): 1 if any id was
+ *               out of range, else 0.
+ *  expert_w     device fp32 [T][top_k] router weights.
+ *  workspace    device buffer (16-B) of at least qg_moe_skinny_workspace_bytes
+ *               bytes; scratch, overwritten by every call.
+ *  Y            device [T][H] bf16 or fp32, written.
+ * Errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN, QG_ESIZE, QG_EUNSUPPORTED, QG_EHIP.
+ */
+int moe_expert_skinny_run(const void *packed_gate, const void *packed_up,
+                          const void *packed_down, size_t bytes_gate,
+                          size_t bytes_up, size_t bytes_down, int64_t E,
+                          int64_t H, int64_t F, int64_t T, const void *X,
+                          int top_k, const int32_t *expert_ids,
+                          const float *expert_w, void *workspace,
+                          size_t workspace_bytes, void *Y, int out_dtype,
+                          void *stream);
+
+/*
  * Grouped launches: many independent products in one kernel launch.
  *
  * A decode step runs every projection of the model once per token; issuing

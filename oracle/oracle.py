@@ -225,3 +225,18 @@ def moe(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales, x
     _load().oracle_moe(E, H, F, pgc, pgs, puc, pus, pdc, pds, px, top_k, pid, pw,
                        vp(g), vp(u), vp(h), vp(d), vp(y))
     return y
+
+
+def moe_positions(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales, X, ids,
+                  w):
+    """Y [T, H] (float64): T positions through the routed experts, each with
+    its own router output.  The positions are independent, so row t is the
+    single-token layer (``moe``) applied to X[t], ids[t], w[t].
+
+    X bf16 bits [T, H]; ids int32 [T, top_k]; w float32 [T, top_k]."""
+    X = np.asarray(X, dtype=np.uint16)
+    ids = np.asarray(ids, dtype=np.int32)
+    w = np.asarray(w, dtype=np.float32)
+    assert X.ndim == 2 and ids.shape == w.shape and ids.shape[0] == X.shape[0]
+    return np.stack([moe(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales,
+                         X[t], ids[t], w[t]) for t in range(X.shape[0])])

@@ -47,6 +47,8 @@ EXPORTS = (
     "hadamard32_quant_run",
     "qg_moe_workspace_bytes",
     "moe_expert_gemv_run",
+    "qg_moe_skinny_workspace_bytes",
+    "moe_expert_skinny_run",
     "qg_batch_worklist_bytes",
     "qg_batch_plan_build",
     "qg_batch_run",
@@ -105,6 +107,11 @@ def raw():
             lib.moe_expert_gemv_run.argtypes = [p, p, p, sz, sz, sz, i64, i64, i64, p, i, p, p,
                                                 p, sz, p, i, p]
             lib.moe_expert_gemv_run.restype = i
+            lib.qg_moe_skinny_workspace_bytes.argtypes = [i64, i64, i64, i64]
+            lib.qg_moe_skinny_workspace_bytes.restype = sz
+            lib.moe_expert_skinny_run.argtypes = [p, p, p, sz, sz, sz, i64, i64, i64, i64, p, i,
+                                                  p, p, p, sz, p, i, p]
+            lib.moe_expert_skinny_run.restype = i
             lib.qg_batch_worklist_bytes.argtypes = [C.c_int32]
             lib.qg_batch_worklist_bytes.restype = sz
             lib.qg_batch_plan_build.argtypes = [i, i64, C.c_int32, C.POINTER(GemvDesc), i, i, p, sz,
@@ -229,6 +236,33 @@ def moe_expert_gemv_run(packed_gate, packed_up, packed_down, E: int, H: int, F: 
                                      _ptr(workspace), workspace.numel(), _ptr(y), out_dtype,
                                      _stream(stream)), "moe_expert_gemv_run")
     return y
+
+
+def moe_skinny_workspace_bytes(T: int, top_k: int, H: int, F: int) -> int:
+    return raw().qg_moe_skinny_workspace_bytes(T, top_k, H, F)
+
+
+def moe_expert_skinny_run(packed_gate, packed_up, packed_down, E: int, H: int, F: int, X,
+                          expert_ids, expert_w, workspace=None, Y=None,
+                          out_dtype: int = OUT_BF16, stream=None):
+    """X [T, H] bf16; expert_ids int32 / expert_w fp32 [T, top_k]; Y [T, H]."""
+    torch = _torch()
+    T = int(X.shape[0])
+    top_k = int(expert_ids.shape[1]) if expert_ids.dim() == 2 else 0
+    if tuple(expert_ids.shape) != (T, top_k) or tuple(expert_w.shape) != (T, top_k):
+        raise ValueError("expert_ids and expert_w must be [T, top_k]")
+    if workspace is None:
+        workspace = torch.empty(moe_skinny_workspace_bytes(T, top_k, H, F), dtype=torch.uint8,
+                                device=X.device)
+    if Y is None:
+        Y = torch.empty(T, H, dtype=_out_torch_dtype(out_dtype), device=X.device)
+    _check(raw().moe_expert_skinny_run(_ptr(packed_gate), _ptr(packed_up), _ptr(packed_down),
+                                       packed_gate.numel(), packed_up.numel(),
+                                       packed_down.numel(), E, H, F, T, _ptr(X), top_k,
+                                       _ptr(expert_ids), _ptr(expert_w), _ptr(workspace),
+                                       workspace.numel(), _ptr(Y), out_dtype, _stream(stream)),
+           "moe_expert_skinny_run")
+    return Y
 
 
 # ------------------------------------------------------------------ grouped launches

@@ -232,24 +232,52 @@ size_t qg_moe_workspace_bytes(int64_t top_k, int64_t H, int64_t F) {
     return (size_t)4 * (size_t)top_k * (size_t)(F + H) + 16;
 }
 
+size_t qg_moe_skinny_workspace_bytes(int64_t T, int64_t top_k, int64_t H, int64_t F) {
+    if (T < 0 || top_k < 0 || H < 0 || F < 0) return 0;
+    const size_t P = (size_t)T * (size_t)top_k;
+    return (size_t)4 * P * (size_t)(F + H) + 16 + (size_t)32 * P;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the MoE entry points (everything but the activations,
+// the workspace size and the output).
+int moe_validate(const void *packed_gate, const void *packed_up, const void *packed_down,
+                 size_t bytes_gate, size_t bytes_up, size_t bytes_down, int64_t E, int64_t H,
+                 int64_t F, int top_k, const int32_t *expert_ids, const float *expert_w,
+                 const void *workspace, int out_dtype) {
+    if (out_dtype != QG_OUT_BF16 && out_dtype != QG_OUT_F32 && out_dtype != QG_OUT_I32_GROUPS)
+        return QG_EINVAL;
+    if (out_dtype == QG_OUT_I32_GROUPS) return QG_EUNSUPPORTED;
+    if (E < 1 || H < 32 || F < 32 || H % 32 || F % 32 || H > MOE_H_MAX || F > MOE_F_MAX ||
+        E * F > N_MAX || E * H > N_MAX)
+        return QG_ESHAPE;
+    if (top_k < 0 || top_k > MOE_TOPK_MAX || top_k > E) return QG_ESHAPE;
+    if (!packed_gate || !packed_up || !packed_down || !workspace) return QG_EINVAL;
+    if (top_k > 0 && (!expert_ids || !expert_w)) return QG_EINVAL;
+    if (bytes_gate != fp4_packed_bytes(E * F, H) || bytes_up != fp4_packed_bytes(E * F, H) ||
+        bytes_down != fp4_packed_bytes(E * H, F))
+        return QG_ESIZE;
+    return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int moe_expert_gemv_run(const void *packed_gate, const void *packed_up, const void *packed_down,
                         size_t bytes_gate, size_t bytes_up, size_t bytes_down, int64_t E,
                         int64_t H, int64_t F, const void *x, int top_k,
                         const int32_t *expert_ids, const float *expert_w, void *workspace,
                         size_t workspace_bytes, void *y, int out_dtype, void *stream) {
     try {
-        if (out_dtype != QG_OUT_BF16 && out_dtype != QG_OUT_F32 && out_dtype != QG_OUT_I32_GROUPS)
-            return QG_EINVAL;
-        if (out_dtype == QG_OUT_I32_GROUPS) return QG_EUNSUPPORTED;
-        if (E < 1 || H < 32 || F < 32 || H % 32 || F % 32 || H > MOE_H_MAX || F > MOE_F_MAX ||
-            E * F > N_MAX || E * H > N_MAX)
-            return QG_ESHAPE;
-        if (top_k < 0 || top_k > MOE_TOPK_MAX || top_k > E) return QG_ESHAPE;
-        if (!packed_gate || !packed_up || !packed_down || !x || !y || !workspace) return QG_EINVAL;
-        if (top_k > 0 && (!expert_ids || !expert_w)) return QG_EINVAL;
-        if (bytes_gate != fp4_packed_bytes(E * F, H) || bytes_up != fp4_packed_bytes(E * F, H) ||
-            bytes_down != fp4_packed_bytes(E * H, F))
-            return QG_ESIZE;
+        int st = moe_validate(packed_gate, packed_up, packed_down, bytes_gate, bytes_up,
+                              bytes_down, E, H, F, top_k, expert_ids, expert_w, workspace,
+                              out_dtype);
+        if (st != QG_OK) return st;
+        if (!x || !y) return QG_EINVAL;
         if (workspace_bytes < qg_moe_workspace_bytes(top_k, H, F)) return QG_ESIZE;
         if (!aligned(packed_gate, 16) || !aligned(packed_up, 16) || !aligned(packed_down, 16) ||
             !aligned(x, 16) || !aligned(workspace, 16) ||
@@ -257,7 +285,7 @@ int moe_expert_gemv_run(const void *packed_gate, const void *packed_up, const vo
             (expert_ids && !aligned(expert_ids, 4)) || (expert_w && !aligned(expert_w, 4)))
             return QG_EALIGN;
         int cus = 0;
-        int st = device_cus(&cus);
+        st = device_cus(&cus);
         if (st != QG_OK) return st;
         return hip_status(launch_moe(reinterpret_cast<const uint8_t *>(packed_gate),
                                      reinterpret_cast<const uint8_t *>(packed_up),
@@ -271,6 +299,39 @@ int moe_expert_gemv_run(const void *packed_gate, const void *packed_up, const vo
     }
 }
 
+int moe_expert_skinny_run(const void *packed_gate, const void *packed_up,
+                          const void *packed_down, size_t bytes_gate, size_t bytes_up,
+                          size_t bytes_down, int64_t E, int64_t H, int64_t F, int64_t T,
+                          const void *X, int top_k, const int32_t *expert_ids,
+                          const float *expert_w, void *workspace, size_t workspace_bytes,
+                          void *Y, int out_dtype, void *stream) {
+    try {
+        int st = moe_validate(packed_gate, packed_up, packed_down, bytes_gate, bytes_up,
+                              bytes_down, E, H, F, top_k, expert_ids, expert_w, workspace,
+                              out_dtype);
+        if (st != QG_OK) return st;
+        if (T < 1 || T > M_MAX || T * top_k > MOE_PAIRS_MAX) return QG_ESHAPE;
+        if (!X || !Y) return QG_EINVAL;
+        if (workspace_bytes < qg_moe_skinny_workspace_bytes(T, top_k, H, F)) return QG_ESIZE;
+        if (!aligned(packed_gate, 16) || !aligned(packed_up, 16) || !aligned(packed_down, 16) ||
+            !aligned(X, 16) || !aligned(workspace, 16) ||
+            !aligned(Y, out_dtype == QG_OUT_F32 ? 4 : 2) ||
+            (expert_ids && !aligned(expert_ids, 4)) || (expert_w && !aligned(expert_w, 4)))
+            return QG_EALIGN;
+        int cus = 0;
+        st = device_cus(&cus);
+        if (st != QG_OK) return st;
+        return hip_status(launch_moe_skinny(
+            reinterpret_cast<const uint8_t *>(packed_gate),
+            reinterpret_cast<const uint8_t *>(packed_up),
+            reinterpret_cast<const uint8_t *>(packed_down), E, H, F, (int)T,
+            reinterpret_cast<const uint16_t *>(X), top_k, expert_ids, expert_w,
+            reinterpret_cast<uint8_t *>(workspace), Y, out_dtype == QG_OUT_F32, cus,
+            reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return QG_EINTERNAL;
+    }
+}
 
 size_t qg_batch_worklist_bytes(int32_t count) {
     if (count < 0) return 0;

@@ -25,7 +25,7 @@
 // before the arithmetic of the same tile of the current one.  A wave folds
 // its sums of a unit into its own LDS slot; the workgroup adds the wave slots
 // in wave order when a block of up to 32 units ends.
-#include "qg_internal.h"
+#include "fp4_stream.h"
 
 namespace qg {
 
@@ -174,28 +174,7 @@ hipError_t launch_fp4_gemv(const uint8_t *packed, const uint16_t *x, void *y, in
 // ------------------------------------------------------------ MoE streaming
 constexpr int MS_WAVES = 4;
 constexpr int MS_THREADS = MS_WAVES * 64;
-constexpr int MS_TPB = 4;     // tiles per batch
 constexpr int MS_RMAX = 32;   // units per output block
-
-struct Fp4Batch {
-    u32x4_t c0[MS_TPB], c1[MS_TPB];
-    unsigned e0[MS_TPB], e1[MS_TPB];
-};
-
-__device__ __forceinline__ unsigned buf_ld_u8(__amdgpu_buffer_rsrc_t r, unsigned voff,
-                                              unsigned soff) {
-    return (unsigned)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 2);
-}
-
-// One tile's slot loads (tile tp of the buffer, clamped to its last of pn).
-__device__ __forceinline__ void fp4_tile_load(Fp4Batch &B, int j, __amdgpu_buffer_rsrc_t rs,
-                                              int tp, int pn, int lane) {
-    const unsigned to = (unsigned)min(tp, pn - 1) * FP4_TILE_BYTES;
-    B.c0[j] = buf_ld_x4(rs, 16u * lane, to);
-    B.c1[j] = buf_ld_x4(rs, 1024u + 16u * lane, to);
-    B.e0[j] = buf_ld_u8(rs, 2048u + lane, to);
-    B.e1[j] = buf_ld_u8(rs, 2112u + lane, to);
-}
 
 // Position in a wave's batch stream: unit i (relative to the block), batch b.
 struct MsCursor {
@@ -516,11 +495,18 @@ moe_down_fused_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ 
 }
 
 // ------------------------------------------------------------ MoE phase C
+// y[t][n] = sum_s w[t][s] * part[t][s][n] in slot order for the position t =
+// blockIdx.y (one position for the single-token layer).  status (when not
+// null) receives 1 if any id of position 0 was out of range.
 __global__ void __launch_bounds__(256)
 moe_combine_kernel(const float *__restrict__ part, const int32_t *__restrict__ ids,
                    const float *__restrict__ w, int E, int H, int top_k, void *__restrict__ y,
                    int out_f32, unsigned *__restrict__ status) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    const int t = blockIdx.y;
+    part += (size_t)t * top_k * H;
+    ids += (size_t)t * top_k;
+    w += (size_t)t * top_k;
     constexpr int C = 16;  // slots whose loads are issued together
     float v = 0.f;
     unsigned bad = 0;
@@ -544,12 +530,22 @@ moe_combine_kernel(const float *__restrict__ part, const int32_t *__restrict__ i
         }
     }
     if (n < H) {
+        const size_t o = (size_t)t * H + n;
         if (out_f32)
-            st_global<float>(y, n, v);
+            st_global<float>(y, o, v);
         else
-            st_global<uint16_t>(y, n, f32_to_bf16(v));
+            st_global<uint16_t>(y, o, f32_to_bf16(v));
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) status[0] = bad;
+    if (status && t == 0 && blockIdx.x == 0 && threadIdx.x == 0) status[0] = bad;
+}
+
+hipError_t launch_moe_combine(const float *part, const int32_t *ids, const float *w, int64_t E,
+                              int64_t H, int top_k, int T, void *y, bool out_f32,
+                              unsigned *status, hipStream_t s) {
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)ceil_div(H, 256), (unsigned)T),
+                       dim3(256), 0, s, part, ids, w, (int)E, (int)H, top_k, y,
+                       out_f32 ? 1 : 0, status);
+    return hipGetLastError();
 }
 
 hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd, int64_t E,
@@ -591,9 +587,7 @@ hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd, i
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)ceil_div(H, 256)), dim3(256), 0, s,
-                       part, ids, w, (int)E, (int)H, top_k, y, out_f32 ? 1 : 0, status);
-    return hipGetLastError();
+    return launch_moe_combine(part, ids, w, E, H, top_k, 1, y, out_f32, status, s);
 }
 
 }  // namespace qg

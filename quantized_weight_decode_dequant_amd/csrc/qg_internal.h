@@ -47,6 +47,11 @@ constexpr int Q8_TILE_BYTES = 2176;
 constexpr int FP4_TILE_K = 256;
 constexpr int FP4_TILE_BYTES = 2176;
 
+// T-position MoE: (position, slot) pairs per call, and the most pairs of
+// one expert that share one read of its weights.
+constexpr int MOE_PAIRS_MAX = 2048;
+constexpr int MOE_GROUP_ROWS_MAX = 4;
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------- work lists
@@ -127,6 +132,17 @@ hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd,
                       int top_k, const int32_t *ids, const float *w,
                       uint8_t *workspace, void *y, bool out_f32, int cus,
                       hipStream_t s);
+
+hipError_t launch_moe_combine(const float *part, const int32_t *ids, const float *w,
+                              int64_t E, int64_t H, int top_k, int T, void *y,
+                              bool out_f32, unsigned *status, hipStream_t s);
+hipError_t launch_moe_skinny(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd,
+                             int64_t E, int64_t H, int64_t F, int T,
+                             const uint16_t *X, int top_k, const int32_t *ids,
+                             const float *w, uint8_t *workspace, void *Y,
+                             bool out_f32, int cus, hipStream_t s);
+// Positions whose x (or h) one group of the T-position MoE stages at once.
+int moe_skinny_group_rows(int64_t H, int64_t F);
 
 size_t q4_packed_bytes(int64_t N, int64_t K);
 size_t q8_packed_bytes(int64_t N, int64_t K);

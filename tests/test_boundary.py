@@ -180,6 +180,42 @@ def test_moe_validation():
     assert call(ids=A + 2) == L.QG_EALIGN
 
 
+def test_moe_skinny_validation():
+    lib = pkg.raw()
+    E, H, F, k, T = 8, 256, 512, 2, 5
+    bg = pkg.packed_bytes(L.FMT_MXFP4_G32, E * F, H)
+    bd = pkg.packed_bytes(L.FMT_MXFP4_G32, E * H, F)
+    ws = pkg.moe_skinny_workspace_bytes(T, k, H, F)
+    assert ws == 4 * T * k * (H + F) + 16 + 32 * T * k
+
+    def call(**kw):
+        a = dict(g=A, u=A, d=A, bg=bg, bu=bg, bd=bd, E=E, H=H, F=F, T=T, X=A, k=k, ids=A, w=A,
+                 ws=A, wsb=ws, Y=A, out=0)
+        a.update(kw)
+        return lib.moe_expert_skinny_run(a["g"], a["u"], a["d"], a["bg"], a["bu"], a["bd"],
+                                         a["E"], a["H"], a["F"], a["T"], a["X"], a["k"],
+                                         a["ids"], a["w"], a["ws"], a["wsb"], a["Y"], a["out"],
+                                         None)
+
+    assert call(out=5) == L.QG_EINVAL
+    assert call(out=L.OUT_I32_GROUPS) == L.QG_EUNSUPPORTED
+    assert call(T=0) == L.QG_ESHAPE
+    assert call(T=33) == L.QG_ESHAPE
+    assert call(k=E + 1) == L.QG_ESHAPE
+    assert call(E=65, k=65, T=32) == L.QG_ESHAPE  # top_k above 64
+    assert call(H=250) == L.QG_ESHAPE
+    assert call(F=12288 + 32) == L.QG_ESHAPE
+    assert call(X=None) == L.QG_EINVAL
+    assert call(Y=None) == L.QG_EINVAL
+    assert call(w=None) == L.QG_EINVAL
+    assert call(bg=bg + 16) == L.QG_ESIZE
+    assert call(wsb=ws - 1) == L.QG_ESIZE
+    assert call(X=A + 8) == L.QG_EALIGN
+    assert call(Y=A + 1) == L.QG_EALIGN
+    assert call(out=L.OUT_F32, Y=A + 2) == L.QG_EALIGN
+    assert call(ws=A + 8) == L.QG_EALIGN
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):

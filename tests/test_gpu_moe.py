@@ -166,3 +166,133 @@ def test_moe_routed_expert_workload_full():
     for p in parts:  # slot order, as the definition sums
         ref += p
     assert_bf16_close(got, ref, what="moe full")
+
+
+# ------------------------------------------------------------ T positions at once
+def run_moe_t(packed, E, H, F, X, ids, w, out_dtype, workspace=None):
+    pg, pu, pd = packed
+    Y = pkg.moe_expert_skinny_run(pg, pu, pd, E, H, F, weights.to_device(X, DEV),
+                                  weights.to_device(ids, DEV), weights.to_device(w, DEV),
+                                  workspace=workspace, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_np(Y)
+
+
+def _routes(seed, E, top_k, T):
+    ids, w = zip(*[synth.router(seed, E, top_k, item=t) for t in range(T)])
+    return np.stack(ids), np.stack(w)
+
+
+def _tokens(seed, H, T):
+    return np.stack([synth.moe_token(seed, H, item=t) for t in range(T)])
+
+
+# experts shared across positions; H not a multiple of the 256-k tile; 320
+# rowblocks of H; F at its maximum and H at its maximum (one position per
+# group); every expert chosen by all 32 positions (8 groups of 4 per expert);
+# T = 1
+@pytest.mark.parametrize("E,H,F,top_k,T", [(6, 256, 512, 3, 5), (4, 96, 160, 4, 3),
+                                           (9, 1024, 256, 2, 16), (5, 5120, 256, 3, 2),
+                                           (3, 64, 12288, 2, 4), (4, 24576, 64, 2, 3),
+                                           (6, 512, 256, 6, 32), (40, 256, 128, 8, 1)])
+def test_moe_positions(E, H, F, top_k, T):
+    note("moe positions E=%d H=%d F=%d top_k=%d T=%d" % (E, H, F, top_k, T))
+    pool = _pool(90, E, H, F)
+    X = _tokens(91, H, T)
+    ids, w = _routes(92, E, top_k, T)
+    ref = oracle.moe_positions(*pool, X, ids, w)
+    packed = _pack_pool(pool, E, H, F)
+    assert_f32_close(run_moe_t(packed, E, H, F, X, ids, w, pkg.OUT_F32), ref, what="f32")
+    assert_bf16_close(run_moe_t(packed, E, H, F, X, ids, w, pkg.OUT_BF16), ref, what="bf16")
+
+
+def test_moe_positions_invalid_duplicate_and_empty():
+    E, H, F, T = 5, 128, 96, 3
+    note("moe positions invalid ids, duplicates, top_k = 0")
+    pool = _pool(93, E, H, F)
+    packed = _pack_pool(pool, E, H, F)
+    X = _tokens(94, H, T)
+    # 7 and -1 are out of range; a position may repeat an expert
+    ids = np.array([[2, 7, 0], [1, 1, 4], [-1, 3, 3]], dtype=np.int32)
+    w = np.array([[0.5, 0.3, 0.2], [0.6, 0.1, 0.3], [0.2, 0.2, 0.6]], dtype=np.float32)
+    ws = torch.empty(pkg.moe_skinny_workspace_bytes(T, 3, H, F), dtype=torch.uint8, device=DEV)
+    got = run_moe_t(packed, E, H, F, X, ids, w, pkg.OUT_F32, workspace=ws)
+    status_off = 4 * T * 3 * (H + F)
+    assert int(ws[status_off:status_off + 4].view(torch.int32).item()) == 1
+    assert_f32_close(got, oracle.moe_positions(*pool, X, ids, w), what="invalid id")
+    ok = np.array([[2, 0], [1, 4], [3, 3]], dtype=np.int32)
+    wok = w[:, :2].copy()
+    got = run_moe_t(packed, E, H, F, X, ok, wok, pkg.OUT_F32, workspace=ws)
+    assert int(ws[4 * T * 2 * (H + F):4 * T * 2 * (H + F) + 4].view(torch.int32).item()) == 0
+    assert_f32_close(got, oracle.moe_positions(*pool, X, ok, wok), what="valid")
+    y0 = run_moe_t(packed, E, H, F, X, np.zeros((T, 0), np.int32), np.zeros((T, 0), np.float32),
+                   pkg.OUT_F32)
+    assert y0.shape == (T, H) and not np.any(y0)
+
+
+def test_moe_positions_rows_are_single_tokens():
+    """Row t of a pass equals the single-token layer on X[t], ids[t], w[t]
+    (both checked against the oracle; the kernels differ, so not bitwise),
+    and reordering the positions reorders the rows bit for bit (the groups
+    depend on the positions only through their ids)."""
+    E, H, F, top_k, T = 12, 512, 256, 4, 6
+    pool = _pool(95, E, H, F)
+    packed = _pack_pool(pool, E, H, F)
+    X = _tokens(96, H, T)
+    ids, w = _routes(97, E, top_k, T)
+    Y = run_moe_t(packed, E, H, F, X, ids, w, pkg.OUT_F32)
+    for t in range(T):
+        ref = oracle.moe(*pool, X[t], ids[t], w[t])
+        assert_f32_close(Y[t], ref, what="pass row %d" % t)
+        assert_f32_close(run_moe(packed, E, H, F, X[t], ids[t], w[t], pkg.OUT_F32), ref,
+                         what="single token %d" % t)
+    perm = np.array([5, 2, 0, 4, 1, 3])
+    Yp = run_moe_t(packed, E, H, F, X[perm], ids[perm], w[perm], pkg.OUT_F32)
+    assert np.array_equal(Yp, Y[perm])
+
+
+def test_moe_positions_full():
+    """The verification tile through the MoE layer at full size: 384 experts,
+    hidden 7168, expert FFN 2048, top-16 per position, 16 positions with
+    independent seeded routes.  Every expert holds seeded codes and E8M0
+    scales (118..128); positions 0, 7 and 15 are checked against the oracle
+    and every row against the single-token layer on the GPU."""
+    E, H, F, top_k, T = 384, 7168, 2048, 16, 16
+    note("moe positions full E=%d H=%d F=%d top_k=%d T=%d" % (E, H, F, top_k, T))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(98)
+
+    def canon(rows, K):
+        codes = torch.randint(0, 256, (E * rows, K // 2), dtype=torch.uint8, device=DEV,
+                              generator=g)
+        scales = torch.randint(118, 129, (E * rows, K // 32), dtype=torch.uint8, device=DEV,
+                               generator=g)
+        return codes, scales
+
+    cg, cu, cd = canon(F, H), canon(F, H), canon(H, F)
+    packed = tuple(pkg.qgemv_pack(FP4, E * rows, K, c, s)
+                   for (c, s), rows, K in ((cg, F, H), (cu, F, H), (cd, H, F)))
+    X = _tokens(99, H, T)
+    ids, w = _routes(100, E, top_k, T)
+    Y = run_moe_t(packed, E, H, F, X, ids, w, pkg.OUT_BF16)
+    Yf = run_moe_t(packed, E, H, F, X, ids, w, pkg.OUT_F32)
+    note("  %d distinct experts over %d pairs" % (len(np.unique(ids)), ids.size))
+    for t in range(T):
+        y1 = run_moe(packed, E, H, F, X[t], ids[t], w[t], pkg.OUT_F32)
+        assert_f32_close(Yf[t], y1, what="row %d vs single token" % t)
+    note("  rows match the single-token layer; oracle for positions 0, 7, 15")
+
+    def one(args):
+        t, s = args
+        e = int(ids[t, s])
+        pool = tuple(a[e * n:(e + 1) * n].cpu().numpy()[None] for (a, n) in (
+            (cg[0], F), (cg[1], F), (cu[0], F), (cu[1], F), (cd[0], H), (cd[1], H)))
+        return oracle.moe(*pool, X[t], np.array([0], np.int32), w[t, s:s + 1])
+
+    for t in (0, 7, 15):
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            parts = list(ex.map(one, [(t, s) for s in range(top_k)]))
+        ref = np.zeros(H)
+        for p in parts:  # slot order, as the definition sums
+            ref += p
+        assert_bf16_close(Y[t], ref, what="position %d" % t)

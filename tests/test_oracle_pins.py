@@ -390,6 +390,48 @@ def test_moe_invariants():
     assert np.array_equal(oracle.moe(gc, gs, uc, us, dc, ds, x, bad, w), keep)
 
 
+def _dequant_mxfp4_numpy(codes, scales, table):
+    """[N, K] float64 from the E2M1 table (golden file) and 2^(e - 127)."""
+    lo = codes & 0xF
+    hi = codes >> 4
+    c = np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+    s = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return table[c] * np.repeat(s, 32, axis=1)
+
+
+def test_moe_positions_brute_force():
+    """T positions through the routed experts, against a brute-force numpy
+    evaluation (golden E2M1 table, float64 matmuls): position 1 and 3 share
+    expert 2, position 2 repeats an expert within its slots and position 3
+    has an out-of-range id.  Also: reordering the positions reorders the
+    rows exactly."""
+    E, H, F = 5, 64, 96
+    ex = [synth.expert(43, e, H, F) for e in range(E)]
+    pool = tuple(np.stack([f(e) for e in ex]) for f in (
+        lambda e: e.gate.codes, lambda e: e.gate.scales, lambda e: e.up.codes,
+        lambda e: e.up.scales, lambda e: e.down.codes, lambda e: e.down.scales))
+    X = np.stack([synth.moe_token(44, H, item=t) for t in range(4)])
+    ids = np.array([[0, 4], [2, 1], [3, 3], [2, E + 1]], dtype=np.int32)
+    w = np.array([[0.75, 0.25], [0.5, 0.5], [0.4, 0.6], [1.0, 0.3]], dtype=np.float32)
+    Y = oracle.moe_positions(*pool, X, ids, w)
+    table = np.array([float(v) for _, v in golden_lines("e2m1_values.txt")])
+    xf = (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    gc, gs, uc, us, dc, ds = pool
+    for t in range(4):
+        ref = np.zeros(H)
+        for s in range(2):
+            e = int(ids[t, s])
+            if not 0 <= e < E:
+                continue
+            g = _dequant_mxfp4_numpy(gc[e], gs[e], table) @ xf[t]
+            u = _dequant_mxfp4_numpy(uc[e], us[e], table) @ xf[t]
+            h = g / (1.0 + np.exp(-g)) * u
+            ref += float(w[t, s]) * (_dequant_mxfp4_numpy(dc[e], ds[e], table) @ h)
+        assert np.allclose(Y[t], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    perm = np.array([3, 1, 0, 2])
+    assert np.array_equal(oracle.moe_positions(*pool, X[perm], ids[perm], w[perm]), Y[perm])
+
+
 def test_router_equal_logits_and_ties():
     ids, w = synth.router_from_logits(np.zeros(384), 16)
     assert ids.tolist() == list(range(16))
