@@ -613,6 +613,27 @@ def main():
         log("moe: %.2f us" % (msm * 1e3))
         del moe
 
+        # the same layer for a verification tile: T positions, each its own route
+        T = 16
+        moet = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16, T=T)
+        mst = workloads.time_graph_ms(moet.run, 32)
+        dist = moet.distinct_experts()
+        bt = roofline.moe_positions_bytes(dist, T, 16, 7168, 2048)
+        flt = plain_read_us(int(bt))
+        result["moe_positions"] = {
+            "workload": "MXFP4 MoE layer as above, %d positions per call, each with its own "
+                        "seeded top-16 route (a different set per call); calls captured in a "
+                        "HIP graph" % T,
+            "T": T, "distinct_experts_mean": round(dist, 1),
+            "us_per_pass": round(mst * 1e3, 3),
+            "us_per_position": round(mst * 1e3 / T, 3),
+            "vs_single_token_calls": round(T * msm / mst, 2),
+            "plain_read_us": round(flt, 2), "pct_of_plain_read": round(100 * flt / (mst * 1e3), 1),
+            "value": round(bt / (mst * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "pct_of_peak": round(100 * bt / (mst * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2)}
+        log("moe T=%d: %.2f us (%.1f distinct experts)" % (T, mst * 1e3, dist))
+        del moet
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_budget)
         threads = max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")), 16))

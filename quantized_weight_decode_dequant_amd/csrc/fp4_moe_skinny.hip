@@ -28,80 +28,91 @@
 // the VALU kernels, which rounding aside gives the same sums.  h is fp32;
 // B splits it into bf16 hi + lo (|h - hi - lo| <= 2^-16 |h|) and multiplies
 // both, so its error stays far below a bf16 output's.
-// Within a unit a wave adds its batches (4 tiles of one rowblock, every 4th
-// batch of the unit) in K order and the workgroup adds the four waves' sums
-// in wave order, so results are deterministic.
+// Each unit is computed by one wave, its tiles in K order, and written from
+// its registers, so results are deterministic.
 #include "fp4_stream.h"
 
 namespace qg {
 
 constexpr int MT_WAVES = 4;
 constexpr int MT_THREADS = MT_WAVES * 64;
-constexpr int MT_RMAX = 8;          // units per block
 constexpr int MT_GREC = 8;          // int32 per group record: e, c, p[4], 0, 0
 constexpr int MT_ROUTE_THREADS = 1024;
 
-struct MtCursor {
-    int i, b;  // unit within the block, batch within the unit
-};
-__device__ __forceinline__ MtCursor mt_advance(MtCursor c, int nbu) {
-    c.b += MT_WAVES;
-    while (c.b >= nbu) {  // uniform
-        c.b -= nbu;
-        ++c.i;
-    }
-    return c;
-}
-
 // ------------------------------------------------------------ R: routing
-// key = expert id of a valid pair, -1 otherwise.  rank = valid pairs of the
-// same expert before it; a pair whose rank is a multiple of mc starts a
-// group, and the group index of a pair is the number of group starts of
-// smaller expert ids plus rank / mc.
+// key = expert id of a valid pair, -1 for an invalid one (-2 pads the arrays
+// to a multiple of 4).  rank = pairs of the same expert before it; a pair
+// whose rank is a multiple of mc starts a group, and the group index of a
+// pair is the number of group starts of smaller expert ids plus rank / mc.
 __global__ void __launch_bounds__(MT_ROUTE_THREADS)
 moe_route_kernel(const int32_t *__restrict__ ids, int P, int E, int mc,
                  int32_t *__restrict__ groups, unsigned *__restrict__ hdr) {
-    __shared__ int key[MOE_PAIRS_MAX], rank[MOE_PAIRS_MAX], start[MOE_PAIRS_MAX];
+    __shared__ __attribute__((aligned(16))) int key[MOE_PAIRS_MAX];
+    __shared__ __attribute__((aligned(16))) int start[MOE_PAIRS_MAX];
     __shared__ unsigned s_bad, s_ng;
     const int tid = threadIdx.x;
+    const int P4 = (P + 3) / 4;
     if (tid == 0) {
         s_bad = 0;
         s_ng = 0;
     }
-    for (int p = tid; p < P; p += MT_ROUTE_THREADS) {
-        const int e = ids[p];
-        key[p] = (e >= 0 && e < E) ? e : -1;
+    for (int p = tid; p < 4 * P4; p += MT_ROUTE_THREADS) {
+        int k = -2;
+        if (p < P) {
+            const int e = ids[p];
+            k = (e >= 0 && e < E) ? e : -1;
+        }
+        key[p] = k;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += MT_ROUTE_THREADS) {
+    const int4 *key4 = reinterpret_cast<const int4 *>(key);
+    const int4 *start4 = reinterpret_cast<const int4 *>(start);
+    int rank[MOE_PAIRS_MAX / MT_ROUTE_THREADS], count[MOE_PAIRS_MAX / MT_ROUTE_THREADS];
+#pragma unroll
+    for (int j = 0; j < MOE_PAIRS_MAX / MT_ROUTE_THREADS; ++j) {
+        const int p = tid + j * MT_ROUTE_THREADS;
+        if (p >= P) break;
         const int kp = key[p];
-        int r = 0;
+        int r = 0, n = 0;
         if (kp >= 0) {
-            for (int q = 0; q < p; ++q) r += key[q] == kp;
+#pragma unroll 4
+            for (int q4 = 0; q4 < P4; ++q4) {
+                const int4 k = key4[q4];
+                const int q = 4 * q4;
+                n += (k.x == kp) + (k.y == kp) + (k.z == kp) + (k.w == kp);
+                r += (k.x == kp && q < p) + (k.y == kp && q + 1 < p) + (k.z == kp && q + 2 < p) +
+                     (k.w == kp && q + 3 < p);
+            }
         } else {
             atomicOr(&s_bad, 1u);
         }
-        rank[p] = r;
+        rank[j] = r;
+        count[j] = n;
         start[p] = (kp >= 0 && r % mc == 0) ? kp : -1;
     }
+    for (int p = P + tid; p < 4 * P4; p += MT_ROUTE_THREADS) start[p] = -1;
     __syncthreads();
-    for (int p = tid; p < P; p += MT_ROUTE_THREADS) {
+#pragma unroll
+    for (int j = 0; j < MOE_PAIRS_MAX / MT_ROUTE_THREADS; ++j) {
+        const int p = tid + j * MT_ROUTE_THREADS;
+        if (p >= P) break;
         const int kp = key[p];
         if (kp < 0) continue;
-        int before = 0, n = 0;
-        for (int q = 0; q < P; ++q) {
-            const int sq = start[q];
-            before += (sq >= 0) & (sq < kp);
-            n += key[q] == kp;
+        int before = 0;  // group starts of smaller expert ids
+#pragma unroll 4
+        for (int q4 = 0; q4 < P4; ++q4) {
+            const int4 sq = start4[q4];
+            before += (sq.x >= 0 && sq.x < kp) + (sq.y >= 0 && sq.y < kp) +
+                      (sq.z >= 0 && sq.z < kp) + (sq.w >= 0 && sq.w < kp);
         }
-        const int r = rank[p], gid = before + r / mc, slot = r % mc;
+        const int r = rank[j], gid = before + r / mc, slot = r % mc;
         int32_t *g = groups + (size_t)gid * MT_GREC;
         st_global<int32_t>(g, 2 + slot, p);
         if (slot == 0) {
-            const int c = min(mc, n - r);
+            const int c = min(mc, count[j] - r);
             st_global<int32_t>(g, 0, kp);
             st_global<int32_t>(g, 1, c);
-            for (int j = 2 + c; j < MT_GREC; ++j) st_global<int32_t>(g, j, 0);
+            for (int i = 2 + c; i < MT_GREC; ++i) st_global<int32_t>(g, i, 0);
             atomicAdd(&s_ng, 1u);
         }
     }
@@ -119,10 +130,32 @@ __device__ __forceinline__ bf16x8_t fp4_word_bf16x8(unsigned w, float sc) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-__device__ __forceinline__ bf16x8_t lds_row8(const uint16_t *p, bool act) {
-    bf16x8_t a = {};
-    if (act) a = *reinterpret_cast<const bf16x8_t *>(p);
-    return a;
+// The A operands of one half of a tile: 4 (or, for split rows, 4 hi then 4
+// lo) 8-element pieces of the lane's activation row, all read inside one
+// branch so that the reads go out together and are waited for once; lanes
+// whose row is not one of the group's keep zeros and read nothing.
+__device__ __forceinline__ void lds_half(const uint16_t *a, bool act, bf16x8_t (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = bf16x8_t{};
+    if (act) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const bf16x8_t *>(a + 8 * i);
+    }
+}
+__device__ __forceinline__ void lds_half2(const uint16_t *ahi, const uint16_t *alo, bool act,
+                                          bf16x8_t (&vh)[4], bf16x8_t (&vl)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        vh[i] = bf16x8_t{};
+        vl[i] = bf16x8_t{};
+    }
+    if (act) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            vh[i] = *reinterpret_cast<const bf16x8_t *>(ahi + 8 * i);
+            vl[i] = *reinterpret_cast<const bf16x8_t *>(alo + 8 * i);
+        }
+    }
 }
 
 // One tile (index tp of the staged rows) against one bf16 activation row per
@@ -133,13 +166,15 @@ __device__ __forceinline__ void mt_tile_x(u32x4_t c0, u32x4_t c1, unsigned e0, u
                                           f32x4_t &D1) {
     const float s0 = e8m0_as_f32(e0), s1 = e8m0_as_f32(e1);
     const uint16_t *a = arow + 256 * tp;
+    bf16x8_t v[4];
+    lds_half(a, act, v);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row8(a + 8 * i, act),
-                                                     fp4_word_bf16x8(c0[i], s0), D0, 0, 0, 0);
-        D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row8(a + 128 + 8 * i, act),
-                                                     fp4_word_bf16x8(c1[i], s1), D1, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+        D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[i], fp4_word_bf16x8(c0[i], s0), D0, 0, 0, 0);
+    lds_half(a + 128, act, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[i], fp4_word_bf16x8(c1[i], s1), D1, 0, 0, 0);
 }
 
 // The same against split fp32 rows: ahi / alo = the hi and lo bf16 rows.
@@ -153,12 +188,13 @@ __device__ __forceinline__ void mt_tile_h(u32x4_t c0, u32x4_t c1, unsigned e0, u
     for (int jh = 0; jh < 2; ++jh) {
         const u32x4_t c = jh ? c1 : c0;
         const float sc = jh ? s1 : s0;
+        bf16x8_t vh[4], vl[4];
+        lds_half2(ahi + o + 128 * jh, alo + o + 128 * jh, act, vh, vl);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bf16x8_t B = fp4_word_bf16x8(c[i], sc);
-            const int k = o + 128 * jh + 8 * i;
-            D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row8(ahi + k, act), B, D0, 0, 0, 0);
-            D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row8(alo + k, act), B, D1, 0, 0, 0);
+            D0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[i], B, D0, 0, 0, 0);
+            D1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl[i], B, D1, 0, 0, 0);
         }
     }
 }
@@ -176,20 +212,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mt_rsrc(const uint8_t *mat, in
     return make_rsrc(uniform_ptr(base), valid ? (unsigned)pn * FP4_TILE_BYTES : 0u);
 }
 
-__device__ __forceinline__ void mt_flush(float *slot, const f32x4_t &D0, const f32x4_t &D1,
-                                         int lane) {
-    // lanes 0..15 hold activation rows 0..3 of output row (lane & 15)
-    if (lane < 16) {
+// The group's pair ids (wave-uniform; entries past c are 0).
+struct MtPairs {
+    int p[MOE_GROUP_ROWS_MAX];
+};
+__device__ __forceinline__ MtPairs mt_pairs(const int32_t *groups, int g) {
+    MtPairs r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) slot[16 * e + lane] += D0[e] + D1[e];
-    }
+    for (int j = 0; j < MOE_GROUP_ROWS_MAX; ++j)
+        r.p[j] = __builtin_amdgcn_readfirstlane(ld_global(groups + (size_t)g * MT_GREC + 2 + j));
+    return r;
 }
 
+constexpr int MT_WAVES_A = 8, MT_THREADS_A = 512;
 // ------------------------------------------------------------ A: gate / up
-// Units u = g * nrbF + rb; a unit has 2 * nb batches: nb of the gate rows,
-// then nb of the up rows.  Blocks of at most MT_RMAX units never span two
-// groups; x is restaged when the group changes.
-__global__ void __launch_bounds__(MT_THREADS, 2)
+// Units u = g * nrbF + rb.  A workgroup's range of units is cut into blocks
+// at group boundaries (x is restaged when the group changes); within a block
+// wave w streams units w, w + 4, ..., each as nb batches of its gate rows
+// then nb of its up rows, double-buffered across unit boundaries, and writes
+// h = silu(g) u of the unit's rows for the group's pairs from registers.
+__global__ void __launch_bounds__(MT_THREADS_A, 2)
 moe_t_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__ pu,
                      const uint16_t *__restrict__ X, int top_k, int H, int F, int PH, int nrbF,
                      int mc, const int32_t *__restrict__ groups, const unsigned *__restrict__ hdr,
@@ -197,8 +239,7 @@ moe_t_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int nb = (PH + MS_TPB - 1) / MS_TPB, nbu = 2 * nb;
     const int XS = nb * MS_TPB * 256 + 8;  // row stride (bf16), 16-byte pad
-    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);                              // [mc][XS]
-    float *part = reinterpret_cast<float *>(smem + (size_t)mc * XS * 2);           // [RMAX][W][2][64]
+    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);  // [mc][XS]
     const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4, m = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ng = __builtin_amdgcn_readfirstlane(ld_global(hdr + 1));
@@ -208,26 +249,25 @@ moe_t_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__
 #pragma unroll 1
     for (int ub = u0; ub < u1;) {
         const int g = ub / nrbF, rb0 = ub - g * nrbF;
-        const int nr = min(min(u1 - ub, nrbF - rb0), MT_RMAX);
+        const int nr = min(u1 - ub, nrbF - rb0);
         const int2 gr = mt_group(groups, g);
         const int e = gr.x, c = gr.y;
-        const int T = nr * nbu;
-        int t = wave;
-        MtCursor ca = {t / nbu, t % nbu};
+        const MtPairs pp = mt_pairs(groups, g);
+        const int nu = nr > wave ? (nr - wave + MT_WAVES_A - 1) / MT_WAVES_A : 0;
+        const int T = nu * nbu;  // this wave's batches in the block
+        int ci = wave, cb = 0;   // current unit (block-relative) and batch
         Fp4Batch A, B;
-        f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = D0;
+        f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = D0, Gs = D0;
         {
-            // the block's first batch loads while x is staged
-            const __amdgpu_buffer_rsrc_t rs =
-                mt_rsrc(ca.b < nb ? pg : pu, e, nrbF, rb0 + ca.i, PH, t < T);
-            const int tb = (ca.b % nb) * MS_TPB;
+            // the first batch loads while x is staged
+            const __amdgpu_buffer_rsrc_t rs = mt_rsrc(pg, e, nrbF, rb0 + ci, PH, T > 0);
 #pragma unroll
-            for (int q = 0; q < MS_TPB; ++q) fp4_tile_load(A, q, rs, tb + q, PH, lane);
+            for (int q = 0; q < MS_TPB; ++q) fp4_tile_load(A, q, rs, q, PH, lane);
         }
-        __syncthreads();  // the previous block is done with x and part
+        __syncthreads();  // the previous block is done with x
         if (g != staged) {
             const int per = XS / 8;  // 16-byte chunks per staged row (the pad included)
-            for (int i = tid; i < mc * per; i += MT_THREADS) {
+            for (int i = tid; i < mc * per; i += MT_THREADS_A) {
                 const int r = i / per, k8 = i - r * per;
                 u32x4_t v = {0u, 0u, 0u, 0u};
                 if (r < c && k8 < H / 8) {
@@ -238,22 +278,25 @@ moe_t_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__
             }
             staged = g;
         }
-        for (int i = tid; i < nr * MT_WAVES * 2 * 64; i += MT_THREADS) part[i] = 0.f;
         __syncthreads();
         const bool act = m < c;
         const uint16_t *arow = xl + (act ? m : 0) * XS + 32 * kg;
 #pragma unroll 1
-        for (;;) {
-            if (t >= T) break;
+        for (int t = 0; t < T;) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 Fp4Batch &Cur = half ? B : A;
                 Fp4Batch &Nxt = half ? A : B;
-                const MtCursor cn = mt_advance(ca, nbu);
-                const bool nvalid = t + MT_WAVES < T;
+                int ni = ci, nbx = cb + 1;
+                if (nbx == nbu) {
+                    nbx = 0;
+                    ni += MT_WAVES_A;
+                }
+                const bool nvalid = t + 1 < T;
                 const __amdgpu_buffer_rsrc_t rs =
-                    mt_rsrc(cn.b < nb ? pg : pu, e, nrbF, rb0 + cn.i, PH, nvalid);
-                const int tbn = (cn.b % nb) * MS_TPB, tbc = (ca.b % nb) * MS_TPB;
+                    mt_rsrc(nbx < nb ? pg : pu, e, nrbF, rb0 + ni, PH, nvalid);
+                const int tbn = (nbx < nb ? nbx : nbx - nb) * MS_TPB;
+                const int tbc = (cb < nb ? cb : cb - nb) * MS_TPB;
 #pragma unroll
                 for (int q = 0; q < MS_TPB; ++q) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -262,48 +305,44 @@ moe_t_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__
                     mt_tile_x(Cur.c0[q], Cur.c1[q], Cur.e0[q], Cur.e1[q], arow, act, tbc + q, D0,
                               D1);
                 }
-                // flush at the wave's last batch of this unit's gate or up rows
-                const bool gate = ca.b < nb;
-                if (!nvalid || cn.i != ca.i || (gate && cn.b >= nb)) {
-                    mt_flush(part + ((ca.i * MT_WAVES + wave) * 2 + (gate ? 0 : 1)) * 64, D0, D1,
-                             lane);
+                if (cb == nb - 1) {  // the unit's gate rows are done
+                    Gs = D0 + D1;
+                    D0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    D1 = D0;
+                } else if (cb == nbu - 1) {  // up rows done: h of the unit's rows
+                    const f32x4_t Us = D0 + D1;
+                    if (lane < 16) {
+                        const size_t row = (size_t)(rb0 + ci) * RB + lane;
+#pragma unroll
+                        for (int r = 0; r < MOE_GROUP_ROWS_MAX; ++r)
+                            if (r < c)
+                                st_global<float>(h_ws, (size_t)pp.p[r] * F + row,
+                                                 Gs[r] / (1.f + expf(-Gs[r])) * Us[r]);
+                    }
                     D0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
                     D1 = D0;
                 }
-                t += MT_WAVES;
-                ca = cn;
+                ci = ni;
+                cb = nbx;
+                ++t;
                 if (t >= T) break;
             }
-        }
-        __syncthreads();
-        for (int r = tid; r < nr * 64; r += MT_THREADS) {
-            const int i = r >> 6, mm = (r >> 4) & 3, row = r & 15;
-            if (mm >= c) continue;
-            float gs = 0.f, us = 0.f;
-#pragma unroll
-            for (int w = 0; w < MT_WAVES; ++w) {
-                gs += part[((i * MT_WAVES + w) * 2 + 0) * 64 + 16 * mm + row];
-                us += part[((i * MT_WAVES + w) * 2 + 1) * 64 + 16 * mm + row];
-            }
-            const int p = ld_global(groups + (size_t)g * MT_GREC + 2 + mm);
-            h_ws[(size_t)p * F + (rb0 + i) * RB + row] = gs / (1.f + expf(-gs)) * us;
         }
         ub += nr;
     }
 }
 
 // ------------------------------------------------------------ B: down
-// Units u = g * nrbH + rb, nb batches each.  h of the group's pairs is
-// staged as bf16 hi rows [0, mc) and lo rows [mc, 2 mc).
-__global__ void __launch_bounds__(MT_THREADS, 2)
+// Units u = g * nrbH + rb, nb batches each, streamed per wave as in A; h of
+// the group's pairs is staged as bf16 hi rows [0, mc) and lo rows [mc, 2 mc).
+__global__ void __launch_bounds__(MT_THREADS, 3)
 moe_t_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws, int H, int F,
                   int PF, int nrbH, int mc, const int32_t *__restrict__ groups,
                   const unsigned *__restrict__ hdr, float *__restrict__ part_ws) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int nb = (PF + MS_TPB - 1) / MS_TPB;
     const int FS = nb * MS_TPB * 256 + 8;  // row stride (bf16), 16-byte pad
-    uint16_t *hl = reinterpret_cast<uint16_t *>(smem);                         // [2][mc][FS]
-    float *part = reinterpret_cast<float *>(smem + (size_t)2 * mc * FS * 2);  // [RMAX][W][64]
+    uint16_t *hl = reinterpret_cast<uint16_t *>(smem);  // [2][mc][FS]
     const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4, m = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ng = __builtin_amdgcn_readfirstlane(ld_global(hdr + 1));
@@ -313,20 +352,21 @@ moe_t_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws
 #pragma unroll 1
     for (int ub = u0; ub < u1;) {
         const int g = ub / nrbH, rb0 = ub - g * nrbH;
-        const int nr = min(min(u1 - ub, nrbH - rb0), MT_RMAX);
+        const int nr = min(u1 - ub, nrbH - rb0);
         const int2 gr = mt_group(groups, g);
         const int e = gr.x, c = gr.y;
-        const int T = nr * nb;
-        int t = wave;
-        MtCursor ca = {t / nb, t % nb};
+        const MtPairs pp = mt_pairs(groups, g);
+        const int nu = nr > wave ? (nr - wave + MT_WAVES - 1) / MT_WAVES : 0;
+        const int T = nu * nb;
+        int ci = wave, cb = 0;
         Fp4Batch A, B;
         f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = D0;
         {
-            const __amdgpu_buffer_rsrc_t rs = mt_rsrc(pd, e, nrbH, rb0 + ca.i, PF, t < T);
+            const __amdgpu_buffer_rsrc_t rs = mt_rsrc(pd, e, nrbH, rb0 + ci, PF, T > 0);
 #pragma unroll
-            for (int q = 0; q < MS_TPB; ++q) fp4_tile_load(A, q, rs, ca.b * MS_TPB + q, PF, lane);
+            for (int q = 0; q < MS_TPB; ++q) fp4_tile_load(A, q, rs, q, PF, lane);
         }
-        __syncthreads();  // the previous block is done with h and part
+        __syncthreads();  // the previous block is done with h
         if (g != staged) {
             const int per = FS / 4;  // 4-element chunks per staged row (the pad included)
             for (int i = tid; i < mc * per; i += MT_THREADS) {
@@ -353,48 +393,47 @@ moe_t_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws
             }
             staged = g;
         }
-        for (int i = tid; i < nr * MT_WAVES * 64; i += MT_THREADS) part[i] = 0.f;
         __syncthreads();
         const bool act = m < c;
         const uint16_t *ahi = hl + (act ? m : 0) * FS + 32 * kg;
         const uint16_t *alo = ahi + (size_t)mc * FS;
 #pragma unroll 1
-        for (;;) {
-            if (t >= T) break;
+        for (int t = 0; t < T;) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 Fp4Batch &Cur = half ? B : A;
                 Fp4Batch &Nxt = half ? A : B;
-                const MtCursor cn = mt_advance(ca, nb);
-                const bool nvalid = t + MT_WAVES < T;
-                const __amdgpu_buffer_rsrc_t rs = mt_rsrc(pd, e, nrbH, rb0 + cn.i, PF, nvalid);
+                int ni = ci, nbx = cb + 1;
+                if (nbx == nb) {
+                    nbx = 0;
+                    ni += MT_WAVES;
+                }
+                const bool nvalid = t + 1 < T;
+                const __amdgpu_buffer_rsrc_t rs = mt_rsrc(pd, e, nrbH, rb0 + ni, PF, nvalid);
 #pragma unroll
                 for (int q = 0; q < MS_TPB; ++q) {
                     __builtin_amdgcn_sched_barrier(0);
-                    fp4_tile_load(Nxt, q, rs, cn.b * MS_TPB + q, PF, lane);
+                    fp4_tile_load(Nxt, q, rs, nbx * MS_TPB + q, PF, lane);
                     __builtin_amdgcn_sched_barrier(0);
                     mt_tile_h(Cur.c0[q], Cur.c1[q], Cur.e0[q], Cur.e1[q], ahi, alo, act,
-                              ca.b * MS_TPB + q, D0, D1);
+                              cb * MS_TPB + q, D0, D1);
                 }
-                if (!nvalid || cn.i != ca.i) {
-                    mt_flush(part + (ca.i * MT_WAVES + wave) * 64, D0, D1, lane);
+                if (cb == nb - 1) {  // the unit is done
+                    const f32x4_t Ys = D0 + D1;
+                    if (lane < 16) {
+                        const size_t row = (size_t)(rb0 + ci) * RB + lane;
+#pragma unroll
+                        for (int r = 0; r < MOE_GROUP_ROWS_MAX; ++r)
+                            if (r < c) st_global<float>(part_ws, (size_t)pp.p[r] * H + row, Ys[r]);
+                    }
                     D0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
                     D1 = D0;
                 }
-                t += MT_WAVES;
-                ca = cn;
+                ci = ni;
+                cb = nbx;
+                ++t;
                 if (t >= T) break;
             }
-        }
-        __syncthreads();
-        for (int r = tid; r < nr * 64; r += MT_THREADS) {
-            const int i = r >> 6, mm = (r >> 4) & 3, row = r & 15;
-            if (mm >= c) continue;
-            float v = 0.f;
-#pragma unroll
-            for (int w = 0; w < MT_WAVES; ++w) v += part[(i * MT_WAVES + w) * 64 + 16 * mm + row];
-            const int p = ld_global(groups + (size_t)g * MT_GREC + 2 + mm);
-            part_ws[(size_t)p * H + (rb0 + i) * RB + row] = v;
         }
         ub += nr;
     }
@@ -430,18 +469,16 @@ hipError_t launch_moe_skinny(const uint8_t *pg, const uint8_t *pu, const uint8_t
         const int nbA = (int)ceil_div(PH, MS_TPB);
         const int64_t unitsA = (int64_t)P * nrbF;
         const int gridA = (int)(unitsA < (int64_t)cus * 2 ? unitsA : (int64_t)cus * 2);
-        const size_t ldsA = (size_t)mc * (nbA * MS_TPB * 256 + 8) * 2 +
-                            (size_t)MT_RMAX * MT_WAVES * 2 * 64 * 4;
-        hipLaunchKernelGGL(moe_t_gate_up_kernel, dim3(gridA), dim3(MT_THREADS), ldsA, s, pg, pu, X,
+        const size_t ldsA = (size_t)mc * (nbA * MS_TPB * 256 + 8) * 2;
+        hipLaunchKernelGGL(moe_t_gate_up_kernel, dim3(gridA), dim3(MT_THREADS_A), ldsA, s, pg, pu, X,
                            top_k, (int)H, (int)F, PH, nrbF, mc, groups, hdr, h_ws);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
         const int PF = (int)ceil_div(F, FP4_TILE_K), nrbH = (int)(H / RB);
         const int nbB = (int)ceil_div(PF, MS_TPB);
         const int64_t unitsB = (int64_t)P * nrbH;
-        const int gridB = (int)(unitsB < (int64_t)cus * 2 ? unitsB : (int64_t)cus * 2);
-        const size_t ldsB = (size_t)2 * mc * (nbB * MS_TPB * 256 + 8) * 2 +
-                            (size_t)MT_RMAX * MT_WAVES * 64 * 4;
+        const int gridB = (int)(unitsB < (int64_t)cus * 3 ? unitsB : (int64_t)cus * 3);
+        const size_t ldsB = (size_t)2 * mc * (nbB * MS_TPB * 256 + 8) * 2;
         hipLaunchKernelGGL(moe_t_down_kernel, dim3(gridB), dim3(MT_THREADS), ldsB, s, pd, h_ws,
                            (int)H, (int)F, PF, nrbH, mc, groups, hdr, part);
         err = hipGetLastError();

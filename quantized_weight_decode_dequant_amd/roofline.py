@@ -57,6 +57,16 @@ def moe_token_bytes(top_k: int, H: int, F: int, out_bytes: int = 2) -> float:
     return top_k * moe_expert_bytes(H, F) + 2.0 * H + float(out_bytes) * H + 2 * 4.0 * top_k * F
 
 
+def moe_positions_bytes(distinct: float, T: int, top_k: int, H: int, F: int,
+                        out_bytes: int = 2) -> float:
+    """A pass of T positions through the layer: each distinct expert's weights
+    once, X in, Y out, and per (position, slot) pair the fp32 SwiGLU
+    activations and the fp32 partial output, each written and read once."""
+    P = T * top_k
+    return (distinct * moe_expert_bytes(H, F) + 2.0 * T * H + float(out_bytes) * T * H +
+            2 * 4.0 * P * F + 2 * 4.0 * P * H)
+
+
 def gemm_flops(M: int, N: int, K: int) -> float:
     return 2.0 * M * N * K
 

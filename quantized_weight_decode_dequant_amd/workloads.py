@@ -197,10 +197,10 @@ class MoeLayer:
     different one per call so the selected experts change between calls."""
 
     def __init__(self, seed: int, E: int, H: int, F: int, top_k: int, routes: int = 64,
-                 device="cuda"):
+                 device="cuda", T: int = 0):
         import numpy as np
         import torch
-        self.E, self.H, self.F, self.top_k = E, H, F, top_k
+        self.E, self.H, self.F, self.top_k, self.T = E, H, F, top_k, T
         g = torch.Generator(device=device)
         g.manual_seed(seed)
 
@@ -216,17 +216,40 @@ class MoeLayer:
         self.gate = stack(F, H)
         self.up = stack(F, H)
         self.down = stack(H, F)
-        ids, ws = zip(*[synth.router(seed, E, top_k, item=r) for r in range(routes)])
-        self.ids = weights.to_device(np.stack(ids), device)
+        if T == 0:
+            # one token per call
+            ids, ws = zip(*[synth.router(seed, E, top_k, item=r) for r in range(routes)])
+            self.x = weights.to_device(synth.moe_token(seed, H), device)
+            self.workspace = torch.empty(_lib.moe_workspace_bytes(top_k, H, F),
+                                         dtype=torch.uint8, device=device)
+            self.y = torch.empty(H, dtype=torch.bfloat16, device=device)
+        else:
+            # T positions per call, each with its own route
+            ids, ws = zip(*[tuple(np.stack(a) for a in zip(*[
+                synth.router(seed, E, top_k, item=r * T + t) for t in range(T)]))
+                for r in range(routes)])
+            self.x = weights.to_device(np.stack([synth.moe_token(seed, H, item=t)
+                                                 for t in range(T)]), device)
+            self.workspace = torch.empty(_lib.moe_skinny_workspace_bytes(T, top_k, H, F),
+                                         dtype=torch.uint8, device=device)
+            self.y = torch.empty(T, H, dtype=torch.bfloat16, device=device)
+        self.ids_host = np.stack(ids)
+        self.ids = weights.to_device(self.ids_host, device)
         self.w = weights.to_device(np.stack(ws), device)
-        self.x = weights.to_device(synth.moe_token(seed, H), device)
-        self.workspace = torch.empty(_lib.moe_workspace_bytes(top_k, H, F), dtype=torch.uint8,
-                                     device=device)
-        self.y = torch.empty(H, dtype=torch.bfloat16, device=device)
         self.i = 0
+
+    def distinct_experts(self) -> float:
+        """Mean number of distinct experts per call over the route sets."""
+        return float(np.mean([len(np.unique(r)) for r in self.ids_host]))
 
     def run(self):
         r = self.i % self.ids.shape[0]
         self.i += 1
-        _lib.moe_expert_gemv_run(self.gate, self.up, self.down, self.E, self.H, self.F, self.x,
-                                 self.ids[r], self.w[r], workspace=self.workspace, y=self.y)
+        if self.T == 0:
+            _lib.moe_expert_gemv_run(self.gate, self.up, self.down, self.E, self.H, self.F,
+                                     self.x, self.ids[r], self.w[r], workspace=self.workspace,
+                                     y=self.y)
+        else:
+            _lib.moe_expert_skinny_run(self.gate, self.up, self.down, self.E, self.H, self.F,
+                                       self.x, self.ids[r], self.w[r], workspace=self.workspace,
+                                       Y=self.y)
