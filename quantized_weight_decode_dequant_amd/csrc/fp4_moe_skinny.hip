@@ -44,11 +44,15 @@ constexpr int MT_ROUTE_THREADS = 1024;
 // to a multiple of 4).  rank = pairs of the same expert before it; a pair
 // whose rank is a multiple of mc starts a group, and the group index of a
 // pair is the number of group starts of smaller expert ids plus rank / mc.
+// Each count scans all pairs; the scans of one pair are split over up to
+// 1024 / P threads, whose partial counts are added with integer LDS atomics
+// (exact and order-independent).
 __global__ void __launch_bounds__(MT_ROUTE_THREADS)
 moe_route_kernel(const int32_t *__restrict__ ids, int P, int E, int mc,
                  int32_t *__restrict__ groups, unsigned *__restrict__ hdr) {
     __shared__ __attribute__((aligned(16))) int key[MOE_PAIRS_MAX];
     __shared__ __attribute__((aligned(16))) int start[MOE_PAIRS_MAX];
+    __shared__ int rank[MOE_PAIRS_MAX], count[MOE_PAIRS_MAX], before[MOE_PAIRS_MAX];
     __shared__ unsigned s_bad, s_ng;
     const int tid = threadIdx.x;
     const int P4 = (P + 3) / 4;
@@ -63,53 +67,65 @@ moe_route_kernel(const int32_t *__restrict__ ids, int P, int E, int mc,
             k = (e >= 0 && e < E) ? e : -1;
         }
         key[p] = k;
+        start[p] = -1;
+        rank[p] = 0;
+        count[p] = 0;
+        before[p] = 0;
     }
     __syncthreads();
     const int4 *key4 = reinterpret_cast<const int4 *>(key);
     const int4 *start4 = reinterpret_cast<const int4 *>(start);
-    int rank[MOE_PAIRS_MAX / MT_ROUTE_THREADS], count[MOE_PAIRS_MAX / MT_ROUTE_THREADS];
-#pragma unroll
-    for (int j = 0; j < MOE_PAIRS_MAX / MT_ROUTE_THREADS; ++j) {
-        const int p = tid + j * MT_ROUTE_THREADS;
-        if (p >= P) break;
+    // slices per pair; work item w = slice * P + p
+    const int S = P > 0 ? max(1, min(MT_ROUTE_THREADS / P, P4)) : 1;
+    for (int w = tid; w < S * P; w += MT_ROUTE_THREADS) {
+        const int sl = w / P, p = w - sl * P;
         const int kp = key[p];
-        int r = 0, n = 0;
-        if (kp >= 0) {
-#pragma unroll 4
-            for (int q4 = 0; q4 < P4; ++q4) {
-                const int4 k = key4[q4];
-                const int q = 4 * q4;
-                n += (k.x == kp) + (k.y == kp) + (k.z == kp) + (k.w == kp);
-                r += (k.x == kp && q < p) + (k.y == kp && q + 1 < p) + (k.z == kp && q + 2 < p) +
-                     (k.w == kp && q + 3 < p);
-            }
-        } else {
-            atomicOr(&s_bad, 1u);
+        if (kp < 0) {
+            if (sl == 0) atomicOr(&s_bad, 1u);
+            continue;
         }
-        rank[j] = r;
-        count[j] = n;
-        start[p] = (kp >= 0 && r % mc == 0) ? kp : -1;
+        const int q0 = sl * P4 / S, q1 = (sl + 1) * P4 / S;
+        int r = 0, n = 0;
+#pragma unroll 8
+        for (int q4 = q0; q4 < q1; ++q4) {
+            const int4 k = key4[q4];
+            const int q = 4 * q4;
+            n += (k.x == kp) + (k.y == kp) + (k.z == kp) + (k.w == kp);
+            r += (k.x == kp && q < p) + (k.y == kp && q + 1 < p) + (k.z == kp && q + 2 < p) +
+                 (k.w == kp && q + 3 < p);
+        }
+        atomicAdd(&rank[p], r);
+        atomicAdd(&count[p], n);
     }
-    for (int p = P + tid; p < 4 * P4; p += MT_ROUTE_THREADS) start[p] = -1;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < MOE_PAIRS_MAX / MT_ROUTE_THREADS; ++j) {
-        const int p = tid + j * MT_ROUTE_THREADS;
-        if (p >= P) break;
+    for (int p = tid; p < P; p += MT_ROUTE_THREADS) {
+        const int kp = key[p];
+        if (kp >= 0 && rank[p] % mc == 0) start[p] = kp;
+    }
+    __syncthreads();
+    for (int w = tid; w < S * P; w += MT_ROUTE_THREADS) {
+        const int sl = w / P, p = w - sl * P;
         const int kp = key[p];
         if (kp < 0) continue;
-        int before = 0;  // group starts of smaller expert ids
-#pragma unroll 4
-        for (int q4 = 0; q4 < P4; ++q4) {
+        const int q0 = sl * P4 / S, q1 = (sl + 1) * P4 / S;
+        int b = 0;  // group starts of smaller expert ids
+#pragma unroll 8
+        for (int q4 = q0; q4 < q1; ++q4) {
             const int4 sq = start4[q4];
-            before += (sq.x >= 0 && sq.x < kp) + (sq.y >= 0 && sq.y < kp) +
-                      (sq.z >= 0 && sq.z < kp) + (sq.w >= 0 && sq.w < kp);
+            b += (sq.x >= 0 && sq.x < kp) + (sq.y >= 0 && sq.y < kp) + (sq.z >= 0 && sq.z < kp) +
+                 (sq.w >= 0 && sq.w < kp);
         }
-        const int r = rank[j], gid = before + r / mc, slot = r % mc;
+        atomicAdd(&before[p], b);
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += MT_ROUTE_THREADS) {
+        const int kp = key[p];
+        if (kp < 0) continue;
+        const int r = rank[p], gid = before[p] + r / mc, slot = r % mc;
         int32_t *g = groups + (size_t)gid * MT_GREC;
         st_global<int32_t>(g, 2 + slot, p);
         if (slot == 0) {
-            const int c = min(mc, count[j] - r);
+            const int c = min(mc, count[p] - r);
             st_global<int32_t>(g, 0, kp);
             st_global<int32_t>(g, 1, c);
             for (int i = 2 + c; i < MT_GREC; ++i) st_global<int32_t>(g, i, 0);
