@@ -272,7 +272,7 @@ def main():
 
     import torch
     import quantized_weight_decode_dequant_amd as pkg
-    from quantized_weight_decode_dequant_amd import roofline, workloads
+    from quantized_weight_decode_dequant_amd import _lib, roofline, synth, weights, workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkg.raw()  # fail loudly if the HIP library is missing
@@ -597,6 +597,30 @@ def main():
         result["int8_verify"] = dict(i8, workload="8-bit sym g32 weights, M=16 activations "
                                      "(1 percent x20 outliers) rotated by randomized Hadamard-32 and "
                                      "quantized to int8; %d copies of each matrix; calls captured in a HIP graph" % 40)
+
+        # weight-only int8 output head (one fp32 scale per row), M = 1
+        NH, KH = 151936, 4096
+        gq = torch.Generator(device="cuda")
+        gq.manual_seed(args.seed)
+        qcodes = torch.randint(-128, 128, (NH, KH), dtype=torch.int8, device="cuda", generator=gq)
+        qscales = (torch.rand(NH, dtype=torch.float32, device="cuda", generator=gq) + 0.5) * 2.0 ** -10
+        qpacked = _lib.qgemv_pack(_lib.FMT_Q8_ROW, NH, KH, qcodes, qscales)
+        del qcodes, qscales
+        qx = weights.to_device(synth.activations(args.seed, 1, KH)[0], "cuda")
+        qy = torch.empty(NH, dtype=torch.bfloat16, device="cuda")
+        msh = workloads.time_graph_ms(
+            lambda: _lib.qgemv_run(_lib.FMT_Q8_ROW, qpacked, NH, KH, qx, y=qy), 16)
+        bh = roofline.q8row_gemv_bytes(NH, KH)
+        flh = plain_read_us(int(bh))
+        result["int8_lm_head"] = {
+            "workload": "weight-only int8 output head 4096->151936, one fp32 scale per row, "
+                        "codes uniform over the int8 range, M=1; calls captured in a HIP graph",
+            "us": round(msh * 1e3, 3), "plain_read_us": round(flh, 2),
+            "pct_of_plain_read": round(100 * flh / (msh * 1e3), 1),
+            "value": round(bh / (msh * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "pct_of_peak": round(100 * bh / (msh * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 2)}
+        log("int8 lm_head: %.2f us" % (msh * 1e3))
+        del qpacked
 
         # MXFP4 routed experts, one token through one layer
         moe = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16)

@@ -25,6 +25,11 @@
  *  - QG_FMT_MXFP4_G32: E2M1 codes with one E8M0 scale per 32 values (Deltafin
  *    / Kimi K3 page, aihot.virxact.com, sections "How it works" and the compute
  *    list: fused MXFP4 dequant + GEMV for the routed experts).
+ *  - QG_FMT_Q8_ROW: int8 codes (the full range -128..127) with one fp32 scale
+ *    per output row, weight = scale[n] * code, against bf16 activations:
+ *    weight-only int8 as in the Deltafin page's resident int8 spine and packed
+ *    int8 output head (sections on the spine and the recent changes: int8 to
+ *    fp32 conversion fused with the row scaling).
  *
  * Canonical (unpacked) layouts accepted by qgemv_pack, all row-major device
  * buffers:
@@ -33,6 +38,7 @@
  *  - Q8:    codes int8 [N][K];  scales fp16 [N][K/32];  biases NULL.
  *  - MXFP4: codes uint8 [N][K/2] (element 2i in the low nibble of byte i);
  *           scales uint8 E8M0 [N][K/32];  biases NULL.
+ *  - Q8_ROW: codes int8 [N][K];  scales fp32 [N];  biases NULL.
  * The packed layout is opaque: a buffer produced by qgemv_pack for a given
  * (fmt, rows, K) is consumed only by calls with the same (fmt, N, K).
  *
@@ -78,7 +84,8 @@ typedef enum {
 typedef enum {
     QG_FMT_Q4_ASYM_G64 = 1,
     QG_FMT_Q8_SYM_G32 = 2,
-    QG_FMT_MXFP4_G32 = 3
+    QG_FMT_MXFP4_G32 = 3,
+    QG_FMT_Q8_ROW = 4
 } qg_format;
 
 typedef enum {
@@ -102,8 +109,8 @@ int qg_version(void);
  *  fmt          one of qg_format.
  *  rows         N, the number of output rows; a stack of E equally shaped
  *               expert matrices is packed as rows = E * N_expert.
- *  K            inputs per row: a multiple of 64 (Q4) or 32 (Q8, MXFP4),
- *               1 <= K <= 2^20.
+ *  K            inputs per row: a multiple of 64 (Q4) or 32 (Q8, MXFP4,
+ *               Q8_ROW), 1 <= K <= 2^20.
  *  codes, scales, biases   canonical device buffers (layouts above); biases is
  *               required for Q4 and must be NULL otherwise.  Read only.
  *  packed       device buffer (16-B) receiving the packed layout, or NULL to
@@ -124,8 +131,8 @@ int qgemv_pack(int fmt, int64_t rows, int64_t K, const void *codes,
  * decoding is memory-bound").  Weights are dequantized in registers and
  * accumulated in fp32.
  *
- *  fmt          QG_FMT_Q4_ASYM_G64 or QG_FMT_MXFP4_G32 (Q8 -> QG_EUNSUPPORTED;
- *               use qgemm_skinny_run with M = 1).
+ *  fmt          QG_FMT_Q4_ASYM_G64, QG_FMT_MXFP4_G32 or QG_FMT_Q8_ROW (Q8 ->
+ *               QG_EUNSUPPORTED; use qgemm_skinny_run with M = 1).
  *  packed, packed_bytes   from qgemv_pack with the same (fmt, N, K); 16-B.
  *  N, K         output rows and inputs; K <= 24576 for this call.
  *  x            device bf16 [K], 16-B.  Read only.
@@ -146,6 +153,8 @@ int qgemv_run(int fmt, const void *packed, size_t packed_bytes, int64_t N,
  *               QG_FMT_Q8_SYM_G32: X is int8 [M][K] (from hadamard32_quant_run,
  *               so the weights must already be in the rotated basis) and
  *               x_scales fp32 [M] is the per-row activation scale.
+ *               Other formats -> QG_EUNSUPPORTED (MXFP4 and Q8_ROW are
+ *               decode GEMVs: qgemv_run).
  *  packed, packed_bytes   from qgemv_pack with the same (fmt, N, K); 16-B.
  *  M            0..32.
  *  X            device [M][K], rows contiguous, 16-B.  Read only.

@@ -312,3 +312,23 @@ void oracle_moe(int64_t E, int64_t H, int64_t F, const uint8_t *gate_codes,
             y[n] += (double)w[s] * d_scratch[n];
     }
 }
+
+/* ------------------------------------------------------------ int8, row scale */
+
+/* Weight-only int8 with one fp32 scale per output row [K3]: the int8 code is
+ * converted to a real number and multiplied by its row's scale,
+ *     w[n][k] = scale[n] * q[n][k],
+ * and y[n] = sum_k w[n][k] * x[k] with x given in bf16.  codes int8 [N][K],
+ * scales fp32 [N]. */
+void oracle_q8row_gemv(int64_t N, int64_t K, const int8_t *codes,
+                       const float *scales, const uint16_t *x, double *y)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double w = (double)scales[n] * (double)codes[n * K + k];
+            acc += w * oracle_bf16_to_f64(x[k]);
+        }
+        y[n] = acc;
+    }
+}

@@ -57,6 +57,7 @@ def _load():
                 "oracle_q8_gemm": ([i64, i64, i64, p, p, p, p, p], None),
                 "oracle_mxfp4_gemv": ([i64, i64, p, p, p, p], None),
                 "oracle_mxfp4_gemv_f64": ([i64, i64, p, p, p, p], None),
+                "oracle_q8row_gemv": ([i64, i64, p, p, p, p], None),
                 "oracle_moe": ([i64, i64, i64, p, p, p, p, p, p, p, i64, p, p, p, p, p, p, p],
                                None),
             }
@@ -194,6 +195,19 @@ def mxfp4_gemv(codes, scales, x) -> np.ndarray:
         x, px = _c(x, np.uint16)
         assert x.shape == (K,)
         _load().oracle_mxfp4_gemv(N, K, pc, ps, px, y.ctypes.data_as(C.c_void_p))
+    return y
+
+
+def q8row_gemv(codes, scales, x):
+    """y [N] (float64) for weight-only int8: codes int8 [N, K], scales float32
+    [N] (one per row), x bf16 bits [K]."""
+    codes, pc = _c(codes, np.int8)
+    scales, ps = _c(scales, np.float32)
+    x, px = _c(x, np.uint16)
+    N, K = codes.shape
+    assert scales.shape == (N,) and x.shape == (K,)
+    y = np.empty(N)
+    _load().oracle_q8row_gemv(N, K, pc, ps, px, y.ctypes.data_as(C.c_void_p))
     return y
 
 

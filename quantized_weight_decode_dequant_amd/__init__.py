@@ -5,7 +5,7 @@ this package is its thin binding plus seeded synthetic inputs (``synth``) and
 host-side byte/roofline accounting (``roofline``).
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, FMT_MXFP4_G32, FMT_Q4_ASYM_G64, FMT_Q8_SYM_G32, OUT_BF16, OUT_F32, OUT_I32_GROUPS,
+    EXPORTS, FMT_MXFP4_G32, FMT_Q4_ASYM_G64, FMT_Q8_SYM_G32, FMT_Q8_ROW, OUT_BF16, OUT_F32, OUT_I32_GROUPS,
     KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA,
     QGError, hadamard32_quant_run, moe_expert_gemv_run, moe_workspace_bytes, packed_bytes,
     moe_expert_skinny_run, moe_skinny_workspace_bytes,

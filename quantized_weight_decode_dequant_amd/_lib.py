@@ -19,6 +19,7 @@ from .build import LIB_PATH
 FMT_Q4_ASYM_G64 = 1
 FMT_Q8_SYM_G32 = 2
 FMT_MXFP4_G32 = 3
+FMT_Q8_ROW = 4
 
 OUT_BF16 = 0
 OUT_F32 = 1

@@ -36,6 +36,7 @@ int format_group(int fmt) {
     case QG_FMT_Q4_ASYM_G64: return 64;
     case QG_FMT_Q8_SYM_G32: return 32;
     case QG_FMT_MXFP4_G32: return 32;
+    case QG_FMT_Q8_ROW: return 32;
     default: return 0;
     }
 }
@@ -45,6 +46,7 @@ size_t packed_bytes_for(int fmt, int64_t N, int64_t K) {
     case QG_FMT_Q4_ASYM_G64: return q4_packed_bytes(N, K);
     case QG_FMT_Q8_SYM_G32: return q8_packed_bytes(N, K);
     case QG_FMT_MXFP4_G32: return fp4_packed_bytes(N, K);
+    case QG_FMT_Q8_ROW: return q8row_packed_bytes(N, K);
     default: return 0;
     }
 }
@@ -114,8 +116,8 @@ int qgemv_pack(int fmt, int64_t rows, int64_t K, const void *codes, const void *
             return QG_ESIZE;
         }
         *packed_bytes = need;
-        if (!aligned(packed, 16) || !aligned(codes, 16) || !aligned(scales, 2) ||
-            (biases && !aligned(biases, 2)))
+        if (!aligned(packed, 16) || !aligned(codes, 16) ||
+            !aligned(scales, fmt == QG_FMT_Q8_ROW ? 4 : 2) || (biases && !aligned(biases, 2)))
             return QG_EALIGN;
         if (rows == 0) return QG_OK;
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -130,6 +132,10 @@ int qgemv_pack(int fmt, int64_t rows, int64_t K, const void *codes, const void *
             return hip_status(launch_pack_q8(reinterpret_cast<const int8_t *>(codes),
                                              reinterpret_cast<const uint16_t *>(scales), rows, K,
                                              out, s));
+        case QG_FMT_Q8_ROW:
+            return hip_status(launch_pack_q8row(reinterpret_cast<const int8_t *>(codes),
+                                                reinterpret_cast<const float *>(scales), rows, K,
+                                                out, s));
         default:
             return hip_status(launch_pack_fp4(reinterpret_cast<const uint8_t *>(codes),
                                               reinterpret_cast<const uint8_t *>(scales), rows, K,
@@ -162,6 +168,7 @@ int qgemv_run(int fmt, const void *packed, size_t packed_bytes, int64_t N, int64
         const uint8_t *p = reinterpret_cast<const uint8_t *>(packed);
         const uint16_t *xx = reinterpret_cast<const uint16_t *>(x);
         if (fmt == QG_FMT_Q4_ASYM_G64) return hip_status(launch_q4_gemv(p, xx, y, 1, N, K, f32, cus, s));
+        if (fmt == QG_FMT_Q8_ROW) return hip_status(launch_q8row_gemv(p, xx, y, N, K, f32, cus, s));
         return hip_status(launch_fp4_gemv(p, xx, y, N, K, f32, cus, s));
     } catch (...) {
         return QG_EINTERNAL;
@@ -176,7 +183,7 @@ int qgemm_skinny_run(int fmt, const void *packed, size_t packed_bytes, int64_t M
             return QG_EINVAL;
         int st = check_matrix(fmt, N, K);
         if (st != QG_OK) return st;
-        if (fmt == QG_FMT_MXFP4_G32) return QG_EUNSUPPORTED;
+        if (fmt == QG_FMT_MXFP4_G32 || fmt == QG_FMT_Q8_ROW) return QG_EUNSUPPORTED;
         if (fmt == QG_FMT_Q4_ASYM_G64 && out_dtype == QG_OUT_I32_GROUPS) return QG_EUNSUPPORTED;
         if (M < 0 || M > M_MAX) return QG_ESHAPE;
         if (!packed || !X || !Y) return QG_EINVAL;

@@ -18,6 +18,11 @@ size_t fp4_packed_bytes(int64_t N, int64_t K) {
     return (size_t)ceil_div(N, RB) * (size_t)ceil_div(K, FP4_TILE_K) * FP4_TILE_BYTES;
 }
 
+size_t q8row_packed_bytes(int64_t N, int64_t K) {
+    return (size_t)ceil_div(N, RB) *
+           ((size_t)ceil_div(K, Q8R_TILE_K) * Q8R_TILE_BYTES + Q8R_RB_TAIL);
+}
+
 // Canonical word: element i (0..7) in bits 4i.  Packed word: element 2j in
 // bits 4j, element 2j+1 in bits 16+4j.
 __device__ __forceinline__ unsigned q4_interleave(unsigned cw) {
@@ -146,6 +151,45 @@ pack_fp4_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ s
 }
 
 static inline unsigned grid_for(int64_t n, int block) { return (unsigned)ceil_div(n, block); }
+
+// Per-row int8: a rowblock is P tiles of 128 slots, then 4 slots of row
+// scales.  Codes are copied in k order (16 bytes = 16 consecutive k).
+__global__ void __launch_bounds__(256)
+pack_q8row_kernel(const int8_t *__restrict__ codes, const float *__restrict__ scales, int64_t N,
+                  int64_t K, int64_t P, int64_t nslots, uint4 *__restrict__ out) {
+    const int64_t slot_id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (slot_id >= nslots) return;
+    const int64_t per_rb = P * 128 + Q8R_RB_TAIL / 16;
+    const int64_t rb = slot_id / per_rb;
+    const int64_t s = slot_id - rb * per_rb;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (s < P * 128) {
+        const int64_t p = s / 128;
+        const int t = (int)(s % 128), j = t >> 6, l = t & 63;
+        const int64_t n = rb * RB + (l & 15);
+        const int64_t k0 = p * Q8R_TILE_K + 64 * j + 16 * (l >> 4);
+        if (n < N && k0 < K) v = *reinterpret_cast<const uint4 *>(codes + n * K + k0);
+    } else {
+        const int q = (int)(s - P * 128);
+        unsigned w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t n = rb * RB + 4 * q + r;
+            w[r] = n < N ? __float_as_uint(scales[n]) : 0u;
+        }
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    out[slot_id] = v;
+}
+
+hipError_t launch_pack_q8row(const int8_t *codes, const float *scales, int64_t N, int64_t K,
+                             uint8_t *packed, hipStream_t s) {
+    const int64_t P = ceil_div(K, Q8R_TILE_K);
+    const int64_t nslots = ceil_div(N, RB) * (P * 128 + Q8R_RB_TAIL / 16);
+    hipLaunchKernelGGL(pack_q8row_kernel, dim3(grid_for(nslots, 256)), dim3(256), 0, s, codes,
+                       scales, N, K, P, nslots, reinterpret_cast<uint4 *>(packed));
+    return hipGetLastError();
+}
 
 hipError_t launch_pack_q4(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                           int64_t N, int64_t K, uint8_t *packed, hipStream_t s) {

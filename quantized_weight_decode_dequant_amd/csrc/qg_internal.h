@@ -37,6 +37,10 @@ namespace qg {
 //                 block 4j + kg (k = 128j + 32kg .. +32), element 2i in the
 //                 low nibble of byte i.
 //   [2048, 2176)  E8M0 scale bytes: half j at 2048 + 64j + l.
+// Q8_ROW (int8, one fp32 scale per row), tile = 128 k, 2048 B:
+//   [0, 2048)     half j (1 KB each): lane l: 16 int8 codes of row l & 15,
+//                 k = 64j + 16(l >> 4) .. +16, in k order.
+//   A rowblock is its tiles followed by 64 B: the fp32 scales of its 16 rows.
 // Rows past N and k past K are zero-filled (zero codes and zero scales).
 
 constexpr int RB = 16;              // rows per rowblock
@@ -46,6 +50,9 @@ constexpr int Q8_TILE_K = 128;
 constexpr int Q8_TILE_BYTES = 2176;
 constexpr int FP4_TILE_K = 256;
 constexpr int FP4_TILE_BYTES = 2176;
+constexpr int Q8R_TILE_K = 128;
+constexpr int Q8R_TILE_BYTES = 2048;
+constexpr int Q8R_RB_TAIL = 64;  // the row scales after a rowblock's tiles
 
 // T-position MoE: (position, slot) pairs per call, and the most pairs of
 // one expert that share one read of its weights.
@@ -143,6 +150,13 @@ hipError_t launch_moe_skinny(const uint8_t *pg, const uint8_t *pu, const uint8_t
                              bool out_f32, int cus, hipStream_t s);
 // Positions whose x (or h) one group of the T-position MoE stages at once.
 int moe_skinny_group_rows(int64_t H, int64_t F);
+
+hipError_t launch_pack_q8row(const int8_t *codes, const float *scales, int64_t N,
+                            int64_t K, uint8_t *packed, hipStream_t s);
+hipError_t launch_q8row_gemv(const uint8_t *packed, const uint16_t *x, void *y,
+                             int64_t N, int64_t K, bool out_f32, int cus,
+                             hipStream_t s);
+size_t q8row_packed_bytes(int64_t N, int64_t K);
 
 size_t q4_packed_bytes(int64_t N, int64_t K);
 size_t q8_packed_bytes(int64_t N, int64_t K);

@@ -45,6 +45,12 @@ def hadamard_quant_bytes(M: int, K: int) -> float:
     return 2.0 * M * K + K + 1.0 * M * K + 4.0 * M
 
 
+def q8row_gemv_bytes(N: int, K: int, out_bytes: int = 2) -> float:
+    """Weight-only int8 GEMV: one byte per weight, an fp32 scale per row, x in
+    (bf16) and y out."""
+    return 1.0 * N * K + 4.0 * N + 2.0 * K + float(out_bytes) * N
+
+
 def moe_expert_bytes(H: int, F: int) -> float:
     """One MXFP4 expert: gate, up [F, H] and down [H, F]."""
     return 3.0 * H * F * MXFP4_BYTES_PER_WEIGHT

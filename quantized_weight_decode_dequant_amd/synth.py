@@ -48,6 +48,7 @@ _S_SIGNS = 5
 _S_EXPERT = 6
 _S_ROUTER = 7
 _S_MOEX = 8
+_S_Q8ROW = 9
 
 
 def rng_for(seed: int, stream: int, i: int = 0, j: int = 0) -> np.random.Generator:
@@ -129,6 +130,24 @@ def q8_matrix(seed: int, N: int, K: int, item: int = 0) -> Q8Matrix:
     r = rng_for(seed, _S_Q8, item, 1)
     sw = f16_bits(r.uniform(2.0 ** -13, 2.0 ** -10, size=(N, K // 32)))
     return Q8Matrix(qw, sw)
+
+
+@dataclass
+class Q8RowMatrix:
+    codes: np.ndarray   # int8 [N, K]
+    scales: np.ndarray  # float32 [N], one per row
+
+
+def q8row_matrix(seed: int, N: int, K: int, item: int = 0) -> Q8RowMatrix:
+    """Weight-only int8 with a row scale: codes = clip(rint(N(0, 40)), -128,
+    127) (the full int8 range), scales = float32(U[2^-11, 2^-9])."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    r = rng_for(seed, _S_Q8ROW, item, 0)
+    codes = np.clip(np.rint(r.standard_normal((N, K)) * 40.0), -128, 127).astype(np.int8)
+    r = rng_for(seed, _S_Q8ROW, item, 1)
+    scales = r.uniform(2.0 ** -11, 2.0 ** -9, size=N).astype(np.float32)
+    return Q8RowMatrix(codes, scales)
 
 
 def q8_activations(seed: int, M: int, K: int, item: int = 0, outlier_frac: float = 0.01,

@@ -40,3 +40,9 @@ def pack_mxfp4(codes: np.ndarray, scales: np.ndarray, device="cuda", stream=None
     rows, K = codes.shape[0], codes.shape[1] * 2
     return _lib.qgemv_pack(_lib.FMT_MXFP4_G32, rows, K, to_device(codes, device),
                            to_device(scales, device), stream=stream)
+
+
+def pack_q8row(m, device="cuda", stream=None):
+    """Weight-only int8: codes int8 [N, K], scales float32 [N]."""
+    return _lib.qgemv_pack(_lib.FMT_Q8_ROW, m.codes.shape[0], m.codes.shape[1],
+                           to_device(m.codes, device), to_device(m.scales, device), stream=stream)

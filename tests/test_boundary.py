@@ -216,6 +216,22 @@ def test_moe_skinny_validation():
     assert call(ws=A + 8) == L.QG_EALIGN
 
 
+def test_q8row_validation():
+    lib = pkg.raw()
+    f = L.FMT_Q8_ROW
+    n = C.c_size_t(0)
+    assert lib.qgemv_pack(f, 40, 288, None, None, None, None, C.byref(n), None) == L.QG_OK
+    assert n.value == 3 * (3 * 2048 + 64)  # 3 rowblocks of 3 tiles and 64 B of row scales
+    cap = C.c_size_t(n.value)
+    assert lib.qgemv_pack(f, 40, 272, A, A, None, A, C.byref(cap), None) == L.QG_ESHAPE
+    assert lib.qgemv_pack(f, 40, 288, A, A, A, A, C.byref(cap), None) == L.QG_EINVAL  # no biases
+    assert lib.qgemv_pack(f, 40, 288, A, A + 2, None, A, C.byref(cap), None) == L.QG_EALIGN
+    assert lib.qgemv_run(f, A, n.value, 40, 288, A, A, 2, None) == L.QG_EUNSUPPORTED
+    assert lib.qgemv_run(f, A, n.value + 1, 40, 288, A, A, 0, None) == L.QG_ESIZE
+    assert lib.qgemv_run(f, A, n.value, 40, 288, A + 8, A, 0, None) == L.QG_EALIGN
+    assert lib.qgemm_skinny_run(f, A, n.value, 2, 40, 288, A, None, A, 0, None) == L.QG_EUNSUPPORTED
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):

@@ -316,6 +316,49 @@ def test_mxfp4_onehot_is_exact_column():
         assert np.array_equal(y, expect)
 
 
+def _q8row_example_codes():
+    k = np.arange(32)
+    row0 = k - 16
+    row1 = np.where(k % 2 == 0, 1, -1) * 4 * (k + 1)
+    return np.stack([row0, row1]).astype(np.int8)
+
+
+def test_q8row_worked_example():
+    lines = list(golden_lines("q8row_worked_example.txt"))
+    scales = np.zeros(2, dtype=np.float32)
+    for _, row, val in (l for l in lines if l[0] == "scale"):
+        scales[int(row)] = float(val)
+    codes = _q8row_example_codes()
+    assert codes[1, 31] == -128 and codes[1, 30] == 124
+    for _, row, kind, idx, expect in (l for l in lines if l[0] == "case"):
+        if kind == "ones":
+            x = ones_bf16(32)
+        elif kind == "alt":
+            x = synth.f32_to_bf16_bits(np.where(np.arange(32) % 2 == 0, 1.0, -1.0))
+        else:
+            x = onehot_bf16(32, int(idx))
+        assert oracle.q8row_gemv(codes, scales, x)[int(row)] == float(expect)
+
+
+def test_q8row_closed_forms():
+    """One-hot x returns the dequantized column exactly; the result is linear
+    in the row scale and in x; a zero code row gives zero; it equals the
+    numpy product of the dequantized matrix."""
+    m = synth.q8row_matrix(31, 6, 96)
+    for k in (0, 17, 95):
+        y = oracle.q8row_gemv(m.codes, m.scales, onehot_bf16(96, k))
+        assert np.array_equal(y, m.scales.astype(np.float64) * m.codes[:, k])
+    x = synth.activations(32, 1, 96)[0]
+    y = oracle.q8row_gemv(m.codes, m.scales, x)
+    assert np.array_equal(oracle.q8row_gemv(m.codes, 2 * m.scales, x), 2 * y)
+    z = m.codes.copy()
+    z[3] = 0
+    assert oracle.q8row_gemv(z, m.scales, x)[3] == 0.0
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = (m.scales.astype(np.float64)[:, None] * m.codes.astype(np.float64)) @ xf
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+
+
 def test_silu_matches_torch():
     a = np.linspace(-30, 30, 601)
     ref = torch.nn.functional.silu(torch.from_numpy(a)).numpy()
