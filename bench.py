@@ -622,6 +622,37 @@ def main():
         log("int8 lm_head: %.2f us" % (msh * 1e3))
         del qpacked
 
+        # the affine family at every width, group 64, fp16 scales: one GEMV
+        # 8192 -> 262144 per width (codes drawn on the device)
+        NA, KA, GA = 262144, 8192, 64
+        rows = []
+        for bits in (2, 3, 4, 5, 6, 8):
+            fa = _lib.affine_format(bits, GA)
+            ga = torch.Generator(device="cuda")
+            ga.manual_seed(args.seed + bits)
+            acodes = torch.randint(0, 1 << bits, (NA, KA), dtype=torch.uint8, device="cuda",
+                                   generator=ga)
+            asc = ((torch.rand(NA, KA // GA, device="cuda", generator=ga) + 0.05) * 0.02 * 15 /
+                   ((1 << bits) - 1)).half().view(torch.int16)
+            abi = (torch.randn(NA, KA // GA, device="cuda", generator=ga) * 0.01).half().view(torch.int16)
+            apacked = _lib.qgemv_pack(fa, NA, KA, acodes, asc, abi)
+            del acodes, asc, abi
+            ax = weights.to_device(synth.activations(args.seed, 1, KA)[0], "cuda")
+            ay = torch.empty(NA, dtype=torch.bfloat16, device="cuda")
+            msa = workloads.time_graph_ms(
+                lambda: _lib.qgemv_run(fa, apacked, NA, KA, ax, y=ay), 8)
+            ba = roofline.affine_gemv_bytes(bits, GA, NA, KA)
+            fla = plain_read_us(int(ba))
+            rows.append({"bits": bits, "us": round(msa * 1e3, 2), "GBs": round(ba / (msa * 1e-3) / 1e9, 1),
+                         "pct_of_peak": round(100 * ba / (msa * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1),
+                         "pct_of_plain_read": round(100 * fla / (msa * 1e3), 1)})
+            log("affine %d-bit g%d: %.2f us" % (bits, GA, msa * 1e3))
+            del apacked
+        result["affine_family"] = {
+            "workload": "affine weights (scale * code + bias per group of 64, fp16), one GEMV "
+                        "8192->262144 per code width, codes uniform, M=1; calls captured in a "
+                        "HIP graph", "rows": rows}
+
         # MXFP4 routed experts, one token through one layer
         moe = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16)
         msm = workloads.time_graph_ms(moe.run, 64)

@@ -25,6 +25,13 @@
  *  - QG_FMT_MXFP4_G32: E2M1 codes with one E8M0 scale per 32 values (Deltafin
  *    / Kimi K3 page, aihot.virxact.com, sections "How it works" and the compute
  *    list: fused MXFP4 dequant + GEMV for the routed experts).
+ *  - QG_FMT_AFFINE(bits, group, bf16_scales): the affine family of "MLX
+ *    Runner" (section "Architecture: one command buffer per token": weights
+ *    stored as codes with a scale and a bias per group; the audit section
+ *    lists its widths): unsigned codes of 2, 3, 4, 5, 6 or 8 bits, groups of
+ *    32, 64 or 128 consecutive k, one scale and one bias per group in fp16
+ *    (bf16_scales = 0) or bf16 (1); weight = scale * code + bias.  Decode
+ *    GEMV (qgemv_run) only.
  *  - QG_FMT_Q8_ROW: int8 codes (the full range -128..127) with one fp32 scale
  *    per output row, weight = scale[n] * code, against bf16 activations:
  *    weight-only int8 as in the Deltafin page's resident int8 spine and packed
@@ -39,6 +46,8 @@
  *  - MXFP4: codes uint8 [N][K/2] (element 2i in the low nibble of byte i);
  *           scales uint8 E8M0 [N][K/32];  biases NULL.
  *  - Q8_ROW: codes int8 [N][K];  scales fp32 [N];  biases NULL.
+ *  - AFFINE: codes uint8 [N][K], one code per byte (< 2^bits); scales and
+ *           biases fp16 or bf16 [N][K/group].
  * The packed layout is opaque: a buffer produced by qgemv_pack for a given
  * (fmt, rows, K) is consumed only by calls with the same (fmt, N, K).
  *
@@ -88,6 +97,14 @@ typedef enum {
     QG_FMT_Q8_ROW = 4
 } qg_format;
 
+/* Format code of an affine-family member: bits in {2, 3, 4, 5, 6, 8}, group
+ * in {32, 64, 128}, bf16_scales 0 (fp16 scales and biases) or 1 (bf16).  Any
+ * other combination gives a code the calls reject with QG_EINVAL. */
+#define QG_FMT_AFFINE(bits, group, bf16_scales)                              \
+    (0x100 | (((bits) & 0xF) << 4) |                                        \
+     (((group) == 32 ? 0 : (group) == 64 ? 1 : (group) == 128 ? 2 : 3) << 2) | \
+     ((bf16_scales) ? 1 : 0))
+
 typedef enum {
     QG_OUT_BF16 = 0,       /* bf16, round to nearest even */
     QG_OUT_F32 = 1,        /* fp32, the accumulator as computed */
@@ -109,10 +126,11 @@ int qg_version(void);
  *  fmt          one of qg_format.
  *  rows         N, the number of output rows; a stack of E equally shaped
  *               expert matrices is packed as rows = E * N_expert.
- *  K            inputs per row: a multiple of 64 (Q4) or 32 (Q8, MXFP4,
- *               Q8_ROW), 1 <= K <= 2^20.
+ *  K            inputs per row: a multiple of 64 (Q4), 32 (Q8, MXFP4,
+ *               Q8_ROW) or of the group (AFFINE), 1 <= K <= 2^20.
  *  codes, scales, biases   canonical device buffers (layouts above); biases is
- *               required for Q4 and must be NULL otherwise.  Read only.
+ *               required for Q4 and AFFINE and must be NULL otherwise.  Read
+ *               only.
  *  packed       device buffer (16-B) receiving the packed layout, or NULL to
  *               query the size only (no device access at all then).
  *  packed_bytes in: capacity of `packed` (ignored when packed is NULL);
@@ -131,8 +149,9 @@ int qgemv_pack(int fmt, int64_t rows, int64_t K, const void *codes,
  * decoding is memory-bound").  Weights are dequantized in registers and
  * accumulated in fp32.
  *
- *  fmt          QG_FMT_Q4_ASYM_G64, QG_FMT_MXFP4_G32 or QG_FMT_Q8_ROW (Q8 ->
- *               QG_EUNSUPPORTED; use qgemm_skinny_run with M = 1).
+ *  fmt          QG_FMT_Q4_ASYM_G64, QG_FMT_MXFP4_G32, QG_FMT_Q8_ROW or an
+ *               affine-family code (Q8 -> QG_EUNSUPPORTED; use
+ *               qgemm_skinny_run with M = 1).
  *  packed, packed_bytes   from qgemv_pack with the same (fmt, N, K); 16-B.
  *  N, K         output rows and inputs; K <= 24576 for this call.
  *  x            device bf16 [K], 16-B.  Read only.
@@ -153,8 +172,8 @@ int qgemv_run(int fmt, const void *packed, size_t packed_bytes, int64_t N,
  *               QG_FMT_Q8_SYM_G32: X is int8 [M][K] (from hadamard32_quant_run,
  *               so the weights must already be in the rotated basis) and
  *               x_scales fp32 [M] is the per-row activation scale.
- *               Other formats -> QG_EUNSUPPORTED (MXFP4 and Q8_ROW are
- *               decode GEMVs: qgemv_run).
+ *               Other formats -> QG_EUNSUPPORTED (MXFP4, Q8_ROW and the
+ *               affine family are decode GEMVs: qgemv_run).
  *  packed, packed_bytes   from qgemv_pack with the same (fmt, N, K); 16-B.
  *  M            0..32.
  *  X            device [M][K], rows contiguous, 16-B.  Read only.

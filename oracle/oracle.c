@@ -332,3 +332,28 @@ void oracle_q8row_gemv(int64_t N, int64_t K, const int8_t *codes,
         y[n] = acc;
     }
 }
+
+/* ------------------------------------------------------------ affine family */
+
+/* The affine family [MLXR]: unsigned codes q (one per byte here, q < 2^bits),
+ * one scale and one bias per group of `group` consecutive k, both fp16
+ * (bf16_scales = 0) or bf16 (1):
+ *     w[n][k] = scale[n][k / group] * q[n][k] + bias[n][k / group],
+ * y[n] = sum_k w[n][k] * x[k], x given in bf16. */
+void oracle_affine_gemv(int64_t N, int64_t K, int64_t group, int bf16_scales,
+                        const uint8_t *codes, const uint16_t *scales,
+                        const uint16_t *biases, const uint16_t *x, double *y)
+{
+    int64_t G = K / group;
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t sb = scales[n * G + k / group], bb = biases[n * G + k / group];
+            double s = bf16_scales ? oracle_bf16_to_f64(sb) : oracle_f16_to_f64(sb);
+            double b = bf16_scales ? oracle_bf16_to_f64(bb) : oracle_f16_to_f64(bb);
+            double w = s * (double)codes[n * K + k] + b;
+            acc += w * oracle_bf16_to_f64(x[k]);
+        }
+        y[n] = acc;
+    }
+}

@@ -58,6 +58,7 @@ def _load():
                 "oracle_mxfp4_gemv": ([i64, i64, p, p, p, p], None),
                 "oracle_mxfp4_gemv_f64": ([i64, i64, p, p, p, p], None),
                 "oracle_q8row_gemv": ([i64, i64, p, p, p, p], None),
+                "oracle_affine_gemv": ([i64, i64, i64, C.c_int, p, p, p, p, p], None),
                 "oracle_moe": ([i64, i64, i64, p, p, p, p, p, p, p, i64, p, p, p, p, p, p, p],
                                None),
             }
@@ -208,6 +209,23 @@ def q8row_gemv(codes, scales, x):
     assert scales.shape == (N,) and x.shape == (K,)
     y = np.empty(N)
     _load().oracle_q8row_gemv(N, K, pc, ps, px, y.ctypes.data_as(C.c_void_p))
+    return y
+
+
+def affine_gemv(codes, scales, biases, x, group: int, bf16_scales: bool):
+    """y [N] (float64) for the affine family: codes uint8 [N, K] (one code
+    per byte), scales and biases fp16 or bf16 bits [N, K/group], x bf16 bits
+    [K]."""
+    codes, pc = _c(codes, np.uint8)
+    scales, ps = _c(scales, np.uint16)
+    biases, pb = _c(biases, np.uint16)
+    x, px = _c(x, np.uint16)
+    N, K = codes.shape
+    assert K % group == 0 and scales.shape == (N, K // group) and biases.shape == scales.shape
+    assert x.shape == (K,)
+    y = np.empty(N)
+    _load().oracle_affine_gemv(N, K, group, 1 if bf16_scales else 0, pc, ps, pb, px,
+                               y.ctypes.data_as(C.c_void_p))
     return y
 
 

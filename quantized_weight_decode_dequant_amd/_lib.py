@@ -21,6 +21,12 @@ FMT_Q8_SYM_G32 = 2
 FMT_MXFP4_G32 = 3
 FMT_Q8_ROW = 4
 
+
+def affine_format(bits: int, group: int, bf16_scales: bool = False) -> int:
+    """QG_FMT_AFFINE(bits, group, bf16_scales) of qgemv.h."""
+    gc = {32: 0, 64: 1, 128: 2}.get(group, 3)
+    return 0x100 | ((bits & 0xF) << 4) | (gc << 2) | (1 if bf16_scales else 0)
+
 OUT_BF16 = 0
 OUT_F32 = 1
 OUT_I32_GROUPS = 2

@@ -37,7 +37,7 @@ int format_group(int fmt) {
     case QG_FMT_Q8_SYM_G32: return 32;
     case QG_FMT_MXFP4_G32: return 32;
     case QG_FMT_Q8_ROW: return 32;
-    default: return 0;
+    default: return affine_decode(fmt).group;
     }
 }
 
@@ -47,7 +47,10 @@ size_t packed_bytes_for(int fmt, int64_t N, int64_t K) {
     case QG_FMT_Q8_SYM_G32: return q8_packed_bytes(N, K);
     case QG_FMT_MXFP4_G32: return fp4_packed_bytes(N, K);
     case QG_FMT_Q8_ROW: return q8row_packed_bytes(N, K);
-    default: return 0;
+    default: {
+        const AffineFmt a = affine_decode(fmt);
+        return a.bits ? affine_packed_bytes(a.bits, a.group, N, K) : 0;
+    }
     }
 }
 
@@ -110,7 +113,8 @@ int qgemv_pack(int fmt, int64_t rows, int64_t K, const void *codes, const void *
             return QG_OK;
         }
         if (!codes || !scales) return QG_EINVAL;
-        if ((fmt == QG_FMT_Q4_ASYM_G64) != (biases != nullptr)) return QG_EINVAL;
+        const AffineFmt aff = affine_decode(fmt);
+        if ((fmt == QG_FMT_Q4_ASYM_G64 || aff.bits) != (biases != nullptr)) return QG_EINVAL;
         if (*packed_bytes < need) {
             *packed_bytes = need;
             return QG_ESIZE;
@@ -132,14 +136,19 @@ int qgemv_pack(int fmt, int64_t rows, int64_t K, const void *codes, const void *
             return hip_status(launch_pack_q8(reinterpret_cast<const int8_t *>(codes),
                                              reinterpret_cast<const uint16_t *>(scales), rows, K,
                                              out, s));
+        case QG_FMT_MXFP4_G32:
+            return hip_status(launch_pack_fp4(reinterpret_cast<const uint8_t *>(codes),
+                                              reinterpret_cast<const uint8_t *>(scales), rows, K,
+                                              out, s));
         case QG_FMT_Q8_ROW:
             return hip_status(launch_pack_q8row(reinterpret_cast<const int8_t *>(codes),
                                                 reinterpret_cast<const float *>(scales), rows, K,
                                                 out, s));
         default:
-            return hip_status(launch_pack_fp4(reinterpret_cast<const uint8_t *>(codes),
-                                              reinterpret_cast<const uint8_t *>(scales), rows, K,
-                                              out, s));
+            return hip_status(launch_pack_affine(reinterpret_cast<const uint8_t *>(codes),
+                                                 reinterpret_cast<const uint16_t *>(scales),
+                                                 reinterpret_cast<const uint16_t *>(biases),
+                                                 aff.bits, aff.group, rows, K, out, s));
         }
     } catch (...) {
         return QG_EINTERNAL;
@@ -169,7 +178,10 @@ int qgemv_run(int fmt, const void *packed, size_t packed_bytes, int64_t N, int64
         const uint16_t *xx = reinterpret_cast<const uint16_t *>(x);
         if (fmt == QG_FMT_Q4_ASYM_G64) return hip_status(launch_q4_gemv(p, xx, y, 1, N, K, f32, cus, s));
         if (fmt == QG_FMT_Q8_ROW) return hip_status(launch_q8row_gemv(p, xx, y, N, K, f32, cus, s));
-        return hip_status(launch_fp4_gemv(p, xx, y, N, K, f32, cus, s));
+        if (fmt == QG_FMT_MXFP4_G32) return hip_status(launch_fp4_gemv(p, xx, y, N, K, f32, cus, s));
+        const AffineFmt a = affine_decode(fmt);
+        return hip_status(launch_affine_gemv(p, xx, y, a.bits, a.group, a.bf16 != 0, N, K, f32,
+                                             cus, s));
     } catch (...) {
         return QG_EINTERNAL;
     }
@@ -183,7 +195,7 @@ int qgemm_skinny_run(int fmt, const void *packed, size_t packed_bytes, int64_t M
             return QG_EINVAL;
         int st = check_matrix(fmt, N, K);
         if (st != QG_OK) return st;
-        if (fmt == QG_FMT_MXFP4_G32 || fmt == QG_FMT_Q8_ROW) return QG_EUNSUPPORTED;
+        if (fmt != QG_FMT_Q4_ASYM_G64 && fmt != QG_FMT_Q8_SYM_G32) return QG_EUNSUPPORTED;
         if (fmt == QG_FMT_Q4_ASYM_G64 && out_dtype == QG_OUT_I32_GROUPS) return QG_EUNSUPPORTED;
         if (M < 0 || M > M_MAX) return QG_ESHAPE;
         if (!packed || !X || !Y) return QG_EINVAL;

@@ -41,6 +41,17 @@ namespace qg {
 //   [0, 2048)     half j (1 KB each): lane l: 16 int8 codes of row l & 15,
 //                 k = 64j + 16(l >> 4) .. +16, in k order.
 //   A rowblock is its tiles followed by 64 B: the fp32 scales of its 16 rows.
+// AFFINE (b-bit unsigned codes, group g, (scale, bias) fp16 or bf16), tile =
+// 128 k, 256 b + 16 (128 / g) 4 bytes:
+//   the codes as bit-planes of width 1, 2 or 4 (b = 2: {2}; 3: {2, 1};
+//   4: {4}; 5: {4, 1}; 6: {4, 2}; 8: {4, 4}; plane p holds bits
+//   [o_p, o_p + w_p) of each code).  Plane p occupies 256 w_p bytes; lane l
+//   holds w_p words at 4 w_p l for the 32 codes c_0..c_31 of row l & 15,
+//   k = 32(l >> 4) .. +32: pair j (codes 2j, 2j+1) sits in word
+//   j / (16 / w_p), at bit w_p (j % (16 / w_p)) (code 2j) and 16 + the same
+//   (code 2j+1), so a shift and an and-or yield both as the two halves.
+//   [256 b, ...)  per (row r, group t of the tile): (scale | bias << 16) at
+//   256 b + 4 (r (128 / g) + t).
 // Rows past N and k past K are zero-filled (zero codes and zero scales).
 
 constexpr int RB = 16;              // rows per rowblock
@@ -53,6 +64,26 @@ constexpr int FP4_TILE_BYTES = 2176;
 constexpr int Q8R_TILE_K = 128;
 constexpr int Q8R_TILE_BYTES = 2048;
 constexpr int Q8R_RB_TAIL = 64;  // the row scales after a rowblock's tiles
+constexpr int AFF_TILE_K = 128;
+
+// Affine-family format codes (QG_FMT_AFFINE in qgemv.h).
+struct AffineFmt {
+    int bits, group, bf16;  // bits 0 = not an affine code
+};
+inline AffineFmt affine_decode(int fmt) {
+    AffineFmt f{0, 0, 0};
+    if ((fmt & ~0xFF) != 0x100) return f;
+    const int bits = (fmt >> 4) & 0xF, gc = (fmt >> 2) & 3;
+    if (!(bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8) || gc == 3)
+        return f;
+    f.bits = bits;
+    f.group = 32 << gc;
+    f.bf16 = fmt & 1;
+    return f;
+}
+__host__ __device__ inline size_t affine_tile_bytes(int bits, int group) {
+    return (size_t)256 * bits + (size_t)16 * (AFF_TILE_K / group) * 4;
+}
 
 // T-position MoE: (position, slot) pairs per call, and the most pairs of
 // one expert that share one read of its weights.
@@ -157,6 +188,14 @@ hipError_t launch_q8row_gemv(const uint8_t *packed, const uint16_t *x, void *y,
                              int64_t N, int64_t K, bool out_f32, int cus,
                              hipStream_t s);
 size_t q8row_packed_bytes(int64_t N, int64_t K);
+size_t affine_packed_bytes(int bits, int group, int64_t N, int64_t K);
+hipError_t launch_pack_affine(const uint8_t *codes, const uint16_t *scales,
+                              const uint16_t *biases, int bits, int group,
+                              int64_t N, int64_t K, uint8_t *packed,
+                              hipStream_t s);
+hipError_t launch_affine_gemv(const uint8_t *packed, const uint16_t *x, void *y,
+                              int bits, int group, bool bf16_scales, int64_t N,
+                              int64_t K, bool out_f32, int cus, hipStream_t s);
 
 size_t q4_packed_bytes(int64_t N, int64_t K);
 size_t q8_packed_bytes(int64_t N, int64_t K);

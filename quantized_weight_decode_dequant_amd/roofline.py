@@ -51,6 +51,12 @@ def q8row_gemv_bytes(N: int, K: int, out_bytes: int = 2) -> float:
     return 1.0 * N * K + 4.0 * N + 2.0 * K + float(out_bytes) * N
 
 
+def affine_gemv_bytes(bits: int, group: int, N: int, K: int, out_bytes: int = 2) -> float:
+    """Affine-family GEMV: bits/8 bytes per weight plus a 2-byte scale and a
+    2-byte bias per group, x in (bf16) and y out."""
+    return N * K * (bits / 8.0 + 4.0 / group) + 2.0 * K + float(out_bytes) * N
+
+
 def moe_expert_bytes(H: int, F: int) -> float:
     """One MXFP4 expert: gate, up [F, H] and down [H, F]."""
     return 3.0 * H * F * MXFP4_BYTES_PER_WEIGHT

@@ -49,6 +49,7 @@ _S_EXPERT = 6
 _S_ROUTER = 7
 _S_MOEX = 8
 _S_Q8ROW = 9
+_S_AFFINE = 10
 
 
 def rng_for(seed: int, stream: int, i: int = 0, j: int = 0) -> np.random.Generator:
@@ -148,6 +149,33 @@ def q8row_matrix(seed: int, N: int, K: int, item: int = 0) -> Q8RowMatrix:
     r = rng_for(seed, _S_Q8ROW, item, 1)
     scales = r.uniform(2.0 ** -11, 2.0 ** -9, size=N).astype(np.float32)
     return Q8RowMatrix(codes, scales)
+
+
+@dataclass
+class AffineMatrix:
+    codes: np.ndarray   # uint8 [N, K], one code per byte
+    scales: np.ndarray  # uint16 fp16 or bf16 bits [N, K/group]
+    biases: np.ndarray  # uint16, same
+    bits: int
+    group: int
+    bf16_scales: bool
+
+
+def affine_matrix(seed: int, N: int, K: int, bits: int, group: int, bf16_scales: bool = False,
+                  item: int = 0) -> AffineMatrix:
+    """Codes uniform over 0..2^bits - 1; scale = (|N(0, 0.02)| + 1e-3) * 15 /
+    (2^bits - 1) (the 4-bit recipe, rescaled so weights keep their range);
+    bias = N(0, 0.01); scales and biases rounded to fp16 or bf16."""
+    if K % group:
+        raise ValueError("K must be a multiple of the group")
+    r = rng_for(seed, _S_AFFINE, item, 0)
+    codes = r.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    r = rng_for(seed, _S_AFFINE, item, 1)
+    sc = (np.abs(r.normal(0.0, 0.02, size=(N, K // group))) + 1e-3) * 15.0 / ((1 << bits) - 1)
+    r = rng_for(seed, _S_AFFINE, item, 2)
+    bi = r.normal(0.0, 0.01, size=(N, K // group))
+    enc = f32_to_bf16_bits if bf16_scales else f16_bits
+    return AffineMatrix(codes, enc(sc), enc(bi), bits, group, bf16_scales)
 
 
 def q8_activations(seed: int, M: int, K: int, item: int = 0, outlier_frac: float = 0.01,

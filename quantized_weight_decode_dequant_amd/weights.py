@@ -46,3 +46,12 @@ def pack_q8row(m, device="cuda", stream=None):
     """Weight-only int8: codes int8 [N, K], scales float32 [N]."""
     return _lib.qgemv_pack(_lib.FMT_Q8_ROW, m.codes.shape[0], m.codes.shape[1],
                            to_device(m.codes, device), to_device(m.scales, device), stream=stream)
+
+
+def pack_affine(m, device="cuda", stream=None):
+    """Affine family (synth.AffineMatrix): codes uint8 [N, K], scales and
+    biases uint16 [N, K/group]."""
+    fmt = _lib.affine_format(m.bits, m.group, m.bf16_scales)
+    return _lib.qgemv_pack(fmt, m.codes.shape[0], m.codes.shape[1], to_device(m.codes, device),
+                           to_device(m.scales, device), to_device(m.biases, device),
+                           stream=stream)

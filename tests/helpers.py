@@ -5,10 +5,13 @@ Tolerances (the dequant paths accumulate in fp32; the oracle is fp64):
    The floor keeps outputs that cancel to nearly zero from dominating a
    relative measure; it is 1% of the typical output magnitude.
  * bf16 output: every element within one bf16 ulp of the exact value (or the
-   same floor, scaled by 2e-3), and, for vectors of at least 64 elements,
-   relative L2 error <= 2e-3.  A literal 2e-3 elementwise bound is below
-   bf16's own rounding (up to 2^-8 relative); over many elements the rounding
-   errors average to well under 2e-3, over a handful they need not.
+   same floor, scaled by 2e-3), and, for vectors of at least 64 elements, the
+   distance to the correctly rounded exact value (bf16 round-to-nearest-even
+   of the reference) at most 2e-3 in relative L2.  A literal 2e-3 bound
+   against the exact value is below bf16's own rounding: elementwise it
+   reaches 2^-8 relative, and even the L2 of the rounding alone is about
+   1.6e-3 (up to 2.1e-3 on 100 outputs), so the correctly rounded answer
+   itself would fail it.
  * integer outputs: bit-exact.
 """
 import sys
@@ -49,6 +52,14 @@ def bf16_ulp(ref):
     return np.exp2(np.floor(np.log2(a)) - 7)
 
 
+def bf16_round(a):
+    """float64 -> nearest bf16 value (round-to-nearest-even, via float32),
+    as float64."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def assert_bf16_close(got, ref, what=""):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -57,7 +68,8 @@ def assert_bf16_close(got, ref, what=""):
     bad = np.abs(got - ref) > lim
     assert not bad.any(), "%s: %d elements beyond 1 bf16 ulp, first at %s (got %r ref %r)" % (
         what, int(bad.sum()), np.argwhere(bad)[0], got[bad][0], ref[bad][0])
-    l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    rounded = bf16_round(ref)
+    l2 = float(np.linalg.norm(got - rounded) / max(np.linalg.norm(ref), 1e-300))
     if ref.size >= 64:
         assert l2 <= TOL, "%s: rel L2 %.3g" % (what, l2)
     return l2

@@ -232,6 +232,26 @@ def test_q8row_validation():
     assert lib.qgemm_skinny_run(f, A, n.value, 2, 40, 288, A, None, A, 0, None) == L.QG_EUNSUPPORTED
 
 
+def test_affine_validation():
+    lib = pkg.raw()
+    f = L.affine_format(3, 32, True)
+    assert f == 0x100 | (3 << 4) | (0 << 2) | 1
+    n = C.c_size_t(0)
+    assert lib.qgemv_pack(f, 40, 96, None, None, None, None, C.byref(n), None) == L.QG_OK
+    assert n.value == 3 * (256 * 3 + 16 * 4 * 4)  # 3 rowblocks x 1 tile
+    for bad in (L.affine_format(7, 32), L.affine_format(1, 32), L.affine_format(4, 16),
+                L.affine_format(4, 256), 0x244, 0x100 | (4 << 4) | (3 << 2)):
+        assert lib.qgemv_pack(bad, 40, 96, None, None, None, None, C.byref(n), None) == L.QG_EINVAL
+    f64 = L.affine_format(4, 64)
+    assert lib.qgemv_pack(f64, 40, 96, None, None, None, None, C.byref(n), None) == L.QG_ESHAPE
+    need = pkg.packed_bytes(f, 40, 96)
+    cap = C.c_size_t(need)
+    assert lib.qgemv_pack(f, 40, 96, A, A, None, A, C.byref(cap), None) == L.QG_EINVAL  # biases
+    assert lib.qgemv_run(f, A, need + 16, 40, 96, A, A, 0, None) == L.QG_ESIZE
+    assert lib.qgemv_run(f, A, need, 40, 96, A + 4, A, 0, None) == L.QG_EALIGN
+    assert lib.qgemm_skinny_run(f, A, need, 2, 40, 96, A, None, A, 0, None) == L.QG_EUNSUPPORTED
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):

@@ -1,0 +1,91 @@
+"""GPU parity: the affine weight family (2/3/4/5/6/8-bit codes, groups of
+32/64/128, fp16 or bf16 scales and biases; "MLX Runner", section
+"Architecture: one command buffer per token") through qgemv_pack and
+qgemv_run, against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_weight_decode_dequant_amd as pkg
+from quantized_weight_decode_dequant_amd import synth, weights
+from helpers import assert_bf16_close, assert_f32_close, note, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BITS = (2, 3, 4, 5, 6, 8)
+
+
+def run(m, packed, x, out_dtype):
+    fmt = pkg.affine_format(m.bits, m.group, m.bf16_scales)
+    N, K = m.codes.shape
+    y = pkg.qgemv_run(fmt, packed, N, K, weights.to_device(x, DEV), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_np(y)
+
+
+def check(m, x):
+    N, K = m.codes.shape
+    ref = oracle.affine_gemv(m.codes, m.scales, m.biases, x, m.group, m.bf16_scales)
+    packed = weights.pack_affine(m, DEV)
+    fmt = pkg.affine_format(m.bits, m.group, m.bf16_scales)
+    assert packed.numel() == pkg.packed_bytes(fmt, N, K)
+    what = "bits=%d g=%d bf16=%d N=%d K=%d" % (m.bits, m.group, m.bf16_scales, N, K)
+    assert_f32_close(run(m, packed, x, pkg.OUT_F32), ref, what=what + " f32")
+    assert_bf16_close(run(m, packed, x, pkg.OUT_BF16), ref, what=what + " bf16")
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("group", (32, 64, 128))
+@pytest.mark.parametrize("bf16", (False, True))
+def test_affine_gemv(bits, group, bf16):
+    """Every member of the family; 100 rows (ragged last rowblock), K = 1536
+    (3 batches of 4 tiles)."""
+    m = synth.affine_matrix(120, 100, 1536, bits, group, bf16)
+    check(m, synth.activations(121, 1, 1536)[0])
+
+
+# partial tiles (K = 96: three groups of 32; K = 320), one row, more than
+# 32 rowblocks per workgroup, K at its maximum
+@pytest.mark.parametrize("bits,group,N,K", [(3, 32, 40, 96), (5, 64, 17, 320), (2, 32, 1, 32),
+                                            (6, 128, 3000, 256), (8, 64, 33, 24576),
+                                            (4, 128, 70, 24576)])
+def test_affine_gemv_shapes(bits, group, N, K):
+    note("affine bits=%d g=%d N=%d K=%d" % (bits, group, N, K))
+    m = synth.affine_matrix(122, N, K, bits, group, bits % 2 == 1)
+    check(m, synth.activations(123, 1, K)[0])
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_affine_extreme_codes_onehot(bits):
+    """Codes 0 and 2^bits - 1; a one-hot x returns scale * code + bias of the
+    column, rounded once to fp32."""
+    N, K, g = 32, 256, 64
+    m = synth.affine_matrix(124, N, K, bits, g, False)
+    m.codes[0, :] = (1 << bits) - 1
+    m.codes[1, :] = 0
+    m.codes[2, ::2] = (1 << bits) - 1
+    packed = weights.pack_affine(m, DEV)
+    for k in (0, 1, 63, 64, 255):
+        x = synth.f32_to_bf16_bits(np.eye(1, K, k, dtype=np.float32)[0])
+        ref = oracle.affine_gemv(m.codes, m.scales, m.biases, x, g, False)
+        got = run(m, packed, x, pkg.OUT_F32)
+        assert np.array_equal(got, ref.astype(np.float32)), (bits, k)
+
+
+def test_affine_4bit_matches_q4_path():
+    """AFFINE(4, 64, fp16) and QG_FMT_Q4_ASYM_G64 are the same weights in two
+    packed layouts and kernels: both agree with the oracle on the 4096 x 4096
+    workload."""
+    q = synth.q4_matrix(0, 4096, 4096)
+    x = synth.activations(0, 1, 4096)[0]
+    words = q.codes.astype(np.uint64)
+    codes = np.stack([(words >> (4 * i)) & 0xF for i in range(8)], axis=-1)
+    m = synth.AffineMatrix(codes.reshape(4096, 4096).astype(np.uint8), q.scales, q.biases, 4, 64,
+                           False)
+    ref = oracle.q4_gemm(q.codes, q.scales, q.biases, x[None])[0]
+    got = run(m, weights.pack_affine(m, DEV), x, pkg.OUT_F32)
+    assert_f32_close(got, ref, what="affine 4-bit")
+    y4 = to_np(pkg.qgemv_run(pkg.FMT_Q4_ASYM_G64, weights.pack_q4(q, DEV), 4096, 4096,
+                             weights.to_device(x, DEV), out_dtype=pkg.OUT_F32))
+    assert_f32_close(y4, ref, what="q4 path")

@@ -359,6 +359,69 @@ def test_q8row_closed_forms():
     assert np.allclose(y, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
 
 
+def _affine_example(name):
+    """(codes, scales, biases, group, bf16) of the worked example `name`."""
+    k = np.arange(128)
+    if name == "A":
+        return ((k[:32] % 8)[None].astype(np.uint8), np.array([[0x3F00]], np.uint16),
+                np.array([[0xBF80]], np.uint16), 32, True)
+    if name == "B":
+        c = np.zeros((1, 32), np.uint8)
+        c[0, 0], c[0, 1] = 255, 128
+        return c, np.array([[0x3C00]], np.uint16), np.array([[0x3E80]], np.uint16), 32, True
+    if name == "C":
+        c = np.where(k < 64, 3, 1)[None].astype(np.uint8)
+        return (c, np.array([[0x3C00, 0x4000]], np.uint16), np.array([[0x0000, 0xB800]], np.uint16),
+                64, False)
+    c = (63 - (k % 64))[None].astype(np.uint8)
+    return c, np.array([[0x3000]], np.uint16), np.array([[0x3C00]], np.uint16), 128, False
+
+
+def test_affine_worked_examples():
+    for _, name, kind, idx, expect in golden_lines("affine_worked_example.txt"):
+        codes, sc, bi, g, bf = _affine_example(name)
+        K = codes.shape[1]
+        x = ones_bf16(K) if kind == "ones" else onehot_bf16(K, int(idx))
+        assert oracle.affine_gemv(codes, sc, bi, x, g, bf)[0] == float(expect), (name, kind)
+
+
+def test_affine_4bit_g64_equals_q4():
+    """The affine family at 4 bits, group 64, fp16 is the Q4 format: the same
+    matrix through both oracles (one code per byte against eight nibbles per
+    word) gives the same result bit for bit."""
+    m = synth.q4_matrix(33, 24, 256)
+    x = synth.activations(34, 1, 256)
+    words = m.codes.astype(np.uint64)
+    codes = np.stack([(words >> (4 * i)) & 0xF for i in range(8)], axis=-1)
+    codes = codes.reshape(24, 256).astype(np.uint8)
+    y4 = oracle.q4_gemm(m.codes, m.scales, m.biases, x)[0]
+    ya = oracle.affine_gemv(codes, m.scales, m.biases, x[0], 64, False)
+    assert np.array_equal(ya, y4)
+
+
+@pytest.mark.parametrize("bits,group,bf16", [(2, 32, False), (3, 128, True), (5, 64, False),
+                                             (6, 32, True), (8, 128, False)])
+def test_affine_closed_forms(bits, group, bf16):
+    """One-hot x returns scale * code + bias of that column exactly; the
+    result equals the numpy product of the dequantized matrix; codes at
+    2^bits - 1 are taken whole."""
+    N, K = 5, 256
+    m = synth.affine_matrix(35, N, K, bits, group, bf16)
+    m.codes[0, :] = (1 << bits) - 1
+    dec = ((lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)) if bf16
+           else (lambda b: b.view(np.float16).astype(np.float64)))
+    s = np.repeat(dec(m.scales), group, axis=1)
+    b = np.repeat(dec(m.biases), group, axis=1)
+    W = s * m.codes + b
+    for k in (0, 31, 32, 255):
+        y = oracle.affine_gemv(m.codes, m.scales, m.biases, onehot_bf16(K, k), group, bf16)
+        assert np.array_equal(y, W[:, k])
+    x = synth.activations(36, 1, K)[0]
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    y = oracle.affine_gemv(m.codes, m.scales, m.biases, x, group, bf16)
+    assert np.allclose(y, W @ xf, rtol=1e-12, atol=1e-12 * np.abs(W @ xf).max())
+
+
 def test_silu_matches_torch():
     a = np.linspace(-30, 30, 601)
     ref = torch.nn.functional.silu(torch.from_numpy(a)).numpy()
