@@ -14,7 +14,7 @@
 // range and streams its batches (4 consecutive 128-k tiles of one rowblock)
 // double-buffered: the load of each tile of the next batch is issued just
 // before the arithmetic of the same tile of the current batch.  The 16 x M
-// results of 6 (2) rowblocks stay in the wave's registers and are stored
+// results of 6 (4) rowblocks stay in the wave's registers and are stored
 // together; when K spans several segments those are the rowblocks whose
 // sums the wave keeps across the segments.  Every rowblock accumulates its
 // tiles in K order within one wave, so single and grouped launches give
@@ -33,7 +33,7 @@ struct SsCfg {
     static constexpr int WAVES = MT == 1 ? 16 : 12;
     static constexpr int THREADS = WAVES * 64;
     // rowblocks whose results a wave keeps in registers (stored together)
-    static constexpr int R = MT == 1 ? 6 : 2;
+    static constexpr int R = MT == 1 ? 6 : 4;
     static constexpr int MP = 16 * MT;               // padded activation rows
     static constexpr int SEGK = 32 / MT;             // tiles per staged segment
     static constexpr int RS = SEGK * 128 + 8;        // LDS row stride in bf16 (16-byte pad)
