@@ -7,16 +7,17 @@
 // becomes the bf16x8 MFMA operand (128 + q); one v_mfma_f32_16x16x32_bf16
 // pair covers one group of 64 and acc += s * C + (b - 128 s) * sum_g X.
 //
-// Work split.  One workgroup per CU (16 waves; 12 for 32 rows) holds a
+// Work split.  One workgroup per CU (16 waves; 8 for 32 rows) holds a
 // whole 4096-k slice of X (16 rows; 2048 k for 32 rows) in LDS, 128 KB, with
 // the per-(group, row) sums of X, so X is staged once per matrix and
-// segment.  Each wave owns every 16th (12th) rowblock of the workgroup's
-// range and streams its batches (4 consecutive 128-k tiles of one rowblock)
-// double-buffered: the load of each tile of the next batch is issued just
-// before the arithmetic of the same tile of the current batch.  The 16 x M
-// results of 6 (4) rowblocks stay in the wave's registers and are stored
-// together; when K spans several segments those are the rowblocks whose
-// sums the wave keeps across the segments.  Every rowblock accumulates its
+// segment.  Each wave owns every 16th (8th) rowblock of the workgroup's
+// range and streams its batches (4 consecutive 128-k tiles of one rowblock;
+// at 32 rows 2 tiles of each of two rowblocks, see pair mode) double-
+// buffered: the load of each tile of the next batch is issued just before
+// the arithmetic of the same tile of the current batch.  The 16 x M results
+// of 6 rowblocks stay in the wave's registers and are stored together; when
+// K spans several segments those are the rowblocks whose sums the wave
+// keeps across the segments.  Every rowblock accumulates its
 // tiles in K order within one wave, so single and grouped launches give
 // identical results.  Tiles past the end of K re-read the
 // last tile; X and its sums are staged as zero there, so they add exactly
@@ -30,10 +31,12 @@ constexpr int SS_TPB = 4;  // tiles per batch
 template <int MT>
 struct SsCfg {
     // waves per workgroup: the most whose registers fit without real spills
-    static constexpr int WAVES = MT == 1 ? 16 : 12;
+    static constexpr int WAVES = MT == 1 ? 16 : 8;
     static constexpr int THREADS = WAVES * 64;
     // rowblocks whose results a wave keeps in registers (stored together)
-    static constexpr int R = MT == 1 ? 6 : 4;
+    static constexpr int R = MT == 1 ? 6 : 6;
+    // two rowblocks per wave at a time (see pair mode below)
+    static constexpr bool PAIR = MT == 2;
     static constexpr int MP = 16 * MT;               // padded activation rows
     static constexpr int SEGK = 32 / MT;             // tiles per staged segment
     static constexpr int RS = SEGK * 128 + 8;        // LDS row stride in bf16 (16-byte pad)
@@ -240,6 +243,148 @@ __device__ __forceinline__ void ss_block(SsBatch &A, SsBatch &B, const WorkItem 
     }
 }
 
+// ---- pair mode (32 rows) ----
+// At 32 rows the tile arithmetic reads 2 x 4 activation pieces and 2 x 2 row
+// sums from LDS per lane, 12 KB per wave and tile, about what a CU's LDS
+// delivers while HBM delivers the tile.  So a wave works on two of its
+// rowblocks at once: a batch is 2 tiles of each, and every activation read
+// feeds both rowblocks.
+
+// One tile (index pl of the staged segment) of rowblocks a and b.
+template <int MT>
+__device__ __forceinline__ void ss_tile2(u32x4_t ca, u32x2_t sba, u32x4_t cb, u32x2_t sbb,
+                                         const uint16_t *xl, const float *xs, int pl, int lane,
+                                         const Q4Consts &kq, f32x4_t acc_a[MT],
+                                         f32x4_t acc_b[MT]) {
+    typedef SsCfg<MT> C;
+    const int kg = lane >> 4, r16 = lane & 15;
+    bf16x8_t Ba[4], Bb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        Ba[q] = q4_word_to_bf16x8(ca[q], kq);
+        Bb[q] = q4_word_to_bf16x8(cb[q], kq);
+    }
+    const float sa0 = f16_lo(sba[0]), sa1 = f16_lo(sba[1]);
+    const float ba0 = fmaf(-128.f, sa0, f16_hi(sba[0])), ba1 = fmaf(-128.f, sa1, f16_hi(sba[1]));
+    const float sb0 = f16_lo(sbb[0]), sb1 = f16_lo(sbb[1]);
+    const float bb0 = fmaf(-128.f, sb0, f16_hi(sbb[0])), bb1 = fmaf(-128.f, sb1, f16_hi(sbb[1]));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const uint16_t *ar = xl + (16 * mt + r16) * C::RS + pl * 128 + 8 * kg;
+        bf16x8_t A[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) A[q] = *reinterpret_cast<const bf16x8_t *>(ar + 32 * q);
+        const f32x4_t xs0 = *reinterpret_cast<const f32x4_t *>(xs + (2 * pl) * C::MP + 16 * mt + 4 * kg);
+        const f32x4_t xs1 = *reinterpret_cast<const f32x4_t *>(xs + (2 * pl + 1) * C::MP + 16 * mt + 4 * kg);
+        const f32x4_t Z = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t Ca0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], Ba[0], Z, 0, 0, 0);
+        f32x4_t Cb0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], Bb[0], Z, 0, 0, 0);
+        f32x4_t Ca1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], Ba[2], Z, 0, 0, 0);
+        f32x4_t Cb1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], Bb[2], Z, 0, 0, 0);
+        Ca0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], Ba[1], Ca0, 0, 0, 0);
+        Cb0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], Bb[1], Cb0, 0, 0, 0);
+        Ca1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], Ba[3], Ca1, 0, 0, 0);
+        Cb1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], Bb[3], Cb1, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float a = acc_a[mt][e];
+            a = fmaf(sa0, Ca0[e], a);
+            a = fmaf(ba0, xs0[e], a);
+            a = fmaf(sa1, Ca1[e], a);
+            a = fmaf(ba1, xs1[e], a);
+            acc_a[mt][e] = a;
+            float b = acc_b[mt][e];
+            b = fmaf(sb0, Cb0[e], b);
+            b = fmaf(bb0, xs0[e], b);
+            b = fmaf(sb1, Cb1[e], b);
+            b = fmaf(bb1, xs1[e], b);
+            acc_b[mt][e] = b;
+        }
+    }
+}
+
+// Issue tile j's loads of the next batch (tiles nb0, nb0 + 1 of rowblocks a
+// and b into N: slots j and 2 + j), then tile j's arithmetic of batch B.
+template <int MT>
+__device__ __forceinline__ void sp_step(SsBatch &N, __amdgpu_buffer_rsrc_t ra,
+                                        __amdgpu_buffer_rsrc_t rb, int nb0, int pn,
+                                        const SsBatch &B, int pl0, const uint16_t *xl,
+                                        const float *xs, int lane, const Q4Consts &kq,
+                                        f32x4_t acc_a[MT], f32x4_t acc_b[MT]) {
+    const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned to = (unsigned)min(nb0 + j, pn - 1) * Q4_TILE_BYTES;
+        N.c[j] = buf_ld_x4(ra, lc, to);
+        N.sb[j] = buf_ld_x2(ra, ls, to);
+        N.c[2 + j] = buf_ld_x4(rb, lc, to);
+        N.sb[2 + j] = buf_ld_x2(rb, ls, to);
+        __builtin_amdgcn_sched_barrier(0);
+        ss_tile2<MT>(B.c[j], B.sb[j], B.c[2 + j], B.sb[2 + j], xl, xs, pl0 + j, lane, kq, acc_a,
+                     acc_b);
+    }
+}
+
+// The first batch (tiles 0, 1 of the segment) of rowblocks a and b.
+__device__ __forceinline__ void sp_first(SsBatch &A, const WorkItem &it, int rba, int rbb,
+                                         int pbase, int pn, bool va, bool vb, int lane) {
+    const __amdgpu_buffer_rsrc_t ra = ss_rsrc(it, rba, pbase, pn, va);
+    const __amdgpu_buffer_rsrc_t rb = ss_rsrc(it, rbb, pbase, pn, vb);
+    const unsigned lc = 16u * lane, ls = 1024u + 8u * (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const unsigned to = (unsigned)min(j, pn - 1) * Q4_TILE_BYTES;
+        A.c[j] = buf_ld_x4(ra, lc, to);
+        A.sb[j] = buf_ld_x2(ra, ls, to);
+        A.c[2 + j] = buf_ld_x4(rb, lc, to);
+        A.sb[2 + j] = buf_ld_x2(rb, ls, to);
+    }
+}
+
+// This wave's rowblocks i0 .. i0 + n - 1 (n <= R, R even) in pairs; the
+// wave's rowblock i is first + WAVES * i and exists while i < mine.  A holds
+// the first batch of the pair (i0, i0 + 1) on entry; the last step of a pair
+// loads the next pair's first batch: the next pair of the block, or, when
+// `cross`, the first pair of the next block.  Pairs past the wave's rowblocks
+// read through empty buffers (zero) and are not stored.
+template <int MT, int R>
+__device__ __forceinline__ void ss_block_pair(SsBatch &A, SsBatch &B, const WorkItem &it,
+                                              int first, int i0, int n, int mine, bool cross,
+                                              int pbase, int pn, const uint16_t *xl,
+                                              const float *xs, int lane, const Q4Consts &kq,
+                                              f32x4_t acc[R][MT]) {
+    typedef SsCfg<MT> C;
+    static_assert(R % 2 == 0, "pairs");
+    const int nb = (pn + 1) / 2, nbe = nb + (nb & 1);  // batches of 2 tiles, even count
+#pragma unroll
+    for (int p = 0; p < R / 2; ++p) {
+        if (2 * p >= n) break;  // uniform
+        const int ia = i0 + 2 * p;
+        const int rba = first + C::WAVES * ia, rbb = rba + C::WAVES;
+        const bool vb = 2 * p + 1 < n;
+        const bool inblock = 2 * p + 2 < n;
+        const int ina = ia + 2;
+        const bool vna = (inblock || cross) && ina < mine;
+        const bool vnb = inblock ? (2 * p + 3 < n) : (cross && ina + 1 < mine);
+        const int rbna = first + C::WAVES * ina, rbnb = rbna + C::WAVES;
+#pragma unroll 1
+        for (int b = 0; b < nbe; b += 2) {
+            sp_step<MT>(B, ss_rsrc(it, rba, pbase, pn, b + 1 < nb),
+                        ss_rsrc(it, rbb, pbase, pn, vb && b + 1 < nb), 2 * (b + 1), pn, A, 2 * b,
+                        xl, xs, lane, kq, acc[2 * p], acc[2 * p + 1]);
+            const bool more = b + 2 < nbe;
+            sp_step<MT>(A,
+                        more ? ss_rsrc(it, rba, pbase, pn, b + 2 < nb)
+                             : ss_rsrc(it, rbna, pbase, pn, vna),
+                        more ? ss_rsrc(it, rbb, pbase, pn, vb && b + 2 < nb)
+                             : ss_rsrc(it, rbnb, pbase, pn, vnb),
+                        more ? 2 * (b + 2) : 0, pn, B, 2 * (b + 1), xl, xs, lane, kq,
+                        acc[2 * p], acc[2 * p + 1]);
+        }
+    }
+}
+
 template <int MT>
 __device__ __forceinline__ void ss_zero_block(f32x4_t acc[SsCfg<MT>::R][MT]) {
 #pragma unroll
@@ -266,14 +411,22 @@ __device__ __forceinline__ void ss_range(const WorkItem &it, int u0, int u1, int
         // all of its rowblocks without a barrier
         const int pn = it.P, nbe = ss_batches_even(pn);
         const int mine = (u1 - u0 > wave) ? (u1 - u0 - wave + C::WAVES - 1) / C::WAVES : 0;
-        ss_first(A, it, first, 0, pn, mine > 0, lane);
+        if constexpr (C::PAIR)
+            sp_first(A, it, first, first + C::WAVES, 0, pn, mine > 0, mine > 1, lane);
+        else
+            ss_first(A, it, first, 0, pn, mine > 0, lane);
         __syncthreads();  // nobody still reads the previous range's X
         ss_stage<MT>(X, M, it.K, 0, nbe * SS_TPB, xl, xs, tid);
 #pragma unroll 1
         for (int i0 = 0; i0 < mine; i0 += R) {
             const int n = min(R, mine - i0);
             ss_zero_block<MT>(acc);
-            ss_block<MT, R>(A, B, it, first, i0, n, i0 + n < mine, 0, pn, xl, xs, lane, kq, acc);
+            if constexpr (C::PAIR)
+                ss_block_pair<MT, R>(A, B, it, first, i0, n, mine, true, 0, pn, xl, xs, lane, kq,
+                                     acc);
+            else
+                ss_block<MT, R>(A, B, it, first, i0, n, i0 + n < mine, 0, pn, xl, xs, lane, kq,
+                                acc);
 #pragma unroll
             for (int r = 0; r < R; ++r)
                 if (r < n) ss_store<MT>(it, first + C::WAVES * (i0 + r), M, acc[r], lane);
@@ -292,10 +445,18 @@ __device__ __forceinline__ void ss_range(const WorkItem &it, int u0, int u1, int
         for (int seg = 0; seg < nseg; ++seg) {
             const int pbase = seg * C::SEGK;
             const int pn = min(C::SEGK, it.P - pbase), nbe = ss_batches_even(pn);
-            ss_first(A, it, first + C::WAVES * i0, pbase, pn, n > 0, lane);
+            if constexpr (C::PAIR)
+                sp_first(A, it, first + C::WAVES * i0, first + C::WAVES * (i0 + 1), pbase, pn,
+                         n > 0, n > 1, lane);
+            else
+                ss_first(A, it, first + C::WAVES * i0, pbase, pn, n > 0, lane);
             __syncthreads();  // nobody still reads the previous segment of X
             ss_stage<MT>(X, M, it.K, seg, nbe * SS_TPB, xl, xs, tid);
-            ss_block<MT, R>(A, B, it, first, i0, n, false, pbase, pn, xl, xs, lane, kq, acc);
+            if constexpr (C::PAIR)
+                ss_block_pair<MT, R>(A, B, it, first, i0, n, i0 + n, false, pbase, pn, xl, xs,
+                                     lane, kq, acc);
+            else
+                ss_block<MT, R>(A, B, it, first, i0, n, false, pbase, pn, xl, xs, lane, kq, acc);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r)
