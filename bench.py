@@ -643,15 +643,26 @@ def main():
                 lambda: _lib.qgemv_run(fa, apacked, NA, KA, ax, y=ay), 8)
             ba = roofline.affine_gemv_bytes(bits, GA, NA, KA)
             fla = plain_read_us(int(ba))
+            # the same matrix against a 16-row activation tile (verification form)
+            aX = weights.to_device(synth.activations(args.seed, 16, KA), "cuda")
+            aY = torch.empty(16, NA, dtype=torch.bfloat16, device="cuda")
+            ms16 = workloads.time_graph_ms(
+                lambda: _lib.qgemm_skinny_run(fa, apacked, 16, NA, KA, aX, Y=aY), 8)
+            b16 = roofline.affine_gemv_bytes(bits, GA, NA, KA) + 2.0 * 16 * KA + 2.0 * 16 * NA - 2.0 * KA - 2.0 * NA
+            fl16 = plain_read_us(int(b16))
             rows.append({"bits": bits, "us": round(msa * 1e3, 2), "GBs": round(ba / (msa * 1e-3) / 1e9, 1),
                          "pct_of_peak": round(100 * ba / (msa * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1),
-                         "pct_of_plain_read": round(100 * fla / (msa * 1e3), 1)})
-            log("affine %d-bit g%d: %.2f us" % (bits, GA, msa * 1e3))
-            del apacked
+                         "pct_of_plain_read": round(100 * fla / (msa * 1e3), 1),
+                         "m16_us": round(ms16 * 1e3, 2),
+                         "m16_GBs": round(b16 / (ms16 * 1e-3) / 1e9, 1),
+                         "m16_pct_of_plain_read": round(100 * fl16 / (ms16 * 1e3), 1)})
+            log("affine %d-bit g%d: %.2f us, M=16 %.2f us" % (bits, GA, msa * 1e3, ms16 * 1e3))
+            del apacked, aX, aY
         result["affine_family"] = {
             "workload": "affine weights (scale * code + bias per group of 64, fp16), one GEMV "
-                        "8192->262144 per code width, codes uniform, M=1; calls captured in a "
-                        "HIP graph", "rows": rows}
+                        "8192->262144 per code width, codes uniform, M=1, and the same matrix "
+                        "against a 16-row bf16 tile (m16_*); calls captured in a HIP graph",
+            "rows": rows}
 
         # MXFP4 routed experts, one token through one layer
         moe = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16)

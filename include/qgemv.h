@@ -31,7 +31,7 @@
  *    lists its widths): unsigned codes of 2, 3, 4, 5, 6 or 8 bits, groups of
  *    32, 64 or 128 consecutive k, one scale and one bias per group in fp16
  *    (bf16_scales = 0) or bf16 (1); weight = scale * code + bias.  Decode
- *    GEMV (qgemv_run) only.
+ *    GEMV (qgemv_run) and skinny product (qgemm_skinny_run).
  *  - QG_FMT_Q8_ROW: int8 codes (the full range -128..127) with one fp32 scale
  *    per output row, weight = scale[n] * code, against bf16 activations:
  *    weight-only int8 as in the Deltafin page's resident int8 spine and packed
@@ -172,8 +172,10 @@ int qgemv_run(int fmt, const void *packed, size_t packed_bytes, int64_t N,
  *               QG_FMT_Q8_SYM_G32: X is int8 [M][K] (from hadamard32_quant_run,
  *               so the weights must already be in the rotated basis) and
  *               x_scales fp32 [M] is the per-row activation scale.
- *               Other formats -> QG_EUNSUPPORTED (MXFP4, Q8_ROW and the
- *               affine family are decode GEMVs: qgemv_run).
+ *               An affine-family code: X is bf16 [M][K], x_scales must be
+ *               NULL (M = 1 runs the decode GEMV).
+ *               Other formats -> QG_EUNSUPPORTED (MXFP4 and Q8_ROW are
+ *               decode GEMVs: qgemv_run).
  *  packed, packed_bytes   from qgemv_pack with the same (fmt, N, K); 16-B.
  *  M            0..32.
  *  X            device [M][K], rows contiguous, 16-B.  Read only.

@@ -229,6 +229,14 @@ def affine_gemv(codes, scales, biases, x, group: int, bf16_scales: bool):
     return y
 
 
+def affine_gemm(codes, scales, biases, X, group: int, bf16_scales: bool):
+    """Y [M, N] (float64): the affine-family product for each row of X (bf16
+    bits [M, K]), row by row through ``affine_gemv``."""
+    X = np.asarray(X, dtype=np.uint16)
+    return np.stack([affine_gemv(codes, scales, biases, X[m], group, bf16_scales)
+                     for m in range(X.shape[0])])
+
+
 def moe(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales, x, ids, w):
     """y [H] (float64) for one token through the routed experts.
 

@@ -9,27 +9,22 @@
 // qg_internal.h) with the two codes of a pair in the two 16-bit halves of a
 // word, so one shift and one and-or per plane give a pair of small integers,
 // and or-ing in 0x4300 makes each half the exact bf16 value 128 + q (q < 128).
-// v_dot2_f32_bf16 accumulates (128 + q) x over a lane's 32 codes; the lane's
-// group term is scale * (acc - 128 sum x) + bias * sum x, with sum x over the
-// same 32 k staged once.  8-bit codes do not fit 128 + q in bf16: their two
-// nibble planes run as two dot chains, D = D_lo + 16 D_hi.
+// A lane's 32 codes are four runs of 8 consecutive k, one per 32-k block of
+// the tile.  The GEMV accumulates (128 + q) x over a run with
+// v_dot2_f32_bf16, and per group adds scale * (acc - 128 sum x) + bias * sum
+// x, with sum x over the lane's k of that group staged once.  8-bit codes do
+// not fit 128 + q in bf16: their two nibble planes run as two dot chains,
+// D = D_lo + 16 D_hi.  The skinny product (M <= 32 rows) takes each run as
+// the B operand of one v_mfma_f32_16x16x32_bf16 step (the 64 lanes' runs i
+// make up the 32-k block i) against X staged in LDS, and applies the group's
+// scale and bias to the step sums.
 //
 // Work split as in the other streaming GEMVs: contiguous ranges of rowblocks
 // per workgroup, batches of 4 tiles round-robin over 4 waves, double-buffered,
 // wave sums folded in LDS and added in wave order per block of 32 rowblocks.
-#include "qg_internal.h"
+#include "affine_tile.h"
 
 namespace qg {
-
-// ------------------------------------------------------------ plane layout
-template <int BITS>
-struct AffPlanes;
-template <> struct AffPlanes<2> { static constexpr int NP = 1, W0 = 2, W1 = 0, O1 = 0; };
-template <> struct AffPlanes<3> { static constexpr int NP = 2, W0 = 2, W1 = 1, O1 = 2; };
-template <> struct AffPlanes<4> { static constexpr int NP = 1, W0 = 4, W1 = 0, O1 = 0; };
-template <> struct AffPlanes<5> { static constexpr int NP = 2, W0 = 4, W1 = 1, O1 = 4; };
-template <> struct AffPlanes<6> { static constexpr int NP = 2, W0 = 4, W1 = 2, O1 = 4; };
-template <> struct AffPlanes<8> { static constexpr int NP = 2, W0 = 4, W1 = 4, O1 = 4; };
 
 struct PlaneSpec {
     int np, w[2], o[2];
@@ -70,9 +65,13 @@ pack_affine_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict
     if (sub < 64) {
         const int l = sub;
         const int64_t n = rb * RB + (l & 15);
-        const int64_t k0 = p * AFF_TILE_K + 32 * (l >> 4);
+        // code 8i + t of the lane is k = 32i + 8(l >> 4) + t of the tile
+        const int64_t kt = p * AFF_TILE_K;
         uint8_t c[32];
-        for (int i = 0; i < 32; ++i) c[i] = (n < N && k0 < K) ? codes[n * K + k0 + i] : 0;
+        for (int i = 0; i < 32; ++i) {
+            const int64_t k = kt + 32 * (i >> 3) + 8 * (l >> 4) + (i & 7);
+            c[i] = (n < N && k < K) ? codes[n * K + k] : 0;
+        }
         const PlaneSpec ps = plane_spec(bits);
         size_t off = 0;
         for (int q = 0; q < ps.np; ++q) {
@@ -116,87 +115,40 @@ constexpr int AG_THREADS = AG_WAVES * 64;
 constexpr int AG_TPB = 4;    // tiles per batch
 constexpr int AG_RMAX = 32;  // rowblocks per output block
 
-__device__ __forceinline__ unsigned buf_ld_x1(__amdgpu_buffer_rsrc_t r, unsigned voff,
-                                              unsigned soff) {
-    return (unsigned)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 2);
-}
-
-template <int W>
-__device__ __forceinline__ void ag_ld(unsigned (&d)[W], __amdgpu_buffer_rsrc_t r, unsigned voff,
-                                      unsigned soff) {
-    if constexpr (W == 4) {
-        const u32x4_t v = buf_ld_x4(r, voff, soff);
-        d[0] = v[0], d[1] = v[1], d[2] = v[2], d[3] = v[3];
-    } else if constexpr (W == 2) {
-        const u32x2_t v = buf_ld_x2(r, voff, soff);
-        d[0] = v[0], d[1] = v[1];
-    } else {
-        d[0] = buf_ld_x1(r, voff, soff);
-    }
-}
-
-template <int BITS>
+template <int BITS, int GPT>
 struct AgBatch {
-    typedef AffPlanes<BITS> PL;
-    unsigned p0[AG_TPB][PL::W0];
-    unsigned p1[AG_TPB][PL::NP == 2 ? PL::W1 : 1];
-    unsigned sb[AG_TPB];
+    AgTile<BITS, GPT> t[AG_TPB];
 };
 
-// Tile tp (clamped to the last of pn) into slot j: this lane's plane words
-// and its group's (scale, bias) word at soff_sb.
-template <int BITS>
-__device__ __forceinline__ void ag_tile_load(AgBatch<BITS> &B, int j, __amdgpu_buffer_rsrc_t rs,
-                                             int tp, int pn, unsigned tb, unsigned soff_sb,
-                                             int lane) {
-    typedef AffPlanes<BITS> PL;
-    const unsigned to = (unsigned)min(tp, pn - 1) * tb;
-    ag_ld<PL::W0>(B.p0[j], rs, 4u * PL::W0 * lane, to);
-    if constexpr (PL::NP == 2) ag_ld<PL::W1>(B.p1[j], rs, 256u * PL::W0 + 4u * PL::W1 * lane, to);
-    B.sb[j] = buf_ld_x1(rs, soff_sb, to);
-}
-
-// Pair j of plane (W, words p) as two small integers in the word's halves.
-template <int W, int NW>
-__device__ __forceinline__ unsigned ag_pair(const unsigned (&p)[NW], int j) {
-    constexpr int PER = 16 / W;
-    constexpr unsigned M = ((1u << W) - 1u) * 0x00010001u;
-    return (p[j / PER] >> (W * (j % PER))) & M;
-}
-
-// One tile: xw = the lane's 16 bf16 pairs of x, xs = their sum.
-template <int BITS, bool BF16S>
-__device__ __forceinline__ float ag_tile(const AgBatch<BITS> &B, int j, const uint4 *xw, float xs,
-                                         float y) {
-    typedef AffPlanes<BITS> PL;
-    constexpr unsigned MAGIC = 0x43004300u;  // bf16 128 in both halves
-    float a0 = 0.f, a1 = 0.f;
+// One tile: xrun = the lane's x of run 0 (run i at xrun + 32 i, 8 bf16),
+// xg = the sums of the lane's x over each of the tile's GPT groups.  One dot
+// chain per group; returns y plus the lane's share of the tile.
+template <int BITS, int GPT, bool BF16S>
+__device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint16_t *xrun,
+                                         const float *xg, float y) {
+    constexpr int CPG = 4 / GPT;  // runs per group
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint4 xv = xw[q];
-        const unsigned xp[4] = {xv.x, xv.y, xv.z, xv.w};
+    for (int t = 0; t < GPT; ++t) {
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int pj = 4 * q + h;
-            const unsigned v0 = ag_pair<PL::W0>(B.p0[j], pj);
-            if constexpr (BITS == 8) {
-                const unsigned v1 = ag_pair<PL::W1>(B.p1[j], pj);
-                a0 = dot2_bf16(v0 | MAGIC, xp[h], a0);
-                a1 = dot2_bf16(v1 | MAGIC, xp[h], a1);
-            } else if constexpr (PL::NP == 2) {
-                const unsigned v1 = ag_pair<PL::W1>(B.p1[j], pj);
-                a0 = dot2_bf16((v1 << PL::O1) | v0 | MAGIC, xp[h], a0);
-            } else {
-                a0 = dot2_bf16(v0 | MAGIC, xp[h], a0);
+        for (int c = 0; c < CPG; ++c) {
+            const int i = t * CPG + c;
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xrun + 32 * i);
+            const unsigned xp[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                a0 = dot2_bf16(ag_bf16_pair<BITS, GPT>(T, 4 * i + h), xp[h], a0);
+                if constexpr (BITS == 8)
+                    a1 = dot2_bf16(ag_pair_hi<BITS, GPT>(T, 4 * i + h), xp[h], a1);
             }
         }
+        const float X = xg[t];
+        float D = fmaf(-128.f, X, a0);
+        if constexpr (BITS == 8) D = fmaf(16.f, fmaf(-128.f, X, a1), D);
+        const unsigned sb = T.sb[t];
+        y = fmaf(ag_scale(sb, BF16S), D, fmaf(ag_bias(sb, BF16S), X, y));
     }
-    float D = fmaf(-128.f, xs, a0);
-    if constexpr (BITS == 8) D = fmaf(16.f, fmaf(-128.f, xs, a1), D);
-    const unsigned sb = B.sb[j];
-    const float sc = BF16S ? bf16_lo(sb) : f16_lo(sb);
-    const float bi = BF16S ? bf16_hi(sb) : f16_hi(sb);
-    return fmaf(sc, D, fmaf(bi, xs, y));
+    return y;
 }
 
 __device__ __forceinline__ float ag_reduce_kslices(float a) {
@@ -205,47 +157,50 @@ __device__ __forceinline__ float ag_reduce_kslices(float a) {
     return a;
 }
 
-template <int BITS, bool BF16S>
+template <int BITS, int GPT, bool BF16S>
 __global__ void __launch_bounds__(AG_THREADS, 4)
 affine_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restrict__ x,
-                   void *__restrict__ y, int N, int K, int P, int nrb, int group, int out_f32) {
+                   void *__restrict__ y, int N, int K, int P, int nrb, int out_f32) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int nb = (P + AG_TPB - 1) / AG_TPB;
     const int KS = nb * AG_TPB * AFF_TILE_K;  // staged x length (zero past K)
     uint16_t *xl = reinterpret_cast<uint16_t *>(smem);                  // [KS] bf16
-    float *xsl = reinterpret_cast<float *>(smem + (size_t)KS * 2);       // [KS / 32]
-    float *part = xsl + KS / 32;                                         // [RMAX][WAVES][16]
+    float *xsl = reinterpret_cast<float *>(smem + (size_t)KS * 2);       // [KS / 32 * GPT]
+    float *part = xsl + KS / 32 * GPT;                                   // [RMAX][WAVES][16]
     const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t G = gridDim.x, jb = blockIdx.x;
     const int u0 = (int)(jb * nrb / G), u1 = (int)((jb + 1) * nrb / G);
     if (u0 >= u1) return;
-    const unsigned tb = (unsigned)affine_tile_bytes(BITS, group);
+    const unsigned tb = (unsigned)affine_tile_bytes(BITS, AFF_TILE_K / GPT);
     const size_t rb_bytes = (size_t)P * tb;
-    const int gpt = AFF_TILE_K / group;
-    const unsigned soff_sb = 256u * BITS + 4u * ((lane & 15) * gpt + (32 * kg) / group);
-    // stage x and the sum of each run of 32 (in k order)
-    for (int i = tid; i < KS / 8; i += AG_THREADS) {
+    // stage x, then the sum of each lane-group's x over each group of each
+    // tile (its runs in k order, each run's 8 values in a fixed tree):
+    // xsl[(4 tp + kg) GPT + t]
+    for (int c = tid; c < KS / 8; c += AG_THREADS) {
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (8 * i < K) v = reinterpret_cast<const uint4 *>(x)[i];
-        reinterpret_cast<uint4 *>(xl)[i] = v;
+        if (8 * c < K) v = reinterpret_cast<const uint4 *>(x)[c];
+        reinterpret_cast<uint4 *>(xl)[c] = v;
     }
     __syncthreads();
-    for (int c = tid; c < KS / 32; c += AG_THREADS) {
-        float s = 0.f;
-        const unsigned *w = reinterpret_cast<const unsigned *>(xl + 32 * c);
-        for (int i = 0; i < 16; ++i) {
-            s += bf16_lo(w[i]);
-            s += bf16_hi(w[i]);
+    for (int e = tid; e < KS / 32 * GPT; e += AG_THREADS) {
+        const int t = e % GPT, tk = e / GPT, tp = tk >> 2, ckg = tk & 3;
+        float sum = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4 / GPT; ++c) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(
+                xl + tp * AFF_TILE_K + 32 * (t * (4 / GPT) + c) + 8 * ckg);
+            sum += ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+                   ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
         }
-        xsl[c] = s;
+        xsl[e] = sum;
     }
 #pragma unroll 1
     for (int ub = u0; ub < u1; ub += AG_RMAX) {
         const int nr = min(u1 - ub, AG_RMAX);
         const int T = nr * nb;
         int t = wave, ci = t / nb, cb = t % nb;
-        AgBatch<BITS> A, B;
+        AgBatch<BITS, GPT> A, B;
         float acc = 0.f;
         {
             const __amdgpu_buffer_rsrc_t rs =
@@ -253,7 +208,7 @@ affine_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restric
                           t < T ? (unsigned)rb_bytes : 0u);
 #pragma unroll
             for (int q = 0; q < AG_TPB; ++q)
-                ag_tile_load<BITS>(A, q, rs, cb * AG_TPB + q, P, tb, soff_sb, lane);
+                ag_tile_load<BITS, GPT>(A.t[q], rs, cb * AG_TPB + q, P, tb, lane);
         }
         __syncthreads();  // x staged; the previous block's partial sums are read
         for (int i = tid; i < nr * AG_WAVES * 16; i += AG_THREADS) part[i] = 0.f;
@@ -263,8 +218,8 @@ affine_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restric
             if (t >= T) break;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                AgBatch<BITS> &Cur = half ? B : A;
-                AgBatch<BITS> &Nxt = half ? A : B;
+                AgBatch<BITS, GPT> &Cur = half ? B : A;
+                AgBatch<BITS, GPT> &Nxt = half ? A : B;
                 int ni = ci, nbx = cb + AG_WAVES;
                 while (nbx >= nb) {  // uniform
                     nbx -= nb;
@@ -277,11 +232,11 @@ affine_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restric
 #pragma unroll
                 for (int q = 0; q < AG_TPB; ++q) {
                     __builtin_amdgcn_sched_barrier(0);
-                    ag_tile_load<BITS>(Nxt, q, rs, nbx * AG_TPB + q, P, tb, soff_sb, lane);
+                    ag_tile_load<BITS, GPT>(Nxt.t[q], rs, nbx * AG_TPB + q, P, tb, lane);
                     __builtin_amdgcn_sched_barrier(0);
                     const int tp = cb * AG_TPB + q;
-                    const uint4 *xw = reinterpret_cast<const uint4 *>(xl + tp * AFF_TILE_K) + 4 * kg;
-                    acc = ag_tile<BITS, BF16S>(Cur, q, xw, xsl[tp * 4 + kg], acc);
+                    acc = ag_tile<BITS, GPT, BF16S>(Cur.t[q], xl + tp * AFF_TILE_K + 8 * kg,
+                                                    xsl + (4 * tp + kg) * GPT, acc);
                 }
                 if (!nvalid || ni != ci) {  // the wave's last batch of this rowblock
                     acc = ag_reduce_kslices(acc);
@@ -311,17 +266,21 @@ affine_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restric
     }
 }
 
-template <int BITS, bool BF16S>
+template <int BITS, int GPT>
 static hipError_t launch_ag(const uint8_t *packed, const uint16_t *x, void *y, int64_t N,
-                            int64_t K, int group, bool out_f32, int cus, hipStream_t s) {
+                            int64_t K, bool bf16, bool out_f32, int cus, hipStream_t s) {
     const int P = (int)ceil_div(K, AFF_TILE_K);
     const int nrb = (int)ceil_div(N, RB);
     const int nb = (int)ceil_div(P, AG_TPB);
     const size_t KS = (size_t)nb * AG_TPB * AFF_TILE_K;
-    const size_t lds = KS * 2 + KS / 32 * 4 + (size_t)AG_RMAX * AG_WAVES * 16 * 4;
+    const size_t lds = KS * 2 + KS / 32 * GPT * 4 + (size_t)AG_RMAX * AG_WAVES * 16 * 4;
     const int grid = nrb < cus * 4 ? nrb : cus * 4;
-    hipLaunchKernelGGL((affine_gemv_kernel<BITS, BF16S>), dim3(grid), dim3(AG_THREADS), lds, s,
-                       packed, x, y, (int)N, (int)K, P, nrb, group, out_f32 ? 1 : 0);
+    if (bf16)
+        hipLaunchKernelGGL((affine_gemv_kernel<BITS, GPT, true>), dim3(grid), dim3(AG_THREADS),
+                           lds, s, packed, x, y, (int)N, (int)K, P, nrb, out_f32 ? 1 : 0);
+    else
+        hipLaunchKernelGGL((affine_gemv_kernel<BITS, GPT, false>), dim3(grid), dim3(AG_THREADS),
+                           lds, s, packed, x, y, (int)N, (int)K, P, nrb, out_f32 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -329,8 +288,11 @@ template <int BITS>
 static hipError_t launch_ag_bits(const uint8_t *packed, const uint16_t *x, void *y, int64_t N,
                                  int64_t K, int group, bool bf16, bool out_f32, int cus,
                                  hipStream_t s) {
-    return bf16 ? launch_ag<BITS, true>(packed, x, y, N, K, group, out_f32, cus, s)
-                : launch_ag<BITS, false>(packed, x, y, N, K, group, out_f32, cus, s);
+    switch (group) {
+    case 32: return launch_ag<BITS, 4>(packed, x, y, N, K, bf16, out_f32, cus, s);
+    case 64: return launch_ag<BITS, 2>(packed, x, y, N, K, bf16, out_f32, cus, s);
+    default: return launch_ag<BITS, 1>(packed, x, y, N, K, bf16, out_f32, cus, s);
+    }
 }
 
 hipError_t launch_affine_gemv(const uint8_t *packed, const uint16_t *x, void *y, int bits,

@@ -1,0 +1,94 @@
+// Device helpers of the affine weight family shared by its GEMV and skinny
+// kernels: the bit-plane layout of a tile (see qg_internal.h), a lane's words
+// of one tile, and their unpacking into bf16 pairs 128 + q.
+#pragma once
+
+#include "qg_internal.h"
+
+namespace qg {
+
+// ------------------------------------------------------------ plane layout
+template <int BITS>
+struct AffPlanes;
+template <> struct AffPlanes<2> { static constexpr int NP = 1, W0 = 2, W1 = 0, O1 = 0; };
+template <> struct AffPlanes<3> { static constexpr int NP = 2, W0 = 2, W1 = 1, O1 = 2; };
+template <> struct AffPlanes<4> { static constexpr int NP = 1, W0 = 4, W1 = 0, O1 = 0; };
+template <> struct AffPlanes<5> { static constexpr int NP = 2, W0 = 4, W1 = 1, O1 = 4; };
+template <> struct AffPlanes<6> { static constexpr int NP = 2, W0 = 4, W1 = 2, O1 = 4; };
+template <> struct AffPlanes<8> { static constexpr int NP = 2, W0 = 4, W1 = 4, O1 = 4; };
+
+__device__ __forceinline__ unsigned buf_ld_x1(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                              unsigned soff) {
+    return (unsigned)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 2);
+}
+
+template <int W>
+__device__ __forceinline__ void ag_ld(unsigned (&d)[W], __amdgpu_buffer_rsrc_t r, unsigned voff,
+                                      unsigned soff) {
+    if constexpr (W == 4) {
+        const u32x4_t v = buf_ld_x4(r, voff, soff);
+        d[0] = v[0], d[1] = v[1], d[2] = v[2], d[3] = v[3];
+    } else if constexpr (W == 2) {
+        const u32x2_t v = buf_ld_x2(r, voff, soff);
+        d[0] = v[0], d[1] = v[1];
+    } else {
+        d[0] = buf_ld_x1(r, voff, soff);
+    }
+}
+
+// One tile's words for this lane: the plane words and the (scale, bias)
+// words of its row's GPT groups.
+template <int BITS, int GPT>
+struct AgTile {
+    typedef AffPlanes<BITS> PL;
+    unsigned p0[PL::W0];
+    unsigned p1[PL::NP == 2 ? PL::W1 : 1];
+    unsigned sb[GPT];
+};
+
+// Tile tp (clamped to the last of pn) of the buffer rs (tiles of tb bytes).
+template <int BITS, int GPT>
+__device__ __forceinline__ void ag_tile_load(AgTile<BITS, GPT> &T, __amdgpu_buffer_rsrc_t rs,
+                                             int tp, int pn, unsigned tb, int lane) {
+    typedef AffPlanes<BITS> PL;
+    const unsigned to = (unsigned)min(tp, pn - 1) * tb;
+    ag_ld<PL::W0>(T.p0, rs, 4u * PL::W0 * lane, to);
+    if constexpr (PL::NP == 2) ag_ld<PL::W1>(T.p1, rs, 256u * PL::W0 + 4u * PL::W1 * lane, to);
+    ag_ld<GPT>(T.sb, rs, 256u * BITS + 4u * GPT * (lane & 15), to);
+}
+
+// Pair j of plane (W, words p) as two small integers in the word's halves.
+template <int W, int NW>
+__device__ __forceinline__ unsigned ag_pair(const unsigned (&p)[NW], int j) {
+    constexpr int PER = 16 / W;
+    constexpr unsigned M = ((1u << W) - 1u) * 0x00010001u;
+    return (p[j / PER] >> (W * (j % PER))) & M;
+}
+
+constexpr unsigned AG_MAGIC = 0x43004300u;  // bf16 128 in both halves
+
+// Pair j as two bf16 values 128 + q (for 8 bits: 128 + the low nibble; the
+// high nibble's pair comes from ag_pair_hi).
+template <int BITS, int GPT>
+__device__ __forceinline__ unsigned ag_bf16_pair(const AgTile<BITS, GPT> &T, int j) {
+    typedef AffPlanes<BITS> PL;
+    const unsigned v0 = ag_pair<PL::W0>(T.p0, j);
+    if constexpr (PL::NP == 2 && BITS != 8)
+        return (ag_pair<PL::W1>(T.p1, j) << PL::O1) | v0 | AG_MAGIC;
+    else
+        return v0 | AG_MAGIC;
+}
+template <int BITS, int GPT>
+__device__ __forceinline__ unsigned ag_pair_hi(const AgTile<BITS, GPT> &T, int j) {
+    typedef AffPlanes<BITS> PL;
+    return ag_pair<PL::W1>(T.p1, j) | AG_MAGIC;
+}
+
+__device__ __forceinline__ float ag_scale(unsigned sb, bool bf16) {
+    return bf16 ? bf16_lo(sb) : f16_lo(sb);
+}
+__device__ __forceinline__ float ag_bias(unsigned sb, bool bf16) {
+    return bf16 ? bf16_hi(sb) : f16_hi(sb);
+}
+
+}  // namespace qg

@@ -25,8 +25,9 @@ constexpr int MOE_TOPK_MAX = 64;
 constexpr int M_MAX = 32;
 // Q4 products with at most this many activation rows run on the VALU GEMV
 // kernel by default; more rows go to the bf16 MFMA kernels.  Measured on
-// MI355X over a decode step's weights: M = 2 takes 0.86 ms on the VALU and
-// 0.74 ms on MFMA, M = 4 1.26 ms and 0.77 ms, so MFMA from M = 2 on.
+// MI355X over a decode step's weights: M = 1 takes 0.643 ms on the VALU and
+// 0.654 ms on MFMA, M = 2 0.761 and 0.671 ms, M = 4 1.181 and 0.701 ms, so
+// MFMA from M = 2 on.
 constexpr int Q4_VALU_ROWS_MAX = 1;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -195,12 +196,14 @@ int qgemm_skinny_run(int fmt, const void *packed, size_t packed_bytes, int64_t M
             return QG_EINVAL;
         int st = check_matrix(fmt, N, K);
         if (st != QG_OK) return st;
-        if (fmt != QG_FMT_Q4_ASYM_G64 && fmt != QG_FMT_Q8_SYM_G32) return QG_EUNSUPPORTED;
-        if (fmt == QG_FMT_Q4_ASYM_G64 && out_dtype == QG_OUT_I32_GROUPS) return QG_EUNSUPPORTED;
+        const AffineFmt aff = affine_decode(fmt);
+        if (fmt != QG_FMT_Q4_ASYM_G64 && fmt != QG_FMT_Q8_SYM_G32 && !aff.bits)
+            return QG_EUNSUPPORTED;
+        if (fmt != QG_FMT_Q8_SYM_G32 && out_dtype == QG_OUT_I32_GROUPS) return QG_EUNSUPPORTED;
         if (M < 0 || M > M_MAX) return QG_ESHAPE;
         if (!packed || !X || !Y) return QG_EINVAL;
         if (fmt == QG_FMT_Q8_SYM_G32 && out_dtype != QG_OUT_I32_GROUPS && !x_scales) return QG_EINVAL;
-        if (fmt == QG_FMT_Q4_ASYM_G64 && x_scales) return QG_EINVAL;
+        if (fmt != QG_FMT_Q8_SYM_G32 && x_scales) return QG_EINVAL;
         if (packed_bytes != packed_bytes_for(fmt, N, K)) return QG_ESIZE;
         const size_t yal = out_dtype == QG_OUT_BF16 ? 2 : 4;
         if (!aligned(packed, 16) || !aligned(X, 16) || !aligned(Y, yal) ||
@@ -219,6 +222,15 @@ int qgemm_skinny_run(int fmt, const void *packed, size_t packed_bytes, int64_t M
             if (q4_skinny_stream_fits(N, cus))
                 return hip_status(launch_q4_skinny_stream(p, xx, Y, M, N, K, f32, cus, s));
             return hip_status(launch_q4_skinny(p, xx, Y, M, N, K, f32, cus, s));
+        }
+        if (aff.bits) {
+            const uint16_t *xx = reinterpret_cast<const uint16_t *>(X);
+            const bool f32 = out_dtype == QG_OUT_F32;
+            if (M == 1)
+                return hip_status(launch_affine_gemv(p, xx, Y, aff.bits, aff.group, aff.bf16 != 0,
+                                                     N, K, f32, cus, s));
+            return hip_status(launch_affine_skinny(p, xx, Y, aff.bits, aff.group, aff.bf16 != 0,
+                                                   M, N, K, f32, cus, s));
         }
         const int mode = out_dtype == QG_OUT_BF16 ? 0 : (out_dtype == QG_OUT_F32 ? 1 : 2);
         return hip_status(launch_q8_skinny(p, reinterpret_cast<const int8_t *>(X), x_scales, Y, M,

@@ -46,8 +46,10 @@ namespace qg {
 //   the codes as bit-planes of width 1, 2 or 4 (b = 2: {2}; 3: {2, 1};
 //   4: {4}; 5: {4, 1}; 6: {4, 2}; 8: {4, 4}; plane p holds bits
 //   [o_p, o_p + w_p) of each code).  Plane p occupies 256 w_p bytes; lane l
-//   holds w_p words at 4 w_p l for the 32 codes c_0..c_31 of row l & 15,
-//   k = 32(l >> 4) .. +32: pair j (codes 2j, 2j+1) sits in word
+//   holds w_p words at 4 w_p l for 32 codes c_0..c_31 of row l & 15 in four
+//   runs of 8: c_{8i+t} is k = 32i + 8(l >> 4) + t (so run i of all 64 lanes
+//   covers k = 32i .. 32i + 32, one 32-k block: the k of one 16x16x32 MFMA
+//   step, inside one group).  Pair j (codes 2j, 2j+1) sits in word
 //   j / (16 / w_p), at bit w_p (j % (16 / w_p)) (code 2j) and 16 + the same
 //   (code 2j+1), so a shift and an and-or yield both as the two halves.
 //   [256 b, ...)  per (row r, group t of the tile): (scale | bias << 16) at
@@ -196,6 +198,10 @@ hipError_t launch_pack_affine(const uint8_t *codes, const uint16_t *scales,
 hipError_t launch_affine_gemv(const uint8_t *packed, const uint16_t *x, void *y,
                               int bits, int group, bool bf16_scales, int64_t N,
                               int64_t K, bool out_f32, int cus, hipStream_t s);
+hipError_t launch_affine_skinny(const uint8_t *packed, const uint16_t *X, void *Y,
+                                int bits, int group, bool bf16_scales, int64_t M,
+                                int64_t N, int64_t K, bool out_f32, int cus,
+                                hipStream_t s);
 
 size_t q4_packed_bytes(int64_t N, int64_t K);
 size_t q8_packed_bytes(int64_t N, int64_t K);

@@ -249,7 +249,12 @@ def test_affine_validation():
     assert lib.qgemv_pack(f, 40, 96, A, A, None, A, C.byref(cap), None) == L.QG_EINVAL  # biases
     assert lib.qgemv_run(f, A, need + 16, 40, 96, A, A, 0, None) == L.QG_ESIZE
     assert lib.qgemv_run(f, A, need, 40, 96, A + 4, A, 0, None) == L.QG_EALIGN
-    assert lib.qgemm_skinny_run(f, A, need, 2, 40, 96, A, None, A, 0, None) == L.QG_EUNSUPPORTED
+    # the skinny product takes affine codes; every call below fails validation
+    assert lib.qgemm_skinny_run(f, A, need, 2, 40, 96, A, A, A, 0, None) == L.QG_EINVAL  # scales
+    assert lib.qgemm_skinny_run(f, A, need, 2, 40, 96, A, None, A, 2, None) == L.QG_EUNSUPPORTED
+    assert lib.qgemm_skinny_run(f, A, need, 33, 40, 96, A, None, A, 0, None) == L.QG_ESHAPE
+    assert lib.qgemm_skinny_run(f, A, need + 16, 2, 40, 96, A, None, A, 0, None) == L.QG_ESIZE
+    assert lib.qgemm_skinny_run(f, A, need, 2, 40, 96, A + 8, None, A, 0, None) == L.QG_EALIGN
 
 
 def test_binding_refuses_host_tensors():

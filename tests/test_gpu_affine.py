@@ -89,3 +89,59 @@ def test_affine_4bit_matches_q4_path():
     y4 = to_np(pkg.qgemv_run(pkg.FMT_Q4_ASYM_G64, weights.pack_q4(q, DEV), 4096, 4096,
                              weights.to_device(x, DEV), out_dtype=pkg.OUT_F32))
     assert_f32_close(y4, ref, what="q4 path")
+
+
+# ------------------------------------------------------------ skinny (M rows)
+def run_skinny(m, packed, X, out_dtype):
+    fmt = pkg.affine_format(m.bits, m.group, m.bf16_scales)
+    N, K = m.codes.shape
+    Y = pkg.qgemm_skinny_run(fmt, packed, X.shape[0], N, K, weights.to_device(X, DEV),
+                             out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_np(Y)
+
+
+def check_skinny(m, X):
+    N, K = m.codes.shape
+    ref = oracle.affine_gemm(m.codes, m.scales, m.biases, X, m.group, m.bf16_scales)
+    packed = weights.pack_affine(m, DEV)
+    what = "skinny bits=%d g=%d bf16=%d M=%d N=%d K=%d" % (m.bits, m.group, m.bf16_scales,
+                                                          X.shape[0], N, K)
+    assert_f32_close(run_skinny(m, packed, X, pkg.OUT_F32), ref, what=what + " f32")
+    assert_bf16_close(run_skinny(m, packed, X, pkg.OUT_BF16).ravel(), ref.ravel(),
+                      what=what + " bf16")
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("group", (32, 64, 128))
+@pytest.mark.parametrize("bf16", (False, True))
+@pytest.mark.parametrize("M", (16, 32))
+def test_affine_skinny(bits, group, bf16, M):
+    """Every member of the family at 16 and 32 rows; 100 output rows (ragged
+    last rowblock), K = 1536."""
+    m = synth.affine_matrix(125, 100, 1536, bits, group, bf16)
+    check_skinny(m, synth.activations(126, M, 1536))
+
+
+# 2 and 17 rows; K over several staged segments (12288 at 16 rows, 6144 at
+# 32); a partial last tile; more rowblocks than one pass of the waves; M = 1
+# (the GEMV)
+@pytest.mark.parametrize("bits,group,M,N,K", [(4, 64, 2, 40, 256), (3, 32, 17, 33, 160),
+                                              (2, 128, 16, 64, 12288), (8, 32, 32, 48, 6144),
+                                              (5, 64, 16, 7000, 512), (6, 32, 32, 3000, 4096),
+                                              (4, 32, 1, 77, 1024)])
+def test_affine_skinny_shapes(bits, group, M, N, K):
+    note("affine skinny bits=%d g=%d M=%d N=%d K=%d" % (bits, group, M, N, K))
+    m = synth.affine_matrix(127, N, K, bits, group, bits % 2 == 0)
+    check_skinny(m, synth.activations(128, M, K))
+
+
+def test_affine_skinny_rows_equal_gemv_rows():
+    """Row m of the skinny product equals the GEMV on X[m] to within the
+    rounding of their different summation orders, and both match the oracle."""
+    m = synth.affine_matrix(129, 300, 2048, 4, 64, False)
+    X = synth.activations(130, 16, 2048)
+    packed = weights.pack_affine(m, DEV)
+    Y = run_skinny(m, packed, X, pkg.OUT_F32)
+    for r in (0, 7, 15):
+        assert_f32_close(run(m, packed, X[r], pkg.OUT_F32), Y[r], what="row %d" % r)
