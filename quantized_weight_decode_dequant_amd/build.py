@@ -27,10 +27,7 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libqgemv.so (always recompiles)."""
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *HIP_FLAGS, "-o", tmp, *sources()]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,6 +38,24 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
     if verbose and err.strip():
         print(err, flush=True)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every HIP source into libqgemv.so (always recompiles): one
+    object per source, compiled in parallel, then one shared-object link."""
+    from concurrent.futures import ThreadPoolExecutor
+    import tempfile
+    srcs = sources()
+    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    with tempfile.TemporaryDirectory(prefix="qgemv_build_") as d:
+        objs = [os.path.join(d, os.path.basename(src) + ".o") for src in srcs]
+        cmds = [[HIPCC, *compile_flags, "-c", "-o", o, src] for src, o in zip(srcs, objs)]
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
