@@ -649,7 +649,7 @@ def main():
             ms16 = workloads.time_graph_ms(
                 lambda: _lib.qgemm_skinny_run(fa, apacked, 16, NA, KA, aX, Y=aY), 8)
             b16 = roofline.affine_gemv_bytes(bits, GA, NA, KA) + 2.0 * 16 * KA + 2.0 * 16 * NA - 2.0 * KA - 2.0 * NA
-            fl16 = plain_read_us(int(b16))
+            fl16 = fla * b16 / ba  # the same plain-read rate over the 16-row call's bytes
             rows.append({"bits": bits, "us": round(msa * 1e3, 2), "GBs": round(ba / (msa * 1e-3) / 1e9, 1),
                          "pct_of_peak": round(100 * ba / (msa * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1),
                          "pct_of_plain_read": round(100 * fla / (msa * 1e3), 1),
