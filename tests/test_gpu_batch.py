@@ -233,3 +233,38 @@ def test_batch_forced_kernel(M, kernel):
         torch.cuda.synchronize()
         for e, a in zip(entries, auto):
             assert torch.equal(e[4], a[4])
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_batch_shared_inputs(M):
+    """One layer's projections with shared inputs in one launch: q, k and v
+    read the same x, gate and up the same x (the fused form of a layer's
+    input projections); each output equals its own single call bit for bit
+    and the oracle."""
+    note("batch shared inputs M=%d" % M)
+    H, Hk, F = 1024, 256, 2048
+    shapes = [("q", H, H), ("k", Hk, H), ("v", Hk, H), ("gate", F, H), ("up", F, H)]
+    mats = [synth.q4_matrix(138, N, K, item=i) for i, (_, N, K) in enumerate(shapes)]
+    xa = synth.activations(139, M, H, item=0)
+    xb = synth.activations(139, M, H, item=1)
+    xa_d = weights.to_device(xa if M > 1 else xa[0], DEV)
+    xb_d = weights.to_device(xb if M > 1 else xb[0], DEV)
+    entries, refs = [], []
+    for (name, N, K), m in zip(shapes, mats):
+        shared = xa_d if name in ("q", "k", "v") else xb_d
+        y = torch.empty((M, N) if M > 1 else (N,), dtype=torch.float32, device=DEV)
+        entries.append((weights.pack_q4(m, DEV), N, K, shared, y))
+        refs.append(oracle.q4_gemm(m.codes, m.scales, m.biases, xa if name in ("q", "k", "v") else xb))
+    plan = pkg.qg_batch_plan_build(Q4, M, entries, pkg.OUT_F32)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    for (p, N, K, x, y), ref in zip(entries, refs):
+        got = to_np(y).reshape(M, N)
+        assert_f32_close(got, ref, what="shared-input product N=%d" % N)
+        if M == 1:
+            single = pkg.qgemv_run(Q4, p, N, K, x, out_dtype=pkg.OUT_F32)
+        else:
+            single = pkg.qgemm_skinny_run(Q4, p, M, N, K, x, out_dtype=pkg.OUT_F32)
+        torch.cuda.synchronize()
+        if M == 1:
+            assert torch.equal(single, y)
