@@ -332,7 +332,8 @@ typedef struct qg_gemv_desc {
  * VALU for M = 1, MFMA for M >= 2 (at M = 2 the MFMA pass over a decode
  * step's weights already takes 0.74 ms against 0.86 ms on the VALU).  The
  * others force a family, e.g. to measure both; results differ between the
- * families only by fp32 rounding order. */
+ * families only by fp32 rounding order.  Affine products (M = 1) have only
+ * the GEMV kernel of qgemv_run: QG_KERNEL_AUTO and QG_KERNEL_VALU take it. */
 typedef enum {
     QG_KERNEL_AUTO = 0,
     QG_KERNEL_VALU = 1,   /* M <= 4, else QG_EUNSUPPORTED */
@@ -356,9 +357,12 @@ size_t qg_batch_worklist_bytes(int32_t count);
  * qg_batch_plan_build -- validate `count` product descriptors and write their
  * work list to `worklist`.
  *
- *  fmt          QG_FMT_Q4_ASYM_G64 (other formats -> QG_EUNSUPPORTED).
+ *  fmt          QG_FMT_Q4_ASYM_G64, or a QG_FMT_AFFINE(bits, group, bf16)
+ *               code for M = 1 only (the affine decode GEMV; M > 1 or
+ *               QG_KERNEL_MFMA -> QG_EUNSUPPORTED).  Other formats ->
+ *               QG_EUNSUPPORTED.  Every descriptor's packed buffer is of `fmt`.
  *  M            activation rows of every product: 1 (decode GEMVs, K <= 24576
- *               each) or 2..32 (a verification pass).
+ *               each) or 2..32 (a verification pass, Q4 only).
  *  count        1..65536 descriptors in `descs` (host array, read only; it
  *               need not outlive the call).
  *  out_dtype    QG_OUT_BF16 or QG_OUT_F32, for every product.

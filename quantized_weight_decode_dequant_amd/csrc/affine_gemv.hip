@@ -157,21 +157,30 @@ __device__ __forceinline__ float ag_reduce_kslices(float a) {
     return a;
 }
 
+// LDS of a workgroup: the partial sums first, at a fixed offset, so that a
+// work-list workgroup can stage the next product's x while other waves still
+// read the previous product's sums; then x and its group sums.
+constexpr size_t AG_LDS_PART = (size_t)AG_RMAX * AG_WAVES * 16 * 4;
+
+template <int GPT>
+static size_t ag_lds_bytes(int64_t K) {
+    const int64_t KS = ceil_div(ceil_div(K, AFF_TILE_K), AG_TPB) * AG_TPB * AFF_TILE_K;
+    return AG_LDS_PART + (size_t)KS * 2 + (size_t)(KS / 32) * GPT * 4;
+}
+
+// Rowblocks [u0, u1) of one product.
 template <int BITS, int GPT, bool BF16S>
-__global__ void __launch_bounds__(AG_THREADS, 4)
-affine_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restrict__ x,
-                   void *__restrict__ y, int N, int K, int P, int nrb, int out_f32) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+__device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, unsigned char *smem,
+                                         int tid, int lane, int wave) {
+    const uint8_t *__restrict__ packed = it.packed;
+    const uint16_t *__restrict__ x = reinterpret_cast<const uint16_t *>(it.x);
+    const int N = it.N, K = it.K, P = it.P;
+    const int kg = lane >> 4;
     const int nb = (P + AG_TPB - 1) / AG_TPB;
     const int KS = nb * AG_TPB * AFF_TILE_K;  // staged x length (zero past K)
-    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);                  // [KS] bf16
-    float *xsl = reinterpret_cast<float *>(smem + (size_t)KS * 2);       // [KS / 32 * GPT]
-    float *part = xsl + KS / 32 * GPT;                                   // [RMAX][WAVES][16]
-    const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t G = gridDim.x, jb = blockIdx.x;
-    const int u0 = (int)(jb * nrb / G), u1 = (int)((jb + 1) * nrb / G);
-    if (u0 >= u1) return;
+    float *part = reinterpret_cast<float *>(smem);                               // [RMAX][WAVES][16]
+    uint16_t *xl = reinterpret_cast<uint16_t *>(smem + AG_LDS_PART);             // [KS] bf16
+    float *xsl = reinterpret_cast<float *>(smem + AG_LDS_PART + (size_t)KS * 2);  // [KS / 32 * GPT]
     const unsigned tb = (unsigned)affine_tile_bytes(BITS, AFF_TILE_K / GPT);
     const size_t rb_bytes = (size_t)P * tb;
     // stage x, then the sum of each lane-group's x over each group of each
@@ -257,56 +266,105 @@ affine_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restric
             for (int w = 0; w < AG_WAVES; ++w) v += part[(i * AG_WAVES + w) * 16 + row];
             const int n = (ub + i) * RB + row;
             if (n < N) {
-                if (out_f32)
-                    st_global<float>(y, n, v);
+                if (it.out_f32)
+                    st_global<float>(it.y, n, v);
                 else
-                    st_global<uint16_t>(y, n, f32_to_bf16(v));
+                    st_global<uint16_t>(it.y, n, f32_to_bf16(v));
             }
         }
     }
 }
 
-template <int BITS, int GPT>
-static hipError_t launch_ag(const uint8_t *packed, const uint16_t *x, void *y, int64_t N,
-                            int64_t K, bool bf16, bool out_f32, int cus, hipStream_t s) {
-    const int P = (int)ceil_div(K, AFF_TILE_K);
-    const int nrb = (int)ceil_div(N, RB);
-    const int nb = (int)ceil_div(P, AG_TPB);
-    const size_t KS = (size_t)nb * AG_TPB * AFF_TILE_K;
-    const size_t lds = KS * 2 + KS / 32 * GPT * 4 + (size_t)AG_RMAX * AG_WAVES * 16 * 4;
-    const int grid = nrb < cus * 4 ? nrb : cus * 4;
+// LIST = false: one product (`single`), a contiguous share of its rowblocks
+// per workgroup; LIST = true: the work list, workgroup j taking the units
+// [starts[j], starts[j+1]).  Separate instantiations, so profiles tell a
+// grouped launch from single GEMVs.
+template <bool LIST, int BITS, int GPT, bool BF16S>
+__global__ void __launch_bounds__(AG_THREADS, 4)
+affine_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
+                   WorkItem single) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (!LIST) {
+        const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
+        const int u0 = (int)(j * n / g), u1 = (int)((j + 1) * n / g);
+        if (u0 < u1) ag_range<BITS, GPT, BF16S>(single, u0, u1, smem, tid, lane, wave);
+        return;
+    }
+    const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
+#pragma unroll 1
+    for (int i = s.item; i < e.item || (i == e.item && e.unit > 0); ++i) {
+        const WorkItem it = items[i];
+        const int u0 = (i == s.item) ? s.unit : 0;
+        const int u1 = (i == e.item) ? e.unit : it.units;
+        if (u0 < u1) ag_range<BITS, GPT, BF16S>(it, u0, u1, smem, tid, lane, wave);
+    }
+}
+
+template <bool LIST, int BITS, int GPT>
+static hipError_t launch_ag(const WorkItem *items, const WorkStart *starts, const WorkItem &it,
+                            int grid, int64_t kmax, bool bf16, hipStream_t s) {
+    const size_t lds = ag_lds_bytes<GPT>(kmax);
     if (bf16)
-        hipLaunchKernelGGL((affine_gemv_kernel<BITS, GPT, true>), dim3(grid), dim3(AG_THREADS),
-                           lds, s, packed, x, y, (int)N, (int)K, P, nrb, out_f32 ? 1 : 0);
+        hipLaunchKernelGGL((affine_gemv_kernel<LIST, BITS, GPT, true>), dim3(grid),
+                           dim3(AG_THREADS), lds, s, items, starts, it);
     else
-        hipLaunchKernelGGL((affine_gemv_kernel<BITS, GPT, false>), dim3(grid), dim3(AG_THREADS),
-                           lds, s, packed, x, y, (int)N, (int)K, P, nrb, out_f32 ? 1 : 0);
+        hipLaunchKernelGGL((affine_gemv_kernel<LIST, BITS, GPT, false>), dim3(grid),
+                           dim3(AG_THREADS), lds, s, items, starts, it);
     return hipGetLastError();
 }
 
-template <int BITS>
-static hipError_t launch_ag_bits(const uint8_t *packed, const uint16_t *x, void *y, int64_t N,
-                                 int64_t K, int group, bool bf16, bool out_f32, int cus,
+template <bool LIST, int BITS>
+static hipError_t launch_ag_bits(const WorkItem *items, const WorkStart *starts,
+                                 const WorkItem &it, int grid, int64_t kmax, int group, bool bf16,
                                  hipStream_t s) {
     switch (group) {
-    case 32: return launch_ag<BITS, 4>(packed, x, y, N, K, bf16, out_f32, cus, s);
-    case 64: return launch_ag<BITS, 2>(packed, x, y, N, K, bf16, out_f32, cus, s);
-    default: return launch_ag<BITS, 1>(packed, x, y, N, K, bf16, out_f32, cus, s);
+    case 32: return launch_ag<LIST, BITS, 4>(items, starts, it, grid, kmax, bf16, s);
+    case 64: return launch_ag<LIST, BITS, 2>(items, starts, it, grid, kmax, bf16, s);
+    default: return launch_ag<LIST, BITS, 1>(items, starts, it, grid, kmax, bf16, s);
     }
 }
+
+template <bool LIST>
+static hipError_t launch_ag_fmt(const WorkItem *items, const WorkStart *starts,
+                                const WorkItem &it, int grid, int64_t kmax, int bits, int group,
+                                bool bf16, hipStream_t s) {
+    switch (bits) {
+    case 2: return launch_ag_bits<LIST, 2>(items, starts, it, grid, kmax, group, bf16, s);
+    case 3: return launch_ag_bits<LIST, 3>(items, starts, it, grid, kmax, group, bf16, s);
+    case 4: return launch_ag_bits<LIST, 4>(items, starts, it, grid, kmax, group, bf16, s);
+    case 5: return launch_ag_bits<LIST, 5>(items, starts, it, grid, kmax, group, bf16, s);
+    case 6: return launch_ag_bits<LIST, 6>(items, starts, it, grid, kmax, group, bf16, s);
+    case 8: return launch_ag_bits<LIST, 8>(items, starts, it, grid, kmax, group, bf16, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int affine_gemv_wgs_per_cu() { return 4; }
 
 hipError_t launch_affine_gemv(const uint8_t *packed, const uint16_t *x, void *y, int bits,
                               int group, bool bf16_scales, int64_t N, int64_t K, bool out_f32,
                               int cus, hipStream_t s) {
-    switch (bits) {
-    case 2: return launch_ag_bits<2>(packed, x, y, N, K, group, bf16_scales, out_f32, cus, s);
-    case 3: return launch_ag_bits<3>(packed, x, y, N, K, group, bf16_scales, out_f32, cus, s);
-    case 4: return launch_ag_bits<4>(packed, x, y, N, K, group, bf16_scales, out_f32, cus, s);
-    case 5: return launch_ag_bits<5>(packed, x, y, N, K, group, bf16_scales, out_f32, cus, s);
-    case 6: return launch_ag_bits<6>(packed, x, y, N, K, group, bf16_scales, out_f32, cus, s);
-    case 8: return launch_ag_bits<8>(packed, x, y, N, K, group, bf16_scales, out_f32, cus, s);
-    default: return hipErrorInvalidValue;
-    }
+    WorkItem it{};
+    it.packed = packed;
+    it.x = x;
+    it.y = y;
+    it.N = (int32_t)N;
+    it.K = (int32_t)K;
+    it.P = (int32_t)ceil_div(K, AFF_TILE_K);
+    it.units = (int32_t)ceil_div(N, RB);
+    it.out_f32 = out_f32 ? 1 : 0;
+    const int64_t cap = (int64_t)cus * affine_gemv_wgs_per_cu();
+    const int grid = (int)(it.units < cap ? it.units : cap);
+    return launch_ag_fmt<false>(nullptr, nullptr, it, grid, K, bits, group, bf16_scales, s);
+}
+
+hipError_t launch_affine_gemv_list(const WorkItem *items, const WorkStart *starts, int grid,
+                                   int64_t kmax, int bits, int group, bool bf16_scales,
+                                   hipStream_t s) {
+    WorkItem none{};
+    return launch_ag_fmt<true>(items, starts, none, grid, kmax, bits, group, bf16_scales, s);
 }
 
 }  // namespace qg

@@ -382,8 +382,14 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
             return QG_EINVAL;
         }
         if (format_group(fmt) == 0) return QG_EINVAL;
-        if (fmt != QG_FMT_Q4_ASYM_G64) return QG_EUNSUPPORTED;
+        const AffineFmt aff = affine_decode(fmt);
+        if (fmt != QG_FMT_Q4_ASYM_G64 && !aff.bits) return QG_EUNSUPPORTED;
         if (M < 1 || M > M_MAX || count < 1 || count > 65536) return QG_ESHAPE;
+        if (aff.bits) {
+            // affine products: the decode GEMV only
+            if (M != 1 || kernel == QG_KERNEL_MFMA) return QG_EUNSUPPORTED;
+            kernel = QG_KERNEL_VALU;
+        }
         if (kernel == QG_KERNEL_AUTO) kernel = M <= Q4_VALU_ROWS_MAX ? QG_KERNEL_VALU : QG_KERNEL_MFMA;
         if (kernel == QG_KERNEL_VALU && M > q4_gemv_rows_max()) return QG_EUNSUPPORTED;
         if (worklist_bytes < qg_batch_worklist_bytes(count)) return QG_ESIZE;
@@ -419,13 +425,15 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
             w.y = d.y;
             w.N = (int32_t)d.N;
             w.K = (int32_t)d.K;
-            w.P = (int32_t)ceil_div(d.K, Q4_TILE_K);
+            w.P = (int32_t)ceil_div(d.K, aff.bits ? AFF_TILE_K : Q4_TILE_K);
             w.units = (int32_t)ceil_div(ceil_div(d.N, RB), rpu);
             w.out_f32 = out_dtype == QG_OUT_F32 ? 1 : 0;
             total_units += w.units;
             total_cost += (int64_t)w.units * ((int64_t)w.P * rpu + 2);
         }
-        const int per_cu = kernel == QG_KERNEL_VALU ? q4_gemv_wgs_per_cu(M) : q4_skinny_stream_wgs_per_cu();
+        const int per_cu = aff.bits                  ? affine_gemv_wgs_per_cu()
+                           : kernel == QG_KERNEL_VALU ? q4_gemv_wgs_per_cu(M)
+                                                      : q4_skinny_stream_wgs_per_cu();
         int64_t grid = (int64_t)cus * per_cu;
         if (grid > WL_GRID_MAX) grid = WL_GRID_MAX;
         if (grid > total_units) grid = total_units;
@@ -482,9 +490,12 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
 int qg_batch_run(const qg_batch_plan *plan, void *stream) {
     try {
         if (!plan || !plan->worklist || !aligned(plan->worklist, 16)) return QG_EINVAL;
-        if (plan->fmt != QG_FMT_Q4_ASYM_G64 || plan->M < 1 || plan->M > M_MAX ||
+        const AffineFmt aff = affine_decode(plan->fmt);
+        if ((plan->fmt != QG_FMT_Q4_ASYM_G64 && !aff.bits) ||
+            (aff.bits && (plan->M != 1 || plan->kernel != QG_KERNEL_VALU)) ||
+            plan->M < 1 || plan->M > M_MAX ||
             plan->count < 1 || plan->count > 65536 || plan->grid < 1 ||
-            plan->grid > WL_GRID_MAX || plan->kmax < 64 ||
+            plan->grid > WL_GRID_MAX || plan->kmax < format_group(plan->fmt) ||
             (plan->M == 1 && plan->kmax > GEMV_K_MAX) ||
             (plan->kernel != QG_KERNEL_VALU && plan->kernel != QG_KERNEL_MFMA) ||
             (plan->kernel == QG_KERNEL_VALU && plan->M > q4_gemv_rows_max()) ||
@@ -494,6 +505,9 @@ int qg_batch_run(const qg_batch_plan *plan, void *stream) {
         const WorkItem *items = reinterpret_cast<const WorkItem *>(base + WL_HEADER_BYTES);
         const WorkStart *starts = reinterpret_cast<const WorkStart *>(items + plan->count);
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        if (aff.bits)
+            return hip_status(launch_affine_gemv_list(items, starts, plan->grid, plan->kmax,
+                                                      aff.bits, aff.group, aff.bf16 != 0, s));
         if (plan->kernel == QG_KERNEL_VALU)
             return hip_status(launch_q4_gemv_list(items, starts, plan->grid, plan->M, s));
         return hip_status(launch_q4_skinny_stream_list(items, starts, plan->grid, plan->M, s));

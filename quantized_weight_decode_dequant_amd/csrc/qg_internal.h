@@ -198,6 +198,12 @@ hipError_t launch_pack_affine(const uint8_t *codes, const uint16_t *scales,
 hipError_t launch_affine_gemv(const uint8_t *packed, const uint16_t *x, void *y,
                               int bits, int group, bool bf16_scales, int64_t N,
                               int64_t K, bool out_f32, int cus, hipStream_t s);
+// the affine GEMV over a device work list (M = 1; every item of one format);
+// kmax = the largest K of the list (sizes the LDS)
+hipError_t launch_affine_gemv_list(const WorkItem *items, const WorkStart *starts, int grid,
+                                   int64_t kmax, int bits, int group, bool bf16_scales,
+                                   hipStream_t s);
+int affine_gemv_wgs_per_cu();
 hipError_t launch_affine_skinny(const uint8_t *packed, const uint16_t *X, void *Y,
                                 int bits, int group, bool bf16_scales, int64_t M,
                                 int64_t N, int64_t K, bool out_f32, int cus,

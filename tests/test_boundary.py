@@ -314,6 +314,18 @@ def test_batch_validation():
     assert build(arr=descs(x=A + 2)) == L.QG_EALIGN
     assert build(arr=descs(y=A + 1)) == L.QG_EALIGN
     assert build(arr=descs(y=A + 2), out=L.OUT_F32) == L.QG_EALIGN
+    # affine products: the decode GEMV only, every descriptor of the plan's format
+    aff = pkg.affine_format(3, 32, False)
+    assert build(fmt=aff, M=2) == L.QG_EUNSUPPORTED
+    assert build(fmt=aff, M=16) == L.QG_EUNSUPPORTED
+    assert build(fmt=aff, kernel=L.KERNEL_MFMA) == L.QG_EUNSUPPORTED
+    assert build(fmt=aff) == L.QG_ESIZE  # the descriptors are sized as Q4
+    good["packed_bytes"] = pkg.packed_bytes(aff, 64, 256)
+    assert build(fmt=aff, arr=descs(K=48)) == L.QG_ESHAPE
+    assert build(fmt=aff, arr=descs(K=24576 + 32)) == L.QG_ESHAPE
+    assert build(fmt=aff, arr=descs(packed_bytes=9216)) == L.QG_ESIZE
+    assert build(fmt=aff, M=2, kernel=L.KERNEL_VALU) == L.QG_EUNSUPPORTED
+    assert build(fmt=pkg.affine_format(7, 32, False)) == L.QG_EINVAL
     # malformed plans are refused before any launch
     assert lib.qg_batch_run(None, None) == L.QG_EINVAL
     bad = L.BatchPlan()
@@ -330,3 +342,9 @@ def test_batch_validation():
     assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # grid > max
     bad.grid, bad.worklist_bytes = 4, wl - 8
     assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # work list too small
+    bad.fmt, bad.worklist_bytes, bad.M = aff, wl, 2
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # affine past one row
+    bad.M, bad.kernel = 1, L.KERNEL_MFMA
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # affine on the MFMA family
+    bad.kernel, bad.kmax = L.KERNEL_VALU, 16
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # K below one group

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import quantized_weight_decode_dequant_amd as pkg
-from quantized_weight_decode_dequant_amd import synth, weights
+from quantized_weight_decode_dequant_amd import synth, weights, workloads
 from helpers import assert_bf16_close, assert_f32_close, note, to_np
 
 pytestmark = pytest.mark.gpu
@@ -145,3 +145,108 @@ def test_affine_skinny_rows_equal_gemv_rows():
     Y = run_skinny(m, packed, X, pkg.OUT_F32)
     for r in (0, 7, 15):
         assert_f32_close(run(m, packed, X[r], pkg.OUT_F32), Y[r], what="row %d" % r)
+
+
+# ------------------------------------------------------------ grouped launch
+BATCH_SHAPES = [(40, 192), (1, 64), (256, 4096), (33, 12288), (100, 1216), (17, 320),
+                (3000, 256), (5, 96), (2, 32), (7, 384)]
+
+
+def _batch(seed, bits, group, bf16, shapes, out_dtype):
+    """Matrices of one affine format with their own x and y, and the single
+    qgemv_run output of each."""
+    fmt = pkg.affine_format(bits, group, bf16)
+    dt = torch.float32 if out_dtype == pkg.OUT_F32 else torch.bfloat16
+    mats, xs, entries, singles = [], [], [], []
+    for i, (N, K) in enumerate(shapes):
+        m = synth.affine_matrix(seed, N, K, bits, group, bf16, item=i)
+        x = synth.activations(seed + 1, 1, K, item=i)[0]
+        p = weights.pack_affine(m, DEV)
+        xd = weights.to_device(x, DEV)
+        entries.append((p, N, K, xd, torch.empty(N, dtype=dt, device=DEV)))
+        singles.append(pkg.qgemv_run(fmt, p, N, K, xd, out_dtype=out_dtype))
+        mats.append(m)
+        xs.append(x)
+    return fmt, mats, xs, entries, singles
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("group", (32, 64, 128))
+def test_affine_batch_mixed_shapes(bits, group):
+    """One grouped launch over affine GEMVs of mixed shapes (partial tiles,
+    one row, K up to 12288): each output against the oracle and bitwise
+    equal to qgemv_run's (same kernel body, same order)."""
+    out_dtype = pkg.OUT_BF16 if group == 64 else pkg.OUT_F32
+    bf16 = bits % 2 == 0
+    note("affine batch bits=%d g=%d" % (bits, group))
+    shapes = [(N, K) for N, K in BATCH_SHAPES if K % group == 0]
+    fmt, mats, xs, entries, singles = _batch(140 + bits, bits, group, bf16, shapes, out_dtype)
+    plan = pkg.qg_batch_plan_build(fmt, 1, entries, out_dtype)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    for (p, N, K, xd, y), s, m, x in zip(entries, singles, mats, xs):
+        ref = oracle.affine_gemv(m.codes, m.scales, m.biases, x, group, bf16)
+        what = "bits=%d g=%d N=%d K=%d" % (bits, group, N, K)
+        if out_dtype == pkg.OUT_F32:
+            assert_f32_close(to_np(y), ref, what=what)
+        else:
+            assert_bf16_close(to_np(y), ref, what=what)
+        assert torch.equal(y, s), "batch differs from qgemv_run: " + what
+
+
+def test_affine_batch_layer_graph_replay():
+    """A decoder layer's seven projections (4096 -> 4096, 1024, 1024, 4096,
+    12288, 12288; 12288 -> 4096) at 3 bits in one launch, captured in a HIP
+    graph: every replay, with eager work between, equals the eager launch,
+    which equals qgemv_run per projection; sampled rows against the oracle."""
+    note("affine batch layer graph")
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (12288, 4096),
+              (12288, 4096), (4096, 12288)]
+    fmt, mats, xs, entries, singles = _batch(150, 3, 64, False, shapes, pkg.OUT_BF16)
+    plan = pkg.qg_batch_plan_build(fmt, 1, entries)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    eager = [e[4].clone() for e in entries]
+    for e, s in zip(eager, singles):
+        assert torch.equal(e, s)
+    rng = np.random.default_rng(151)
+    for (p, N, K, xd, y), m, x in zip(entries, mats, xs):
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 48, replace=False)]))
+        ref = oracle.affine_gemv(m.codes[rows], m.scales[rows], m.biases[rows], x, 64, False)
+        assert_bf16_close(to_np(y)[rows], ref, what="N=%d K=%d" % (N, K))
+    g = workloads.capture_graph(lambda: pkg.qg_batch_run(plan))
+    for rep in range(3):
+        for e in entries:
+            e[4].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, ref in zip(entries, eager):
+            assert torch.equal(e[4], ref), "replay %d differs" % rep
+        _ = torch.randn(1000, device=DEV).sum().item()  # unrelated eager work in between
+
+
+def test_affine_batch_shared_input():
+    """q, k and v on one x and gate, up on another: the plan points several
+    products at the same activation buffer."""
+    note("affine batch shared inputs")
+    shapes = [(512, 2048), (128, 2048), (128, 2048), (1024, 2048), (1024, 2048)]
+    bits, group = 5, 32
+    fmt = pkg.affine_format(bits, group, True)
+    x1 = synth.activations(160, 1, 2048, item=0)[0]
+    x2 = synth.activations(160, 1, 2048, item=1)[0]
+    xd1, xd2 = weights.to_device(x1, DEV), weights.to_device(x2, DEV)
+    entries, mats, which = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        m = synth.affine_matrix(161, N, K, bits, group, True, item=i)
+        use2 = i >= 3
+        entries.append((weights.pack_affine(m, DEV), N, K, xd2 if use2 else xd1,
+                        torch.empty(N, dtype=torch.float32, device=DEV)))
+        mats.append(m)
+        which.append(x2 if use2 else x1)
+    plan = pkg.qg_batch_plan_build(fmt, 1, entries, pkg.OUT_F32)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    for (p, N, K, xd, y), m, x in zip(entries, mats, which):
+        ref = oracle.affine_gemv(m.codes, m.scales, m.biases, x, group, True)
+        assert_f32_close(to_np(y), ref, what="N=%d" % N)
