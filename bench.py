@@ -664,6 +664,34 @@ def main():
                         "against a 16-row bf16 tile (m16_*); calls captured in a HIP graph",
             "rows": rows}
 
+        # the decode step's 253 projection shapes as 4-bit affine weights (group
+        # 64, fp16; the Q4 step's bytes), all in one grouped launch
+        fs = _lib.affine_format(4, GA)
+        gs = torch.Generator(device="cuda")
+        gs.manual_seed(args.seed + 100)
+        sentries, bs = [], 0.0
+        for item, name, N, K in synth.decode_step_shapes():
+            scodes = torch.randint(0, 16, (N, K), dtype=torch.uint8, device="cuda", generator=gs)
+            ssc = ((torch.rand(N, K // GA, device="cuda", generator=gs) + 0.05) * 0.02).half().view(torch.int16)
+            sbi = (torch.randn(N, K // GA, device="cuda", generator=gs) * 0.01).half().view(torch.int16)
+            sp = _lib.qgemv_pack(fs, N, K, scodes, ssc, sbi)
+            del scodes, ssc, sbi
+            sx = torch.randn(K, device="cuda", generator=gs).to(torch.bfloat16)
+            sentries.append((sp, N, K, sx, torch.empty(N, dtype=torch.bfloat16, device="cuda")))
+            bs += roofline.affine_gemv_bytes(4, GA, N, K)
+        splan = _lib.qg_batch_plan_build(fs, 1, sentries)
+        mss = workloads.time_graph_ms(lambda: _lib.qg_batch_run(splan), 20)
+        result["affine_family"]["step_one_launch"] = {
+            "workload": "the decode step's 253 projection shapes (36 layers of q, k, v, o, gate, "
+                        "up, down and the 4096->151936 head) as 4-bit affine weights, group 64, "
+                        "fp16 scale and bias, one seeded x each, M=1, one grouped launch per step "
+                        "captured in a HIP graph",
+            "ms": round(mss, 4), "GBs": round(bs / (mss * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * bs / (mss * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1),
+            "pct_of_plain_read": round(100 * bs / (mss * 1e-3) / 1e9 / plain_best, 1)}
+        log("affine 4-bit decode step, one launch: %.4f ms" % mss)
+        del splan, sentries
+
         # MXFP4 routed experts, one token through one layer
         moe = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16)
         msm = workloads.time_graph_ms(moe.run, 64)
