@@ -125,7 +125,7 @@ struct AgBatch {
 // chain per group; returns y plus the lane's share of the tile.
 template <int BITS, int GPT, bool BF16S>
 __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint16_t *xrun,
-                                         const float *xg, float y) {
+                                         const float *xg, float y, const AgConsts &k) {
     constexpr int CPG = 4 / GPT;  // runs per group
 #pragma unroll
     for (int t = 0; t < GPT; ++t) {
@@ -137,9 +137,9 @@ __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint1
             const unsigned xp[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                a0 = dot2_bf16(ag_bf16_pair<BITS, GPT>(T, 4 * i + h), xp[h], a0);
+                a0 = dot2_bf16(ag_bf16_pair<BITS, GPT>(T, 4 * i + h, k), xp[h], a0);
                 if constexpr (BITS == 8)
-                    a1 = dot2_bf16(ag_pair_hi<BITS, GPT>(T, 4 * i + h), xp[h], a1);
+                    a1 = dot2_bf16(ag_pair_hi<BITS, GPT>(T, 4 * i + h, k), xp[h], a1);
             }
         }
         const float X = xg[t];
@@ -183,6 +183,7 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
     float *xsl = reinterpret_cast<float *>(smem + AG_LDS_PART + (size_t)KS * 2);  // [KS / 32 * GPT]
     const unsigned tb = (unsigned)affine_tile_bytes(BITS, AFF_TILE_K / GPT);
     const size_t rb_bytes = (size_t)P * tb;
+    const AgConsts kc = ag_consts<BITS>();
     // stage x, then the sum of each lane-group's x over each group of each
     // tile (its runs in k order, each run's 8 values in a fixed tree):
     // xsl[(4 tp + kg) GPT + t]
@@ -245,7 +246,7 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
                     __builtin_amdgcn_sched_barrier(0);
                     const int tp = cb * AG_TPB + q;
                     acc = ag_tile<BITS, GPT, BF16S>(Cur.t[q], xl + tp * AFF_TILE_K + 8 * kg,
-                                                    xsl + (4 * tp + kg) * GPT, acc);
+                                                    xsl + (4 * tp + kg) * GPT, acc, kc);
                 }
                 if (!nvalid || ni != ci) {  // the wave's last batch of this rowblock
                     acc = ag_reduce_kslices(acc);

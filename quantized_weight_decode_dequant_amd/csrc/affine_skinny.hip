@@ -86,7 +86,8 @@ __device__ __forceinline__ void as_stage(const uint16_t *X, int M, int K, int se
 // One tile (index pl within the staged segment) into acc.
 template <int BITS, int GPT, int MT, bool BF16S>
 __device__ __forceinline__ void as_tile(const AgTile<BITS, GPT> &T, const uint16_t *xl,
-                                        const float *xs, int pl, int lane, f32x4_t acc[MT]) {
+                                        const float *xs, int pl, int lane, f32x4_t acc[MT],
+                                        const AgConsts &k) {
     typedef AsCfg<MT> C;
     constexpr int CPG = 4 / GPT;  // MFMA steps (32-k blocks) per group
     const int kg = lane >> 4, r16 = lane & 15;
@@ -96,13 +97,15 @@ __device__ __forceinline__ void as_tile(const AgTile<BITS, GPT> &T, const uint16
     for (int mt = 0; mt < MT; ++mt) Cl[mt] = Ch[mt] = Z;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const u32x4_t bl = {ag_bf16_pair<BITS, GPT>(T, 4 * i), ag_bf16_pair<BITS, GPT>(T, 4 * i + 1),
-                            ag_bf16_pair<BITS, GPT>(T, 4 * i + 2),
-                            ag_bf16_pair<BITS, GPT>(T, 4 * i + 3)};
+        const u32x4_t bl = {ag_bf16_pair<BITS, GPT>(T, 4 * i, k),
+                            ag_bf16_pair<BITS, GPT>(T, 4 * i + 1, k),
+                            ag_bf16_pair<BITS, GPT>(T, 4 * i + 2, k),
+                            ag_bf16_pair<BITS, GPT>(T, 4 * i + 3, k)};
         u32x4_t bh = {0u, 0u, 0u, 0u};
         if constexpr (BITS == 8)
-            bh = u32x4_t{ag_pair_hi<BITS, GPT>(T, 4 * i), ag_pair_hi<BITS, GPT>(T, 4 * i + 1),
-                         ag_pair_hi<BITS, GPT>(T, 4 * i + 2), ag_pair_hi<BITS, GPT>(T, 4 * i + 3)};
+            bh = u32x4_t{ag_pair_hi<BITS, GPT>(T, 4 * i, k), ag_pair_hi<BITS, GPT>(T, 4 * i + 1, k),
+                         ag_pair_hi<BITS, GPT>(T, 4 * i + 2, k),
+                         ag_pair_hi<BITS, GPT>(T, 4 * i + 3, k)};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(
@@ -165,7 +168,7 @@ __device__ __forceinline__ void as_block(AsBatch<BITS, GPT> &A, AsBatch<BITS, GP
                                          const uint8_t *packed, size_t rb_bytes, unsigned tb,
                                          int first, int i0, int n, int pbase, int pn,
                                          const uint16_t *xl, const float *xs, int lane,
-                                         f32x4_t acc[AsCfg<MT>::R][MT]) {
+                                         f32x4_t acc[AsCfg<MT>::R][MT], const AgConsts &k) {
     typedef AsCfg<MT> C;
     constexpr int TPB = AsBatchSize<BITS, GPT>::TPB;
     const int nbs = (pn + TPB - 1) / TPB, nbe = nbs + (nbs & 1);
@@ -187,7 +190,7 @@ __device__ __forceinline__ void as_block(AsBatch<BITS, GPT> &A, AsBatch<BITS, GP
                     __builtin_amdgcn_sched_barrier(0);
                     ag_tile_load<BITS, GPT>(B.t[q], rs, (bt + 1) * TPB + q, pn, tb, lane);
                     __builtin_amdgcn_sched_barrier(0);
-                    as_tile<BITS, GPT, MT, BF16S>(A.t[q], xl, xs, bt * TPB + q, lane, acc[r]);
+                    as_tile<BITS, GPT, MT, BF16S>(A.t[q], xl, xs, bt * TPB + q, lane, acc[r], k);
                 }
             }
             // batch bt + 1 (in B) computed while bt + 2, or the next
@@ -203,7 +206,7 @@ __device__ __forceinline__ void as_block(AsBatch<BITS, GPT> &A, AsBatch<BITS, GP
                     __builtin_amdgcn_sched_barrier(0);
                     ag_tile_load<BITS, GPT>(A.t[q], rs, tn + q, pn, tb, lane);
                     __builtin_amdgcn_sched_barrier(0);
-                    as_tile<BITS, GPT, MT, BF16S>(B.t[q], xl, xs, (bt + 1) * TPB + q, lane, acc[r]);
+                    as_tile<BITS, GPT, MT, BF16S>(B.t[q], xl, xs, (bt + 1) * TPB + q, lane, acc[r], k);
                 }
             }
         }
@@ -244,6 +247,7 @@ affine_skinny_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restr
     const int first = u0 + wave;
     const int mine = (u1 - u0 > wave) ? (u1 - u0 - wave + C::WAVES - 1) / C::WAVES : 0;
     const int slots = (u1 - u0 + C::WAVES - 1) / C::WAVES;  // wave 0 has the most
+    const AgConsts kc = ag_consts<BITS>();
     AsBatch<BITS, GPT> A, B;
     f32x4_t acc[R][MT];
 #pragma unroll 1
@@ -265,7 +269,7 @@ affine_skinny_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restr
             }
             if (n > 0)
                 as_block<BITS, GPT, MT, BF16S>(A, B, packed, rb_bytes, tb, first, i0, n, pbase, pn,
-                                               xl, xs, lane, acc);
+                                               xl, xs, lane, acc, kc);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r)

@@ -57,31 +57,63 @@ __device__ __forceinline__ void ag_tile_load(AgTile<BITS, GPT> &T, __amdgpu_buff
     ag_ld<GPT>(T.sb, rs, 256u * BITS + 4u * GPT * (lane & 15), to);
 }
 
-// Pair j of plane (W, words p) as two small integers in the word's halves.
-template <int W, int NW>
-__device__ __forceinline__ unsigned ag_pair(const unsigned (&p)[NW], int j) {
-    constexpr int PER = 16 / W;
-    constexpr unsigned M = ((1u << W) - 1u) * 0x00010001u;
-    return (p[j / PER] >> (W * (j % PER))) & M;
-}
-
 constexpr unsigned AG_MAGIC = 0x43004300u;  // bf16 128 in both halves
 
-// Pair j as two bf16 values 128 + q (for 8 bits: 128 + the low nibble; the
-// high nibble's pair comes from ag_pair_hi).
-template <int BITS, int GPT>
-__device__ __forceinline__ unsigned ag_bf16_pair(const AgTile<BITS, GPT> &T, int j) {
+// The constants of the unpack, held in VGPRs: gfx9 VOP3 instructions read at
+// most one SGPR or literal, so with the mask and the magic both in registers
+// (v & mask) | magic selects to one v_and_or_b32.  Made opaque once per
+// kernel so that the compiler does not re-materialize them as literals at
+// every use.  m0 masks a code of plane 0 in both halves; m1 a code of plane
+// 1 moved to its place above plane 0 (8 bits: the high nibble in place).
+struct AgConsts {
+    unsigned magic, m0, m1;
+};
+
+__device__ __forceinline__ unsigned ag_opaque(unsigned c) {
+    asm volatile("" : "+v"(c));
+    return c;
+}
+
+template <int BITS>
+__device__ __forceinline__ AgConsts ag_consts() {
     typedef AffPlanes<BITS> PL;
-    const unsigned v0 = ag_pair<PL::W0>(T.p0, j);
-    if constexpr (PL::NP == 2 && BITS != 8)
-        return (ag_pair<PL::W1>(T.p1, j) << PL::O1) | v0 | AG_MAGIC;
-    else
-        return v0 | AG_MAGIC;
+    constexpr unsigned m0 = ((1u << PL::W0) - 1u) * 0x00010001u;
+    constexpr unsigned m1 =
+        BITS == 8 ? 0x000F000Fu : ((((1u << PL::W1) - 1u) << PL::O1) * 0x00010001u);
+    return AgConsts{ag_opaque(AG_MAGIC), ag_opaque(m0), PL::NP == 2 ? ag_opaque(m1) : 0u};
+}
+
+// (a & m) | c as one v_and_or_b32, written out for the two-plane merge: the
+// compiler would otherwise regroup two of them into two ands and an or3.
+__device__ __forceinline__ unsigned ag_and_or(unsigned a, unsigned m, unsigned c) {
+    unsigned r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+    return r;
+}
+
+// Pair j (0..15; a compile-time index once unrolled) as two bf16 values
+// 128 + q, one per 16-bit half (for 8 bits: 128 + the low nibble; the high
+// nibble's pair comes from ag_pair_hi).  Plane 1's bits are shifted straight
+// to their place above plane 0's and merged in by a second and-or.
+template <int BITS, int GPT>
+__device__ __forceinline__ unsigned ag_bf16_pair(const AgTile<BITS, GPT> &T, int j,
+                                                 const AgConsts &k) {
+    typedef AffPlanes<BITS> PL;
+    constexpr int PER0 = 16 / PL::W0;
+    const unsigned a = T.p0[j / PER0] >> (PL::W0 * (j % PER0));
+    if constexpr (PL::NP == 2 && BITS != 8) {
+        constexpr int PER1 = 16 / PL::W1;
+        const int sh = PL::W1 * (j % PER1) - PL::O1;
+        const unsigned w = T.p1[j / PER1];
+        return ag_and_or(sh >= 0 ? w >> sh : w << -sh, k.m1, ag_and_or(a, k.m0, k.magic));
+    } else {
+        return (a & k.m0) | k.magic;
+    }
 }
 template <int BITS, int GPT>
-__device__ __forceinline__ unsigned ag_pair_hi(const AgTile<BITS, GPT> &T, int j) {
-    typedef AffPlanes<BITS> PL;
-    return ag_pair<PL::W1>(T.p1, j) | AG_MAGIC;
+__device__ __forceinline__ unsigned ag_pair_hi(const AgTile<BITS, GPT> &T, int j,
+                                               const AgConsts &k) {
+    return ((T.p1[j / 4] >> (4 * (j % 4))) & k.m1) | k.magic;
 }
 
 __device__ __forceinline__ float ag_scale(unsigned sb, bool bf16) {
