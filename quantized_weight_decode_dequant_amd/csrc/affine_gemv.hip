@@ -120,12 +120,45 @@ struct AgBatch {
     AgTile<BITS, GPT> t[AG_TPB];
 };
 
+// 2-bit codes with fewer shifts.  The bf16 exponent decides where a code's
+// bits sit in the mantissa: with the exponent of 128 a code in bits 0-1
+// reads as 128 + q, with that of 32 a code in bits 2-3 as 32 + q, with that
+// of 8 a code in bits 4-5 as 8 + q.  So one word gives the pairs at its
+// positions 0, 1, 2 by masking alone, its copy shifted by 6 those at 3, 4, 5
+// and its copy shifted by 12 those at 6, 7: two shifts per word instead of
+// seven.  The dot products then carry sum_k off(k) x_k, off = 128, 32 or 8
+// by position, which is staged per group beside the plain sums of x.
+struct Ag2Consts {
+    unsigned m[3], g[3];
+};
+
+__device__ __forceinline__ Ag2Consts ag2_consts() {
+    return Ag2Consts{{ag_opaque(0x00030003u), ag_opaque(0x000C000Cu), ag_opaque(0x00300030u)},
+                     {ag_opaque(0x43004300u), ag_opaque(0x42004200u), ag_opaque(0x41004100u)}};
+}
+
+// The offset of pair position s (0..7) of a 2-bit word.
+__host__ __device__ constexpr float ag2_off(int s) {
+    return s % 3 == 0 ? 128.f : s % 3 == 1 ? 32.f : 8.f;
+}
+
+// Pair j (0..15, compile-time once unrolled): off(j % 8) + q in both halves.
+template <int GPT>
+__device__ __forceinline__ unsigned ag2_pair(const AgTile<2, GPT> &T, int j, const Ag2Consts &k) {
+    const unsigned w = T.p0[j / 8];
+    const int s = j % 8;
+    const unsigned u = s < 3 ? w : s < 6 ? w >> 6 : w >> 12;
+    return (u & k.m[s % 3]) | k.g[s % 3];
+}
+
 // One tile: xrun = the lane's x of run 0 (run i at xrun + 32 i, 8 bf16),
-// xg = the sums of the lane's x over each of the tile's GPT groups.  One dot
+// xg = the sums of the lane's x over each of the tile's GPT groups (and, for
+// 2-bit codes, xw = the same sums weighted by the pairs' offsets).  One dot
 // chain per group; returns y plus the lane's share of the tile.
 template <int BITS, int GPT, bool BF16S>
 __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint16_t *xrun,
-                                         const float *xg, float y, const AgConsts &k) {
+                                         const float *xg, const float *xw, float y,
+                                         const AgConsts &k, const Ag2Consts &k2) {
     constexpr int CPG = 4 / GPT;  // runs per group
 #pragma unroll
     for (int t = 0; t < GPT; ++t) {
@@ -137,13 +170,16 @@ __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint1
             const unsigned xp[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                a0 = dot2_bf16(ag_bf16_pair<BITS, GPT>(T, 4 * i + h, k), xp[h], a0);
+                if constexpr (BITS == 2)
+                    a0 = dot2_bf16(ag2_pair<GPT>(T, 4 * i + h, k2), xp[h], a0);
+                else
+                    a0 = dot2_bf16(ag_bf16_pair<BITS, GPT>(T, 4 * i + h, k), xp[h], a0);
                 if constexpr (BITS == 8)
                     a1 = dot2_bf16(ag_pair_hi<BITS, GPT>(T, 4 * i + h, k), xp[h], a1);
             }
         }
         const float X = xg[t];
-        float D = fmaf(-128.f, X, a0);
+        float D = BITS == 2 ? a0 - xw[t] : fmaf(-128.f, X, a0);
         if constexpr (BITS == 8) D = fmaf(16.f, fmaf(-128.f, X, a1), D);
         const unsigned sb = T.sb[t];
         y = fmaf(ag_scale(sb, BF16S), D, fmaf(ag_bias(sb, BF16S), X, y));
@@ -162,10 +198,10 @@ __device__ __forceinline__ float ag_reduce_kslices(float a) {
 // read the previous product's sums; then x and its group sums.
 constexpr size_t AG_LDS_PART = (size_t)AG_RMAX * AG_WAVES * 16 * 4;
 
-template <int GPT>
+template <int BITS, int GPT>
 static size_t ag_lds_bytes(int64_t K) {
     const int64_t KS = ceil_div(ceil_div(K, AFF_TILE_K), AG_TPB) * AG_TPB * AFF_TILE_K;
-    return AG_LDS_PART + (size_t)KS * 2 + (size_t)(KS / 32) * GPT * 4;
+    return AG_LDS_PART + (size_t)KS * 2 + (size_t)(KS / 32) * GPT * 4 * (BITS == 2 ? 2 : 1);
 }
 
 // Rowblocks [u0, u1) of one product.
@@ -181,12 +217,16 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
     float *part = reinterpret_cast<float *>(smem);                               // [RMAX][WAVES][16]
     uint16_t *xl = reinterpret_cast<uint16_t *>(smem + AG_LDS_PART);             // [KS] bf16
     float *xsl = reinterpret_cast<float *>(smem + AG_LDS_PART + (size_t)KS * 2);  // [KS / 32 * GPT]
+    float *xwl = xsl + KS / 32 * GPT;  // 2-bit codes: [KS / 32 * GPT]
     const unsigned tb = (unsigned)affine_tile_bytes(BITS, AFF_TILE_K / GPT);
     const size_t rb_bytes = (size_t)P * tb;
     const AgConsts kc = ag_consts<BITS>();
+    Ag2Consts k2{};
+    if constexpr (BITS == 2) k2 = ag2_consts();
     // stage x, then the sum of each lane-group's x over each group of each
     // tile (its runs in k order, each run's 8 values in a fixed tree):
-    // xsl[(4 tp + kg) GPT + t]
+    // xsl[(4 tp + kg) GPT + t]; for 2-bit codes also the offset-weighted sums
+    // xwl, pair h of run i weighted by ag2_off(4 (i % 2) + h)
     for (int c = tid; c < KS / 8; c += AG_THREADS) {
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (8 * c < K) v = reinterpret_cast<const uint4 *>(x)[c];
@@ -195,15 +235,22 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
     __syncthreads();
     for (int e = tid; e < KS / 32 * GPT; e += AG_THREADS) {
         const int t = e % GPT, tk = e / GPT, tp = tk >> 2, ckg = tk & 3;
-        float sum = 0.f;
+        float sum = 0.f, wsum = 0.f;
 #pragma unroll
         for (int c = 0; c < 4 / GPT; ++c) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(
-                xl + tp * AFF_TILE_K + 32 * (t * (4 / GPT) + c) + 8 * ckg);
-            sum += ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
-                   ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+            const int i = t * (4 / GPT) + c;
+            const uint4 v = *reinterpret_cast<const uint4 *>(xl + tp * AFF_TILE_K + 32 * i + 8 * ckg);
+            const float p0 = bf16_lo(v.x) + bf16_hi(v.x), p1 = bf16_lo(v.y) + bf16_hi(v.y);
+            const float p2 = bf16_lo(v.z) + bf16_hi(v.z), p3 = bf16_lo(v.w) + bf16_hi(v.w);
+            sum += (p0 + p1) + (p2 + p3);
+            if constexpr (BITS == 2) {
+                const int s0 = 4 * (i % 2);
+                wsum += (ag2_off(s0) * p0 + ag2_off(s0 + 1) * p1) +
+                        (ag2_off(s0 + 2) * p2 + ag2_off(s0 + 3) * p3);
+            }
         }
         xsl[e] = sum;
+        if constexpr (BITS == 2) xwl[e] = wsum;
     }
 #pragma unroll 1
     for (int ub = u0; ub < u1; ub += AG_RMAX) {
@@ -246,7 +293,8 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
                     __builtin_amdgcn_sched_barrier(0);
                     const int tp = cb * AG_TPB + q;
                     acc = ag_tile<BITS, GPT, BF16S>(Cur.t[q], xl + tp * AFF_TILE_K + 8 * kg,
-                                                    xsl + (4 * tp + kg) * GPT, acc, kc);
+                                                    xsl + (4 * tp + kg) * GPT,
+                                                    xwl + (4 * tp + kg) * GPT, acc, kc, k2);
                 }
                 if (!nvalid || ni != ci) {  // the wave's last batch of this rowblock
                     acc = ag_reduce_kslices(acc);
@@ -306,7 +354,7 @@ affine_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restri
 template <bool LIST, int BITS, int GPT>
 static hipError_t launch_ag(const WorkItem *items, const WorkStart *starts, const WorkItem &it,
                             int grid, int64_t kmax, bool bf16, hipStream_t s) {
-    const size_t lds = ag_lds_bytes<GPT>(kmax);
+    const size_t lds = ag_lds_bytes<BITS, GPT>(kmax);
     if (bf16)
         hipLaunchKernelGGL((affine_gemv_kernel<LIST, BITS, GPT, true>), dim3(grid),
                            dim3(AG_THREADS), lds, s, items, starts, it);
