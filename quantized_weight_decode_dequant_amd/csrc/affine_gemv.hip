@@ -120,40 +120,59 @@ struct AgBatch {
     AgTile<BITS, GPT> t[AG_TPB];
 };
 
-// 2-bit codes with fewer shifts.  The bf16 exponent decides where a code's
-// bits sit in the mantissa: with the exponent of 128 a code in bits 0-1
-// reads as 128 + q, with that of 32 a code in bits 2-3 as 32 + q, with that
-// of 8 a code in bits 4-5 as 8 + q.  So one word gives the pairs at its
-// positions 0, 1, 2 by masking alone, its copy shifted by 6 those at 3, 4, 5
-// and its copy shifted by 12 those at 6, 7: two shifts per word instead of
-// seven.  The dot products then carry sum_k off(k) x_k, off = 128, 32 or 8
-// by position, which is staged per group beside the plain sums of x.
+// 2- and 3-bit codes with fewer shifts.  The bf16 exponent decides where a
+// code's bits sit in the mantissa: with the exponent of 128 a code in bits
+// 0-2 reads as 128 + q, with that of 32 a code in bits 2-4 as 32 + q, with
+// that of 8 a code in bits 4-6 as 8 + q.  So one plane-0 word (2-bit fields)
+// gives the pairs at its positions 0, 1, 2 by masking alone, its copy shifted
+// by 6 those at 3, 4, 5 and its copy shifted by 12 those at 6, 7: two shifts
+// per word instead of seven.  A 3-bit code's plane-1 bit is shifted to just
+// above its plane-0 field and merged in.  The dot products then carry
+// sum_k off(k) x_k, off = 128, 32 or 8 by position, which is staged per
+// group beside the plain sums of x.
+constexpr bool ag_inplace(int bits) { return bits <= 3; }
+
 struct Ag2Consts {
-    unsigned m[3], g[3];
+    unsigned m[3], g[3], b[3];
 };
 
+template <int BITS>
 __device__ __forceinline__ Ag2Consts ag2_consts() {
-    return Ag2Consts{{ag_opaque(0x00030003u), ag_opaque(0x000C000Cu), ag_opaque(0x00300030u)},
-                     {ag_opaque(0x43004300u), ag_opaque(0x42004200u), ag_opaque(0x41004100u)}};
+    Ag2Consts k{{ag_opaque(0x00030003u), ag_opaque(0x000C000Cu), ag_opaque(0x00300030u)},
+                {ag_opaque(0x43004300u), ag_opaque(0x42004200u), ag_opaque(0x41004100u)},
+                {0u, 0u, 0u}};
+    if constexpr (BITS == 3) {
+        k.b[0] = ag_opaque(0x00040004u);
+        k.b[1] = ag_opaque(0x00100010u);
+        k.b[2] = ag_opaque(0x00400040u);
+    }
+    return k;
 }
 
-// The offset of pair position s (0..7) of a 2-bit word.
+// The offset of pair position s (0..7) of a plane-0 word.
 __host__ __device__ constexpr float ag2_off(int s) {
     return s % 3 == 0 ? 128.f : s % 3 == 1 ? 32.f : 8.f;
 }
 
 // Pair j (0..15, compile-time once unrolled): off(j % 8) + q in both halves.
-template <int GPT>
-__device__ __forceinline__ unsigned ag2_pair(const AgTile<2, GPT> &T, int j, const Ag2Consts &k) {
+template <int BITS, int GPT>
+__device__ __forceinline__ unsigned ag2_pair(const AgTile<BITS, GPT> &T, int j,
+                                             const Ag2Consts &k) {
     const unsigned w = T.p0[j / 8];
-    const int s = j % 8;
+    const int s = j % 8, r = s % 3;
     const unsigned u = s < 3 ? w : s < 6 ? w >> 6 : w >> 12;
-    return (u & k.m[s % 3]) | k.g[s % 3];
+    if constexpr (BITS == 3) {
+        const unsigned w1 = T.p1[0];
+        const int sh = j - (2 * r + 2);  // plane-1 bit j goes to bit 2 r + 2
+        return ag_and_or(sh >= 0 ? w1 >> sh : w1 << -sh, k.b[r], ag_and_or(u, k.m[r], k.g[r]));
+    } else {
+        return (u & k.m[r]) | k.g[r];
+    }
 }
 
 // One tile: xrun = the lane's x of run 0 (run i at xrun + 32 i, 8 bf16),
 // xg = the sums of the lane's x over each of the tile's GPT groups (and, for
-// 2-bit codes, xw = the same sums weighted by the pairs' offsets).  One dot
+// 2- and 3-bit codes, xw = the same sums weighted by the pairs' offsets).  One dot
 // chain per group; returns y plus the lane's share of the tile.
 template <int BITS, int GPT, bool BF16S>
 __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint16_t *xrun,
@@ -170,8 +189,8 @@ __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint1
             const unsigned xp[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                if constexpr (BITS == 2)
-                    a0 = dot2_bf16(ag2_pair<GPT>(T, 4 * i + h, k2), xp[h], a0);
+                if constexpr (ag_inplace(BITS))
+                    a0 = dot2_bf16(ag2_pair<BITS, GPT>(T, 4 * i + h, k2), xp[h], a0);
                 else
                     a0 = dot2_bf16(ag_bf16_pair<BITS, GPT>(T, 4 * i + h, k), xp[h], a0);
                 if constexpr (BITS == 8)
@@ -179,7 +198,7 @@ __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint1
             }
         }
         const float X = xg[t];
-        float D = BITS == 2 ? a0 - xw[t] : fmaf(-128.f, X, a0);
+        float D = ag_inplace(BITS) ? a0 - xw[t] : fmaf(-128.f, X, a0);
         if constexpr (BITS == 8) D = fmaf(16.f, fmaf(-128.f, X, a1), D);
         const unsigned sb = T.sb[t];
         y = fmaf(ag_scale(sb, BF16S), D, fmaf(ag_bias(sb, BF16S), X, y));
@@ -201,7 +220,7 @@ constexpr size_t AG_LDS_PART = (size_t)AG_RMAX * AG_WAVES * 16 * 4;
 template <int BITS, int GPT>
 static size_t ag_lds_bytes(int64_t K) {
     const int64_t KS = ceil_div(ceil_div(K, AFF_TILE_K), AG_TPB) * AG_TPB * AFF_TILE_K;
-    return AG_LDS_PART + (size_t)KS * 2 + (size_t)(KS / 32) * GPT * 4 * (BITS == 2 ? 2 : 1);
+    return AG_LDS_PART + (size_t)KS * 2 + (size_t)(KS / 32) * GPT * 4 * (ag_inplace(BITS) ? 2 : 1);
 }
 
 // Rowblocks [u0, u1) of one product.
@@ -217,15 +236,15 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
     float *part = reinterpret_cast<float *>(smem);                               // [RMAX][WAVES][16]
     uint16_t *xl = reinterpret_cast<uint16_t *>(smem + AG_LDS_PART);             // [KS] bf16
     float *xsl = reinterpret_cast<float *>(smem + AG_LDS_PART + (size_t)KS * 2);  // [KS / 32 * GPT]
-    float *xwl = xsl + KS / 32 * GPT;  // 2-bit codes: [KS / 32 * GPT]
+    float *xwl = xsl + KS / 32 * GPT;  // 2- and 3-bit codes: [KS / 32 * GPT]
     const unsigned tb = (unsigned)affine_tile_bytes(BITS, AFF_TILE_K / GPT);
     const size_t rb_bytes = (size_t)P * tb;
     const AgConsts kc = ag_consts<BITS>();
     Ag2Consts k2{};
-    if constexpr (BITS == 2) k2 = ag2_consts();
+    if constexpr (ag_inplace(BITS)) k2 = ag2_consts<BITS>();
     // stage x, then the sum of each lane-group's x over each group of each
     // tile (its runs in k order, each run's 8 values in a fixed tree):
-    // xsl[(4 tp + kg) GPT + t]; for 2-bit codes also the offset-weighted sums
+    // xsl[(4 tp + kg) GPT + t]; for 2- and 3-bit codes also the offset-weighted sums
     // xwl, pair h of run i weighted by ag2_off(4 (i % 2) + h)
     for (int c = tid; c < KS / 8; c += AG_THREADS) {
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -243,14 +262,14 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
             const float p0 = bf16_lo(v.x) + bf16_hi(v.x), p1 = bf16_lo(v.y) + bf16_hi(v.y);
             const float p2 = bf16_lo(v.z) + bf16_hi(v.z), p3 = bf16_lo(v.w) + bf16_hi(v.w);
             sum += (p0 + p1) + (p2 + p3);
-            if constexpr (BITS == 2) {
+            if constexpr (ag_inplace(BITS)) {
                 const int s0 = 4 * (i % 2);
                 wsum += (ag2_off(s0) * p0 + ag2_off(s0 + 1) * p1) +
                         (ag2_off(s0 + 2) * p2 + ag2_off(s0 + 3) * p3);
             }
         }
         xsl[e] = sum;
-        if constexpr (BITS == 2) xwl[e] = wsum;
+        if constexpr (ag_inplace(BITS)) xwl[e] = wsum;
     }
 #pragma unroll 1
     for (int ub = u0; ub < u1; ub += AG_RMAX) {
