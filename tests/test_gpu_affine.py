@@ -46,10 +46,12 @@ def test_affine_gemv(bits, group, bf16):
 
 
 # partial tiles (K = 96: three groups of 32; K = 320), one row, more than
-# 32 rowblocks per workgroup, K at its maximum
+# 32 rowblocks per workgroup, K at its maximum (2 and 3 bits at group 32 take
+# the most LDS: x, its group sums and the offset-weighted sums, 80 KB)
 @pytest.mark.parametrize("bits,group,N,K", [(3, 32, 40, 96), (5, 64, 17, 320), (2, 32, 1, 32),
                                             (6, 128, 3000, 256), (8, 64, 33, 24576),
-                                            (4, 128, 70, 24576)])
+                                            (4, 128, 70, 24576), (2, 32, 50, 24576),
+                                            (3, 32, 20, 24576)])
 def test_affine_gemv_shapes(bits, group, N, K):
     note("affine bits=%d g=%d N=%d K=%d" % (bits, group, N, K))
     m = synth.affine_matrix(122, N, K, bits, group, bits % 2 == 1)
@@ -149,7 +151,7 @@ def test_affine_skinny_rows_equal_gemv_rows():
 
 # ------------------------------------------------------------ grouped launch
 BATCH_SHAPES = [(40, 192), (1, 64), (256, 4096), (33, 12288), (100, 1216), (17, 320),
-                (3000, 256), (5, 96), (2, 32), (7, 384)]
+                (3000, 256), (5, 96), (2, 32), (7, 384), (9, 24576)]
 
 
 def _batch(seed, bits, group, bf16, shapes, out_dtype):
