@@ -1,7 +1,7 @@
 """HIP-graph capture of the calls that launch several kernels or read their
 routing from the device: the T-position MoE layer (its grouping kernel
 writes the records the expert kernels read), the M = 16 grouped verification
-pass, and the int8 row-scale and affine GEMVs.  Each captured graph is
+pass, the int8 row-scale and affine GEMVs and the affine 16-row product.  Each captured graph is
 replayed several times with eager work and synchronizations in between, and
 every replay is compared bit for bit with the eager call on the same
 inputs; for the MoE the router output is changed in place between replays,
@@ -110,3 +110,24 @@ def test_graph_weight_only_gemv(kind):
         x.copy_(weights.to_device(synth.activations(137, 1, K, item=rep)[0], DEV))
 
     _replay_matches(graph, y, lambda: run(ye), prepare=perturb)
+
+
+@pytest.mark.parametrize("bits", [2, 5])
+def test_graph_affine_skinny(bits):
+    """The affine verification product (16 rows) captured in a HIP graph: each
+    replay, with a new X staged between replays, equals the eager call on the
+    same X."""
+    M, N, K = 16, 2000, 4096
+    note("graph affine skinny bits=%d" % bits)
+    m = synth.affine_matrix(138, N, K, bits, 64, False)
+    fmt, packed = pkg.affine_format(bits, 64, False), weights.pack_affine(m, DEV)
+    X = weights.to_device(synth.activations(139, M, K), DEV)
+    Y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    Ye = torch.empty_like(Y)
+    run = lambda out: pkg.qgemm_skinny_run(fmt, packed, M, N, K, X, Y=out, out_dtype=pkg.OUT_F32)  # noqa: E731
+    graph = workloads.capture_graph(lambda: run(Y))
+
+    def perturb(rep):
+        X.copy_(weights.to_device(synth.activations(140, M, K, item=rep), DEV))
+
+    _replay_matches(graph, Y, lambda: run(Ye), prepare=perturb)
