@@ -131,6 +131,333 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, command: str):
     print(json.dumps(out, indent=1))
 
 
+def _pmc_dispatches(path, counter):
+    """{kernel name: [counter value per dispatch, in dispatch order]}."""
+    rows = []
+    for r in _csv_rows(path):
+        if _col(r, "Counter_Name", "counter_name") != counter:
+            continue
+        rows.append((int(_col(r, "Dispatch_Id", "dispatch_id")), _col(r, "Kernel_Name", "kernel_name"),
+                     float(_col(r, "Counter_Value", "counter_value"))))
+    out = {}
+    for _, name, v in sorted(rows):
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def _manifest_match(disp, manifest):
+    """Pair the manifest entries of each kernel, in order, with that kernel's
+    last dispatches (the counter pass launches each measured kernel after any
+    incidental use of it, such as copies during set-up); returns
+    [(entry, kernel name, value)] in manifest order."""
+    names = {}
+    for ent in manifest:
+        hit = [k for k in disp if ent["kernel"] in k]
+        if len(hit) != 1:
+            raise SystemExit("kernel %r matches %d dispatch names" % (ent["kernel"], len(hit)))
+        names.setdefault(hit[0], []).append(ent)
+    pos = {}
+    for name, ents in names.items():
+        if len(disp[name]) < len(ents):
+            raise SystemExit("too few dispatches of %r" % name)
+        pos[name] = len(disp[name]) - len(ents)
+    out = []
+    for ent in manifest:
+        name = [k for k in disp if ent["kernel"] in k][0]
+        out.append((ent, name, disp[name][pos[name]]))
+        pos[name] += 1
+    return out
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, manifest_json: str, out_md: str,
+                       command: str):
+    """HBM traffic of every hot kernel from two rocprofv3 --pmc runs of
+    `bench.py --counter-pass` (FETCH_SIZE, then WRITE_SIZE), each counter
+    scaled by what it reads for two reference kernels of known size: a plain
+    1 GiB read (the library's qg_plain_read) and torch's 1 GiB device copy.
+    Writes a markdown table against the algorithmic bytes of each launch, and
+    the decode-step kernel's figure to profiles/traffic_q4_gemv_step.json."""
+    with open(manifest_json) as f:
+        man = json.load(f)
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        disp = _pmc_dispatches(path, counter)
+        res[counter] = _manifest_match(disp, man["kernels"])
+    cal = {}
+    for counter, kind in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+        for ent, name, kib in res[counter]:
+            if ent.get("calibration"):
+                cal.setdefault(counter, {})[ent["calibration"]] = (
+                    kib * 1024 / ent[kind] if ent[kind] else None, name, kib)
+    f_read = cal["FETCH_SIZE"]["plain_read"][0]
+    f_copy_r = cal["FETCH_SIZE"]["copy"][0]
+    f_write = cal["WRITE_SIZE"]["copy"][0]
+    lines = ["# HBM traffic per launch of the hot-path kernels (rocprofv3 counters)", "",
+             "MI355X (gfx950), one GPU. Kernel sources hash `%s` (sha256 over every file "
+             "under csrc/, as bench.py computes it)." % all_sources_hash(), "",
+             "Commands (one counter per run):", "",
+             "```", command, "```", "",
+             "Calibration: FETCH_SIZE reads %.4f x the bytes of a plain 1 GiB read "
+             "(`qg_plain_read`, non-temporal 16-byte loads) and %.4f x the bytes read by "
+             "torch's 1 GiB device copy; WRITE_SIZE reads %.4f x the bytes that copy writes. "
+             "Each kernel's counters below are divided by these factors (read: the plain-read "
+             "factor; write: the copy factor)." % (f_read, f_copy_r, f_write), "",
+             "| kernel | launch | algorithmic read (B) | counted read (B) | ratio | "
+             "algorithmic write (B) | counted write (B) | ratio |",
+             "|---|---|---|---|---|---|---|---|"]
+    rows = []
+    for (ent, name, fk), (_, _, wk) in zip(res["FETCH_SIZE"], res["WRITE_SIZE"]):
+        if ent.get("calibration"):
+            continue
+        rd = fk * 1024 / f_read
+        wr = wk * 1024 / f_write
+        rows.append({"kernel": ent["kernel"], "what": ent["what"], "algorithmic_read": ent["read"],
+                     "counted_read": rd, "algorithmic_write": ent["write"], "counted_write": wr})
+        lines.append("| `%s` | %s | %d | %d | %.4f | %d | %d | %.3f |" % (
+            ent["kernel"], ent["what"], ent["read"], rd, rd / ent["read"], ent["write"], wr,
+            wr / ent["write"] if ent["write"] else float("nan")))
+    lines += ["", "Raw counter values (KiB per dispatch) are in the CSVs of the same commands; "
+              "counted bytes = raw KiB x 1024 / factor."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    step = [r for r in rows if r["kernel"] == STEP_KERNEL]
+    if step:
+        s = step[0]
+        rec = {"command": command, "kernel_source_hash": kernel_source_hash(),
+               "FETCH_SIZE": {"step_kernel": STEP_KERNEL, "plain_read_factor": f_read,
+                              "copy_read_factor": f_copy_r,
+                              "step_bytes_scaled": s["counted_read"]},
+               "WRITE_SIZE": {"step_kernel": STEP_KERNEL, "copy_factor": f_write,
+                              "step_bytes_scaled": s["counted_write"]},
+               "hbm_bytes_per_launch": int(s["counted_read"] + s["counted_write"])}
+        with open(os.path.join(ROOT, "profiles", "traffic_q4_gemv_step.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+
+
+MI355X_CUS, MI355X_SIMDS, MI355X_XCDS = 256, 1024, 8
+
+
+def summarize_sq(csvs, manifest_json: str, out_md: str, command: str):
+    """Per-launch SQ / TCC counters of `bench.py --counter-pass` runs (one
+    rocprofv3 --pmc run per CSV, each with GRBM_GUI_ACTIVE), with the
+    derived figures (GPU cycles = GRBM_GUI_ACTIVE per XCD): VALU busy =
+    SQ_ACTIVE_INST_VALU / CUs / GPU cycles, MFMA
+    busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / GPU cycles, LDS active =
+    SQ_ACTIVE_INST_LDS / CUs / GPU cycles, and instruction counts per 1 KB of
+    algorithmic read bytes."""
+    with open(manifest_json) as f:
+        man = [e for e in json.load(f)["kernels"] if not e.get("calibration")]
+    vals = [dict() for _ in man]
+    counters = []
+    for path in csvs:
+        rows = _csv_rows(path)
+        for c in sorted({_col(r, "Counter_Name", "counter_name") for r in rows}):
+            disp = _pmc_dispatches(path, c)
+            try:
+                hits = _manifest_match(disp, man)
+            except SystemExit:
+                continue
+            if c not in counters:
+                counters.append(c)
+            for i, (_, _, v) in enumerate(hits):
+                vals[i]["%s@%s" % (c, path)] = v
+    lines = ["# SQ / TCC counters per launch of the hot-path kernels", "",
+             "MI355X (gfx950), one GPU. Kernel sources hash `%s`." % all_sources_hash(), "",
+             "Commands (one counter set per run, each with GRBM_GUI_ACTIVE for the busy "
+             "percentages of that run):", "", "```", command, "```", ""]
+    derived = []
+    for i, ent in enumerate(man):
+        row = {"kernel": ent["kernel"], "what": ent["what"]}
+        kb = ent["read"] / 1024.0
+        for path in csvs:
+            g = vals[i].get("GRBM_GUI_ACTIVE@%s" % path)
+            if g:
+                # rocprofv3 sums the counter over its 8 instances (one per
+                # XCD); the busy percentages use the per-XCD cycle count
+                g = g / MI355X_XCDS
+            for c in counters:
+                v = vals[i].get("%s@%s" % (c, path))
+                if v is None or c == "GRBM_GUI_ACTIVE":
+                    continue
+                row[c] = v
+                if g:
+                    if c == "SQ_ACTIVE_INST_VALU":
+                        row["VALU busy %"] = 100 * v / MI355X_CUS / g
+                    elif c == "SQ_VALU_MFMA_BUSY_CYCLES":
+                        row["MFMA busy %"] = 100 * v / MI355X_SIMDS / g
+                    elif c == "SQ_ACTIVE_INST_LDS":
+                        row["LDS active %"] = 100 * v / MI355X_CUS / g
+                    elif c == "SQ_LDS_BANK_CONFLICT":
+                        row["LDS bank conflict %"] = 100 * v / MI355X_CUS / g
+                if c.startswith("SQ_INSTS_"):
+                    row[c + " per KB"] = v / kb
+            if g:
+                row["GPU cycles"] = g
+        derived.append(row)
+    keys = []
+    for r in derived:
+        for k in r:
+            if k not in ("kernel", "what") and k not in keys:
+                keys.append(k)
+    lines.append("| kernel | launch | " + " | ".join(keys) + " |")
+    lines.append("|---|---|" + "---|" * len(keys))
+    for r in derived:
+        cells = []
+        for k in keys:
+            v = r.get(k)
+            cells.append("" if v is None else ("%.1f" % v if abs(v) < 1e4 else "%.4g" % v))
+        lines.append("| `%s` | %s | %s |" % (r["kernel"], r["what"], " | ".join(cells)))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def all_sources_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_weight_decode_dequant_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_pass(manifest_path: str, seed: int = 0):
+    """Launch every measured hot-path kernel once, plus the two calibration
+    kernels, and write the manifest: per launch, in launch order, the kernel
+    and its algorithmic read and write bytes (for --summarize-counters)."""
+    import torch
+    import quantized_weight_decode_dequant_amd as pkg
+    from quantized_weight_decode_dequant_amd import _lib, roofline, synth, weights, workloads
+    assert torch.cuda.is_available(), "the counter pass needs a GPU"
+    pkg.raw()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    man = []
+
+    def add(kernel, what, read, write, calibration=None):
+        e = {"kernel": kernel, "what": what, "read": int(read), "write": int(write)}
+        if calibration:
+            e["calibration"] = calibration
+        man.append(e)
+
+    Q4 = pkg.FMT_Q4_ASYM_G64
+    step = workloads.build_decode_step(seed, log=log)
+    wbytes = sum(roofline.Q4_BYTES_PER_WEIGHT * g.N * g.K for g in step.gemvs)
+    sumK = sum(g.K for g in step.gemvs)
+    sumN = sum(g.N for g in step.gemvs)
+    plan = pkg.qg_batch_plan_build(Q4, 1, [(g.packed, g.N, g.K, g.x, g.y) for g in step.gemvs])
+    torch.cuda.synchronize()
+    pkg.qg_batch_run(plan)
+    add(STEP_KERNEL, "decode step, 253 Q4 GEMVs, M=1, one launch", wbytes + 2 * sumK, 2 * sumN)
+    for M, kern in ((16, "q4_skinny_stream_kernel<true, 1>"), (32, "q4_skinny_stream_kernel<true, 2>")):
+        Xs = [workloads.verification_tile(seed, g, M) for g in step.gemvs]
+        Ys = [torch.empty((M, g.N), dtype=torch.bfloat16, device=dev) for g in step.gemvs]
+        planM = pkg.qg_batch_plan_build(Q4, M, [(g.packed, g.N, g.K, X, Y)
+                                                for g, X, Y in zip(step.gemvs, Xs, Ys)])
+        torch.cuda.synchronize()
+        pkg.qg_batch_run(planM)
+        add(kern, "verification pass, 253 Q4 products, M=%d, one launch" % M,
+            wbytes + 2 * M * sumK, 2 * M * sumN)
+        torch.cuda.synchronize()
+        del Xs, Ys, planM
+    del plan, step
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    for N, K in ((12288, 4096), (4096, 12288)):
+        wl = workloads.Int8Verify(seed, N, K, copies=1)
+        torch.cuda.synchronize()
+        wl.quantize()
+        add("had32_quant_kernel", "Hadamard-32 + int8 quant, 16 x %d" % K,
+            2 * 16 * K + K, 16 * K + 4 * 16)
+        wl.gemm()
+        add("q8_skinny_kernel<1, %d, false>" % (2 if K == 4096 else 3),
+            "int8 x int8 group-32, M=16, %d -> %d" % (K, N),
+            roofline.Q8_BYTES_PER_WEIGHT * N * K + 16 * K + 4 * 16, 2 * 16 * N)
+        torch.cuda.synchronize()
+        del wl
+
+    H, F, E, k = 7168, 2048, 384, 16
+    eb = roofline.MXFP4_BYTES_PER_WEIGHT * H * F
+    moe = workloads.MoeLayer(seed, E, H, F, k, routes=1)
+    torch.cuda.synchronize()
+    moe.run()
+    add("qg::moe_gate_up_kernel", "MXFP4 MoE, one token: gate/up + SwiGLU of 16 experts",
+        2 * k * eb + 2 * H, 4 * k * F)
+    add("qg::moe_down_fused_kernel", "MXFP4 MoE, one token: down + combine of 16 experts",
+        k * eb + 4 * k * F, 2 * H)
+    torch.cuda.synchronize()
+    del moe
+    T = 16
+    moet = workloads.MoeLayer(seed, E, H, F, k, routes=1, T=T)
+    torch.cuda.synchronize()
+    moet.run()
+    dist = moet.distinct_experts()
+    P = T * k
+    add("moe_t_gate_up_kernel", "MXFP4 MoE, 16 positions: gate/up of %d distinct experts" % dist,
+        2 * dist * eb + 2 * T * H, 4 * P * F)
+    add("moe_t_down_kernel", "MXFP4 MoE, 16 positions: down of %d distinct experts" % dist,
+        dist * eb + 4 * P * F, 4 * P * H)
+    add("moe_combine_kernel", "MXFP4 MoE, 16 positions: combine", 4 * P * H, 2 * T * H)
+    torch.cuda.synchronize()
+    del moet
+    torch.cuda.empty_cache()
+
+    NH, KH = 151936, 4096
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(seed)
+    qcodes = torch.randint(-128, 128, (NH, KH), dtype=torch.int8, device="cuda", generator=gq)
+    qscales = (torch.rand(NH, dtype=torch.float32, device="cuda", generator=gq) + 0.5) * 2.0 ** -10
+    qpacked = _lib.qgemv_pack(_lib.FMT_Q8_ROW, NH, KH, qcodes, qscales)
+    del qcodes, qscales
+    qx = weights.to_device(synth.activations(seed, 1, KH)[0], "cuda")
+    qy = torch.empty(NH, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    _lib.qgemv_run(_lib.FMT_Q8_ROW, qpacked, NH, KH, qx, y=qy)
+    add("q8row_gemv_kernel", "weight-only int8 head 4096 -> 151936", NH * KH + 4 * NH + 2 * KH,
+        2 * NH)
+    torch.cuda.synchronize()
+    del qpacked
+
+    NA, KA, GA = 262144, 8192, 64
+    for bits in (2, 3):
+        fa = _lib.affine_format(bits, GA)
+        ga = torch.Generator(device="cuda")
+        ga.manual_seed(seed + bits)
+        acodes = torch.randint(0, 1 << bits, (NA, KA), dtype=torch.uint8, device="cuda", generator=ga)
+        asc = ((torch.rand(NA, KA // GA, device="cuda", generator=ga) + 0.05) * 0.02 * 15 /
+               ((1 << bits) - 1)).half().view(torch.int16)
+        abi = (torch.randn(NA, KA // GA, device="cuda", generator=ga) * 0.01).half().view(torch.int16)
+        apacked = _lib.qgemv_pack(fa, NA, KA, acodes, asc, abi)
+        del acodes, asc, abi
+        ax = weights.to_device(synth.activations(seed, 1, KA)[0], "cuda")
+        ay = torch.empty(NA, dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        _lib.qgemv_run(fa, apacked, NA, KA, ax, y=ay)
+        add("affine_gemv_kernel<false, %d, 2," % bits, "affine %d-bit g64 GEMV 8192 -> 262144" % bits,
+            NA * KA * (bits / 8 + 4 / GA) + 2 * KA, 2 * NA)
+        torch.cuda.synchronize()
+        del apacked
+
+    # calibration: a plain read and a device copy of 1 GiB each
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    pkg.qg_plain_read(src, sink, 1024)
+    add("plain_read_kernel", "calibration: plain read of 1 GiB", COPY_BYTES, 0,
+        calibration="plain_read")
+    dst.copy_(src)
+    add("copyBuffer", "calibration: torch device copy of 1 GiB", COPY_BYTES, COPY_BYTES,
+        calibration="copy")
+    torch.cuda.synchronize()
+    with open(manifest_path, "w") as f:
+        json.dump({"kernels": man}, f, indent=1)
+    log("counter pass: %d launches recorded in %s" % (len(man), manifest_path))
+
+
 def summarize_trace(stats_csv: str, command: str, trace_csv: str = None, timed=None):
     """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv;
     with the dispatch trace and the (first, count) of the timed launches that
@@ -251,6 +578,13 @@ def main():
     ap.add_argument("--traffic-pass", action="store_true",
                     help="run one decode step and one plain 1 GiB copy, for counter collection")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
+    ap.add_argument("--counter-pass", metavar="MANIFEST_JSON",
+                    help="launch every measured hot-path kernel once (and two calibration "
+                         "kernels) for counter collection; write their algorithmic bytes")
+    ap.add_argument("--summarize-counters", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "MANIFEST_JSON", "OUT_MD"))
+    ap.add_argument("--summarize-sq", nargs="+", metavar="ARG",
+                    help="MANIFEST_JSON OUT_MD CSV [CSV ...]: per-launch SQ/TCC counters")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--trace-csv", metavar="KERNEL_TRACE_CSV",
                     help="with --summarize-trace: the dispatch trace of the same run")
@@ -260,6 +594,16 @@ def main():
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, command=args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, command=args.command)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq[2:], args.summarize_sq[0], args.summarize_sq[1],
+                     command=args.command)
+        return
+    if args.counter_pass:
+        counter_pass(args.counter_pass, args.seed)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.command, args.trace_csv,

@@ -44,7 +44,13 @@
  *           first); scales, biases fp16 [N][K/64].
  *  - Q8:    codes int8 [N][K];  scales fp16 [N][K/32];  biases NULL.
  *  - MXFP4: codes uint8 [N][K/2] (element 2i in the low nibble of byte i);
- *           scales uint8 E8M0 [N][K/32];  biases NULL.
+ *           scales uint8 E8M0 [N][K/32];  biases NULL.  Supported scale
+ *           bytes are 1..254 (2^-126 .. 2^127).  Bytes 0 and 255 (2^-127
+ *           and NaN in the OCP MX definition) are outside the supported
+ *           range: the kernels use the byte as the exponent field of an
+ *           fp32 scale, so 0 acts as a scale of 0 and 255 as infinity, and
+ *           the results for blocks with such scales are unspecified (the
+ *           scales live in device memory, so the call cannot reject them).
  *  - Q8_ROW: codes int8 [N][K];  scales fp32 [N];  biases NULL.
  *  - AFFINE: codes uint8 [N][K], one code per byte (< 2^bits); scales and
  *           biases fp16 or bf16 [N][K/group].

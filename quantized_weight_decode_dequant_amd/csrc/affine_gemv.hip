@@ -275,7 +275,12 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
     for (int ub = u0; ub < u1; ub += AG_RMAX) {
         const int nr = min(u1 - ub, AG_RMAX);
         const int T = nr * nb;
-        int t = wave, ci = t / nb, cb = t % nb;
+        // wave w takes the batches whose absolute index (rowblock * nb +
+        // batch) is w mod AG_WAVES, so a rowblock's split over the waves, and
+        // hence its rounding, does not depend on where the workgroup's range
+        // starts: single and grouped launches agree bit for bit
+        int t = (wave - (int)(((int64_t)ub * nb) % AG_WAVES) + AG_WAVES) % AG_WAVES;
+        int ci = t / nb, cb = t % nb;
         AgBatch<BITS, GPT> A, B;
         float acc = 0.f;
         {

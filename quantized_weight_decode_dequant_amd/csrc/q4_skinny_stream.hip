@@ -96,47 +96,58 @@ __device__ __forceinline__ void ss_stage(const uint16_t *X, int M, int K, int se
     __syncthreads();
 }
 
-// One tile (index pl within the staged segment) into acc.
+// One tile (index pl within the staged segment): the two groups' products
+// C_g = sum_k X (128 + q) on the bf16 MFMA, acc += s_g * C_g on the VALU.
 template <int MT>
-__device__ __forceinline__ void ss_tile(u32x4_t c, u32x2_t sb, const uint16_t *xl,
-                                        const float *xs, int pl, int lane, const Q4Consts &kq,
-                                        f32x4_t acc[MT]) {
+__device__ __forceinline__ void ss_tile(u32x4_t c, u32x2_t sb, const uint16_t *xl, int pl,
+                                        int lane, const Q4Consts &kq, f32x4_t acc[MT]) {
     typedef SsCfg<MT> C;
     const int kg = lane >> 4, r16 = lane & 15;
     bf16x8_t B[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) B[q] = q4_word_to_bf16x8(c[q], kq);
-    const float s0 = f16_lo(sb[0]), b0 = f16_hi(sb[0]);
-    const float s1 = f16_lo(sb[1]), b1 = f16_hi(sb[1]);
-    const float bb0 = fmaf(-128.f, s0, b0), bb1 = fmaf(-128.f, s1, b1);
+    const float s0 = f16_lo(sb[0]), s1 = f16_lo(sb[1]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const uint16_t *ar = xl + (16 * mt + r16) * C::RS + pl * 128 + 8 * kg;
         bf16x8_t A[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) A[q] = *reinterpret_cast<const bf16x8_t *>(ar + 32 * q);
-        const f32x4_t xs0 = *reinterpret_cast<const f32x4_t *>(xs + (2 * pl) * C::MP + 16 * mt + 4 * kg);
-        const f32x4_t xs1 = *reinterpret_cast<const f32x4_t *>(xs + (2 * pl + 1) * C::MP + 16 * mt + 4 * kg);
         f32x4_t C0 = {0.f, 0.f, 0.f, 0.f}, C1 = {0.f, 0.f, 0.f, 0.f};
         C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], C0, 0, 0, 0);
         C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[1], C0, 0, 0, 0);
         C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], B[2], C1, 0, 0, 0);
         C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], B[3], C1, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float a = acc[mt][e];
-            a = fmaf(s0, C0[e], a);
-            a = fmaf(bb0, xs0[e], a);
-            a = fmaf(s1, C1[e], a);
-            a = fmaf(bb1, xs1[e], a);
-            acc[mt][e] = a;
-        }
+        for (int e = 0; e < 4; ++e) acc[mt][e] = fmaf(s1, C1[e], fmaf(s0, C0[e], acc[mt][e]));
+    }
+}
+
+// The bias terms of the two tiles pl, pl + 1 (groups 2 pl .. 2 pl + 3 of the
+// segment): sum_g (b_g - 128 s_g)[n] * (sum_{k in g} X[m, k]), a product of
+// rank 4, as one fp32 MFMA 16x16x4 per 16 activation rows into acc.  Lane l
+// supplies the A operand element (row 16 mt + (l & 15), group 2 pl + (l >> 4))
+// and the B operand element (group 2 pl + (l >> 4), output row l & 15), which
+// is its own row's (scale, bias) word of tile pl + (l >> 5), group (l >> 4) & 1.
+template <int MT>
+__device__ __forceinline__ void ss_bias2(u32x2_t sba, u32x2_t sbb, const float *xs, int pl,
+                                         int lane, f32x4_t acc[MT]) {
+    typedef SsCfg<MT> C;
+    const int kg = lane >> 4, r16 = lane & 15;
+    const unsigned wa = (kg & 1) ? sba[1] : sba[0];
+    const unsigned wb = (kg & 1) ? sbb[1] : sbb[0];
+    const unsigned w = (kg & 2) ? wb : wa;
+    const float bb = fmaf(-128.f, f16_lo(w), f16_hi(w));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const float a = xs[(2 * pl + kg) * C::MP + 16 * mt + r16];
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc[mt], 0, 0, 0);
     }
 }
 
 // Issue tile j's loads of batch N (tiles nb0 .. nb0 + 3 of the buffer rs,
 // clamped to the last of pn tiles), then tile j's arithmetic of batch B
-// (tiles pl0 ..), for j = 0..3.
+// (tiles pl0 ..), for j = 0..3; the bias terms after each pair of tiles.
 template <int MT>
 __device__ __forceinline__ void ss_step(SsBatch &N, __amdgpu_buffer_rsrc_t rs, int nb0, int pn,
                                         const SsBatch &B, int pl0, const uint16_t *xl,
@@ -150,7 +161,8 @@ __device__ __forceinline__ void ss_step(SsBatch &N, __amdgpu_buffer_rsrc_t rs, i
         N.c[j] = buf_ld_x4(rs, lc, to);
         N.sb[j] = buf_ld_x2(rs, ls, to);
         __builtin_amdgcn_sched_barrier(0);
-        ss_tile<MT>(B.c[j], B.sb[j], xl, xs, pl0 + j, lane, kq, cur);
+        ss_tile<MT>(B.c[j], B.sb[j], xl, pl0 + j, lane, kq, cur);
+        if (j & 1) ss_bias2<MT>(B.sb[j - 1], B.sb[j], xs, pl0 + j - 1, lane, cur);
     }
 }
 
@@ -250,10 +262,11 @@ __device__ __forceinline__ void ss_block(SsBatch &A, SsBatch &B, const WorkItem 
 // rowblocks at once: a batch is 2 tiles of each, and every activation read
 // feeds both rowblocks.
 
-// One tile (index pl of the staged segment) of rowblocks a and b.
+// One tile (index pl of the staged segment) of rowblocks a and b: the scale
+// terms (the bias terms follow per pair of tiles, ss_bias2_pair).
 template <int MT>
 __device__ __forceinline__ void ss_tile2(u32x4_t ca, u32x2_t sba, u32x4_t cb, u32x2_t sbb,
-                                         const uint16_t *xl, const float *xs, int pl, int lane,
+                                         const uint16_t *xl, int pl, int lane,
                                          const Q4Consts &kq, f32x4_t acc_a[MT],
                                          f32x4_t acc_b[MT]) {
     typedef SsCfg<MT> C;
@@ -265,17 +278,13 @@ __device__ __forceinline__ void ss_tile2(u32x4_t ca, u32x2_t sba, u32x4_t cb, u3
         Bb[q] = q4_word_to_bf16x8(cb[q], kq);
     }
     const float sa0 = f16_lo(sba[0]), sa1 = f16_lo(sba[1]);
-    const float ba0 = fmaf(-128.f, sa0, f16_hi(sba[0])), ba1 = fmaf(-128.f, sa1, f16_hi(sba[1]));
     const float sb0 = f16_lo(sbb[0]), sb1 = f16_lo(sbb[1]);
-    const float bb0 = fmaf(-128.f, sb0, f16_hi(sbb[0])), bb1 = fmaf(-128.f, sb1, f16_hi(sbb[1]));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const uint16_t *ar = xl + (16 * mt + r16) * C::RS + pl * 128 + 8 * kg;
         bf16x8_t A[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) A[q] = *reinterpret_cast<const bf16x8_t *>(ar + 32 * q);
-        const f32x4_t xs0 = *reinterpret_cast<const f32x4_t *>(xs + (2 * pl) * C::MP + 16 * mt + 4 * kg);
-        const f32x4_t xs1 = *reinterpret_cast<const f32x4_t *>(xs + (2 * pl + 1) * C::MP + 16 * mt + 4 * kg);
         const f32x4_t Z = {0.f, 0.f, 0.f, 0.f};
         f32x4_t Ca0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], Ba[0], Z, 0, 0, 0);
         f32x4_t Cb0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], Bb[0], Z, 0, 0, 0);
@@ -287,24 +296,35 @@ __device__ __forceinline__ void ss_tile2(u32x4_t ca, u32x2_t sba, u32x4_t cb, u3
         Cb1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], Bb[3], Cb1, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float a = acc_a[mt][e];
-            a = fmaf(sa0, Ca0[e], a);
-            a = fmaf(ba0, xs0[e], a);
-            a = fmaf(sa1, Ca1[e], a);
-            a = fmaf(ba1, xs1[e], a);
-            acc_a[mt][e] = a;
-            float b = acc_b[mt][e];
-            b = fmaf(sb0, Cb0[e], b);
-            b = fmaf(bb0, xs0[e], b);
-            b = fmaf(sb1, Cb1[e], b);
-            b = fmaf(bb1, xs1[e], b);
-            acc_b[mt][e] = b;
+            acc_a[mt][e] = fmaf(sa1, Ca1[e], fmaf(sa0, Ca0[e], acc_a[mt][e]));
+            acc_b[mt][e] = fmaf(sb1, Cb1[e], fmaf(sb0, Cb0[e], acc_b[mt][e]));
         }
     }
 }
 
+// ss_bias2 for rowblocks a and b at once: one read of the row sums of X
+// feeds both.
+template <int MT>
+__device__ __forceinline__ void ss_bias2_pair(const SsBatch &B, const float *xs, int pl, int lane,
+                                              f32x4_t acc_a[MT], f32x4_t acc_b[MT]) {
+    typedef SsCfg<MT> C;
+    const int kg = lane >> 4, r16 = lane & 15;
+    const bool hi = kg & 1, t1 = kg & 2;
+    const unsigned wa = t1 ? (hi ? B.sb[1][1] : B.sb[1][0]) : (hi ? B.sb[0][1] : B.sb[0][0]);
+    const unsigned wb = t1 ? (hi ? B.sb[3][1] : B.sb[3][0]) : (hi ? B.sb[2][1] : B.sb[2][0]);
+    const float ba = fmaf(-128.f, f16_lo(wa), f16_hi(wa));
+    const float bb = fmaf(-128.f, f16_lo(wb), f16_hi(wb));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const float x = xs[(2 * pl + kg) * C::MP + 16 * mt + r16];
+        acc_a[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, ba, acc_a[mt], 0, 0, 0);
+        acc_b[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, bb, acc_b[mt], 0, 0, 0);
+    }
+}
+
 // Issue tile j's loads of the next batch (tiles nb0, nb0 + 1 of rowblocks a
-// and b into N: slots j and 2 + j), then tile j's arithmetic of batch B.
+// and b into N: slots j and 2 + j), then tile j's arithmetic of batch B; the
+// bias terms of both tiles after the second.
 template <int MT>
 __device__ __forceinline__ void sp_step(SsBatch &N, __amdgpu_buffer_rsrc_t ra,
                                         __amdgpu_buffer_rsrc_t rb, int nb0, int pn,
@@ -321,9 +341,10 @@ __device__ __forceinline__ void sp_step(SsBatch &N, __amdgpu_buffer_rsrc_t ra,
         N.c[2 + j] = buf_ld_x4(rb, lc, to);
         N.sb[2 + j] = buf_ld_x2(rb, ls, to);
         __builtin_amdgcn_sched_barrier(0);
-        ss_tile2<MT>(B.c[j], B.sb[j], B.c[2 + j], B.sb[2 + j], xl, xs, pl0 + j, lane, kq, acc_a,
+        ss_tile2<MT>(B.c[j], B.sb[j], B.c[2 + j], B.sb[2 + j], xl, pl0 + j, lane, kq, acc_a,
                      acc_b);
     }
+    ss_bias2_pair<MT>(B, xs, pl0, lane, acc_a, acc_b);
 }
 
 // The first batch (tiles 0, 1 of the segment) of rowblocks a and b.
@@ -474,13 +495,14 @@ q4_skinny_stream_kernel(const WorkItem *__restrict__ items, const WorkStart *__r
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Q4Consts kq = q4_consts();
+    const int wg = xcd_work_index(blockIdx.x, gridDim.x);
     if (!LIST) {
-        const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
+        const int64_t n = single.units, g = gridDim.x, j = wg;
         const int u0 = (int)(j * n / g), u1 = (int)((j + 1) * n / g);
         if (u0 < u1) ss_range<MT>(single, u0, u1, M, xl, xs, tid, lane, wave, kq);
         return;
     }
-    const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
+    const WorkStart s = starts[wg], e = starts[wg + 1];
 #pragma unroll 1
     for (int i = s.item; i < e.item || (i == e.item && e.unit > 0); ++i) {
         const WorkItem it = items[i];

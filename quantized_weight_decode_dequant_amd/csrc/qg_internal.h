@@ -277,6 +277,20 @@ __device__ __forceinline__ f32x2_t fp4_pair_f32(unsigned w, float scale) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
 }
 
+// MI355X dispatches the workgroups of a launch to its 8 XCDs in turn
+// (workgroup b runs on XCD b mod 8), and each XCD has its own L2.  This maps
+// the hardware index b to a work index so that consecutive work indices run
+// on the same XCD: XCD x takes the x-th run of about grid / 8 consecutive
+// indices.  Work split into contiguous ranges in index order (rowblocks of
+// one matrix, one activation tile) then shares the L2 of one XCD instead of
+// being spread over all eight.  A bijection of [0, grid) for every grid.
+constexpr int XCDS = 8;
+__device__ __forceinline__ int xcd_work_index(int b, int grid) {
+    const int q = grid / XCDS, r = grid % XCDS;
+    const int x = b % XCDS, i = b / XCDS;
+    return x * q + min(x, r) + i;
+}
+
 // Streaming (non-temporal) load through the global address space.  Pointers
 // read from memory (work lists) are otherwise generic, which makes the
 // compiler emit FLAT loads; those also count against the LDS counter, so every

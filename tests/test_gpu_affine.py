@@ -196,6 +196,28 @@ def test_affine_batch_mixed_shapes(bits, group):
         assert torch.equal(y, s), "batch differs from qgemv_run: " + what
 
 
+@pytest.mark.parametrize("bits", (3, 4))
+def test_affine_batch_split_items_bit_identical(bits):
+    """Items with more rowblocks than the grid has workgroups times four, whose
+    batches per rowblock (ceil(K / 512) = 7, 5, 3) are not a multiple of the
+    four waves, so the grouped launch and qgemv_run cut them into workgroup
+    ranges at different rowblocks: the outputs still agree bit for bit, and
+    sampled rows match the oracle."""
+    note("affine batch split items bits=%d" % bits)
+    shapes = [(100, 1216), (18944, 3584), (7, 384), (6000, 2560), (4100, 1536)]
+    fmt, mats, xs, entries, singles = _batch(170 + bits, bits, 64, False, shapes, pkg.OUT_F32)
+    plan = pkg.qg_batch_plan_build(fmt, 1, entries, pkg.OUT_F32)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(171)
+    for (p, N, K, xd, y), s, m, x in zip(entries, singles, mats, xs):
+        what = "bits=%d N=%d K=%d" % (bits, N, K)
+        assert torch.equal(y, s), "batch differs from qgemv_run: " + what
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, 64), replace=False)]))
+        ref = oracle.affine_gemv(m.codes[rows], m.scales[rows], m.biases[rows], x, 64, False)
+        assert_f32_close(to_np(y)[rows], ref, what=what)
+
+
 def test_affine_batch_layer_graph_replay():
     """A decoder layer's seven projections (4096 -> 4096, 1024, 1024, 4096,
     12288, 12288; 12288 -> 4096) at 3 bits in one launch, captured in a HIP
