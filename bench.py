@@ -555,6 +555,123 @@ def cpu_baseline_all_cores(step, budget_s: float, threads: int):
                       "%.3f GB algorithmic, %.1f s" % (n, threads, done_bytes / 1e9, elapsed)}
 
 
+def _split_rows(fn, N: int, threads: int, pool):
+    """fn(r0, r1) for `threads` contiguous row slices, concurrently (the
+    oracle releases the interpreter while it runs)."""
+    cuts = [N * i // threads for i in range(threads + 1)]
+    return list(pool.map(lambda j: fn(cuts[j], cuts[j + 1]), range(threads)))
+
+
+def _timed(fn):
+    t = time.perf_counter()
+    fn()
+    return time.perf_counter() - t
+
+
+def cpu_baseline_configs(seed: int, threads: int):
+    """The oracle, as it stands, on the other workloads of the path, timed
+    whole on one thread and on `threads` threads (output rows, or experts,
+    split over concurrent oracle calls); input generation is not timed.
+      cfg1  the single 4-bit g64 GEMV 4096 x 4096, M = 1
+      cfg4  the int8 verification at M = 16: Hadamard-32 + int8 quantization
+            and the int8 x int8 group-32 product, for 4096 -> 12288 and
+            12288 -> 4096
+      cfg5  the MXFP4 MoE layer for one token: 16 of 384 experts (7168 x 2048)
+      cfg3  the verification pass over the decode step's 253 projections at
+            M = 16 and 32, extrapolated (in proportion to the weights, which
+            fix the oracle's multiply-adds at a given M) from one timed
+            decoder layer (q, k, v, o, gate, up, down) on `threads` threads;
+            the config-1 matrix at M = 16 and 32 is timed beside it."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    from quantized_weight_decode_dequant_amd import roofline, synth
+    out = {}
+    with ThreadPoolExecutor(threads) as pool:
+        # cfg1
+        m = synth.q4_matrix(seed, 4096, 4096)
+        x = synth.activations(seed, 1, 4096)
+        one = _timed(lambda: oracle.q4_gemm(m.codes, m.scales, m.biases, x))
+        allc = _timed(lambda: _split_rows(lambda a, b: oracle.q4_gemm(
+            m.codes[a:b], m.scales[a:b], m.biases[a:b], x), 4096, threads, pool))
+        b = roofline.q4_gemm_bytes(1, 4096, 4096)
+        out["cfg1_q4_gemv_4096x4096_m1"] = {
+            "one_thread_s": round(one, 4), "all_cores_s": round(allc, 4),
+            "one_thread_GBs": round(b / one / 1e9, 4), "all_cores_GBs": round(b / allc / 1e9, 4),
+            "algorithmic_bytes": int(b)}
+        # cfg4
+        rows = {}
+        for N, K in ((12288, 4096), (4096, 12288)):
+            w = synth.q8_matrix(seed, N, K)
+            X = synth.q8_activations(seed, 16, K)
+            signs = synth.rotation_signs(seed, K)
+            res = {}
+            tq = _timed(lambda: res.setdefault("q", oracle.had32_quant(X, signs)))
+            q, sx = res["q"]
+            tg = _timed(lambda: oracle.q8_gemm(w.qw, w.sw, q, sx))
+            tga = _timed(lambda: _split_rows(lambda a, c: oracle.q8_gemm(
+                w.qw[a:c], w.sw[a:c], q, sx), N, threads, pool))
+            bt = roofline.hadamard_quant_bytes(16, K) + roofline.q8_gemm_bytes(16, N, K)
+            rows["%dx%d" % (K, N)] = {
+                "hadamard_quant_s": round(tq, 4), "gemm_one_thread_s": round(tg, 4),
+                "gemm_all_cores_s": round(tga, 4),
+                "one_thread_GBs": round(bt / (tq + tg) / 1e9, 4),
+                "all_cores_GBs": round(bt / (tq + tga) / 1e9, 4), "algorithmic_bytes": int(bt)}
+        out["cfg4_int8_verification_m16"] = rows
+        # cfg5: only the 16 selected experts are generated (the oracle reads
+        # nothing else); ids renumbered into that pool
+        H, F, k = 7168, 2048, 16
+        ids, wts = synth.router(seed, 384, k)
+        ex = [synth.expert(seed, int(e), H, F) for e in ids]
+        st = lambda f, sel: np.stack([f(ex[i]) for i in sel])  # noqa: E731
+        xm = synth.moe_token(seed, H)
+
+        def moe_part(sel):
+            return oracle.moe(st(lambda e: e.gate.codes, sel), st(lambda e: e.gate.scales, sel),
+                              st(lambda e: e.up.codes, sel), st(lambda e: e.up.scales, sel),
+                              st(lambda e: e.down.codes, sel), st(lambda e: e.down.scales, sel),
+                              xm, np.arange(len(sel), dtype=np.int32), wts[list(sel)])
+
+        one = _timed(lambda: moe_part(range(k)))
+        parts = [list(range(k))[j::threads] for j in range(min(threads, k))]
+        allc = _timed(lambda: np.sum(list(pool.map(moe_part, parts)), axis=0))
+        b = roofline.moe_token_bytes(k, H, F)
+        out["cfg5_moe_one_token_top16"] = {
+            "one_thread_s": round(one, 4), "all_cores_s": round(allc, 4),
+            "all_cores_threads": len(parts),
+            "one_thread_GBs": round(b / one / 1e9, 4), "all_cores_GBs": round(b / allc / 1e9, 4),
+            "algorithmic_bytes": int(b)}
+        # cfg3
+        shapes = synth.decode_step_shapes()
+        step_w = sum(N * K for _, _, N, K in shapes)
+        layer = [s for s in shapes if s[1].startswith("L0.")]
+        layer_w = sum(N * K for _, _, N, K in layer)
+        mats = [(synth.q4_matrix(seed, N, K, item=it), N, K) for it, _, N, K in layer]
+        ext = {}
+        for M in (16, 32):
+            Xc = synth.activations(seed + 1, M, 4096)
+            t1 = _timed(lambda: _split_rows(lambda a, c: oracle.q4_gemm(
+                m.codes[a:c], m.scales[a:c], m.biases[a:c], Xc), 4096, threads, pool))
+            tl = 0.0
+            for mm, N, K in mats:
+                X = synth.activations(seed + 1, M, K)
+                tl += _timed(lambda: _split_rows(lambda a, c: oracle.q4_gemm(
+                    mm.codes[a:c], mm.scales[a:c], mm.biases[a:c], X), N, threads, pool))
+            tpass = tl * step_w / layer_w
+            bpass = sum(roofline.q4_gemm_bytes(M, N, K) for _, _, N, K in shapes)
+            ext["m%d" % M] = {
+                "cfg1_matrix_all_cores_s": round(t1, 4), "layer_all_cores_s": round(tl, 4),
+                "pass_all_cores_s_extrapolated": round(tpass, 3),
+                "passes_per_s": round(1.0 / tpass, 6),
+                "all_cores_GBs": round(bpass / tpass / 1e9, 4)}
+        out["cfg3_verification_pass"] = dict(
+            ext, kind="extrapolated", threads=threads,
+            sample="one decoder layer (7 projections, %d weights) timed at M rows on %d threads, "
+                   "scaled by the step's %d weights / the layer's (the lm_head included by that "
+                   "ratio)" % (layer_w, threads, step_w))
+    out["threads"] = threads
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -566,6 +683,8 @@ def main():
                          "GPU clocks reach their sustained state")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-configs", action="store_true",
+                    help="time the oracle on the decode step only (not configs 1, 3, 4, 5)")
     ap.add_argument("--no-m16", action="store_true", help="skip the verification passes")
     ap.add_argument("--verify-m", default="16,32",
                     help="activation rows of the timed verification passes (comma separated)")
@@ -1078,6 +1197,10 @@ def main():
         result["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(step, args.cpu_budget / 2,
                                                                      threads)
         result["cpu_baseline"]["host"] = host_cpu_model()
+        if not args.no_cpu_configs:
+            t = time.time()
+            result["cpu_baseline"]["configs"] = cpu_baseline_configs(args.seed, threads)
+            log("cpu baseline, other configs: %.1f s" % (time.time() - t))
     print(json.dumps(result), flush=True)
 
 

@@ -45,12 +45,15 @@
  *  - Q8:    codes int8 [N][K];  scales fp16 [N][K/32];  biases NULL.
  *  - MXFP4: codes uint8 [N][K/2] (element 2i in the low nibble of byte i);
  *           scales uint8 E8M0 [N][K/32];  biases NULL.  Supported scale
- *           bytes are 1..254 (2^-126 .. 2^127).  Bytes 0 and 255 (2^-127
- *           and NaN in the OCP MX definition) are outside the supported
- *           range: the kernels use the byte as the exponent field of an
- *           fp32 scale, so 0 acts as a scale of 0 and 255 as infinity, and
- *           the results for blocks with such scales are unspecified (the
- *           scales live in device memory, so the call cannot reject them).
+ *           bytes are 1..252 (2^-126 .. 2^125), the range in which every
+ *           E2M1 value times the scale is finite in bf16 and fp32.  From 253
+ *           on, +-6 times the scale overflows (to infinity, and a zero
+ *           activation times it to NaN); bytes 0 and 255 (2^-127 and NaN in
+ *           the OCP MX definition) are outside the range too: the kernels
+ *           use the byte as the exponent field of an fp32 scale, so 0 acts
+ *           as a scale of 0 and 255 as infinity.  Results for blocks with
+ *           unsupported scales are unspecified (the scales live in device
+ *           memory, so the call cannot reject them).
  *  - Q8_ROW: codes int8 [N][K];  scales fp32 [N];  biases NULL.
  *  - AFFINE: codes uint8 [N][K], one code per byte (< 2^bits); scales and
  *           biases fp16 or bf16 [N][K/group].
@@ -336,7 +339,7 @@ typedef struct qg_gemv_desc {
  * 1..4 rows) and the bf16 MFMA kernel (16x16x32 tiles of 16 or 32 rows,
  * whatever M is).  QG_KERNEL_AUTO takes the one measured faster on MI355X:
  * VALU for M = 1, MFMA for M >= 2 (at M = 2 the MFMA pass over a decode
- * step's weights already takes 0.74 ms against 0.86 ms on the VALU).  The
+ * step's weights already takes 0.671 ms against 0.761 ms on the VALU).  The
  * others force a family, e.g. to measure both; results differ between the
  * families only by fp32 rounding order.  Affine products (M = 1) have only
  * the GEMV kernel of qgemv_run: QG_KERNEL_AUTO and QG_KERNEL_VALU take it. */

@@ -412,13 +412,74 @@ __device__ __forceinline__ void ss_zero_block(f32x4_t acc[SsCfg<MT>::R][MT]) {
     for (int r = 0; r < SsCfg<MT>::R; ++r) ss_zero<MT>(acc[r]);
 }
 
+// ---- staged output (16 rows, bf16) ----
+// The results of a block of rowblocks are written through LDS: each wave
+// puts its rowblocks' 16 x 16 bf16 results into a staging buffer, and the
+// workgroup then stores the block's rowblocks, which are consecutive, as
+// runs of 16 bytes that cover whole cache lines of each output row (768
+// outputs = 1536 contiguous bytes per row and half block), instead of 32-byte
+// pieces of 16 rows per rowblock.  The staging buffer holds half a block
+// (WAVES * SS_STG_R rowblocks), so a block is stored in two halves.
+constexpr int SS_STG_R = 3;                          // rowblocks per wave and half block
+constexpr int SS_STG_N = 16 * SsCfg<1>::WAVES * SS_STG_R;  // outputs per row in the buffer
+constexpr int SS_STG_RS = SS_STG_N + 8;              // row stride (16-byte pad)
+static_assert(SsCfg<1>::R == 2 * SS_STG_R, "a block is two staged halves");
+static_assert(SsCfg<1>::LDS + (size_t)16 * SS_STG_RS * 2 <= 160 * 1024, "LDS budget");
+
+// Whether the items' outputs can go through the staging buffer: 16 rows at
+// most, bf16 output, every output row 16-byte aligned.
+__device__ __forceinline__ bool ss_staged(const WorkItem &it) {
+    return !it.out_f32 && (it.N % 8) == 0 && (reinterpret_cast<uintptr_t>(it.y) & 15) == 0;
+}
+
+// Store this block's results (rowblocks first + WAVES * (i0 + r), r < n, of
+// every wave; the block's rowblocks are [rb0, rb0 + WAVES * R) clipped to
+// u1) through the staging buffer.  Every wave of the workgroup calls this
+// with the same rb0 (the barriers inside are workgroup-wide).
+template <int R>
+__device__ __forceinline__ void ss_store_staged(const WorkItem &it, int rb0, int u1, int M, int n,
+                                                const f32x4_t acc[R][1], uint16_t *stg, int tid,
+                                                int lane, int wave) {
+    typedef SsCfg<1> C;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int nend = min(u1 * RB, it.N);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        __syncthreads();  // the previous half's stores have read the buffer
+#pragma unroll
+        for (int r = SS_STG_R * h; r < SS_STG_R * (h + 1); ++r) {
+            if (r < n) {
+                const int p = wave + C::WAVES * (r - SS_STG_R * h);  // rowblock within the half
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    stg[(4 * kg + e) * SS_STG_RS + 16 * p + r16] = f32_to_bf16(acc[r][0][e]);
+            }
+        }
+        __syncthreads();
+        const int n0 = (rb0 + C::WAVES * SS_STG_R * h) * RB;  // first output of the half
+        constexpr int CH = SS_STG_N / 8;                     // 16-byte chunks per row
+        for (int c = tid; c < 16 * CH; c += C::THREADS) {
+            const int m = c / CH, q = c - m * CH;
+            const int nn = n0 + 8 * q;
+            if (m >= M || nn >= nend) continue;
+            const uint16_t *src = stg + m * SS_STG_RS + 8 * q;
+            const size_t o = (size_t)m * it.N + nn;
+            if (nn + 8 <= nend) {
+                st_global<u32x4_t>(it.y, o / 8, *reinterpret_cast<const u32x4_t *>(src));
+            } else {
+                for (int j = 0; j < nend - nn; ++j) st_global<uint16_t>(it.y, o + j, src[j]);
+            }
+        }
+    }
+}
+
 // Rowblocks [u0, u1) of one matrix; wave w owns rowblocks u0 + w + WAVES * i.
 // Results are kept in registers for R rowblocks and stored together (a store
 // in the middle of the load stream makes the wave wait for loads issued
 // before it).
 template <int MT>
 __device__ __forceinline__ void ss_range(const WorkItem &it, int u0, int u1, int M, uint16_t *xl,
-                                         float *xs, int tid, int lane, int wave,
+                                         float *xs, uint16_t *stg, int tid, int lane, int wave,
                                          const Q4Consts &kq) {
     typedef SsCfg<MT> C;
     constexpr int R = C::R;
@@ -438,16 +499,32 @@ __device__ __forceinline__ void ss_range(const WorkItem &it, int u0, int u1, int
             ss_first(A, it, first, 0, pn, mine > 0, lane);
         __syncthreads();  // nobody still reads the previous range's X
         ss_stage<MT>(X, M, it.K, 0, nbe * SS_TPB, xl, xs, tid);
+        // staged: blocks of WAVES * R consecutive rowblocks, the same number
+        // for every wave (the staged store is workgroup-wide); otherwise each
+        // wave runs through its own rowblocks
+        const bool staged = !C::PAIR && ss_staged(it);
+        const int blocks = staged ? (u1 - u0 + C::WAVES * R - 1) / (C::WAVES * R)
+                                  : (mine + R - 1) / R;
 #pragma unroll 1
-        for (int i0 = 0; i0 < mine; i0 += R) {
-            const int n = min(R, mine - i0);
+        for (int bi = 0; bi < blocks; ++bi) {
+            const int i0 = bi * R;
+            const int n = max(0, min(R, mine - i0));
             ss_zero_block<MT>(acc);
-            if constexpr (C::PAIR)
-                ss_block_pair<MT, R>(A, B, it, first, i0, n, mine, true, 0, pn, xl, xs, lane, kq,
-                                     acc);
-            else
-                ss_block<MT, R>(A, B, it, first, i0, n, i0 + n < mine, 0, pn, xl, xs, lane, kq,
-                                acc);
+            if (n > 0) {
+                if constexpr (C::PAIR)
+                    ss_block_pair<MT, R>(A, B, it, first, i0, n, mine, true, 0, pn, xl, xs, lane,
+                                         kq, acc);
+                else
+                    ss_block<MT, R>(A, B, it, first, i0, n, i0 + n < mine, 0, pn, xl, xs, lane,
+                                    kq, acc);
+            }
+            if constexpr (!C::PAIR) {
+                if (staged) {
+                    ss_store_staged<R>(it, u0 + C::WAVES * i0, u1, M, n, acc, stg, tid, lane,
+                                       wave);
+                    continue;
+                }
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r)
                 if (r < n) ss_store<MT>(it, first + C::WAVES * (i0 + r), M, acc[r], lane);
@@ -479,6 +556,12 @@ __device__ __forceinline__ void ss_range(const WorkItem &it, int u0, int u1, int
             else
                 ss_block<MT, R>(A, B, it, first, i0, n, false, pbase, pn, xl, xs, lane, kq, acc);
         }
+        if constexpr (!C::PAIR) {
+            if (ss_staged(it)) {
+                ss_store_staged<R>(it, ub, u1, M, n, acc, stg, tid, lane, wave);
+                continue;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (r < n) ss_store<MT>(it, first + C::WAVES * (i0 + r), M, acc[r], lane);
@@ -492,6 +575,7 @@ q4_skinny_stream_kernel(const WorkItem *__restrict__ items, const WorkStart *__r
     typedef SsCfg<MT> C;
     __shared__ __attribute__((aligned(16))) uint16_t xl[C::MP * C::RS];
     __shared__ __attribute__((aligned(16))) float xs[2 * C::SEGK * C::MP];
+    __shared__ __attribute__((aligned(16))) uint16_t stg[MT == 1 ? 16 * SS_STG_RS : 8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Q4Consts kq = q4_consts();
@@ -499,7 +583,7 @@ q4_skinny_stream_kernel(const WorkItem *__restrict__ items, const WorkStart *__r
     if (!LIST) {
         const int64_t n = single.units, g = gridDim.x, j = wg;
         const int u0 = (int)(j * n / g), u1 = (int)((j + 1) * n / g);
-        if (u0 < u1) ss_range<MT>(single, u0, u1, M, xl, xs, tid, lane, wave, kq);
+        if (u0 < u1) ss_range<MT>(single, u0, u1, M, xl, xs, stg, tid, lane, wave, kq);
         return;
     }
     const WorkStart s = starts[wg], e = starts[wg + 1];
@@ -508,7 +592,7 @@ q4_skinny_stream_kernel(const WorkItem *__restrict__ items, const WorkStart *__r
         const WorkItem it = items[i];
         const int u0 = (i == s.item) ? s.unit : 0;
         const int u1 = (i == e.item) ? e.unit : it.units;
-        if (u0 < u1) ss_range<MT>(it, u0, u1, M, xl, xs, tid, lane, wave, kq);
+        if (u0 < u1) ss_range<MT>(it, u0, u1, M, xl, xs, stg, tid, lane, wave, kq);
     }
 }
 

@@ -15,6 +15,20 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running test")
 
 
+def gpu_visible() -> bool:
+    """Whether torch sees a GPU (counting devices does not initialize one)."""
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# environment that hides every GPU from HIP and the ROCm runtime
+HIDE_GPUS = {"HIP_VISIBLE_DEVICES": "-1", "CUDA_VISIBLE_DEVICES": "-1",
+             "ROCR_VISIBLE_DEVICES": "-1"}
+
+
 def golden_path(name: str) -> str:
     return os.path.join(GOLDEN, name)
 

@@ -11,13 +11,26 @@ import re
 
 import pytest
 
-from conftest import ROOT
+from conftest import ROOT, gpu_visible
 import quantized_weight_decode_dequant_amd as pkg
 from quantized_weight_decode_dequant_amd import _lib as L
 
 HEADER = os.path.join(ROOT, "include", "qgemv.h")
 A = 0x10000  # an aligned fake device address: only used in calls that fail validation
 SZ = C.c_size_t
+
+# The calls below pass fake device addresses and rely on the library
+# rejecting them before any HIP call.  Where a GPU is visible, a regression
+# of one host check would launch a kernel on such an address, so there this
+# module runs only in a child process with every GPU hidden
+# (test_zz_boundary_isolated.py), where a launch fails with QG_EHIP instead.
+CHILD = os.environ.get("QG_BOUNDARY_CHILD") == "1"
+if CHILD:
+    assert not gpu_visible(), "the boundary child process still sees a GPU"
+pytestmark = pytest.mark.skipif(
+    not CHILD and gpu_visible(),
+    reason="a GPU is visible: runs in a child process with every GPU hidden "
+           "(test_zz_boundary_isolated.py)")
 
 
 def declared_functions():
