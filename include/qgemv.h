@@ -272,6 +272,39 @@ int moe_expert_gemv_run(const void *packed_gate, const void *packed_up,
 size_t qg_moe_skinny_workspace_bytes(int64_t T, int64_t top_k, int64_t H,
                                      int64_t F);
 
+/* The largest workspace moe_expert_gemv_run_noalloc serves (its
+ * qg_moe_workspace_bytes(top_k, H, F) must not exceed this): 2 MiB, e.g.
+ * top_k = 16 with H + F up to 32767.  The library holds one array of this
+ * size on each GPU it runs the call on, until the process ends. */
+#define QG_MOE_NOALLOC_SCRATCH_BYTES ((size_t)2 << 20)
+
+/*
+ * moe_expert_gemv_run_noalloc -- moe_expert_gemv_run for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The same computation, kernels and
+ * results as moe_expert_gemv_run (bit for bit); instead of a caller
+ * workspace it uses the library's array of QG_MOE_NOALLOC_SCRATCH_BYTES on
+ * the current device.  It allocates and frees nothing (the array's device
+ * address is looked up once per device, on the first call there).
+ *
+ *  status       optional device uint32 (4-B aligned), written: 1 if any id
+ *               was out of range, else 0.  NULL: not reported.
+ *  other arguments as in moe_expert_gemv_run (no workspace).
+ * The array keeps the previous call's contents; every call writes whatever
+ * it reads from it first, so nothing needs clearing.  All calls on one GPU
+ * share the one array: calls that overlap on a GPU (concurrent streams or
+ * host threads) race on it and must be serialized by the caller.
+ * Errors: those of moe_expert_gemv_run; QG_ESIZE when
+ * qg_moe_workspace_bytes(top_k, H, F) > QG_MOE_NOALLOC_SCRATCH_BYTES;
+ * QG_EUNSUPPORTED on a device index of 64 or more.
+ */
+int moe_expert_gemv_run_noalloc(const void *packed_gate, const void *packed_up,
+                                const void *packed_down, size_t bytes_gate,
+                                size_t bytes_up, size_t bytes_down, int64_t E,
+                                int64_t H, int64_t F, const void *x, int top_k,
+                                const int32_t *expert_ids, const float *expert_w,
+                                uint32_t *status, void *y, int out_dtype, void *stream);
+
 /*
  * moe_expert_skinny_run -- T positions (a verification tile of draft tokens)
  * through the routed experts of one MoE layer in MXFP4, each position with

@@ -8,7 +8,8 @@ from ._lib import (  # noqa: F401
     EXPORTS, FMT_MXFP4_G32, FMT_Q4_ASYM_G64, FMT_Q8_SYM_G32, FMT_Q8_ROW, OUT_BF16, OUT_F32, OUT_I32_GROUPS,
     KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA,
     QGError, affine_format, hadamard32_quant_run, moe_expert_gemv_run, moe_workspace_bytes, packed_bytes,
-    moe_expert_skinny_run, moe_skinny_workspace_bytes,
+    moe_expert_skinny_run, moe_skinny_workspace_bytes, moe_expert_gemv_run_noalloc,
+    MOE_NOALLOC_SCRATCH_BYTES, QG_ESIZE,
     qgemm_skinny_run, qgemv_pack, qgemv_run, raw, status_string, qg_batch_plan_build,
     qg_batch_run, qg_batch_worklist_bytes, qg_plain_read, GemvDesc, BatchPlan, Plan,
 )

@@ -54,6 +54,7 @@ EXPORTS = (
     "hadamard32_quant_run",
     "qg_moe_workspace_bytes",
     "moe_expert_gemv_run",
+    "moe_expert_gemv_run_noalloc",
     "qg_moe_skinny_workspace_bytes",
     "moe_expert_skinny_run",
     "qg_batch_worklist_bytes",
@@ -114,6 +115,9 @@ def raw():
             lib.moe_expert_gemv_run.argtypes = [p, p, p, sz, sz, sz, i64, i64, i64, p, i, p, p,
                                                 p, sz, p, i, p]
             lib.moe_expert_gemv_run.restype = i
+            lib.moe_expert_gemv_run_noalloc.argtypes = [p, p, p, sz, sz, sz, i64, i64, i64, p, i,
+                                                        p, p, p, p, i, p]
+            lib.moe_expert_gemv_run_noalloc.restype = i
             lib.qg_moe_skinny_workspace_bytes.argtypes = [i64, i64, i64, i64]
             lib.qg_moe_skinny_workspace_bytes.restype = sz
             lib.moe_expert_skinny_run.argtypes = [p, p, p, sz, sz, sz, i64, i64, i64, i64, p, i,
@@ -242,6 +246,28 @@ def moe_expert_gemv_run(packed_gate, packed_up, packed_down, E: int, H: int, F: 
                                      E, H, F, _ptr(x), top_k, _ptr(expert_ids), _ptr(expert_w),
                                      _ptr(workspace), workspace.numel(), _ptr(y), out_dtype,
                                      _stream(stream)), "moe_expert_gemv_run")
+    return y
+
+
+# the largest workspace moe_expert_gemv_run_noalloc serves (QG_MOE_NOALLOC_SCRATCH_BYTES)
+MOE_NOALLOC_SCRATCH_BYTES = 2 << 20
+
+
+def moe_expert_gemv_run_noalloc(packed_gate, packed_up, packed_down, E: int, H: int, F: int, x,
+                                expert_ids, expert_w, status=None, y=None,
+                                out_dtype: int = OUT_BF16, stream=None):
+    """moe_expert_gemv_run on the library's own device array instead of a
+    workspace; status: optional int32 device tensor [1] receiving the
+    invalid-id flag."""
+    torch = _torch()
+    top_k = int(expert_ids.numel())
+    if y is None:
+        y = torch.empty(H, dtype=_out_torch_dtype(out_dtype), device=x.device)
+    _check(raw().moe_expert_gemv_run_noalloc(
+        _ptr(packed_gate), _ptr(packed_up), _ptr(packed_down), packed_gate.numel(),
+        packed_up.numel(), packed_down.numel(), E, H, F, _ptr(x), top_k, _ptr(expert_ids),
+        _ptr(expert_w), _ptr(status), _ptr(y), out_dtype, _stream(stream)),
+        "moe_expert_gemv_run_noalloc")
     return y
 
 

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/qgemv.h"
@@ -278,7 +279,7 @@ namespace {
 int moe_validate(const void *packed_gate, const void *packed_up, const void *packed_down,
                  size_t bytes_gate, size_t bytes_up, size_t bytes_down, int64_t E, int64_t H,
                  int64_t F, int top_k, const int32_t *expert_ids, const float *expert_w,
-                 const void *workspace, int out_dtype) {
+                 int out_dtype) {
     if (out_dtype != QG_OUT_BF16 && out_dtype != QG_OUT_F32 && out_dtype != QG_OUT_I32_GROUPS)
         return QG_EINVAL;
     if (out_dtype == QG_OUT_I32_GROUPS) return QG_EUNSUPPORTED;
@@ -286,7 +287,7 @@ int moe_validate(const void *packed_gate, const void *packed_up, const void *pac
         E * F > N_MAX || E * H > N_MAX)
         return QG_ESHAPE;
     if (top_k < 0 || top_k > MOE_TOPK_MAX || top_k > E) return QG_ESHAPE;
-    if (!packed_gate || !packed_up || !packed_down || !workspace) return QG_EINVAL;
+    if (!packed_gate || !packed_up || !packed_down) return QG_EINVAL;
     if (top_k > 0 && (!expert_ids || !expert_w)) return QG_EINVAL;
     if (bytes_gate != fp4_packed_bytes(E * F, H) || bytes_up != fp4_packed_bytes(E * F, H) ||
         bytes_down != fp4_packed_bytes(E * H, F))
@@ -305,9 +306,9 @@ int moe_expert_gemv_run(const void *packed_gate, const void *packed_up, const vo
                         size_t workspace_bytes, void *y, int out_dtype, void *stream) {
     try {
         int st = moe_validate(packed_gate, packed_up, packed_down, bytes_gate, bytes_up,
-                              bytes_down, E, H, F, top_k, expert_ids, expert_w, workspace,
-                              out_dtype);
+                              bytes_down, E, H, F, top_k, expert_ids, expert_w, out_dtype);
         if (st != QG_OK) return st;
+        if (!workspace) return QG_EINVAL;
         if (!x || !y) return QG_EINVAL;
         if (workspace_bytes < qg_moe_workspace_bytes(top_k, H, F)) return QG_ESIZE;
         if (!aligned(packed_gate, 16) || !aligned(packed_up, 16) || !aligned(packed_down, 16) ||
@@ -330,6 +331,75 @@ int moe_expert_gemv_run(const void *packed_gate, const void *packed_up, const vo
     }
 }
 
+}  // extern "C"
+
+// ---- the allocation-free MoE call
+// Its workspace is this array, one per GPU the library runs on (each device
+// holds its own copy, at its own address, until the process ends).  In host
+// code `qg_moe_scratch` names a host-side stand-in, not device memory: its
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char qg_moe_scratch[QG_MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_DEVICES];  // device address per device, null until looked up
+
+int moe_scratch_ptr(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QG_EHIP;
+    if (dev < 0 || dev >= SCRATCH_DEVICES) return QG_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(qg_moe_scratch)) != hipSuccess || !p)
+            return QG_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_gemv_run_noalloc(const void *packed_gate, const void *packed_up,
+                                const void *packed_down, size_t bytes_gate, size_t bytes_up,
+                                size_t bytes_down, int64_t E, int64_t H, int64_t F,
+                                const void *x, int top_k, const int32_t *expert_ids,
+                                const float *expert_w, uint32_t *status, void *y, int out_dtype,
+                                void *stream) {
+    try {
+        int st = moe_validate(packed_gate, packed_up, packed_down, bytes_gate, bytes_up,
+                              bytes_down, E, H, F, top_k, expert_ids, expert_w, out_dtype);
+        if (st != QG_OK) return st;
+        if (!x || !y) return QG_EINVAL;
+        if (qg_moe_workspace_bytes(top_k, H, F) > QG_MOE_NOALLOC_SCRATCH_BYTES) return QG_ESIZE;
+        if (!aligned(packed_gate, 16) || !aligned(packed_up, 16) || !aligned(packed_down, 16) ||
+            !aligned(x, 16) || !aligned(y, out_dtype == QG_OUT_F32 ? 4 : 2) ||
+            (status && !aligned(status, 4)) || (expert_ids && !aligned(expert_ids, 4)) ||
+            (expert_w && !aligned(expert_w, 4)))
+            return QG_EALIGN;
+        int cus = 0;
+        if ((st = device_cus(&cus)) != QG_OK) return st;
+        void *ws = nullptr;
+        if ((st = moe_scratch_ptr(&ws)) != QG_OK) return st;
+        return hip_status(launch_moe(reinterpret_cast<const uint8_t *>(packed_gate),
+                                     reinterpret_cast<const uint8_t *>(packed_up),
+                                     reinterpret_cast<const uint8_t *>(packed_down), E, H, F,
+                                     reinterpret_cast<const uint16_t *>(x), top_k, expert_ids,
+                                     expert_w, reinterpret_cast<uint8_t *>(ws), y,
+                                     out_dtype == QG_OUT_F32, cus,
+                                     reinterpret_cast<hipStream_t>(stream),
+                                     reinterpret_cast<unsigned *>(status)));
+    } catch (...) {
+        return QG_EINTERNAL;
+    }
+}
+
 int moe_expert_skinny_run(const void *packed_gate, const void *packed_up,
                           const void *packed_down, size_t bytes_gate, size_t bytes_up,
                           size_t bytes_down, int64_t E, int64_t H, int64_t F, int64_t T,
@@ -338,9 +408,9 @@ int moe_expert_skinny_run(const void *packed_gate, const void *packed_up,
                           void *Y, int out_dtype, void *stream) {
     try {
         int st = moe_validate(packed_gate, packed_up, packed_down, bytes_gate, bytes_up,
-                              bytes_down, E, H, F, top_k, expert_ids, expert_w, workspace,
-                              out_dtype);
+                              bytes_down, E, H, F, top_k, expert_ids, expert_w, out_dtype);
         if (st != QG_OK) return st;
+        if (!workspace) return QG_EINVAL;
         if (T < 1 || T > M_MAX || T * top_k > MOE_PAIRS_MAX) return QG_ESHAPE;
         if (!X || !Y) return QG_EINVAL;
         if (workspace_bytes < qg_moe_skinny_workspace_bytes(T, top_k, H, F)) return QG_ESIZE;

@@ -551,10 +551,11 @@ hipError_t launch_moe_combine(const float *part, const int32_t *ids, const float
 hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd, int64_t E,
                       int64_t H, int64_t F, const uint16_t *x, int top_k, const int32_t *ids,
                       const float *w, uint8_t *workspace, void *y, bool out_f32, int cus,
-                      hipStream_t s) {
+                      hipStream_t s, unsigned *status_out) {
     float *h_ws = reinterpret_cast<float *>(workspace);
     float *part = h_ws + (size_t)top_k * F;
-    unsigned *status = reinterpret_cast<unsigned *>(part + (size_t)top_k * H);
+    unsigned *status =
+        status_out ? status_out : reinterpret_cast<unsigned *>(part + (size_t)top_k * H);
     if (top_k > 0) {
         const int PH = (int)ceil_div(H, FP4_TILE_K);  // tiles along H (gate/up rows)
         const int nrbF = (int)(F / RB);

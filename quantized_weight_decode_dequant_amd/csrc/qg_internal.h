@@ -167,11 +167,13 @@ hipError_t launch_had32_quant(const uint16_t *X, const int8_t *signs,
                               int64_t M, int64_t K, int8_t *Xq,
                               float *x_scales, double denom,
                               hipStream_t s);
+// The single-token MoE layer; h, the per-slot partials and (unless
+// status_out is given) the status word live in `workspace`.
 hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd,
                       int64_t E, int64_t H, int64_t F, const uint16_t *x,
                       int top_k, const int32_t *ids, const float *w,
                       uint8_t *workspace, void *y, bool out_f32, int cus,
-                      hipStream_t s);
+                      hipStream_t s, unsigned *status_out = nullptr);
 
 hipError_t launch_moe_combine(const float *part, const int32_t *ids, const float *w,
                               int64_t E, int64_t H, int top_k, int T, void *y,

@@ -191,6 +191,44 @@ def test_moe_validation():
     assert call(wsb=ws - 1) == L.QG_ESIZE
     assert call(ws=A + 8) == L.QG_EALIGN
     assert call(ids=A + 2) == L.QG_EALIGN
+    assert call(ws=None) == L.QG_EINVAL
+
+
+def test_moe_noalloc_validation():
+    """The allocation-free MoE call: the checks of moe_expert_gemv_run, and
+    QG_ESIZE for a layer whose workspace exceeds the library's array."""
+    lib = pkg.raw()
+    E, H, F, k = 8, 256, 512, 2
+    bg = pkg.packed_bytes(L.FMT_MXFP4_G32, E * F, H)
+    bd = pkg.packed_bytes(L.FMT_MXFP4_G32, E * H, F)
+
+    def call(**kw):
+        a = dict(g=A, u=A, d=A, bg=bg, bu=bg, bd=bd, E=E, H=H, F=F, x=A, k=k, ids=A, w=A,
+                 st=A, y=A, out=0)
+        a.update(kw)
+        return lib.moe_expert_gemv_run_noalloc(a["g"], a["u"], a["d"], a["bg"], a["bu"], a["bd"],
+                                               a["E"], a["H"], a["F"], a["x"], a["k"], a["ids"],
+                                               a["w"], a["st"], a["y"], a["out"], None)
+
+    assert call(out=5) == L.QG_EINVAL
+    assert call(out=L.OUT_I32_GROUPS) == L.QG_EUNSUPPORTED
+    assert call(k=E + 1) == L.QG_ESHAPE
+    assert call(H=250) == L.QG_ESHAPE
+    assert call(g=None) == L.QG_EINVAL
+    assert call(x=None) == L.QG_EINVAL
+    assert call(y=None) == L.QG_EINVAL
+    assert call(ids=None) == L.QG_EINVAL
+    assert call(bd=bd + 16) == L.QG_ESIZE
+    assert call(x=A + 8) == L.QG_EALIGN
+    assert call(st=A + 2) == L.QG_EALIGN
+    assert call(y=A + 1) == L.QG_EALIGN
+    # top-16 of H = 24576, F = 12288 needs 4 * 16 * 36864 + 16 bytes > 2 MiB
+    E2, H2, F2, k2 = 16, 24576, 12288, 16
+    assert pkg.moe_workspace_bytes(k2, H2, F2) > L.MOE_NOALLOC_SCRATCH_BYTES
+    assert pkg.moe_workspace_bytes(16, 7168, 2048) <= L.MOE_NOALLOC_SCRATCH_BYTES
+    bg2 = pkg.packed_bytes(L.FMT_MXFP4_G32, E2 * F2, H2)
+    bd2 = pkg.packed_bytes(L.FMT_MXFP4_G32, E2 * H2, F2)
+    assert call(E=E2, H=H2, F=F2, k=k2, bg=bg2, bu=bg2, bd=bd2) == L.QG_ESIZE
 
 
 def test_moe_skinny_validation():
