@@ -1153,7 +1153,50 @@ def main():
             "pct_of_peak": round(100 * bs / (mss * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1),
             "pct_of_plain_read": round(100 * bs / (mss * 1e-3) / 1e9 / plain_best, 1)}
         log("affine 4-bit decode step, one launch: %.4f ms" % mss)
-        del splan, sentries
+        # the same weights against a 16-row activation tile per projection:
+        # the verification pass in one grouped launch
+        M16 = 16
+        mentries, bm16 = [], 0.0
+        for (sp, N, K, sx, sy) in sentries:
+            mX = torch.randn(M16, K, device="cuda", generator=gs).to(torch.bfloat16)
+            mentries.append((sp, N, K, mX, torch.empty((M16, N), dtype=torch.bfloat16,
+                                                       device="cuda")))
+            bm16 += roofline.affine_gemv_bytes(4, GA, N, K) + 2.0 * (M16 - 1) * (K + N)
+        mplan = _lib.qg_batch_plan_build(fs, M16, mentries)
+        msm16 = workloads.time_graph_ms(lambda: _lib.qg_batch_run(mplan), 20)
+        result["affine_family"]["step_one_launch_m16"] = {
+            "workload": "the same 253 affine products against a 16-row bf16 tile each (the "
+                        "verification pass), one grouped launch captured in a HIP graph",
+            "ms": round(msm16, 4), "GBs": round(bm16 / (msm16 * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * bm16 / (msm16 * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1),
+            "pct_of_plain_read": round(100 * bm16 / (msm16 * 1e-3) / 1e9 / plain_best, 1)}
+        log("affine 4-bit verification pass M=16, one launch: %.4f ms" % msm16)
+        del splan, sentries, mplan, mentries
+
+        # the decode step's 253 shapes as weight-only int8 with row scales
+        # (7.57 GB), all in one grouped launch
+        gi = torch.Generator(device="cuda")
+        gi.manual_seed(args.seed + 200)
+        ientries, bi8 = [], 0.0
+        for item, name, N, K in synth.decode_step_shapes():
+            icodes = torch.randint(-128, 128, (N, K), dtype=torch.int8, device="cuda", generator=gi)
+            isc = (torch.rand(N, dtype=torch.float32, device="cuda", generator=gi) + 0.5) * 2.0 ** -10
+            ip = _lib.qgemv_pack(_lib.FMT_Q8_ROW, N, K, icodes, isc)
+            del icodes, isc
+            ix = torch.randn(K, device="cuda", generator=gi).to(torch.bfloat16)
+            ientries.append((ip, N, K, ix, torch.empty(N, dtype=torch.bfloat16, device="cuda")))
+            bi8 += roofline.q8row_gemv_bytes(N, K)
+        iplan = _lib.qg_batch_plan_build(_lib.FMT_Q8_ROW, 1, ientries)
+        msi = workloads.time_graph_ms(lambda: _lib.qg_batch_run(iplan), 10)
+        result["int8_step_one_launch"] = {
+            "workload": "the decode step's 253 projection shapes as weight-only int8 (one fp32 "
+                        "scale per row, codes uniform over the int8 range), one seeded x each, "
+                        "M=1, one grouped launch per step captured in a HIP graph",
+            "ms": round(msi, 4), "GBs": round(bi8 / (msi * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * bi8 / (msi * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 1),
+            "pct_of_plain_read": round(100 * bi8 / (msi * 1e-3) / 1e9 / plain_best, 1)}
+        log("int8 decode step, one launch: %.4f ms" % msi)
+        del iplan, ientries
 
         # MXFP4 routed experts, one token through one layer
         moe = workloads.MoeLayer(args.seed, 384, 7168, 2048, 16)

@@ -374,8 +374,11 @@ typedef struct qg_gemv_desc {
  * VALU for M = 1, MFMA for M >= 2 (at M = 2 the MFMA pass over a decode
  * step's weights already takes 0.671 ms against 0.761 ms on the VALU).  The
  * others force a family, e.g. to measure both; results differ between the
- * families only by fp32 rounding order.  Affine products (M = 1) have only
- * the GEMV kernel of qgemv_run: QG_KERNEL_AUTO and QG_KERNEL_VALU take it. */
+ * families only by fp32 rounding order.  Affine products have one kernel per
+ * M: at M = 1 the GEMV kernel of qgemv_run (QG_KERNEL_AUTO or
+ * QG_KERNEL_VALU), for more rows the MFMA kernel of qgemm_skinny_run
+ * (QG_KERNEL_AUTO or QG_KERNEL_MFMA); int8 row-scale GEMVs (M = 1) only the
+ * kernel of qgemv_run (QG_KERNEL_AUTO or QG_KERNEL_VALU). */
 typedef enum {
     QG_KERNEL_AUTO = 0,
     QG_KERNEL_VALU = 1,   /* M <= 4, else QG_EUNSUPPORTED */
@@ -399,12 +402,15 @@ size_t qg_batch_worklist_bytes(int32_t count);
  * qg_batch_plan_build -- validate `count` product descriptors and write their
  * work list to `worklist`.
  *
- *  fmt          QG_FMT_Q4_ASYM_G64, or a QG_FMT_AFFINE(bits, group, bf16)
- *               code for M = 1 only (the affine decode GEMV; M > 1 or
+ *  fmt          QG_FMT_Q4_ASYM_G64; a QG_FMT_AFFINE(bits, group, bf16) code
+ *               (M = 1: the affine decode GEMV, QG_KERNEL_MFMA ->
+ *               QG_EUNSUPPORTED; M > 1: the affine skinny product on the
+ *               bf16 MFMA, QG_KERNEL_VALU -> QG_EUNSUPPORTED); or
+ *               QG_FMT_Q8_ROW (M = 1 only, the weight-only int8 GEMV; M > 1 or
  *               QG_KERNEL_MFMA -> QG_EUNSUPPORTED).  Other formats ->
  *               QG_EUNSUPPORTED.  Every descriptor's packed buffer is of `fmt`.
  *  M            activation rows of every product: 1 (decode GEMVs, K <= 24576
- *               each) or 2..32 (a verification pass, Q4 only).
+ *               each) or 2..32 (a verification pass; Q4 and affine).
  *  count        1..65536 descriptors in `descs` (host array, read only; it
  *               need not outlive the call).
  *  out_dtype    QG_OUT_BF16 or QG_OUT_F32, for every product.
@@ -424,9 +430,14 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
 
 /*
  * qg_batch_run -- enqueue one kernel computing every product of the plan:
- * Y_i = X_i W_i^T (y_i = W_i x_i for M = 1), with the arithmetic of
- * qgemv_run (M = 1) or qgemm_skinny_run (M > 1).  The buffers named in the
- * descriptors must still be valid.  Safe to capture in a HIP graph.
+ * Y_i = X_i W_i^T (y_i = W_i x_i for M = 1).  Every output equals the single
+ * call's bit for bit: qgemv_run's at M = 1 (every format), and for M > 1
+ * qgemm_skinny_run's for affine products, and for Q4 products where that
+ * call takes the streaming kernel too (matrices of at least 2 * 16 rowblocks
+ * per CU, such as an output head); smaller single Q4 products split K over
+ * waves and differ from the grouped ones by fp32 rounding order only.  The
+ * buffers named in the descriptors must still be valid.  Safe to capture in
+ * a HIP graph.
  * Errors: QG_EINVAL (NULL or malformed plan), QG_EHIP.
  */
 int qg_batch_run(const qg_batch_plan *plan, void *stream);

@@ -226,28 +226,25 @@ __device__ __forceinline__ void as_first(AsBatch<BITS, GPT> &A, const uint8_t *p
     for (int q = 0; q < TPB; ++q) ag_tile_load<BITS, GPT>(A.t[q], rs, q, pn, tb, lane);
 }
 
+// Rowblocks [u0, u1) of one matrix: wave w owns rowblocks u0 + w + WAVES i;
+// X staged per segment (once for the range when K is one segment).
 template <int BITS, int GPT, int MT, bool BF16S>
-__global__ void __launch_bounds__(AsCfg<MT>::THREADS, 1)
-affine_skinny_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restrict__ X,
-                     void *__restrict__ Y, int M, int N, int K, int P, int nrb, int out_f32) {
+__device__ __forceinline__ void as_range(const WorkItem &it, int u0, int u1, int M, uint16_t *xl,
+                                         float *xs, int tid, int lane, int wave,
+                                         const AgConsts &kc) {
     typedef AsCfg<MT> C;
     constexpr int R = C::R;
     constexpr int TPB = AsBatchSize<BITS, GPT>::TPB;
-    __shared__ __attribute__((aligned(16))) uint16_t xl[C::MP * C::RS];
-    __shared__ __attribute__((aligned(16))) float xs[C::SEGK * 4 * C::MP];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t G = gridDim.x, j = blockIdx.x;
-    const int u0 = (int)(j * nrb / G), u1 = (int)((j + 1) * nrb / G);
-    if (u0 >= u1) return;
     const int group = AFF_TILE_K / GPT;
     const unsigned tb = (unsigned)affine_tile_bytes(BITS, group);
+    const int P = it.P;
     const size_t rb_bytes = (size_t)P * tb;
+    const uint8_t *packed = it.packed;
+    const uint16_t *X = reinterpret_cast<const uint16_t *>(it.x);
     const int nseg = (P + C::SEGK - 1) / C::SEGK;
     const int first = u0 + wave;
     const int mine = (u1 - u0 > wave) ? (u1 - u0 - wave + C::WAVES - 1) / C::WAVES : 0;
     const int slots = (u1 - u0 + C::WAVES - 1) / C::WAVES;  // wave 0 has the most
-    const AgConsts kc = ag_consts<BITS>();
     AsBatch<BITS, GPT> A, B;
     f32x4_t acc[R][MT];
 #pragma unroll 1
@@ -265,7 +262,7 @@ affine_skinny_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restr
                                 lane);
             if (nseg > 1 || i0 == 0) {
                 __syncthreads();  // nobody still reads the previous segment of X
-                as_stage<MT>(X, M, K, seg, nbe * TPB, group, xl, xs, tid);
+                as_stage<MT>(X, M, it.K, seg, nbe * TPB, group, xl, xs, tid);
             }
             if (n > 0)
                 as_block<BITS, GPT, MT, BF16S>(A, B, packed, rb_bytes, tb, first, i0, n, pbase, pn,
@@ -273,66 +270,116 @@ affine_skinny_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restr
         }
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            if (r < n) as_store<MT>(Y, out_f32 != 0, N, M, first + C::WAVES * (i0 + r), acc[r], lane);
+            if (r < n)
+                as_store<MT>(it.y, it.out_f32 != 0, it.N, M, first + C::WAVES * (i0 + r), acc[r],
+                             lane);
     }
 }
 
-template <int BITS, int GPT, int MT, bool BF16S>
-static void launch_as1(const uint8_t *packed, const uint16_t *X, void *Y, int M, int N, int K,
-                       int P, int nrb, int grid, bool out_f32, hipStream_t s) {
-    hipLaunchKernelGGL((affine_skinny_kernel<BITS, GPT, MT, BF16S>), dim3(grid),
-                       dim3(AsCfg<MT>::THREADS), 0, s, packed, X, Y, M, N, K, P, nrb,
-                       out_f32 ? 1 : 0);
+// LIST = false: one matrix (`single`, workgroup j takes rowblocks
+// [j n / G, (j + 1) n / G)); LIST = true: the work list (workgroup j walks
+// the (matrix, rowblock) range [starts[j], starts[j + 1])).  Work index j is
+// XCD-aware, so consecutive ranges share an L2.
+template <bool LIST, int BITS, int GPT, int MT, bool BF16S>
+__global__ void __launch_bounds__(AsCfg<MT>::THREADS, 1)
+affine_skinny_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
+                     WorkItem single, int M) {
+    typedef AsCfg<MT> C;
+    __shared__ __attribute__((aligned(16))) uint16_t xl[C::MP * C::RS];
+    __shared__ __attribute__((aligned(16))) float xs[C::SEGK * 4 * C::MP];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const AgConsts kc = ag_consts<BITS>();
+    const int wg = xcd_work_index(blockIdx.x, gridDim.x);
+    if (!LIST) {
+        const int64_t G = gridDim.x, n = single.units;
+        const int u0 = (int)(wg * n / G), u1 = (int)((wg + 1) * n / G);
+        if (u0 < u1) as_range<BITS, GPT, MT, BF16S>(single, u0, u1, M, xl, xs, tid, lane, wave, kc);
+        return;
+    }
+    const WorkStart s = starts[wg], e = starts[wg + 1];
+#pragma unroll 1
+    for (int i = s.item; i < e.item || (i == e.item && e.unit > 0); ++i) {
+        const WorkItem it = items[i];
+        const int u0 = (i == s.item) ? s.unit : 0;
+        const int u1 = (i == e.item) ? e.unit : it.units;
+        if (u0 < u1) as_range<BITS, GPT, MT, BF16S>(it, u0, u1, M, xl, xs, tid, lane, wave, kc);
+    }
 }
 
-template <int BITS, int GPT>
-static hipError_t launch_as(const uint8_t *packed, const uint16_t *X, void *Y, int64_t M,
-                            int64_t N, int64_t K, bool bf16, bool out_f32, int cus,
-                            hipStream_t s) {
-    const int P = (int)ceil_div(K, AFF_TILE_K);
-    const int nrb = (int)ceil_div(N, RB);
-    const int grid = nrb < cus ? nrb : cus;
+template <bool LIST, int BITS, int GPT, int MT, bool BF16S>
+static void launch_as1(const WorkItem *items, const WorkStart *starts, const WorkItem &it, int M,
+                       int grid, hipStream_t s) {
+    hipLaunchKernelGGL((affine_skinny_kernel<LIST, BITS, GPT, MT, BF16S>), dim3(grid),
+                       dim3(AsCfg<MT>::THREADS), 0, s, items, starts, it, M);
+}
+
+template <bool LIST, int BITS, int GPT>
+static hipError_t launch_as(const WorkItem *items, const WorkStart *starts, const WorkItem &it,
+                            int64_t M, bool bf16, int grid, hipStream_t s) {
     if (M <= 16) {
         if (bf16)
-            launch_as1<BITS, GPT, 1, true>(packed, X, Y, (int)M, (int)N, (int)K, P, nrb, grid,
-                                           out_f32, s);
+            launch_as1<LIST, BITS, GPT, 1, true>(items, starts, it, (int)M, grid, s);
         else
-            launch_as1<BITS, GPT, 1, false>(packed, X, Y, (int)M, (int)N, (int)K, P, nrb, grid,
-                                            out_f32, s);
+            launch_as1<LIST, BITS, GPT, 1, false>(items, starts, it, (int)M, grid, s);
     } else {
         if (bf16)
-            launch_as1<BITS, GPT, 2, true>(packed, X, Y, (int)M, (int)N, (int)K, P, nrb, grid,
-                                           out_f32, s);
+            launch_as1<LIST, BITS, GPT, 2, true>(items, starts, it, (int)M, grid, s);
         else
-            launch_as1<BITS, GPT, 2, false>(packed, X, Y, (int)M, (int)N, (int)K, P, nrb, grid,
-                                            out_f32, s);
+            launch_as1<LIST, BITS, GPT, 2, false>(items, starts, it, (int)M, grid, s);
     }
     return hipGetLastError();
 }
 
-template <int BITS>
-static hipError_t launch_as_bits(const uint8_t *packed, const uint16_t *X, void *Y, int64_t M,
-                                 int64_t N, int64_t K, int group, bool bf16, bool out_f32,
-                                 int cus, hipStream_t s) {
+template <bool LIST, int BITS>
+static hipError_t launch_as_bits(const WorkItem *items, const WorkStart *starts,
+                                 const WorkItem &it, int64_t M, int group, bool bf16, int grid,
+                                 hipStream_t s) {
     switch (group) {
-    case 32: return launch_as<BITS, 4>(packed, X, Y, M, N, K, bf16, out_f32, cus, s);
-    case 64: return launch_as<BITS, 2>(packed, X, Y, M, N, K, bf16, out_f32, cus, s);
-    default: return launch_as<BITS, 1>(packed, X, Y, M, N, K, bf16, out_f32, cus, s);
+    case 32: return launch_as<LIST, BITS, 4>(items, starts, it, M, bf16, grid, s);
+    case 64: return launch_as<LIST, BITS, 2>(items, starts, it, M, bf16, grid, s);
+    default: return launch_as<LIST, BITS, 1>(items, starts, it, M, bf16, grid, s);
+    }
+}
+
+template <bool LIST>
+static hipError_t launch_as_fmt(const WorkItem *items, const WorkStart *starts,
+                                const WorkItem &it, int bits, int group, bool bf16, int64_t M,
+                                int grid, hipStream_t s) {
+    switch (bits) {
+    case 2: return launch_as_bits<LIST, 2>(items, starts, it, M, group, bf16, grid, s);
+    case 3: return launch_as_bits<LIST, 3>(items, starts, it, M, group, bf16, grid, s);
+    case 4: return launch_as_bits<LIST, 4>(items, starts, it, M, group, bf16, grid, s);
+    case 5: return launch_as_bits<LIST, 5>(items, starts, it, M, group, bf16, grid, s);
+    case 6: return launch_as_bits<LIST, 6>(items, starts, it, M, group, bf16, grid, s);
+    case 8: return launch_as_bits<LIST, 8>(items, starts, it, M, group, bf16, grid, s);
+    default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_affine_skinny(const uint8_t *packed, const uint16_t *X, void *Y, int bits,
                                 int group, bool bf16_scales, int64_t M, int64_t N, int64_t K,
                                 bool out_f32, int cus, hipStream_t s) {
-    switch (bits) {
-    case 2: return launch_as_bits<2>(packed, X, Y, M, N, K, group, bf16_scales, out_f32, cus, s);
-    case 3: return launch_as_bits<3>(packed, X, Y, M, N, K, group, bf16_scales, out_f32, cus, s);
-    case 4: return launch_as_bits<4>(packed, X, Y, M, N, K, group, bf16_scales, out_f32, cus, s);
-    case 5: return launch_as_bits<5>(packed, X, Y, M, N, K, group, bf16_scales, out_f32, cus, s);
-    case 6: return launch_as_bits<6>(packed, X, Y, M, N, K, group, bf16_scales, out_f32, cus, s);
-    case 8: return launch_as_bits<8>(packed, X, Y, M, N, K, group, bf16_scales, out_f32, cus, s);
-    default: return hipErrorInvalidValue;
-    }
+    WorkItem it{};
+    it.packed = packed;
+    it.x = X;
+    it.y = Y;
+    it.N = (int32_t)N;
+    it.K = (int32_t)K;
+    it.P = (int32_t)ceil_div(K, AFF_TILE_K);
+    it.units = (int32_t)ceil_div(N, RB);
+    it.out_f32 = out_f32 ? 1 : 0;
+    const int grid = it.units < cus ? it.units : cus;
+    return launch_as_fmt<false>(nullptr, nullptr, it, bits, group, bf16_scales, M, grid, s);
+}
+
+int affine_skinny_wgs_per_cu() { return 1; }
+
+hipError_t launch_affine_skinny_list(const WorkItem *items, const WorkStart *starts, int grid,
+                                     int bits, int group, bool bf16_scales, int64_t M,
+                                     hipStream_t s) {
+    WorkItem none{};
+    return launch_as_fmt<true>(items, starts, none, bits, group, bf16_scales, M, grid, s);
 }
 
 }  // namespace qg

@@ -83,8 +83,13 @@ __device__ __forceinline__ AgConsts ag_consts() {
     return AgConsts{ag_opaque(AG_MAGIC), ag_opaque(m0), PL::NP == 2 ? ag_opaque(m1) : 0u};
 }
 
-// (a & m) | c as one v_and_or_b32, written out for the two-plane merge: the
-// compiler would otherwise regroup two of them into two ands and an or3.
+// (a & m) | c as one v_and_or_b32, written out for the first and-or of the
+// two-plane merge: with both in plain code the compiler regroups them into
+// two ands and an or3.  Only this inner one is inline asm.  The compiler does
+// not count an asm instruction as a VALU write in its hazard checks, and an
+// MFMA that reads a VGPR fewer than 2 wait states after a VALU wrote it reads
+// the old value; so the value an MFMA takes comes from the outer and-or,
+// which the compiler emits and pads itself.
 __device__ __forceinline__ unsigned ag_and_or(unsigned a, unsigned m, unsigned c) {
     unsigned r;
     asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
@@ -105,7 +110,7 @@ __device__ __forceinline__ unsigned ag_bf16_pair(const AgTile<BITS, GPT> &T, int
         constexpr int PER1 = 16 / PL::W1;
         const int sh = PL::W1 * (j % PER1) - PL::O1;
         const unsigned w = T.p1[j / PER1];
-        return ag_and_or(sh >= 0 ? w >> sh : w << -sh, k.m1, ag_and_or(a, k.m0, k.magic));
+        return ((sh >= 0 ? w >> sh : w << -sh) & k.m1) | ag_and_or(a, k.m0, k.magic);
     } else {
         return (a & k.m0) | k.magic;
     }

@@ -453,12 +453,24 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
         }
         if (format_group(fmt) == 0) return QG_EINVAL;
         const AffineFmt aff = affine_decode(fmt);
-        if (fmt != QG_FMT_Q4_ASYM_G64 && !aff.bits) return QG_EUNSUPPORTED;
+        const bool q8row = fmt == QG_FMT_Q8_ROW;
+        if (fmt != QG_FMT_Q4_ASYM_G64 && !aff.bits && !q8row) return QG_EUNSUPPORTED;
         if (M < 1 || M > M_MAX || count < 1 || count > 65536) return QG_ESHAPE;
-        if (aff.bits) {
-            // affine products: the decode GEMV only
+        if (q8row) {
+            // the weight-only int8 GEMV: one activation row
             if (M != 1 || kernel == QG_KERNEL_MFMA) return QG_EUNSUPPORTED;
             kernel = QG_KERNEL_VALU;
+        }
+        if (aff.bits) {
+            // affine products: the decode GEMV at M = 1, the MFMA skinny
+            // product for more rows
+            if (M == 1) {
+                if (kernel == QG_KERNEL_MFMA) return QG_EUNSUPPORTED;
+                kernel = QG_KERNEL_VALU;
+            } else {
+                if (kernel == QG_KERNEL_VALU) return QG_EUNSUPPORTED;
+                kernel = QG_KERNEL_MFMA;
+            }
         }
         if (kernel == QG_KERNEL_AUTO) kernel = M <= Q4_VALU_ROWS_MAX ? QG_KERNEL_VALU : QG_KERNEL_MFMA;
         if (kernel == QG_KERNEL_VALU && M > q4_gemv_rows_max()) return QG_EUNSUPPORTED;
@@ -495,13 +507,14 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
             w.y = d.y;
             w.N = (int32_t)d.N;
             w.K = (int32_t)d.K;
-            w.P = (int32_t)ceil_div(d.K, aff.bits ? AFF_TILE_K : Q4_TILE_K);
+            w.P = (int32_t)ceil_div(d.K, aff.bits ? AFF_TILE_K : q8row ? Q8R_TILE_K : Q4_TILE_K);
             w.units = (int32_t)ceil_div(ceil_div(d.N, RB), rpu);
             w.out_f32 = out_dtype == QG_OUT_F32 ? 1 : 0;
             total_units += w.units;
             total_cost += (int64_t)w.units * ((int64_t)w.P * rpu + 2);
         }
-        const int per_cu = aff.bits                  ? affine_gemv_wgs_per_cu()
+        const int per_cu = aff.bits ? (M == 1 ? affine_gemv_wgs_per_cu() : affine_skinny_wgs_per_cu())
+                           : q8row                    ? q8row_gemv_wgs_per_cu()
                            : kernel == QG_KERNEL_VALU ? q4_gemv_wgs_per_cu(M)
                                                       : q4_skinny_stream_wgs_per_cu();
         int64_t grid = (int64_t)cus * per_cu;
@@ -561,8 +574,10 @@ int qg_batch_run(const qg_batch_plan *plan, void *stream) {
     try {
         if (!plan || !plan->worklist || !aligned(plan->worklist, 16)) return QG_EINVAL;
         const AffineFmt aff = affine_decode(plan->fmt);
-        if ((plan->fmt != QG_FMT_Q4_ASYM_G64 && !aff.bits) ||
-            (aff.bits && (plan->M != 1 || plan->kernel != QG_KERNEL_VALU)) ||
+        const bool q8row = plan->fmt == QG_FMT_Q8_ROW;
+        if ((plan->fmt != QG_FMT_Q4_ASYM_G64 && !aff.bits && !q8row) ||
+            (q8row && (plan->M != 1 || plan->kernel != QG_KERNEL_VALU)) ||
+            (aff.bits && ((plan->M == 1) != (plan->kernel == QG_KERNEL_VALU))) ||
             plan->M < 1 || plan->M > M_MAX ||
             plan->count < 1 || plan->count > 65536 || plan->grid < 1 ||
             plan->grid > WL_GRID_MAX || plan->kmax < format_group(plan->fmt) ||
@@ -575,9 +590,14 @@ int qg_batch_run(const qg_batch_plan *plan, void *stream) {
         const WorkItem *items = reinterpret_cast<const WorkItem *>(base + WL_HEADER_BYTES);
         const WorkStart *starts = reinterpret_cast<const WorkStart *>(items + plan->count);
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-        if (aff.bits)
+        if (q8row)
+            return hip_status(launch_q8row_gemv_list(items, starts, plan->grid, plan->kmax, s));
+        if (aff.bits && plan->M == 1)
             return hip_status(launch_affine_gemv_list(items, starts, plan->grid, plan->kmax,
                                                       aff.bits, aff.group, aff.bf16 != 0, s));
+        if (aff.bits)
+            return hip_status(launch_affine_skinny_list(items, starts, plan->grid, aff.bits,
+                                                        aff.group, aff.bf16 != 0, plan->M, s));
         if (plan->kernel == QG_KERNEL_VALU)
             return hip_status(launch_q4_gemv_list(items, starts, plan->grid, plan->M, s));
         return hip_status(launch_q4_skinny_stream_list(items, starts, plan->grid, plan->M, s));

@@ -50,31 +50,42 @@
 
 namespace qg {
 
-constexpr int GV_WAVES = 4;
 constexpr int GV_TPW = 4;                     // tiles per batch
-constexpr int GV_THREADS = GV_WAVES * 64;
 constexpr int GV_RMAX = 16;                   // rowblocks per output block
 constexpr int GV_MR_MAX = 4;                  // most activation rows per launch
+// Waves per workgroup: 4 for the work list and large matrices; 8 for single
+// matrices with few rowblocks, whose workgroups each get one or two
+// rowblocks: with 8 waves every batch of a 4096-k rowblock has a wave of its
+// own, so a call waits on one memory latency per wave instead of two.
+constexpr int GV_WAVES = 4;
+constexpr int GV_WAVES_SMALL = 8;
 
 int q4_gemv_rows_max() { return GV_MR_MAX; }
 
-// Per row count MR (1, 2 or 4 staged activation rows): tiles per staged
-// segment (6144 k for one row; fewer for more rows, so that the staged x of
-// all rows stays at 12 KB) and the LDS of one workgroup.
-template <int MR>
+// Per row count MR (1, 2 or 4 staged activation rows) and wave count W:
+// tiles per staged segment (6144 k for one row; fewer for more rows, so that
+// the staged x of all rows stays at 12 KB) and the LDS of one workgroup.
+template <int MR, int W = GV_WAVES>
 struct GvCfg {
+    static constexpr int WAVES = W;
+    static constexpr int THREADS = W * 64;
     static constexpr int SEG = 48 / MR;
     static constexpr int ROW4 = SEG * 16;     // uint4 of staged x per row
     static constexpr int ROWS = SEG * 8;      // x sums per row
     static constexpr size_t LDS_X = (size_t)ROW4 * 16 * MR;
     static constexpr size_t LDS_XSUM = (size_t)ROWS * 4 * MR;
-    static constexpr size_t LDS_PART = (size_t)GV_RMAX * GV_WAVES * MR * 16 * 4;
+    // partial-sum slots per rowblock: a batch's sums go to slot (absolute
+    // batch index) mod SLOTS; one row: 8 slots for 4 or 8 waves alike, so the
+    // rounding does not depend on the wave count (slot mod W is the wave)
+    static constexpr int SLOTS = MR == 1 ? 8 : W;
+    static_assert(SLOTS % W == 0, "a slot belongs to one wave");
+    static constexpr size_t LDS_PART = (size_t)GV_RMAX * SLOTS * MR * 16 * 4;
     static constexpr size_t LDS = LDS_X + LDS_XSUM + LDS_PART;
     // resident workgroups per CU, set by registers: at most 102 VGPRs for 5
-    // (1 or 2 rows), 128 for 4 (4 rows); LDS allows more
-    static constexpr int WPC = MR <= 2 ? 5 : 4;
+    // 4-wave workgroups (1 or 2 rows), 128 for 4 (4 rows); 8-wave
+    // workgroups: 2 (at most 128 VGPRs); LDS allows more
+    static constexpr int WPC = W == 4 ? (MR <= 2 ? 5 : 4) : 2;
     static_assert(SEG % GV_TPW == 0, "segments hold whole batches");
-    static_assert((ROW4 * MR) % GV_THREADS == 0, "staging covers the segment evenly");
     static_assert(LDS * WPC <= 160 * 1024, "LDS must not limit residency");
 };
 
@@ -90,7 +101,7 @@ size_t q4_gemv_lds_bytes(int64_t M) {
 struct GemvLds {
     unsigned *xl;   // bf16 pairs of the staged segment, [MR][SEG*64]
     float *xsum;    // [MR][SEG*8]: per (tile, group, k-slice)
-    float *part;    // [GV_RMAX][GV_WAVES][MR][16] per-wave row sums of the block
+    float *part;    // [GV_RMAX][slots][MR][16] row sums of the block per batch slot
 };
 
 // Staging of tiles [0, nt) of segment `seg` of the M activation rows (rows
@@ -101,43 +112,44 @@ struct GemvLds {
 // segment), sums them and ends with a barrier.  The x loads go out before
 // the segment's first weight loads: a wave's loads complete in issue order,
 // so x issued after the weights would wait for them.
-template <int MR>
+template <int MR, int W>
 struct GvStage {
-    static constexpr int U = (GvCfg<MR>::ROW4 * MR) / GV_THREADS;
+    static constexpr int U = (GvCfg<MR, W>::ROW4 * MR + GvCfg<MR, W>::THREADS - 1) /
+                             GvCfg<MR, W>::THREADS;
     u32x4_t v[U];
 };
 
-template <int MR>
-__device__ __forceinline__ void gv_stage_load(GvStage<MR> &st, const uint16_t *x, int M, int K,
+template <int MR, int W>
+__device__ __forceinline__ void gv_stage_load(GvStage<MR, W> &st, const uint16_t *x, int M, int K,
                                               int seg, int nt, int tid) {
-    typedef GvCfg<MR> C;
+    typedef GvCfg<MR, W> C;
     const int k0 = seg * C::SEG * Q4_TILE_K;
     const int n4 = nt * 16;                    // uint4 to stage per row
     const int nx4 = (K - k0) / 8;              // valid uint4 per row (K is a multiple of 64)
 #pragma unroll
-    for (int u = 0; u < GvStage<MR>::U; ++u) {
-        const int i = tid + u * GV_THREADS, m = i / C::ROW4, j = i - m * C::ROW4;
-        st.v[u] = (m < M && j < nx4 && j < n4)
+    for (int u = 0; u < GvStage<MR, W>::U; ++u) {
+        const int i = tid + u * C::THREADS, m = i / C::ROW4, j = i - m * C::ROW4;
+        st.v[u] = (m < M && m < MR && j < nx4 && j < n4)
                       ? ld_global(reinterpret_cast<const u32x4_t *>(x + (size_t)m * K + k0) + j)
                       : u32x4_t{0u, 0u, 0u, 0u};
     }
 }
 
-template <int MR>
-__device__ __forceinline__ void gv_stage_store(const GvStage<MR> &st, const GemvLds &L, int nt,
+template <int MR, int W>
+__device__ __forceinline__ void gv_stage_store(const GvStage<MR, W> &st, const GemvLds &L, int nt,
                                                int tid) {
-    typedef GvCfg<MR> C;
+    typedef GvCfg<MR, W> C;
     const int n4 = nt * 16;
 #pragma unroll
-    for (int u = 0; u < GvStage<MR>::U; ++u) {
-        const int i = tid + u * GV_THREADS, m = i / C::ROW4, j = i - m * C::ROW4;
-        if (j < n4) reinterpret_cast<u32x4_t *>(L.xl)[i] = st.v[u];
+    for (int u = 0; u < GvStage<MR, W>::U; ++u) {
+        const int i = tid + u * C::THREADS, m = i / C::ROW4, j = i - m * C::ROW4;
+        if (m < MR && j < n4) reinterpret_cast<u32x4_t *>(L.xl)[i] = st.v[u];
     }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         const uint4 *xr = reinterpret_cast<const uint4 *>(L.xl) + m * C::ROW4;
-        for (int i = tid; i < nt * 8; i += GV_THREADS) {
+        for (int i = tid; i < nt * 8; i += C::THREADS) {
             const int p = i >> 3, t = (i >> 2) & 1, kg = i & 3;
             float s = 0.f;
 #pragma unroll
@@ -197,9 +209,10 @@ struct GvCursor {
     int r, b;
 };
 
+template <int W>
 __device__ __forceinline__ GvCursor gv_advance(GvCursor c, int nb) {
-    c.b += GV_WAVES;
-    while (c.b >= nb) {  // uniform; at most GV_WAVES steps
+    c.b += W;
+    while (c.b >= nb) {  // uniform; at most W steps
         c.b -= nb;
         ++c.r;
     }
@@ -235,11 +248,12 @@ __device__ __forceinline__ void gv_load(GvBatch &B, const WorkItem &it, int ub, 
 // rowblock the row sums go to the wave's LDS slot of that rowblock.  Tiles
 // past the segment's end re-read its last tile; their staged x and x sums
 // are zero, so they add exactly zero.
-template <int MR>
+template <int MR, int W>
 __device__ __forceinline__ void gv_step(GvBatch &N, const WorkItem &it, int ub, int pbase, int pn,
                                         GvCursor cn, bool valid, const GvBatch &B, GvCursor c,
-                                        int nb, const GemvLds &L, int lane, int wave,
+                                        int nb, int slot, const GemvLds &L, int lane,
                                         const Q4Consts &magic, float (&acc)[MR]) {
+    constexpr int S = GvCfg<MR, W>::SLOTS;
     const uint8_t *base = it.packed + ((size_t)(ub + cn.r) * it.P + pbase) * Q4_TILE_BYTES;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(uniform_ptr(base), valid ? (unsigned)pn * Q4_TILE_BYTES : 0u);
@@ -256,13 +270,18 @@ __device__ __forceinline__ void gv_step(GvBatch &N, const WorkItem &it, int ub, 
         __builtin_amdgcn_sched_barrier(0);
         gv_tile<MR>(B.c[j], B.sb[j], xp + 16 * j, xs + 8 * j, magic, acc);
     }
-    if (c.b + GV_WAVES >= nb) {
+    // the row sums into the batch's slot of the rowblock: with one row after
+    // every batch (a slot holds every 8th batch, and 4 or 8 waves must add
+    // the batches of a slot alike); with more rows every batch of the
+    // wave's rowblock goes to the slot of the wave, which takes them after
+    // its last batch of the rowblock
+    if (MR == 1 || c.b + W >= nb) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             float a = acc[m];
             a += __shfl_xor(a, 16);
             a += __shfl_xor(a, 32);
-            if (lane < 16) L.part[((c.r * GV_WAVES + wave) * MR + m) * 16 + lane] += a;
+            if (lane < 16) L.part[((c.r * S + slot) * MR + m) * 16 + lane] += a;
             acc[m] = 0.f;
         }
     }
@@ -271,51 +290,53 @@ __device__ __forceinline__ void gv_step(GvBatch &N, const WorkItem &it, int ub, 
 // Rowblocks [u0, u1) of one matrix, in blocks of GV_RMAX: for every segment
 // of K, stage that slice of the M activation rows once and stream the
 // block's batches.
-template <int MR>
+template <int MR, int W>
 __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, int M,
                                          const GemvLds &L, int tid, int lane, int wave,
                                          const Q4Consts &magic) {
-    typedef GvCfg<MR> C;
+    typedef GvCfg<MR, W> C;
+    constexpr int S = C::SLOTS;
     const int nseg = (it.P + C::SEG - 1) / C::SEG;
     const uint16_t *x = reinterpret_cast<const uint16_t *>(it.x);
 #pragma unroll 1
     for (int ub = u0; ub < u1; ub += GV_RMAX) {
         const int nr = min(u1 - ub, GV_RMAX);
         __syncthreads();  // the previous block's partial sums have been written out
-        for (int i = tid; i < nr * GV_WAVES * MR * 16; i += GV_THREADS) L.part[i] = 0.f;
+        for (int i = tid; i < nr * S * MR * 16; i += C::THREADS) L.part[i] = 0.f;
 #pragma unroll 1
         for (int seg = 0; seg < nseg; ++seg) {
             const int pbase = seg * C::SEG;
             const int pn = min(C::SEG, it.P - pbase);
             const int nb = (pn + GV_TPW - 1) / GV_TPW;
             const int T = nr * nb;  // batches of the block in this segment
-            // wave w takes the batches whose absolute index (rowblock * nb +
-            // batch) is w mod GV_WAVES, so how a rowblock's batches are split over
-            // the waves, and hence its rounding, does not depend on where the
-            // workgroup's range starts (single and grouped launches agree
-            // bit for bit)
-            int t = (wave - (int)(((int64_t)ub * nb) % GV_WAVES) + GV_WAVES) % GV_WAVES;
+            // batch t of the block has the absolute index A = ub * nb + t
+            // (rowblock * nb + batch); its sums go to slot A mod S and wave
+            // A mod W computes it, so neither where the workgroup's range
+            // starts nor the wave count changes how a rowblock's sums are
+            // rounded (single and grouped launches agree bit for bit)
+            const int a0 = (int)(((int64_t)ub * nb) % S);
+            int t = (wave - a0 % W + W) % W;
             GvCursor ca = {t / nb, t % nb};
             GvBatch A, B;
             float acc[MR];
 #pragma unroll
             for (int m = 0; m < MR; ++m) acc[m] = 0.f;
-            GvStage<MR> st;
-            gv_stage_load<MR>(st, x, M, it.K, seg, nb * GV_TPW, tid);
+            GvStage<MR, W> st;
+            gv_stage_load<MR, W>(st, x, M, it.K, seg, nb * GV_TPW, tid);
             gv_load(A, it, ub, pbase, pn, ca, t < T, lane);
             __syncthreads();  // nobody still reads the previous segment
-            gv_stage_store<MR>(st, L, nb * GV_TPW, tid);
+            gv_stage_store<MR, W>(st, L, nb * GV_TPW, tid);
 #pragma unroll 1
             for (;;) {
                 if (t >= T) break;
-                const GvCursor cb = gv_advance(ca, nb);
-                gv_step<MR>(B, it, ub, pbase, pn, cb, t + GV_WAVES < T, A, ca, nb, L, lane, wave,
-                            magic, acc);
-                if (t + GV_WAVES >= T) break;
-                const GvCursor cc = gv_advance(cb, nb);
-                gv_step<MR>(A, it, ub, pbase, pn, cc, t + 2 * GV_WAVES < T, B, cb, nb, L, lane,
-                            wave, magic, acc);
-                t += 2 * GV_WAVES;
+                const GvCursor cb = gv_advance<W>(ca, nb);
+                gv_step<MR, W>(B, it, ub, pbase, pn, cb, t + W < T, A, ca, nb, (a0 + t) % S, L,
+                               lane, magic, acc);
+                if (t + W >= T) break;
+                const GvCursor cc = gv_advance<W>(cb, nb);
+                gv_step<MR, W>(A, it, ub, pbase, pn, cc, t + 2 * W < T, B, cb, nb,
+                               (a0 + t + W) % S, L, lane, magic, acc);
+                t += 2 * W;
                 ca = cc;
             }
         }
@@ -323,12 +344,12 @@ __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, int
         // global store between the loads of the sweep above)
         __syncthreads();
         const int r0 = ub * RB, nrow = min((ub + nr) * RB, it.N) - r0;
-        for (int i = tid; i < M * nrow; i += GV_THREADS) {
+        for (int i = tid; i < M * nrow; i += C::THREADS) {
             const int m = i / nrow, r = i - m * nrow;
-            const float *pp = L.part + (((r >> 4) * GV_WAVES) * MR + m) * 16 + (r & 15);
+            const float *pp = L.part + (((r >> 4) * S) * MR + m) * 16 + (r & 15);
             float v = pp[0];
 #pragma unroll
-            for (int w = 1; w < GV_WAVES; ++w) v += pp[16 * MR * w];
+            for (int w = 1; w < S; ++w) v += pp[16 * MR * w];
             const size_t o = (size_t)m * it.N + r0 + r;
             if (it.out_f32)
                 st_global<float>(it.y, o, v);
@@ -340,11 +361,11 @@ __device__ __forceinline__ void gv_range(const WorkItem &it, int u0, int u1, int
 
 // LIST = false: one matrix (`single`); LIST = true: the work list.  Separate
 // instantiations, so profiles tell a whole decode step from single GEMVs.
-template <bool LIST, int MR>
-__global__ void __launch_bounds__(GV_THREADS, GvCfg<MR>::WPC)
+template <bool LIST, int MR, int NW>
+__global__ void __launch_bounds__(NW * 64, (GvCfg<MR, NW>::WPC))
 q4_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
                WorkItem single, int M) {
-    typedef GvCfg<MR> C;
+    typedef GvCfg<MR, NW> C;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     GemvLds L;
     L.xl = reinterpret_cast<unsigned *>(smem);
@@ -355,8 +376,8 @@ q4_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__
     if (!LIST) {
         // single matrix: a contiguous share of the rowblocks per workgroup
         const int64_t n = single.units, g = gridDim.x, j = blockIdx.x;
-        gv_range<MR>(single, (int)(j * n / g), (int)((j + 1) * n / g), M, L, tid, lane, wave,
-                     magic);
+        gv_range<MR, NW>(single, (int)(j * n / g), (int)((j + 1) * n / g), M, L, tid, lane, wave,
+                         magic);
         return;
     }
     const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
@@ -365,24 +386,28 @@ q4_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__
         const WorkItem it = items[i];
         const int u0 = (i == s.item) ? s.unit : 0;
         const int u1 = (i == e.item) ? e.unit : it.units;
-        if (u0 < u1) gv_range<MR>(it, u0, u1, M, L, tid, lane, wave, magic);
+        if (u0 < u1) gv_range<MR, NW>(it, u0, u1, M, L, tid, lane, wave, magic);
     }
 }
 
 template <bool LIST>
 static hipError_t gv_launch(const WorkItem *items, const WorkStart *starts, const WorkItem &it,
-                            int grid, int64_t M, hipStream_t s) {
+                            int grid, int64_t M, bool small, hipStream_t s) {
     const int mr = gv_rows(M);
     const size_t lds = q4_gemv_lds_bytes(M);
-    if (mr == 1)
-        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 1>), dim3(grid), dim3(GV_THREADS), lds, s, items,
-                           starts, it, (int)M);
+    constexpr size_t lds_small = GvCfg<1, GV_WAVES_SMALL>::LDS;
+    if (mr == 1 && small)
+        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 1, GV_WAVES_SMALL>), dim3(grid),
+                           dim3(GV_WAVES_SMALL * 64), lds_small, s, items, starts, it, (int)M);
+    else if (mr == 1)
+        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 1, GV_WAVES>), dim3(grid), dim3(GV_WAVES * 64),
+                           lds, s, items, starts, it, (int)M);
     else if (mr == 2)
-        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 2>), dim3(grid), dim3(GV_THREADS), lds, s, items,
-                           starts, it, (int)M);
+        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 2, GV_WAVES>), dim3(grid), dim3(GV_WAVES * 64),
+                           lds, s, items, starts, it, (int)M);
     else
-        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 4>), dim3(grid), dim3(GV_THREADS), lds, s, items,
-                           starts, it, (int)M);
+        hipLaunchKernelGGL((q4_gemv_kernel<LIST, 4, GV_WAVES>), dim3(grid), dim3(GV_WAVES * 64),
+                           lds, s, items, starts, it, (int)M);
     return hipGetLastError();
 }
 
@@ -398,16 +423,19 @@ hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int
     it.P = (int32_t)ceil_div(K, Q4_TILE_K);
     it.units = (int32_t)ceil_div(N, RB);
     it.out_f32 = out_f32 ? 1 : 0;
-    const int64_t cap = (int64_t)cus * q4_gemv_wgs_per_cu(M);
+    // one activation row and at most two rowblocks per CU: 8-wave workgroups
+    // of one rowblock each (see GV_WAVES_SMALL)
+    const bool small = M == 1 && it.units <= (int64_t)2 * cus;
+    const int64_t cap = small ? it.units : (int64_t)cus * q4_gemv_wgs_per_cu(M);
     const int grid = (int)(it.units < cap ? it.units : cap);
-    return gv_launch<false>(nullptr, nullptr, it, grid, M, s);
+    return gv_launch<false>(nullptr, nullptr, it, grid, M, small, s);
 }
 
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts, int grid,
                                int64_t M, hipStream_t s) {
     if (M < 1 || M > GV_MR_MAX) return hipErrorInvalidValue;
     WorkItem none{};
-    return gv_launch<true>(items, starts, none, grid, M, s);
+    return gv_launch<true>(items, starts, none, grid, M, false, s);
 }
 
 }  // namespace qg

@@ -15,7 +15,7 @@
 // at 32 rows 2 tiles of each of two rowblocks, see pair mode) double-
 // buffered: the load of each tile of the next batch is issued just before
 // the arithmetic of the same tile of the current batch.  The 16 x M results
-// of 6 rowblocks stay in the wave's registers and are stored together; when
+// of 6 rowblocks (8 at 32 rows) stay in the wave's registers and are stored together; when
 // K spans several segments those are the rowblocks whose sums the wave
 // keeps across the segments.  Every rowblock accumulates its
 // tiles in K order within one wave, so single and grouped launches give
@@ -34,7 +34,7 @@ struct SsCfg {
     static constexpr int WAVES = MT == 1 ? 16 : 8;
     static constexpr int THREADS = WAVES * 64;
     // rowblocks whose results a wave keeps in registers (stored together)
-    static constexpr int R = MT == 1 ? 6 : 6;
+    static constexpr int R = MT == 1 ? 6 : 8;
     // two rowblocks per wave at a time (see pair mode below)
     static constexpr bool PAIR = MT == 2;
     static constexpr int MP = 16 * MT;               // padded activation rows
@@ -340,7 +340,10 @@ __device__ __forceinline__ void sp_step(SsBatch &N, __amdgpu_buffer_rsrc_t ra,
         N.sb[j] = buf_ld_x2(ra, ls, to);
         N.c[2 + j] = buf_ld_x4(rb, lc, to);
         N.sb[2 + j] = buf_ld_x2(rb, ls, to);
-        __builtin_amdgcn_sched_barrier(0);
+        // the loads stay here; ALU, MFMA and LDS work may move across, so
+        // the scheduler can overlap one tile's MFMA latency with the next
+        // tile's unpacking (mask: everything but vector memory)
+        __builtin_amdgcn_sched_barrier(0x078F);
         ss_tile2<MT>(B.c[j], B.sb[j], B.c[2 + j], B.sb[2 + j], xl, pl0 + j, lane, kq, acc_a,
                      acc_b);
     }

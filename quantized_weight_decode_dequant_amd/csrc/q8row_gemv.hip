@@ -59,27 +59,33 @@ __device__ __forceinline__ float rg_reduce_kslices(float a) {
     return a;
 }
 
-__global__ void __launch_bounds__(RG_THREADS, 4)
-q8row_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restrict__ x,
-                  void *__restrict__ y, int N, int K, int P, int nrb, int out_f32) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// LDS of one workgroup for inputs of up to kmax.
+static size_t rg_lds_bytes(int64_t kmax) {
+    const int64_t nb = ceil_div(ceil_div(kmax, Q8R_TILE_K), RG_TPB);
+    return (size_t)nb * RG_TPB * Q8R_TILE_K * 4 + (size_t)RG_RMAX * RG_WAVES * 16 * 4 +
+           (size_t)RG_THREADS * 4;
+}
+
+// Rowblocks [u0, u1) of one matrix.
+__device__ __forceinline__ void rg_range(const WorkItem &it, int u0, int u1, unsigned char *smem,
+                                         int tid, int lane, int wave) {
+    const uint8_t *__restrict__ packed = it.packed;
+    const uint16_t *__restrict__ x = reinterpret_cast<const uint16_t *>(it.x);
+    const int N = it.N, K = it.K, P = it.P;
+    const int kg = lane >> 4;
     const int nb = (P + RG_TPB - 1) / RG_TPB;
     const int KS = nb * RG_TPB * Q8R_TILE_K;  // staged x length (zero past K)
     float *xl = reinterpret_cast<float *>(smem);                  // [KS]
     float *part = xl + KS;                                         // [RMAX][WAVES][16]
     float *red = part + RG_RMAX * RG_WAVES * 16;                   // [THREADS]
-    const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t G = gridDim.x, j = blockIdx.x;
-    const int u0 = (int)(j * nrb / G), u1 = (int)((j + 1) * nrb / G);
-    if (u0 >= u1) return;
     const size_t rb_bytes = (size_t)P * Q8R_TILE_BYTES + Q8R_RB_TAIL;
     // stage x as fp32 and take sum_k x: each thread adds its elements in k
     // order, then the threads' sums are added pairwise in a fixed tree
+    __syncthreads();  // nobody still reads the previous range's x
     float own = 0.f;
     for (int k = tid; k < KS; k += RG_THREADS) {
         float v = 0.f;
-        if (k < K) v = bf16_lo((unsigned)x[k]);
+        if (k < K) v = bf16_lo((unsigned)ld_global(x + k));
         xl[k] = v;
         own += v;
     }
@@ -95,7 +101,12 @@ q8row_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restrict
     for (int ub = u0; ub < u1; ub += RG_RMAX) {
         const int nr = min(u1 - ub, RG_RMAX);
         const int T = nr * nb;
-        int t = wave, ci = t / nb, cb = t % nb;
+        // wave w takes the batches whose absolute index (rowblock * nb +
+        // batch) is w mod RG_WAVES, so a rowblock's split over the waves,
+        // and hence its rounding, does not depend on where the range starts
+        // (single and grouped launches agree bit for bit)
+        int t = (wave - (int)(((int64_t)ub * nb) % RG_WAVES) + RG_WAVES) % RG_WAVES;
+        int ci = t / nb, cb = t % nb;
         RgBatch A, B;
         float acc = 0.f;
         {
@@ -156,25 +167,65 @@ q8row_gemv_kernel(const uint8_t *__restrict__ packed, const uint16_t *__restrict
                 const float sc = ld_global(reinterpret_cast<const float *>(
                     packed + (size_t)(ub + i) * rb_bytes + (size_t)P * Q8R_TILE_BYTES) + row);
                 const float out = sc * (v - 128.f * xsum);
-                if (out_f32)
-                    st_global<float>(y, n, out);
+                if (it.out_f32)
+                    st_global<float>(it.y, n, out);
                 else
-                    st_global<uint16_t>(y, n, f32_to_bf16(out));
+                    st_global<uint16_t>(it.y, n, f32_to_bf16(out));
             }
         }
     }
 }
 
+// LIST = false: one matrix (`single`, workgroup j takes rowblocks
+// [j n / G, (j + 1) n / G)); LIST = true: a device work list of GEMVs
+// (workgroup j walks the (matrix, rowblock) range [starts[j], starts[j + 1])).
+template <bool LIST>
+__global__ void __launch_bounds__(RG_THREADS, 4)
+q8row_gemv_kernel(const WorkItem *__restrict__ items, const WorkStart *__restrict__ starts,
+                  WorkItem single) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (!LIST) {
+        const int64_t G = gridDim.x, j = blockIdx.x, n = single.units;
+        const int u0 = (int)(j * n / G), u1 = (int)((j + 1) * n / G);
+        if (u0 < u1) rg_range(single, u0, u1, smem, tid, lane, wave);
+        return;
+    }
+    const WorkStart s = starts[blockIdx.x], e = starts[blockIdx.x + 1];
+#pragma unroll 1
+    for (int i = s.item; i < e.item || (i == e.item && e.unit > 0); ++i) {
+        const WorkItem it = items[i];
+        const int u0 = (i == s.item) ? s.unit : 0;
+        const int u1 = (i == e.item) ? e.unit : it.units;
+        if (u0 < u1) rg_range(it, u0, u1, smem, tid, lane, wave);
+    }
+}
+
 hipError_t launch_q8row_gemv(const uint8_t *packed, const uint16_t *x, void *y, int64_t N,
                              int64_t K, bool out_f32, int cus, hipStream_t s) {
-    const int P = (int)ceil_div(K, Q8R_TILE_K);
-    const int nrb = (int)ceil_div(N, RB);
-    const int nb = (int)ceil_div(P, RG_TPB);
-    const size_t lds = (size_t)nb * RG_TPB * Q8R_TILE_K * 4 + (size_t)RG_RMAX * RG_WAVES * 16 * 4 +
-                       (size_t)RG_THREADS * 4;
-    const int grid = nrb < cus * 4 ? nrb : cus * 4;
-    hipLaunchKernelGGL(q8row_gemv_kernel, dim3(grid), dim3(RG_THREADS), lds, s, packed, x, y,
-                       (int)N, (int)K, P, nrb, out_f32 ? 1 : 0);
+    WorkItem it{};
+    it.packed = packed;
+    it.x = x;
+    it.y = y;
+    it.N = (int32_t)N;
+    it.K = (int32_t)K;
+    it.P = (int32_t)ceil_div(K, Q8R_TILE_K);
+    it.units = (int32_t)ceil_div(N, RB);
+    it.out_f32 = out_f32 ? 1 : 0;
+    const int grid = it.units < cus * 4 ? it.units : cus * 4;
+    hipLaunchKernelGGL((q8row_gemv_kernel<false>), dim3(grid), dim3(RG_THREADS), rg_lds_bytes(K),
+                       s, (const WorkItem *)nullptr, (const WorkStart *)nullptr, it);
+    return hipGetLastError();
+}
+
+int q8row_gemv_wgs_per_cu() { return 4; }
+
+hipError_t launch_q8row_gemv_list(const WorkItem *items, const WorkStart *starts, int grid,
+                                  int64_t kmax, hipStream_t s) {
+    WorkItem none{};
+    hipLaunchKernelGGL((q8row_gemv_kernel<true>), dim3(grid), dim3(RG_THREADS), rg_lds_bytes(kmax),
+                       s, items, starts, none);
     return hipGetLastError();
 }
 

@@ -191,6 +191,10 @@ hipError_t launch_pack_q8row(const int8_t *codes, const float *scales, int64_t N
 hipError_t launch_q8row_gemv(const uint8_t *packed, const uint16_t *x, void *y,
                              int64_t N, int64_t K, bool out_f32, int cus,
                              hipStream_t s);
+// the row-scale int8 GEMV over a device work list (kmax = the largest K)
+hipError_t launch_q8row_gemv_list(const WorkItem *items, const WorkStart *starts, int grid,
+                                  int64_t kmax, hipStream_t s);
+int q8row_gemv_wgs_per_cu();
 size_t q8row_packed_bytes(int64_t N, int64_t K);
 size_t affine_packed_bytes(int bits, int group, int64_t N, int64_t K);
 hipError_t launch_pack_affine(const uint8_t *codes, const uint16_t *scales,
@@ -210,6 +214,12 @@ hipError_t launch_affine_skinny(const uint8_t *packed, const uint16_t *X, void *
                                 int bits, int group, bool bf16_scales, int64_t M,
                                 int64_t N, int64_t K, bool out_f32, int cus,
                                 hipStream_t s);
+// the affine skinny product over a device work list (M = 2..32; every item
+// of one format), one workgroup per CU
+hipError_t launch_affine_skinny_list(const WorkItem *items, const WorkStart *starts, int grid,
+                                     int bits, int group, bool bf16_scales, int64_t M,
+                                     hipStream_t s);
+int affine_skinny_wgs_per_cu();
 
 size_t q4_packed_bytes(int64_t N, int64_t K);
 size_t q8_packed_bytes(int64_t N, int64_t K);

@@ -18,18 +18,25 @@
 // Within a rowblock the 16 waves split K: wave w takes T consecutive tiles
 // of each segment, so even a matrix of 256 rowblocks keeps every wave of
 // every CU loading.  When K is one segment, X is staged once and the next
-// rowblock's weight loads go out before the current rowblock's arithmetic;
-// otherwise each segment's loads go out before its X is staged.  The 16 wave
-// partials of a rowblock are added in LDS in wave order (deterministic) and
-// written by wave 0.  Weight tiles past the end of K read as zero (their
+// rowblock's weight loads go out before the current rowblock's arithmetic.
+// When K spans segments, the segments are the outer loop: a workgroup with
+// several rowblocks (up to 4) stages each segment's X once for all of them,
+// adds each (rowblock, segment) partial of its 16 waves into the rowblock's
+// sums in LDS and loads the next rowblock's weights during the current one's
+// arithmetic; a workgroup with one rowblock keeps its sums in registers.
+// The 16 wave partials of a rowblock are added in wave order, the segments
+// in order (deterministic).  Weight tiles past the end of K read as zero (their
 // offsets sit in the range-checked part of the buffer address), and so does
 // X past K and past row M, so ragged shapes need no branches.
+#include <algorithm>
+
 #include "qg_internal.h"
 
 namespace qg {
 
 constexpr int SK_WAVES = 16;
 constexpr int SK_THREADS = SK_WAVES * 64;
+constexpr int SK_RMAX = 4;  // rowblocks per workgroup when K spans several segments
 
 template <int MT, int T>
 struct SkCfg {
@@ -39,7 +46,9 @@ struct SkCfg {
     static constexpr size_t LDS_X = (size_t)MP * RS * 2;
     static constexpr size_t LDS_XS = (size_t)2 * SEGT * MP * 4;
     static constexpr size_t LDS_RED = (size_t)SK_WAVES * 64 * 16;
-    static_assert(LDS_X + LDS_XS + LDS_RED <= 160 * 1024, "LDS budget");
+    // the workgroup's rowblock sums across segments: [SK_RMAX][MT][64] f32x4
+    static constexpr size_t LDS_ACC = (size_t)SK_RMAX * MT * 64 * 16;
+    static_assert(LDS_X + LDS_XS + LDS_RED + LDS_ACC <= 160 * 1024, "LDS budget");
 };
 
 template <int T>
@@ -186,6 +195,46 @@ __device__ __forceinline__ void sk_finish(const f32x4_t acc[MT], f32x4_t (*red)[
     }
 }
 
+// Add this segment's partials of a rowblock (the 16 waves' acc, in wave
+// order) to the rowblock's sums in LDS (set on the first segment): segments
+// are added in order, so the result is deterministic.
+template <int MT>
+__device__ __forceinline__ void sk_accumulate(const f32x4_t acc[MT], f32x4_t (*red)[64],
+                                              f32x4_t *accl, bool first, int wave, int lane) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        red[wave][lane] = acc[mt];
+        __syncthreads();
+        if (wave == mt) {
+            f32x4_t s = red[0][lane];
+#pragma unroll
+            for (int w = 1; w < SK_WAVES; ++w) s += red[w][lane];
+            accl[mt * 64 + lane] = first ? s : accl[mt * 64 + lane] + s;
+        }
+        __syncthreads();
+    }
+}
+
+// Write a rowblock's sums from LDS (wave mt writes m-tile mt).
+template <int MT>
+__device__ __forceinline__ void sk_write(const f32x4_t *accl, int wave, int lane, int rb, int M,
+                                         const WorkItem &it) {
+    if (wave >= MT) return;
+    const int kg = lane >> 4, n = rb * RB + (lane & 15);
+    if (n >= it.N) return;
+    const f32x4_t s = accl[wave * 64 + lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int m = 16 * wave + 4 * kg + e;
+        if (m < M) {
+            if (it.out_f32)
+                st_global<float>(it.y, (size_t)m * it.N + n, s[e]);
+            else
+                st_global<uint16_t>(it.y, (size_t)m * it.N + n, f32_to_bf16(s[e]));
+        }
+    }
+}
+
 template <int MT>
 __device__ __forceinline__ void sk_zero(f32x4_t a[MT]) {
 #pragma unroll
@@ -199,6 +248,7 @@ q4_skinny_kernel(WorkItem it, int M) {
     __shared__ __attribute__((aligned(16))) uint16_t xl[C::MP * C::RS];
     __shared__ __attribute__((aligned(16))) float xs[2 * C::SEGT * C::MP];
     __shared__ f32x4_t red[SK_WAVES][64];
+    __shared__ f32x4_t accl[SK_RMAX * MT * 64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Q4Consts kq = q4_consts();
@@ -236,10 +286,15 @@ q4_skinny_kernel(WorkItem it, int M) {
         }
         return;
     }
-    // several segments per rowblock: X re-staged per segment, each segment's
-    // weight loads issued before its staging
-#pragma unroll 1
-    for (; rb < nrb; rb += gridDim.x) {
+    // several segments per rowblock: segments outermost.  The workgroup's
+    // rowblocks (at most SK_RMAX, grid-strided) keep their sums in LDS across
+    // the segments, so X is staged once per segment; the weights of the next
+    // (rowblock, segment) load during the current one's arithmetic, and the
+    // first rowblock's weights of a segment before its X is staged.
+    const int rpw = (nrb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    if (rpw == 1) {
+        // one rowblock: its sums stay in registers across the segments, each
+        // segment's weight loads issued before its X is staged
         sk_zero<MT>(acc);
 #pragma unroll 1
         for (int seg = 0; seg < nseg; ++seg) {
@@ -249,8 +304,54 @@ q4_skinny_kernel(WorkItem it, int M) {
             sk_compute<MT, T>(A, xl, xs, wave * T, lane, kq, acc);
         }
         sk_finish<MT>(acc, red, wave, lane, rb, M, it);
+        return;
     }
-    (void)B;
+    sk_load<T>(A, sk_rsrc(it.packed, rb, P, true), wave * T, lane);
+#pragma unroll 1
+    for (int seg = 0; seg < nseg; ++seg) {
+        __syncthreads();  // nobody still reads the previous segment
+        sk_stage<MT, T>(X, M, it.K, seg, xl, xs, tid);
+        const int p0 = seg * C::SEGT + wave * T;
+        const bool nseg_next = seg + 1 < nseg;
+#pragma unroll 1
+        for (int i = 0; i < rpw; i += 2) {
+            // rowblock i from A while the next (rowblock i + 1, or the first
+            // of the next segment) loads into B
+            {
+                const bool more = i + 1 < rpw;
+                sk_load<T>(B, sk_rsrc(it.packed, more ? rb + (i + 1) * (int)gridDim.x : rb, P,
+                                      more || nseg_next),
+                           more ? p0 : p0 + C::SEGT, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                sk_zero<MT>(acc);
+                sk_compute<MT, T>(A, xl, xs, wave * T, lane, kq, acc);
+                sk_accumulate<MT>(acc, red, accl + i * MT * 64, seg == 0, wave, lane);
+                if (!more) {
+                    // the next segment starts from A
+#pragma unroll
+                    for (int j = 0; j < T; ++j) {
+                        A.c[j] = B.c[j];
+                        A.sb[j] = B.sb[j];
+                    }
+                    break;
+                }
+            }
+            // rowblock i + 1 from B while the next loads into A
+            {
+                const bool more = i + 2 < rpw;
+                sk_load<T>(A, sk_rsrc(it.packed, more ? rb + (i + 2) * (int)gridDim.x : rb, P,
+                                      more || nseg_next),
+                           more ? p0 : p0 + C::SEGT, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                sk_zero<MT>(acc);
+                sk_compute<MT, T>(B, xl, xs, wave * T, lane, kq, acc);
+                sk_accumulate<MT>(acc, red, accl + (i + 1) * MT * 64, seg == 0, wave, lane);
+            }
+        }
+    }
+#pragma unroll 1
+    for (int i = 0; i < rpw; ++i)
+        sk_write<MT>(accl + i * MT * 64, wave, lane, rb + i * (int)gridDim.x, M, it);
 }
 
 hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y, int64_t M,
@@ -264,7 +365,12 @@ hipError_t launch_q4_skinny(const uint8_t *packed, const uint16_t *X, void *Y, i
     it.P = (int32_t)ceil_div(K, Q4_TILE_K);
     it.units = (int32_t)ceil_div(N, RB);
     it.out_f32 = out_f32 ? 1 : 0;
-    const int grid = it.units < cus ? it.units : cus;
+    const int segt = M <= 16 ? (it.P <= SkCfg<1, 1>::SEGT ? SkCfg<1, 1>::SEGT : SkCfg<1, 2>::SEGT)
+                             : SkCfg<2, 1>::SEGT;
+    // one workgroup per CU (fewer CUs for fewer rowblocks), and when K spans
+    // segments at most SK_RMAX rowblocks per workgroup
+    int grid = it.units < cus ? it.units : cus;
+    if (it.P > segt) grid = (int)std::max<int64_t>(ceil_div(it.units, SK_RMAX), grid);
     if (M <= 16) {
         // 2 tiles per wave (4096 k per segment) unless one tile per wave
         // already covers K in one segment

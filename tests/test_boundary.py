@@ -365,12 +365,26 @@ def test_batch_validation():
     assert build(arr=descs(x=A + 2)) == L.QG_EALIGN
     assert build(arr=descs(y=A + 1)) == L.QG_EALIGN
     assert build(arr=descs(y=A + 2), out=L.OUT_F32) == L.QG_EALIGN
-    # affine products: the decode GEMV only, every descriptor of the plan's format
+    # affine products: the GEMV kernel at M = 1, the MFMA kernel for more rows;
+    # every descriptor of the plan's format
     aff = pkg.affine_format(3, 32, False)
-    assert build(fmt=aff, M=2) == L.QG_EUNSUPPORTED
-    assert build(fmt=aff, M=16) == L.QG_EUNSUPPORTED
     assert build(fmt=aff, kernel=L.KERNEL_MFMA) == L.QG_EUNSUPPORTED
+    assert build(fmt=aff, M=2, kernel=L.KERNEL_VALU) == L.QG_EUNSUPPORTED
+    assert build(fmt=aff, M=16, kernel=L.KERNEL_VALU) == L.QG_EUNSUPPORTED
     assert build(fmt=aff) == L.QG_ESIZE  # the descriptors are sized as Q4
+    assert build(fmt=aff, M=2) == L.QG_ESIZE
+    assert build(fmt=aff, M=32, kernel=L.KERNEL_MFMA) == L.QG_ESIZE
+    # int8 row-scale GEMVs: one activation row, the GEMV kernel only
+    q8r = L.FMT_Q8_ROW
+    assert build(fmt=q8r, M=2) == L.QG_EUNSUPPORTED
+    assert build(fmt=q8r, kernel=L.KERNEL_MFMA) == L.QG_EUNSUPPORTED
+    assert build(fmt=q8r) == L.QG_ESIZE  # the descriptors are sized as Q4
+    q4_bytes = good["packed_bytes"]
+    good["packed_bytes"] = pkg.packed_bytes(q8r, 64, 256)
+    assert build(fmt=q8r, arr=descs(K=48)) == L.QG_ESHAPE
+    assert build(fmt=q8r, arr=descs(K=24576 + 32,
+                                     packed_bytes=pkg.packed_bytes(q8r, 64, 24576 + 32))) == L.QG_ESHAPE
+    good["packed_bytes"] = q4_bytes
     good["packed_bytes"] = pkg.packed_bytes(aff, 64, 256)
     assert build(fmt=aff, arr=descs(K=48)) == L.QG_ESHAPE
     assert build(fmt=aff, arr=descs(K=24576 + 32)) == L.QG_ESHAPE
@@ -394,8 +408,13 @@ def test_batch_validation():
     bad.grid, bad.worklist_bytes = 4, wl - 8
     assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # work list too small
     bad.fmt, bad.worklist_bytes, bad.M = aff, wl, 2
-    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # affine past one row
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # affine GEMV kernel past one row
     bad.M, bad.kernel = 1, L.KERNEL_MFMA
-    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # affine on the MFMA family
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # affine MFMA kernel at one row
+    bad.fmt = L.FMT_Q8_ROW
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # int8 rows on the MFMA family
+    bad.kernel, bad.M = L.KERNEL_VALU, 2
+    assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # int8 rows past one row
+    bad.fmt, bad.M, bad.kernel = aff, 1, L.KERNEL_MFMA
     bad.kernel, bad.kmax = L.KERNEL_VALU, 16
     assert lib.qg_batch_run(C.byref(bad), None) == L.QG_EINVAL  # K below one group

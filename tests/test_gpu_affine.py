@@ -218,6 +218,41 @@ def test_affine_batch_split_items_bit_identical(bits):
         assert_f32_close(to_np(y)[rows], ref, what=what)
 
 
+@pytest.mark.parametrize("bits,group,M", [(4, 64, 16), (2, 32, 2), (3, 128, 32), (8, 64, 17),
+                                          (5, 32, 16), (6, 64, 32)])
+def test_affine_batch_skinny_mixed_shapes(bits, group, M):
+    """Affine verification products (M rows each) of mixed shapes in one
+    grouped launch: ragged rowblocks, K over several staged segments, more
+    rowblocks than one workgroup takes.  Every output bitwise equal to
+    qgemm_skinny_run's (each rowblock adds its tiles in K order within one
+    wave in both), sampled rows against the oracle."""
+    note("affine batch skinny bits=%d g=%d M=%d" % (bits, group, M))
+    bf16 = bits % 2 == 1
+    fmt = pkg.affine_format(bits, group, bf16)
+    shapes = [(N, K) for N, K in ((40, 256), (300, 4096), (33, 12288), (1000, 1280), (17, 384),
+                                  (9000, 2048)) if K % group == 0]
+    entries, singles, mats, Xs = [], [], [], []
+    for i, (N, K) in enumerate(shapes):
+        m = synth.affine_matrix(180 + bits, N, K, bits, group, bf16, item=i)
+        X = synth.activations(181, M, K, item=i)
+        p = weights.pack_affine(m, DEV)
+        Xd = weights.to_device(X, DEV)
+        entries.append((p, N, K, Xd, torch.empty((M, N), dtype=torch.bfloat16, device=DEV)))
+        singles.append(pkg.qgemm_skinny_run(fmt, p, M, N, K, Xd))
+        mats.append(m)
+        Xs.append(X)
+    plan = pkg.qg_batch_plan_build(fmt, M, entries)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(182)
+    for (p, N, K, Xd, Y), s, m, X in zip(entries, singles, mats, Xs):
+        what = "bits=%d g=%d M=%d N=%d K=%d" % (bits, group, M, N, K)
+        assert torch.equal(Y, s), "batch differs from qgemm_skinny_run: " + what
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, 24), replace=False)]))
+        ref = oracle.affine_gemm(m.codes[rows], m.scales[rows], m.biases[rows], X, group, bf16)
+        assert_bf16_close(to_np(Y)[:, rows].ravel(), ref.ravel(), what=what)
+
+
 def test_affine_batch_layer_graph_replay():
     """A decoder layer's seven projections (4096 -> 4096, 1024, 1024, 4096,
     12288, 12288; 12288 -> 4096) at 3 bits in one launch, captured in a HIP

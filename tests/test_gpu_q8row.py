@@ -77,3 +77,32 @@ def test_q8row_lm_head_full():
     ref = oracle.q8row_gemv(codes[sel].cpu().numpy(), scales[sel].cpu().numpy(), x)
     assert_f32_close(got_f[rows], ref, what="f32")
     assert_bf16_close(got_b[rows], ref, what="bf16")
+
+
+def test_q8row_batch_mixed_shapes():
+    """Weight-only int8 GEMVs of mixed shapes (ragged rowblocks and tiles, K up
+    to its maximum, more rowblocks than one workgroup takes) in one grouped
+    launch: every output bitwise equal to qgemv_run's, sampled rows against
+    the oracle."""
+    note("q8row batch mixed shapes")
+    shapes = [(40, 192), (1, 64), (3000, 4096), (33, 24576), (100, 1216), (17, 320), (4096, 4096)]
+    entries, singles, mats, xs = [], [], [], []
+    for i, (N, K) in enumerate(shapes):
+        m = synth.q8row_matrix(112, N, K, item=i)
+        x = synth.activations(113, 1, K, item=i)[0]
+        p = weights.pack_q8row(m, DEV)
+        xd = weights.to_device(x, DEV)
+        entries.append((p, N, K, xd, torch.empty(N, dtype=torch.bfloat16, device=DEV)))
+        singles.append(pkg.qgemv_run(Q8R, p, N, K, xd))
+        mats.append(m)
+        xs.append(x)
+    plan = pkg.qg_batch_plan_build(Q8R, 1, entries)
+    pkg.qg_batch_run(plan)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(114)
+    for (p, N, K, xd, y), s, m, x in zip(entries, singles, mats, xs):
+        what = "N=%d K=%d" % (N, K)
+        assert torch.equal(y, s), "batch differs from qgemv_run: " + what
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, 96), replace=False)]))
+        ref = oracle.q8row_gemv(m.codes[rows], m.scales[rows], x)
+        assert_bf16_close(to_np(y)[rows], ref, what=what)
