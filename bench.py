@@ -64,7 +64,7 @@ def traffic_from_profiles(kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-STEP_KERNEL = "q4_gemv_kernel<true, 1>"
+STEP_KERNEL = "q4_gemv_kernel<true, 1, 4>"
 COPY_BYTES = 1 << 30
 PLAIN_READ_BYTES = 4 << 30   # larger than every cache level
 
@@ -419,6 +419,48 @@ def counter_pass(manifest_path: str, seed: int = 0):
         2 * NH)
     torch.cuda.synchronize()
     del qpacked
+
+    # single skinny calls that span several staged K segments
+    for name, N, K, M, kern in (("gate", 12288, 4096, 32, "q4_skinny_kernel<2, 1>"),
+                                ("down", 4096, 12288, 16, "q4_skinny_kernel<1, 2>"),
+                                ("down", 4096, 12288, 32, "q4_skinny_kernel<2, 1>")):
+        m4 = synth.q4_matrix(seed, N, K, item=7)
+        p4 = weights.pack_q4(m4, "cuda")
+        del m4
+        X4 = weights.to_device(synth.activations(seed + 1, M, K, item=7), "cuda")
+        Y4 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        _lib.qgemm_skinny_run(Q4, p4, M, N, K, X4, Y=Y4)
+        add(kern, "single Q4 skinny product %s %d -> %d, M=%d" % (name, K, N, M),
+            roofline.Q4_BYTES_PER_WEIGHT * N * K + 2 * M * K, 2 * M * N)
+        torch.cuda.synchronize()
+        del p4, X4, Y4
+
+    # one layer's seven affine verification products (3-bit g64, M = 16), one launch
+    M3, B3, G3 = 16, 3, 64
+    f3 = _lib.affine_format(B3, G3)
+    g3 = torch.Generator(device="cuda")
+    g3.manual_seed(seed + 30)
+    ents, rd3, wr3 = [], 0, 0
+    for name, k_in, n_out in synth.DECODE_PROJECTIONS:
+        c3 = torch.randint(0, 1 << B3, (n_out, k_in), dtype=torch.uint8, device="cuda", generator=g3)
+        s3 = ((torch.rand(n_out, k_in // G3, device="cuda", generator=g3) + 0.05) * 0.02 * 15 /
+              ((1 << B3) - 1)).half().view(torch.int16)
+        b3 = (torch.randn(n_out, k_in // G3, device="cuda", generator=g3) * 0.01).half().view(torch.int16)
+        p3 = _lib.qgemv_pack(f3, n_out, k_in, c3, s3, b3)
+        del c3, s3, b3
+        X3 = weights.to_device(synth.activations(seed + 1, M3, k_in, item=len(ents)), "cuda")
+        Y3 = torch.empty((M3, n_out), dtype=torch.bfloat16, device="cuda")
+        ents.append((p3, n_out, k_in, X3, Y3))
+        rd3 += n_out * k_in * (B3 / 8 + 4 / G3) + 2 * M3 * k_in
+        wr3 += 2 * M3 * n_out
+    plan3 = pkg.qg_batch_plan_build(f3, M3, ents)
+    torch.cuda.synchronize()
+    pkg.qg_batch_run(plan3)
+    add("affine_skinny_kernel<true, 3, 2, 1, false>",
+        "affine 3-bit g64 verification, one layer's 7 products, M=16, one launch", rd3, wr3)
+    torch.cuda.synchronize()
+    del ents, plan3
 
     NA, KA, GA = 262144, 8192, 64
     for bits in (2, 3):

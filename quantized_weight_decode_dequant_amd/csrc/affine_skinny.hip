@@ -30,7 +30,9 @@ struct AsCfg {
     static constexpr int THREADS = WAVES * 64;
     static constexpr int MP = 16 * MT;                // padded activation rows
     static constexpr int SEGK = 32 / MT;              // tiles per staged segment
-    static constexpr int RS = SEGK * AFF_TILE_K + 8;  // LDS row stride (bf16), 16-byte pad
+    // LDS row stride in bf16: rows 8 dwords apart modulo the 128 banks, so the
+    // 16-byte operand reads of 16 rows x 2 k-pieces hit distinct banks
+    static constexpr int RS = SEGK * AFF_TILE_K + 16;
     static constexpr int R = 4;                       // rowblocks kept across segments
     static constexpr size_t LDS_X = (size_t)MP * RS * 2;
     // group sums: at most SEGK * 4 groups (group 32) per segment

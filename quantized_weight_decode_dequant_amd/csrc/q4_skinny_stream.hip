@@ -39,7 +39,9 @@ struct SsCfg {
     static constexpr bool PAIR = MT == 2;
     static constexpr int MP = 16 * MT;               // padded activation rows
     static constexpr int SEGK = 32 / MT;             // tiles per staged segment
-    static constexpr int RS = SEGK * 128 + 8;        // LDS row stride in bf16 (16-byte pad)
+    // LDS row stride in bf16: rows 8 dwords apart modulo the 128 banks, so the
+    // 16-byte operand reads of 16 rows x 2 k-pieces hit distinct banks
+    static constexpr int RS = SEGK * 128 + 16;
     static constexpr size_t LDS_X = (size_t)MP * RS * 2;
     static constexpr size_t LDS = LDS_X + (size_t)2 * SEGK * MP * 4;
 };

@@ -42,7 +42,9 @@ template <int MT, int T>
 struct SkCfg {
     static constexpr int MP = 16 * MT;               // padded activation rows
     static constexpr int SEGT = SK_WAVES * T;        // tiles per staged segment
-    static constexpr int RS = SEGT * Q4_TILE_K + 8;  // LDS row stride in bf16
+    // LDS row stride in bf16: rows 8 dwords apart modulo the 128 banks, so the
+    // 16-byte operand reads of 16 rows x 2 k-pieces hit distinct banks
+    static constexpr int RS = SEGT * Q4_TILE_K + 16;
     static constexpr size_t LDS_X = (size_t)MP * RS * 2;
     static constexpr size_t LDS_XS = (size_t)2 * SEGT * MP * 4;
     static constexpr size_t LDS_RED = (size_t)SK_WAVES * 64 * 16;
