@@ -470,7 +470,7 @@ __device__ __forceinline__ void ss_store_staged(const WorkItem &it, int rb0, int
             const uint16_t *src = stg + m * SS_STG_RS + 8 * q;
             const size_t o = (size_t)m * it.N + nn;
             if (nn + 8 <= nend) {
-                st_global<u32x4_t>(it.y, o / 8, *reinterpret_cast<const u32x4_t *>(src));
+                st_global_nt<u32x4_t>(it.y, o / 8, *reinterpret_cast<const u32x4_t *>(src));
             } else {
                 for (int j = 0; j < nend - nn; ++j) st_global<uint16_t>(it.y, o + j, src[j]);
             }

@@ -355,6 +355,14 @@ __device__ __forceinline__ void st_global(void *base, size_t i, T v) {
     ((__attribute__((address_space(1))) T *)base)[i] = v;
 }
 
+// The same with the non-temporal hint: for whole-line runs of output written
+// in the middle of a weight stream (measured: lighter on the read stream than
+// plain stores; slower for 2-byte pieces).
+template <typename T>
+__device__ __forceinline__ void st_global_nt(void *base, size_t i, T v) {
+    __builtin_nontemporal_store(v, ((__attribute__((address_space(1))) T *)base) + i);
+}
+
 // The two constants of the nibble unpack, held in VGPRs.  gfx9 VOP3
 // instructions read at most one SGPR or literal, so with both operands in
 // registers (a & mask) | magic selects to a single v_and_or_b32.  They are

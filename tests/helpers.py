@@ -75,6 +75,24 @@ def assert_bf16_close(got, ref, what=""):
     return l2
 
 
+def assert_same(got, want, what=""):
+    """Bitwise equality of two device tensors; on a mismatch the message
+    names how many elements differ, where, and their values."""
+    import torch
+    if torch.equal(got, want):
+        return
+    a, b = got.flatten(), want.flatten()
+    if a.shape != b.shape:
+        raise AssertionError("%s: shapes %s and %s" % (what, tuple(got.shape), tuple(want.shape)))
+    if a.dtype in (torch.bfloat16, torch.float16):
+        diff = a.view(torch.int16) != b.view(torch.int16)
+    else:
+        diff = a != b
+    idx = torch.nonzero(diff).flatten()[:8].tolist()
+    raise AssertionError("%s: %d of %d elements differ, first at %s: got %s want %s" % (
+        what, int(diff.sum()), a.numel(), idx, a[idx].float().tolist(), b[idx].float().tolist()))
+
+
 def to_np(t):
     """Device tensor -> float64 numpy (bf16/fp32 widen exactly)."""
     import torch

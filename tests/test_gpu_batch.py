@@ -9,7 +9,7 @@ import torch
 import oracle
 import quantized_weight_decode_dequant_amd as pkg
 from quantized_weight_decode_dequant_amd import synth, weights, workloads
-from helpers import assert_bf16_close, assert_f32_close, note, to_np
+from helpers import assert_bf16_close, assert_f32_close, assert_same, note, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -45,7 +45,7 @@ def test_batch_m1_mixed_shapes(out_dtype):
             assert_f32_close(got, ref, what="N=%d K=%d" % (N, K))
         else:
             assert_bf16_close(got, ref, what="N=%d K=%d" % (N, K))
-        assert torch.equal(y, s), "batch differs from qgemv_run for N=%d K=%d" % (N, K)
+        assert_same(y, s, "batch vs qgemv_run N=%d K=%d" % (N, K))
 
 
 @pytest.mark.parametrize("M", [2, 3, 4, 5, 16, 17, 32])
@@ -96,7 +96,7 @@ def test_batch_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         for e, ref in zip(entries, eager):
-            assert torch.equal(e[4], ref), "replay %d differs" % rep
+            assert_same(e[4], ref, "replay %d" % rep)
         _ = torch.randn(1000, device=DEV).sum().item()  # unrelated eager work in between
 
 
@@ -113,7 +113,7 @@ def test_batch_decode_step_full():
     workloads.run_step_eager(step)
     torch.cuda.synchronize()
     for g, b in zip(step.gemvs, got):
-        assert torch.equal(g.y, b), g.name
+        assert_same(b, g.y, "grouped vs qgemv_run " + g.name)
     rng = np.random.default_rng(96)
     for idx in (0, 1, 4, 6, 250, 252):
         item, name, N, K = synth.decode_step_shapes()[idx]
@@ -149,7 +149,7 @@ def test_batch_verification_pass_full(M, kernel):
         g = step.gemvs[-1]
         single = pkg.qgemm_skinny_run(Q4, g.packed, M, g.N, g.K, g.X)
         torch.cuda.synchronize()
-        assert torch.equal(single, g.Y)
+        assert_same(g.Y, single, "grouped vs single " + g.name)
 
 
 @pytest.mark.parametrize("M,kernel", [(2, pkg.KERNEL_AUTO), (3, pkg.KERNEL_AUTO),
@@ -232,7 +232,7 @@ def test_batch_forced_kernel(M, kernel):
         pkg.qg_batch_run(plan_a)
         torch.cuda.synchronize()
         for e, a in zip(entries, auto):
-            assert torch.equal(e[4], a[4])
+            assert_same(e[4], a[4], "repeat")
 
 
 @pytest.mark.parametrize("M", [1, 16])
@@ -267,4 +267,4 @@ def test_batch_shared_inputs(M):
             single = pkg.qgemm_skinny_run(Q4, p, M, N, K, x, out_dtype=pkg.OUT_F32)
         torch.cuda.synchronize()
         if M == 1:
-            assert torch.equal(single, y)
+            assert_same(y, single, "grouped vs single")
