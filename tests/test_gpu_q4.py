@@ -113,6 +113,22 @@ def test_q4_skinny_ragged(M, N, K):
     assert_bf16_close(run_skinny(m, X, pkg.OUT_BF16), ref, what="bf16")
 
 
+@pytest.mark.parametrize("M", [5, 32])
+def test_q4_skinny_several_passes(M):
+    """More rowblocks than 4 per workgroup of a one-per-CU grid (1250 of
+    them, a ragged last one): a workgroup takes its rowblocks in several
+    passes; sampled output columns against the oracle."""
+    note("q4 skinny passes M=%d" % M)
+    N, K = 19990, 1216
+    m = synth.q4_matrix(24, N, K)
+    X = synth.activations(25, M, K)
+    got = run_skinny(m, X, pkg.OUT_F32)
+    rows = np.unique(np.concatenate([[0, N - 1], np.arange(16 * 1020, 16 * 1030),
+                                     np.random.default_rng(26).choice(N, 128, replace=False)]))
+    ref = oracle.q4_gemm(m.codes[rows], m.scales[rows], m.biases[rows], X)
+    assert_f32_close(got[:, rows], ref, what="M=%d" % M)
+
+
 def test_q4_skinny_m1_matches_gemv():
     """One activation row through qgemm_skinny_run takes the GEMV kernel:
     the same result as qgemv_run, bit for bit."""
