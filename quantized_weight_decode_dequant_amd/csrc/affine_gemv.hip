@@ -12,7 +12,11 @@
 // A lane's 32 codes are four runs of 8 consecutive k, one per 32-k block of
 // the tile.  The GEMV accumulates (128 + q) x over a run with
 // v_dot2_f32_bf16, and per group adds scale * (acc - 128 sum x) + bias * sum
-// x, with sum x over the lane's k of that group staged once.  8-bit codes do
+// x, with sum x over the lane's k of that group staged once.  2- and 3-bit
+// codes, whose unpacking costs the most VALU work per byte, take each run as
+// the B operand of one v_mfma_f32_16x16x32_bf16 step against x (the same x
+// in all 16 rows of A) instead: the matrix unit does the multiply-adds and
+// the sum over the k-slices, the VALU only the unpack.  8-bit codes do
 // not fit 128 + q in bf16: their two nibble planes run as two dot chains,
 // D = D_lo + 16 D_hi.  The skinny product (M <= 32 rows) takes each run as
 // the B operand of one v_mfma_f32_16x16x32_bf16 step (the 64 lanes' runs i
@@ -164,20 +168,19 @@ __device__ __forceinline__ unsigned ag2_pair(const AgTile<BITS, GPT> &T, int j,
     if constexpr (BITS == 3) {
         const unsigned w1 = T.p1[0];
         const int sh = j - (2 * r + 2);  // plane-1 bit j goes to bit 2 r + 2
-        return ag_and_or(sh >= 0 ? w1 >> sh : w1 << -sh, k.b[r], ag_and_or(u, k.m[r], k.g[r]));
+        return ((sh >= 0 ? w1 >> sh : w1 << -sh) & k.b[r]) | ag_and_or(u, k.m[r], k.g[r]);
     } else {
         return (u & k.m[r]) | k.g[r];
     }
 }
 
-// One tile: xrun = the lane's x of run 0 (run i at xrun + 32 i, 8 bf16),
-// xg = the sums of the lane's x over each of the tile's GPT groups (and, for
-// 2- and 3-bit codes, xw = the same sums weighted by the pairs' offsets).  One dot
-// chain per group; returns y plus the lane's share of the tile.
+// One tile (4-, 5-, 6- and 8-bit codes): xrun = the lane's x of run 0 (run
+// i at xrun + 32 i, 8 bf16), xg = the sums of the lane's x over each of the
+// tile's GPT groups.  One dot chain per group; returns y plus the lane's
+// share of the tile.
 template <int BITS, int GPT, bool BF16S>
 __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint16_t *xrun,
-                                         const float *xg, const float *xw, float y,
-                                         const AgConsts &k, const Ag2Consts &k2) {
+                                         const float *xg, float y, const AgConsts &k) {
     constexpr int CPG = 4 / GPT;  // runs per group
 #pragma unroll
     for (int t = 0; t < GPT; ++t) {
@@ -189,19 +192,45 @@ __device__ __forceinline__ float ag_tile(const AgTile<BITS, GPT> &T, const uint1
             const unsigned xp[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                if constexpr (ag_inplace(BITS))
-                    a0 = dot2_bf16(ag2_pair<BITS, GPT>(T, 4 * i + h, k2), xp[h], a0);
-                else
-                    a0 = dot2_bf16(ag_bf16_pair<BITS, GPT>(T, 4 * i + h, k), xp[h], a0);
+                a0 = dot2_bf16(ag_bf16_pair<BITS, GPT>(T, 4 * i + h, k), xp[h], a0);
                 if constexpr (BITS == 8)
                     a1 = dot2_bf16(ag_pair_hi<BITS, GPT>(T, 4 * i + h, k), xp[h], a1);
             }
         }
         const float X = xg[t];
-        float D = ag_inplace(BITS) ? a0 - xw[t] : fmaf(-128.f, X, a0);
+        float D = fmaf(-128.f, X, a0);
         if constexpr (BITS == 8) D = fmaf(16.f, fmaf(-128.f, X, a1), D);
         const unsigned sb = T.sb[t];
         y = fmaf(ag_scale(sb, BF16S), D, fmaf(ag_bias(sb, BF16S), X, y));
+    }
+    return y;
+}
+
+// 2- and 3-bit codes: the dot products of a 32-k run on the bf16 MFMA, x as
+// the A operand (the same in all 16 rows), the lane's 8 codes as its B column:
+// every lane gets its row's dot over all four k-slices, so no shuffle folds
+// them.  xg, xw: the sums of x (plain and offset-weighted) over each of the
+// tile's GPT groups.
+template <int BITS, int GPT, bool BF16S>
+__device__ __forceinline__ float ag_tile_mfma(const AgTile<BITS, GPT> &T, const uint16_t *xrun,
+                                              const float *xg, const float *xw, float y,
+                                              const Ag2Consts &k2) {
+    constexpr int CPG = 4 / GPT;  // runs per group
+#pragma unroll
+    for (int t = 0; t < GPT; ++t) {
+        f32x4_t C = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CPG; ++c) {
+            const int i = t * CPG + c;
+            const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(xrun + 32 * i);
+            const u32x4_t b = {ag2_pair<BITS, GPT>(T, 4 * i, k2), ag2_pair<BITS, GPT>(T, 4 * i + 1, k2),
+                               ag2_pair<BITS, GPT>(T, 4 * i + 2, k2),
+                               ag2_pair<BITS, GPT>(T, 4 * i + 3, k2)};
+            C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, b), C, 0, 0,
+                                                        0);
+        }
+        const unsigned sb = T.sb[t];
+        y = fmaf(ag_scale(sb, BF16S), C[0] - xw[t], fmaf(ag_bias(sb, BF16S), xg[t], y));
     }
     return y;
 }
@@ -220,7 +249,10 @@ constexpr size_t AG_LDS_PART = (size_t)AG_RMAX * AG_WAVES * 16 * 4;
 template <int BITS, int GPT>
 static size_t ag_lds_bytes(int64_t K) {
     const int64_t KS = ceil_div(ceil_div(K, AFF_TILE_K), AG_TPB) * AG_TPB * AFF_TILE_K;
-    return AG_LDS_PART + (size_t)KS * 2 + (size_t)(KS / 32) * GPT * 4 * (ag_inplace(BITS) ? 2 : 1);
+    // x sums: per (tile, k-slice, group) for the dot chains; per (tile,
+    // group), plain and offset-weighted, for the MFMA path
+    const int64_t nsum = ag_inplace(BITS) ? 2 * (KS / AFF_TILE_K) * GPT : (KS / 32) * GPT;
+    return AG_LDS_PART + (size_t)KS * 2 + (size_t)nsum * 4;
 }
 
 // Rowblocks [u0, u1) of one product.
@@ -235,8 +267,10 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
     const int KS = nb * AG_TPB * AFF_TILE_K;  // staged x length (zero past K)
     float *part = reinterpret_cast<float *>(smem);                               // [RMAX][WAVES][16]
     uint16_t *xl = reinterpret_cast<uint16_t *>(smem + AG_LDS_PART);             // [KS] bf16
-    float *xsl = reinterpret_cast<float *>(smem + AG_LDS_PART + (size_t)KS * 2);  // [KS / 32 * GPT]
-    float *xwl = xsl + KS / 32 * GPT;  // 2- and 3-bit codes: [KS / 32 * GPT]
+    // x sums: [KS / 32 * GPT] per (tile, k-slice, group); 2- and 3-bit codes:
+    // [KS / 128 * GPT] per (tile, group), then the offset-weighted ones xwl
+    float *xsl = reinterpret_cast<float *>(smem + AG_LDS_PART + (size_t)KS * 2);
+    float *xwl = xsl + KS / AFF_TILE_K * GPT;
     const unsigned tb = (unsigned)affine_tile_bytes(BITS, AFF_TILE_K / GPT);
     const size_t rb_bytes = (size_t)P * tb;
     const AgConsts kc = ag_consts<BITS>();
@@ -252,24 +286,44 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
         reinterpret_cast<uint4 *>(xl)[c] = v;
     }
     __syncthreads();
-    for (int e = tid; e < KS / 32 * GPT; e += AG_THREADS) {
-        const int t = e % GPT, tk = e / GPT, tp = tk >> 2, ckg = tk & 3;
-        float sum = 0.f, wsum = 0.f;
+    if constexpr (ag_inplace(BITS)) {
+        // sums over each group of each tile (all four k-slices)
+        for (int e = tid; e < KS / AFF_TILE_K * GPT; e += AG_THREADS) {
+            const int t = e % GPT, tp = e / GPT;
+            float sum = 0.f, wsum = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4 / GPT; ++c) {
-            const int i = t * (4 / GPT) + c;
-            const uint4 v = *reinterpret_cast<const uint4 *>(xl + tp * AFF_TILE_K + 32 * i + 8 * ckg);
-            const float p0 = bf16_lo(v.x) + bf16_hi(v.x), p1 = bf16_lo(v.y) + bf16_hi(v.y);
-            const float p2 = bf16_lo(v.z) + bf16_hi(v.z), p3 = bf16_lo(v.w) + bf16_hi(v.w);
-            sum += (p0 + p1) + (p2 + p3);
-            if constexpr (ag_inplace(BITS)) {
-                const int s0 = 4 * (i % 2);
-                wsum += (ag2_off(s0) * p0 + ag2_off(s0 + 1) * p1) +
-                        (ag2_off(s0 + 2) * p2 + ag2_off(s0 + 3) * p3);
+            for (int ckg = 0; ckg < 4; ++ckg) {
+#pragma unroll
+                for (int c = 0; c < 4 / GPT; ++c) {
+                    const int i = t * (4 / GPT) + c;
+                    const uint4 v =
+                        *reinterpret_cast<const uint4 *>(xl + tp * AFF_TILE_K + 32 * i + 8 * ckg);
+                    const float p0 = bf16_lo(v.x) + bf16_hi(v.x), p1 = bf16_lo(v.y) + bf16_hi(v.y);
+                    const float p2 = bf16_lo(v.z) + bf16_hi(v.z), p3 = bf16_lo(v.w) + bf16_hi(v.w);
+                    const int s0 = 4 * (i % 2);
+                    sum += (p0 + p1) + (p2 + p3);
+                    wsum += (ag2_off(s0) * p0 + ag2_off(s0 + 1) * p1) +
+                            (ag2_off(s0 + 2) * p2 + ag2_off(s0 + 3) * p3);
+                }
             }
+            xsl[e] = sum;
+            xwl[e] = wsum;
         }
-        xsl[e] = sum;
-        if constexpr (ag_inplace(BITS)) xwl[e] = wsum;
+    } else {
+        for (int e = tid; e < KS / 32 * GPT; e += AG_THREADS) {
+            const int t = e % GPT, tk = e / GPT, tp = tk >> 2, ckg = tk & 3;
+            float sum = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4 / GPT; ++c) {
+                const int i = t * (4 / GPT) + c;
+                const uint4 v =
+                    *reinterpret_cast<const uint4 *>(xl + tp * AFF_TILE_K + 32 * i + 8 * ckg);
+                const float p0 = bf16_lo(v.x) + bf16_hi(v.x), p1 = bf16_lo(v.y) + bf16_hi(v.y);
+                const float p2 = bf16_lo(v.z) + bf16_hi(v.z), p3 = bf16_lo(v.w) + bf16_hi(v.w);
+                sum += (p0 + p1) + (p2 + p3);
+            }
+            xsl[e] = sum;
+        }
     }
 #pragma unroll 1
     for (int ub = u0; ub < u1; ub += AG_RMAX) {
@@ -316,12 +370,15 @@ __device__ __forceinline__ void ag_range(const WorkItem &it, int u0, int u1, uns
                     ag_tile_load<BITS, GPT>(Nxt.t[q], rs, nbx * AG_TPB + q, P, tb, lane);
                     __builtin_amdgcn_sched_barrier(0);
                     const int tp = cb * AG_TPB + q;
-                    acc = ag_tile<BITS, GPT, BF16S>(Cur.t[q], xl + tp * AFF_TILE_K + 8 * kg,
-                                                    xsl + (4 * tp + kg) * GPT,
-                                                    xwl + (4 * tp + kg) * GPT, acc, kc, k2);
+                    if constexpr (ag_inplace(BITS))
+                        acc = ag_tile_mfma<BITS, GPT, BF16S>(Cur.t[q], xl + tp * AFF_TILE_K + 8 * kg,
+                                                             xsl + tp * GPT, xwl + tp * GPT, acc, k2);
+                    else
+                        acc = ag_tile<BITS, GPT, BF16S>(Cur.t[q], xl + tp * AFF_TILE_K + 8 * kg,
+                                                        xsl + (4 * tp + kg) * GPT, acc, kc);
                 }
                 if (!nvalid || ni != ci) {  // the wave's last batch of this rowblock
-                    acc = ag_reduce_kslices(acc);
+                    if constexpr (!ag_inplace(BITS)) acc = ag_reduce_kslices(acc);
                     if (lane < 16) part[(ci * AG_WAVES + wave) * 16 + lane] += acc;
                     acc = 0.f;
                 }

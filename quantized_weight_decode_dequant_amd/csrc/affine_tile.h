@@ -83,16 +83,16 @@ __device__ __forceinline__ AgConsts ag_consts() {
     return AgConsts{ag_opaque(AG_MAGIC), ag_opaque(m0), PL::NP == 2 ? ag_opaque(m1) : 0u};
 }
 
-// (a & m) | c as one v_and_or_b32, written out for the first and-or of the
-// two-plane merge: with both in plain code the compiler regroups them into
-// two ands and an or3.  Only this inner one is inline asm.  The compiler does
-// not count an asm instruction as a VALU write in its hazard checks, and an
-// MFMA that reads a VGPR fewer than 2 wait states after a VALU wrote it reads
-// the old value; so the value an MFMA takes comes from the outer and-or,
-// which the compiler emits and pads itself.
+// (a & m) | c, kept whole: the result passes through an empty asm statement
+// (no instruction), so the compiler cannot regroup it with the and-or it
+// feeds (two and-ors would become two ands and an or3).  No instruction of
+// these kernels is written in asm: the compiler does not count an asm
+// instruction in its hazard checks, and an asm VALU write next to an MFMA
+// (to a VGPR the MFMA reads within 2 wait states, or to one it has yet to
+// write) corrupts the product.
 __device__ __forceinline__ unsigned ag_and_or(unsigned a, unsigned m, unsigned c) {
-    unsigned r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+    unsigned r = (a & m) | c;
+    asm("" : "+v"(r));
     return r;
 }
 

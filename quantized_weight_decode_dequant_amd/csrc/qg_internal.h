@@ -366,17 +366,18 @@ __device__ __forceinline__ void st_global_nt(void *base, size_t i, T v) {
 // The two constants of the nibble unpack, held in VGPRs.  gfx9 VOP3
 // instructions read at most one SGPR or literal, so with both operands in
 // registers (a & mask) | magic selects to a single v_and_or_b32.  They are
-// materialized once through an opaque move so the compiler does not
-// re-materialize them at every use.
+// moved into VGPRs once and made opaque by an empty asm statement (no
+// instruction), so the compiler does not re-materialize them as literals at
+// every use.
 struct Q4Consts {
     unsigned mask;   // 0x000F000F
     unsigned magic;  // bf16 128.0 twice
 };
 
 __device__ __forceinline__ Q4Consts q4_consts() {
-    Q4Consts k;
-    asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(k.mask));
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.magic));
+    Q4Consts k{0x000F000Fu, 0x43004300u};
+    asm volatile("" : "+v"(k.mask));
+    asm volatile("" : "+v"(k.magic));
     return k;
 }
 

@@ -1,13 +1,18 @@
-"""The built gfx950 code keeps every MFMA at least 2 wait states behind the
-VALU instruction that wrote one of its source VGPRs.
+"""The built gfx950 code keeps its VALU writes clear of the MFMAs around them.
 
-An MFMA that reads a VGPR fewer than 2 wait states after a VALU wrote it reads
-the old value.  The compiler pads its own VALU writes (to exactly 2 where it
-has to), but it does not count an inline-asm instruction as a VALU write, so
-an asm-written MFMA operand can end up one instruction ahead of its reader and
-give wrong sums without any error.  This test disassembles the library built
-here (its device code objects, extracted from the host library's fat binary)
-and checks every MFMA; the scanner itself is checked on planted snippets."""
+Two rules, both of which the compiler keeps for its own instructions but not
+for an instruction written in inline asm, which its hazard checks do not see
+as a VALU write:
+  - an MFMA that reads a VGPR fewer than 2 wait states after a VALU wrote it
+    reads the old value;
+  - a VALU write to a VGPR that an MFMA issued before it has yet to write (a
+    16x16 MFMA writes its result 8 passes after issue) is overwritten by the
+    MFMA's result.
+Either gives wrong sums without any error.  This test disassembles the
+library built here (its device code objects, extracted from the host
+library's fat binary) and checks every MFMA against both rules; the scanners
+are checked on planted snippets; and the kernel sources hold no asm statement
+with an instruction in it (only empty ones, which make a value opaque)."""
 import os
 import re
 import struct
@@ -22,6 +27,19 @@ LIB = os.path.join(ROOT, "quantized_weight_decode_dequant_amd", "libqgemv.so")
 LLVM = "/opt/rocm/llvm/bin"
 BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 MIN_WAIT_STATES = 2
+CSRC = os.path.join(ROOT, "quantized_weight_decode_dequant_amd", "csrc")
+
+
+def mfma_result_passes(opcode):
+    """Wait states before a VALU may write a destination VGPR of the MFMA
+    (its passes): 8 for the 16x16 shapes, 16 for 32x32, 2 for 4x4."""
+    if "_32x32x" in opcode:
+        return 16
+    if "_16x16x" in opcode:
+        return 8
+    if "_4x4x" in opcode:
+        return 2
+    return 16
 
 
 def _vgprs(operand_text):
@@ -60,6 +78,35 @@ def mfma_hazards(lines, min_wait=MIN_WAIT_STATES):
                     break
             waits += 1
             k -= 1
+    return found
+
+
+def mfma_result_hazards(lines):
+    """(wait states, writer, mfma) for every non-MFMA VALU write of a VGPR
+    that an earlier MFMA writes, before that MFMA's passes have elapsed."""
+    found = []
+    for j, ins in enumerate(lines):
+        if not ins or not ins.startswith("v_mfma"):
+            continue
+        need = mfma_result_passes(ins.split()[0])
+        dst = _vgprs(ins.split(None, 1)[1].split(",")[0])
+        waits, k = 0, j + 1
+        while k < len(lines) and waits < need:
+            nxt = lines[k]
+            if nxt is None or nxt.startswith(("s_cbranch", "s_branch", "s_setpc")):
+                break
+            if nxt.startswith("s_nop"):
+                waits += int(nxt.split()[1], 0) + 1
+                k += 1
+                continue
+            if nxt.startswith("v_"):
+                parts = nxt.split(None, 1)
+                if len(parts) > 1 and _vgprs(parts[1].split(",")[0]) & dst:
+                    if not nxt.startswith("v_mfma"):
+                        found.append((waits, nxt, ins))
+                    break
+            waits += 1
+            k += 1
     return found
 
 
@@ -114,6 +161,39 @@ def test_scanner_flags_planted_hazards():
     assert not mfma_hazards(["v_and_or_b32 v9, v1, v2, v3", None, mfma])
 
 
+def test_scanner_flags_planted_result_overwrites():
+    """A VALU write to the destination of an MFMA issued 0..7 wait states
+    before is flagged; after 8 wait states, to another register, or when a
+    later MFMA writes the register first, it is not."""
+    mfma = "v_mfma_f32_16x16x32_bf16 v[4:7], v[8:11], v[12:15], 0"
+    fill = ["v_mov_b32 v40, 0"] * 7
+    assert len(mfma_result_hazards([mfma, "v_and_or_b32 v5, v1, v2, v3"])) == 1
+    assert len(mfma_result_hazards([mfma] + fill + ["v_and_or_b32 v7, v1, v2, v3"])) == 1
+    assert not mfma_result_hazards([mfma] + fill + ["v_mov_b32 v41, 0", "v_and_or_b32 v7, v1, v2, v3"])
+    assert not mfma_result_hazards([mfma, "s_nop 7", "v_and_or_b32 v5, v1, v2, v3"])
+    assert not mfma_result_hazards([mfma, "v_and_or_b32 v20, v1, v2, v3"])
+    assert not mfma_result_hazards([mfma, "v_mfma_f32_16x16x32_bf16 v[4:7], v[8:11], v[12:15], 0",
+                                    "s_nop 7", "v_and_or_b32 v5, v1, v2, v3"])
+
+
+def test_kernel_sources_have_no_asm_instructions():
+    """Every asm statement in the kernel sources is empty (it only makes a
+    value opaque to the optimizer); no instruction is written in asm."""
+    found = []
+    for name in sorted(os.listdir(CSRC)):
+        if not name.endswith((".hip", ".h")):
+            continue
+        with open(os.path.join(CSRC, name)) as f:
+            for no, line in enumerate(f, 1):
+                code = line.split("//")[0]
+                for m in re.finditer(r"\basm\b\s*(?:volatile\s*)?\(\s*\"([^\"]*)\"", code):
+                    if m.group(1).strip():
+                        found.append("%s:%d: %s" % (name, no, line.strip()))
+                if re.search(r"\basm\b", code) and not re.search(r"\basm\b\s*(?:volatile\s*)?\(\s*\"", code):
+                    found.append("%s:%d: %s" % (name, no, line.strip()))
+    assert not found, "asm with instructions: %s" % found
+
+
 def test_built_library_has_no_valu_to_mfma_hazard():
     if not os.path.exists(LIB):
         pytest.skip("libqgemv.so is not built")
@@ -122,7 +202,7 @@ def test_built_library_has_no_valu_to_mfma_hazard():
             pytest.skip(tool + " not available")
     objs = _code_objects(LIB)
     assert objs, "no gfx950 code object in the library"
-    mfmas, bad = 0, []
+    mfmas, bad, overwritten = 0, [], []
     with tempfile.TemporaryDirectory() as d:
         for i, obj in enumerate(objs):
             path = os.path.join(d, "co%d.o" % i)
@@ -133,6 +213,9 @@ def test_built_library_has_no_valu_to_mfma_hazard():
             lines = _instruction_lines(out)
             mfmas += sum(1 for t in lines if t and t.startswith("v_mfma"))
             bad += mfma_hazards(lines)
+            overwritten += mfma_result_hazards(lines)
     assert mfmas > 1000, "expected the MFMA kernels in the library (%d MFMAs found)" % mfmas
     assert not bad, "%d MFMAs read a VGPR written < %d wait states before, e.g. %s" % (
         len(bad), MIN_WAIT_STATES, bad[:3])
+    assert not overwritten, "%d VALU writes land in an MFMA's result before it is written, e.g. %s" % (
+        len(overwritten), overwritten[:3])
