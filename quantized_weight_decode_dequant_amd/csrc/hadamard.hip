@@ -17,12 +17,14 @@
 // is exact for activations of ordinary range, so the quantization decision
 // sees the exact z.  A row of up to 24576 elements is loaded once, with every
 // load issued up front, and its z kept in registers; the row maximum amax =
-// max |z| is reduced through LDS.  Each code is round-half-even(z * 127 /
-// amax) of the correctly rounded fp64 quotient: it is taken from the product
-// with 1 / amax unless that product lies within 1e-9 of a rounding boundary
-// (its error is below 1e-13), in which case the quotient is computed by a
-// true division.  Longer rows are processed in rounds of 24576 and
-// recomputed from x for the second pass.
+// max |z| is reduced within each wave by DPP moves and across the waves
+// through LDS.  Each code is round-half-even(z * 127 / amax) of the
+// correctly rounded fp64 quotient: it is taken from the product with
+// 1 / amax unless that product lies within 1e-9 of a rounding boundary (its
+// error is below 1e-13), in which case the quotient is computed by a true
+// division (a branch taken only by waves with such an element).  Longer
+// rows are processed in rounds of 24576 and recomputed from x for the
+// second pass.
 #include "qg_internal.h"
 
 namespace qg {
@@ -39,6 +41,35 @@ __device__ __forceinline__ double quad_xor(double v) {
     const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, ctrl, 0xF, 0xF, false);
     const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), ctrl, 0xF, 0xF, false);
     return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// v moved across lanes by the DPP control ctrl (both 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// The largest v of the wave, in every lane: within each row of 16 lanes by
+// DPP moves (quad exchanges, then rotations by 4 and 8), then the four row
+// maxima read from lanes 0, 16, 32 and 48.  VALU work only, no trip through
+// the LDS crossbar per step.
+__device__ __forceinline__ double wave_max(double v) {
+    v = fmax(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmax(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmax(v, dpp64<0x124>(v));  // row_ror:4
+    v = fmax(v, dpp64<0x128>(v));  // row_ror:8
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    double r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, 16 * i);
+        const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), 16 * i);
+        r[i] = __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+    }
+    return fmax(fmax(r[0], r[1]), fmax(r[2], r[3]));
 }
 
 // The five butterfly stages over this lane's 8 elements (part p of the block).
@@ -126,8 +157,7 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
             for (int e = 0; e < 8; ++e) amax = fmax(amax, fabs(z[i][e]));
     }
     // row maximum: wave, then across waves
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) amax = fmax(amax, __shfl_xor(amax, s));
+    amax = wave_max(amax);
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
     amax = 0.0;
@@ -145,14 +175,29 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
             const int u = (r * HQ_R + i) * HQ_WAVES + wave;
             const int b = 16 * u + (lane >> 2);
             if (u >= nunit) break;  // uniform
+            // codes from the product with 1 / amax; only when some lane of the
+            // wave meets a product within 1e-9 of a rounding boundary do the
+            // flagged elements take the true quotient (one uniform branch)
+            double q[8];
+            bool near = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double p = z[i][e] * 127.0 * rinv;
+                q[e] = rint(p);
+                near = near || fabs(fabs(p - q[e]) - 0.5) < 1e-9;
+            }
+            if (__any(near)) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double t = z[i][e] * 127.0;
+                    if (fabs(fabs(t * rinv - q[e]) - 0.5) < 1e-9) q[e] = rint(t / amax);
+                }
+            }
             unsigned packed[2] = {0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const double t = z[i][e] * 127.0;
-                double q = rint(t * rinv);
-                if (fabs(fabs(t * rinv - q) - 0.5) < 1e-9) q = rint(t / amax);
-                q = fmin(fmax(q, -127.0), 127.0);
-                packed[e >> 2] |= ((unsigned)(int)q & 0xFFu) << (8 * (e & 3));
+                const double c = fmin(fmax(q[e], -127.0), 127.0);
+                packed[e >> 2] |= ((unsigned)(int)c & 0xFFu) << (8 * (e & 3));
             }
             if (b < nblk)
                 *reinterpret_cast<u32x2_t *>(qr + 32 * b + 8 * (lane & 3)) =
