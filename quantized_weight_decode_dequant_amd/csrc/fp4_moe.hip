@@ -11,7 +11,8 @@
 //
 // MoE, three launches on one stream, the expert ids never leave the device:
 //   A  unit = (slot s, rowblock of F): the g and u rows of expert ids[s]
-//      against x (bf16 in LDS), h = silu(g) * u in fp32 -> workspace h[s][F].
+//      against x (bf16 in LDS, multiply-adds on the bf16 MFMA), h = silu(g)
+//      * u in fp32 -> workspace h[s][F].
 //   B  unit = (slot s, rowblock of H): Wdown[ids[s]] rows against h[s]
 //      (fp32 in LDS) -> workspace part[s][H].
 //   C  y[n] = sum_s w[s] * part[s][n] in slot order (deterministic, no
@@ -47,6 +48,36 @@ __device__ __forceinline__ float fp4_tile_dot_bf16(u32x4_t c0, u32x4_t c1, unsig
         }
     }
     return acc;
+}
+
+// One 256-k tile of 16 rows against bf16 x on the MFMA, for a single token:
+// the decoded weights are the B operand exactly as loaded (lane l: row l & 15,
+// k-slice l >> 4; its dword i of half j is the k-group of 8 at 128j + 32(l >>
+// 4) + 8i), and every row of the A operand is x (each lane reads the 8
+// values of x that match its own k-group, as the lanes of one k-slice share
+// them, one broadcast LDS read).  The k-groups of the four slices fill the
+// MFMA's 32 k in a fixed order, the same for both operands, so every element
+// of C holds the dot product of row n = lane & 15 (the 16 rows of C are the
+// same sum); the caller takes C[0] of lanes 0..15.  Per tile: 32 conversions
+// and 8 MFMAs instead of 32 conversions and 32 two-element dot products.
+__device__ __forceinline__ f32x4_t fp4_tile_mfma_bf16(u32x4_t c0, u32x4_t c1, unsigned e0,
+                                                      unsigned e1, const uint4 *xp, f32x4_t C) {
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh) {
+        const u32x4_t c = jh ? c1 : c0;
+        const float sc = e8m0_as_f32(jh ? e1 : e0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4_t w = {fp4_pair_bf16<0>(c[i], sc), fp4_pair_bf16<1>(c[i], sc),
+                               fp4_pair_bf16<2>(c[i], sc), fp4_pair_bf16<3>(c[i], sc)};
+            const uint4 xv = xp[16 * jh + i];
+            const u32x4_t xa = {xv.x, xv.y, xv.z, xv.w};
+            C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
+                                                        __builtin_bit_cast(bf16x8_t, w), C, 0,
+                                                        0, 0);
+        }
+    }
+    return C;
 }
 
 // Dot of one 256-k tile with fp32 activations in LDS (the SwiGLU output).
@@ -225,7 +256,7 @@ moe_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__ p
         int t = (wave - (ub & 3) * (nbu & 3)) & 3;  // absolute batch index = wave mod 4
         MsCursor ca = {t / nbu, t % nbu};
         Fp4Batch A, B;
-        float acc = 0.f;
+        f32x4_t C = {0.f, 0.f, 0.f, 0.f};
         {
             // the first batch loads while x is staged and the sums cleared
             const __amdgpu_buffer_rsrc_t rs =
@@ -254,17 +285,16 @@ moe_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__ p
                     __builtin_amdgcn_sched_barrier(0);
                     fp4_tile_load(Nxt, q, rs, tbn + q, PH, lane);
                     __builtin_amdgcn_sched_barrier(0);
-                    acc = fp4_tile_dot_bf16(Cur.c0[q], Cur.c1[q], Cur.e0[q], Cur.e1[q],
-                                            xl + 32 * (tbc + q) + 4 * kg, acc);
+                    C = fp4_tile_mfma_bf16(Cur.c0[q], Cur.c1[q], Cur.e0[q], Cur.e1[q],
+                                           xl + 32 * (tbc + q) + 4 * kg, C);
                 }
                 // flush at the wave's last batch of this unit's gate or up rows
                 const bool gate = ca.b < nb;
                 const bool last = !nvalid || cn.i != ca.i || (gate && cn.b >= nb);
                 if (last) {
-                    acc = reduce_kslices(acc);
                     if (lane < 16)
-                        part[((ca.i * MS_WAVES + wave) * 2 + (gate ? 0 : 1)) * 16 + lane] += acc;
-                    acc = 0.f;
+                        part[((ca.i * MS_WAVES + wave) * 2 + (gate ? 0 : 1)) * 16 + lane] += C[0];
+                    C = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
                 t += MS_WAVES;
                 ca = cn;
