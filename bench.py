@@ -64,7 +64,7 @@ def traffic_from_profiles(kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-STEP_KERNEL = "q4_gemv_kernel<true, 1, 4>"
+STEP_KERNEL = "q4_gemv_kernel<true, 1, 8>"
 COPY_BYTES = 1 << 30
 PLAIN_READ_BYTES = 4 << 30   # larger than every cache level
 
@@ -851,7 +851,7 @@ def main():
     rd.fill_(1)
     sink = torch.empty(65536, dtype=torch.int32, device=dev)
     plain_best, plain_grid = 0.0, 0
-    for per_cu in (2, 4, 8):
+    for per_cu in (2, 4, 8, 16):
         grid = props.multi_processor_count * per_cu
         pkg.qg_plain_read(rd, sink, grid)
         torch.cuda.synchronize()

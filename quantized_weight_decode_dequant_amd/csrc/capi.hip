@@ -515,7 +515,7 @@ int qg_batch_plan_build(int fmt, int64_t M, int32_t count, const qg_gemv_desc *d
         }
         const int per_cu = aff.bits ? (M == 1 ? affine_gemv_wgs_per_cu() : affine_skinny_wgs_per_cu())
                            : q8row                    ? q8row_gemv_wgs_per_cu()
-                           : kernel == QG_KERNEL_VALU ? q4_gemv_wgs_per_cu(M)
+                           : kernel == QG_KERNEL_VALU ? q4_gemv_list_wgs_per_cu(M)
                                                       : q4_skinny_stream_wgs_per_cu();
         int64_t grid = (int64_t)cus * per_cu;
         if (grid > WL_GRID_MAX) grid = WL_GRID_MAX;

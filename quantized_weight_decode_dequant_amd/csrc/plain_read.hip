@@ -4,18 +4,21 @@
 // a known ceiling", and the Uzu page, section "Why batch-one decoding is
 // memory-bound", both rate a decode against bandwidth divided by bytes).
 //
-// Workgroup j reads the contiguous 16-byte slots [j*n/G, (j+1)*n/G) with
-// non-temporal 16-byte loads, 8 slots in flight per lane (each wave step
-// covers 8 consecutive 1 KB slabs), XORs every word it read and writes the
-// result to sink[j], so no load can be dropped.  On MI355X this layout (a
-// contiguous chunk per workgroup, non-temporal) read fastest of the grid-
-// stride and regular-load variants tried.
+// Workgroup j (8 waves) reads the contiguous 16-byte slots [j*n/G,
+// (j+1)*n/G) with non-temporal 16-byte loads, 8 slots in flight per lane
+// (each wave step covers 8 consecutive 1 KB slabs, a workgroup step 64 KB),
+// XORs every word it read and writes the result to sink[j], so no load can be
+// dropped.  On MI355X this layout (a contiguous chunk per workgroup,
+// non-temporal) read fastest of the grid-stride and regular-load variants
+// tried, and 8-wave workgroups 1-2% faster than 4- or 12-wave ones (4 GiB:
+// 7.13-7.26 TB/s against 6.99-7.14; 4 or 16 slots in flight per lane, or
+// loads without the non-temporal hint, are slower).
 #include "qg_internal.h"
 
 namespace qg {
 
 constexpr int PR_U = 8;
-constexpr int PR_THREADS = 256;
+constexpr int PR_THREADS = 512;
 
 __global__ void __launch_bounds__(PR_THREADS)
 plain_read_kernel(const u32x4_t *__restrict__ p, size_t n16, uint32_t *__restrict__ sink) {

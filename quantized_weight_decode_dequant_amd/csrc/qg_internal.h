@@ -136,7 +136,8 @@ hipError_t launch_pack_fp4(const uint8_t *codes, const uint8_t *scales,
 hipError_t launch_q4_gemv(const uint8_t *packed, const uint16_t *x, void *y, int64_t M,
                           int64_t N, int64_t K, bool out_f32, int cus, hipStream_t s);
 size_t q4_gemv_lds_bytes(int64_t M);
-int q4_gemv_wgs_per_cu(int64_t M);
+int q4_gemv_wgs_per_cu(int64_t M);       // single matrices
+int q4_gemv_list_wgs_per_cu(int64_t M);  // the work list
 int q4_gemv_rows_max();
 hipError_t launch_q4_gemv_list(const WorkItem *items, const WorkStart *starts,
                                int grid, int64_t M, hipStream_t s);
