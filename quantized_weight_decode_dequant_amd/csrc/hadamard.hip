@@ -19,10 +19,11 @@
 // load issued up front, and its z kept in registers; the row maximum amax =
 // max |z| is reduced within each wave by DPP moves and across the waves
 // through LDS.  Each code is round-half-even(z * 127 / amax) of the
-// correctly rounded fp64 quotient: it is taken from the product with
-// 1 / amax unless that product lies within 1e-9 of a rounding boundary (its
+// correctly rounded fp64 quotient: it is taken from the product z * (127 /
+// amax) unless that product lies within 1e-9 of a rounding boundary (its
 // error is below 1e-13), in which case the quotient is computed by a true
-// division (a branch taken only by waves with such an element).  Longer
+// division (a branch taken only by waves with such an element).  Since |z|
+// <= amax, both give codes within [-127, 127]: no clamp is needed.  Longer
 // rows are processed in rounds of 24576 and recomputed from x for the
 // second pass.
 #include "qg_internal.h"
@@ -163,7 +164,8 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
     amax = 0.0;
 #pragma unroll
     for (int w = 0; w < HQ_WAVES; ++w) amax = fmax(amax, wmax[w]);
-    const double rinv = amax > 0.0 ? 1.0 / amax : 0.0;
+    // amax is 0 or at least the smallest bf16 magnitude (2^-133), so s is finite
+    const double s = amax > 0.0 ? 127.0 / amax : 0.0;
 
     int8_t *qr = Xq + (size_t)m * K;
 #pragma unroll 1
@@ -175,30 +177,28 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
             const int u = (r * HQ_R + i) * HQ_WAVES + wave;
             const int b = 16 * u + (lane >> 2);
             if (u >= nunit) break;  // uniform
-            // codes from the product with 1 / amax; only when some lane of the
-            // wave meets a product within 1e-9 of a rounding boundary do the
-            // flagged elements take the true quotient (one uniform branch)
+            // codes from the product with 127 / amax; only when some lane of
+            // the wave meets a product within 1e-9 of a rounding boundary do
+            // the flagged elements take the true quotient (one uniform branch)
             double q[8];
             bool near = false;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const double p = z[i][e] * 127.0 * rinv;
+                const double p = z[i][e] * s;
                 q[e] = rint(p);
-                near = near || fabs(fabs(p - q[e]) - 0.5) < 1e-9;
+                near = near || fabs(p - q[e]) > 0.5 - 1e-9;
             }
             if (__any(near)) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const double t = z[i][e] * 127.0;
-                    if (fabs(fabs(t * rinv - q[e]) - 0.5) < 1e-9) q[e] = rint(t / amax);
+                    const double p = z[i][e] * s;
+                    if (fabs(p - rint(p)) > 0.5 - 1e-9) q[e] = rint(z[i][e] * 127.0 / amax);
                 }
             }
             unsigned packed[2] = {0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const double c = fmin(fmax(q[e], -127.0), 127.0);
-                packed[e >> 2] |= ((unsigned)(int)c & 0xFFu) << (8 * (e & 3));
-            }
+            for (int e = 0; e < 8; ++e)
+                packed[e >> 2] |= ((unsigned)(int)q[e] & 0xFFu) << (8 * (e & 3));
             if (b < nblk)
                 *reinterpret_cast<u32x2_t *>(qr + 32 * b + 8 * (lane & 3)) =
                     u32x2_t{packed[0], packed[1]};
