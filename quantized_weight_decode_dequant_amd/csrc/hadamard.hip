@@ -84,16 +84,13 @@ __device__ __forceinline__ void fwht32_oct(double z[8], int p) {
                 z[e] = a + c;
                 z[e + s] = a - c;
             }
+    // the upper index of a pair takes o - z, the lower z + o: one fma with
+    // z * (-1 or +1) + o, rounded once like the add or subtract it replaces
+    const double sg1 = (p & 1) ? -1.0 : 1.0, sg2 = (p & 2) ? -1.0 : 1.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const double o = quad_xor<1>(z[e]);
-        z[e] = (p & 1) ? (o - z[e]) : (z[e] + o);
-    }
+    for (int e = 0; e < 8; ++e) z[e] = fma(z[e], sg1, quad_xor<1>(z[e]));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const double o = quad_xor<2>(z[e]);
-        z[e] = (p & 2) ? (o - z[e]) : (z[e] + o);
-    }
+    for (int e = 0; e < 8; ++e) z[e] = fma(z[e], sg2, quad_xor<2>(z[e]));
 }
 
 // Load and transform this wave's units of one round.  Unit u covers blocks
