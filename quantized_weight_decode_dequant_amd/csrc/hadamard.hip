@@ -6,7 +6,8 @@
 // quantized to 8 bits on the fly so verification runs on the int8 matrix
 // path).
 //
-// One workgroup of 1024 threads per activation row.  Four lanes own one
+// One workgroup per activation row: 8 waves for rows of up to 12288 (one
+// round, three 16-block units per wave), 16 for longer ones.  Four lanes own one
 // block of 32: lane part p holds elements 8p .. 8p + 7, so the first three
 // butterfly stages (index bits 0, 1, 2) are register adds and subtracts and
 // the last two (bits 3, 4) exchange with the lanes p ^ 1 and p ^ 2 of the
@@ -30,9 +31,7 @@
 
 namespace qg {
 
-constexpr int HQ_THREADS = 1024;
-constexpr int HQ_WAVES = HQ_THREADS / 64;
-constexpr int HQ_R = 3;  // 16-block units per wave per round (24576 k per round)
+constexpr int HQ_R = 3;  // 16-block units per wave per round (512 k each)
 
 // Exchange with the lane p ^ S of the quad (S = 1 or 2), by DPP quad_perm.
 template <int S>
@@ -96,6 +95,7 @@ __device__ __forceinline__ void fwht32_oct(double z[8], int p) {
 // Load and transform this wave's units of one round.  Unit u covers blocks
 // 16u .. 16u + 15, lane l takes block 16u + (l >> 2), part l & 3.  Buffer
 // loads past the row read as zero.
+template <int HQ_WAVES>
 __device__ __forceinline__ void hq_round(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsg,
                                          int nunit, int round, int wave, int lane,
                                          double z[HQ_R][8]) {
@@ -132,7 +132,8 @@ __device__ __forceinline__ void hq_round(__amdgpu_buffer_rsrc_t rx, __amdgpu_buf
     }
 }
 
-__global__ void __launch_bounds__(HQ_THREADS)
+template <int HQ_WAVES>
+__global__ void __launch_bounds__(HQ_WAVES * 64)
 had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ signs, int K,
                    int8_t *__restrict__ Xq, float *__restrict__ x_scales, double denom) {
     __shared__ double wmax[HQ_WAVES];
@@ -148,7 +149,7 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
     double amax = 0.0;
 #pragma unroll 1
     for (int r = 0; r < nround; ++r) {
-        hq_round(rx, rsg, nunit, r, wave, lane, z);
+        hq_round<HQ_WAVES>(rx, rsg, nunit, r, wave, lane, z);
 #pragma unroll
         for (int i = 0; i < HQ_R; ++i)
 #pragma unroll
@@ -168,7 +169,7 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
 #pragma unroll 1
     for (int r = nround - 1; r >= 0; --r) {
         // the last round is still in registers
-        if (r != nround - 1) hq_round(rx, rsg, nunit, r, wave, lane, z);
+        if (r != nround - 1) hq_round<HQ_WAVES>(rx, rsg, nunit, r, wave, lane, z);
 #pragma unroll
         for (int i = 0; i < HQ_R; ++i) {
             const int u = (r * HQ_R + i) * HQ_WAVES + wave;
@@ -206,8 +207,16 @@ had32_quant_kernel(const uint16_t *__restrict__ X, const int8_t *__restrict__ si
 
 hipError_t launch_had32_quant(const uint16_t *X, const int8_t *signs, int64_t M, int64_t K,
                               int8_t *Xq, float *x_scales, double denom, hipStream_t s) {
-    hipLaunchKernelGGL(had32_quant_kernel, dim3((unsigned)M), dim3(HQ_THREADS), 0, s, X, signs,
-                       (int)K, Xq, x_scales, denom);
+    // 8 waves take a row of up to 8 * HQ_R units (12288 k) in one round and
+    // ran 16 x 4096 in 3.23 us and 16 x 12288 in 4.68 us against 3.93 and
+    // 4.95 with 16 waves (4 waves: 3.27 / 6.11, 12: 3.39 / 4.75); longer rows
+    // take 16 waves, so that 24576 k is still one round
+    if (K <= 8 * HQ_R * 512)
+        hipLaunchKernelGGL((had32_quant_kernel<8>), dim3((unsigned)M), dim3(8 * 64), 0, s, X,
+                           signs, (int)K, Xq, x_scales, denom);
+    else
+        hipLaunchKernelGGL((had32_quant_kernel<16>), dim3((unsigned)M), dim3(16 * 64), 0, s, X,
+                           signs, (int)K, Xq, x_scales, denom);
     return hipGetLastError();
 }
 
