@@ -102,8 +102,8 @@ def test_batch_graph_replay():
 
 def test_batch_decode_step_full():
     """The whole synthetic decode step (253 GEMVs, 4.26 GB) in one launch:
-    every output bitwise equal to qgemv_run's, and sampled rows of several
-    projections against the oracle."""
+    every output bitwise equal to qgemv_run's, and sampled rows of every
+    projection kind against the oracle."""
     note("batch decode step full")
     step = workloads.build_decode_step(0)
     plan = pkg.qg_batch_plan_build(Q4, 1, [(g.packed, g.N, g.K, g.x, g.y) for g in step.gemvs])
@@ -115,7 +115,9 @@ def test_batch_decode_step_full():
     for g, b in zip(step.gemvs, got):
         assert_same(b, g.y, "grouped vs qgemv_run " + g.name)
     rng = np.random.default_rng(96)
-    for idx in (0, 1, 4, 6, 250, 252):
+    # every projection kind of the first layer (q, k, v, o, gate, up, down),
+    # one of the last layer and the lm_head
+    for idx in (0, 1, 2, 3, 4, 5, 6, 250, 252):
         item, name, N, K = synth.decode_step_shapes()[idx]
         m = synth.q4_matrix(0, N, K, item=item)
         x = synth.activations(0, 1, K, item=item)
@@ -138,7 +140,7 @@ def test_batch_verification_pass_full(M, kernel):
     pkg.qg_batch_run(plan)
     torch.cuda.synchronize()
     rng = np.random.default_rng(97)
-    for idx in (0, 1, 4, 6, 251, 252):
+    for idx in (0, 1, 2, 3, 4, 5, 6, 251, 252):
         item, name, N, K = synth.decode_step_shapes()[idx]
         m = synth.q4_matrix(0, N, K, item=item)
         X = synth.activations(1, M, K, item=item)
