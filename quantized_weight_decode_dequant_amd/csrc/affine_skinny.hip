@@ -56,18 +56,35 @@ struct AsBatch {
 
 // Stage tiles [0, nt) of segment seg of X (rows past M and k past K zero) and
 // the sum of each row over each group: xs[gi * MP + m].
+constexpr int AS_SU = 8;  // staging chunks per thread in flight
+
 template <int MT>
 __device__ __forceinline__ void as_stage(const uint16_t *X, int M, int K, int seg, int nt,
                                          int group, uint16_t *xl, float *xs, int tid) {
     typedef AsCfg<MT> C;
     const int k0 = seg * C::SEGK * AFF_TILE_K;
     const int per_row = nt * (AFF_TILE_K / 8);  // 16-byte chunks per row
-    for (int i = tid; i < C::MP * per_row; i += C::THREADS) {
-        const int m = i / per_row, c8 = i - m * per_row;
-        const int k = k0 + 8 * c8;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (m < M && k < K) v = ld_global(reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k));
-        *reinterpret_cast<u32x4_t *>(xl + m * C::RS + 8 * c8) = v;
+    const int total = C::MP * per_row;
+    // each thread issues the loads of AS_SU chunks before it writes any of
+    // them; buffer loads, so a chunk past the rows or past K reads zero
+    const unsigned xbytes = (unsigned)M * (unsigned)K * 2u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, xbytes);
+    for (int i0 = tid; i0 < total; i0 += AS_SU * C::THREADS) {
+        u32x4_t v[AS_SU];
+#pragma unroll
+        for (int u = 0; u < AS_SU; ++u) {
+            const int i = i0 + u * C::THREADS, m = i / per_row, c8 = i - m * per_row;
+            const int k = k0 + 8 * c8;
+            const unsigned off =
+                (m < M && k < K) ? 2u * ((unsigned)m * (unsigned)K + (unsigned)k) : xbytes;
+            v[u] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < AS_SU; ++u) {
+            const int i = i0 + u * C::THREADS, m = i / per_row, c8 = i - m * per_row;
+            if (i < total) *reinterpret_cast<u32x4_t *>(xl + m * C::RS + 8 * c8) = v[u];
+        }
     }
     __syncthreads();
     const int ng = nt * (AFF_TILE_K / group);

@@ -123,15 +123,35 @@ __device__ __forceinline__ Fp4Slot fp4_load(const uint8_t *tb, int lane) {
     return r;
 }
 
+// Fill n 16-byte chunks of LDS, chunk i taken from src(i) (a global load, or
+// zero).  Each thread issues the loads of U chunks before it writes any of
+// them, so a fill costs about n / (U * nthreads) memory round trips rather
+// than one per chunk.
+template <int U, typename Src>
+__device__ __forceinline__ void lds_fill16(uint4 *dst, int n, int tid, int nthreads, Src src) {
+    for (int i0 = tid; i0 < n; i0 += U * nthreads) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * nthreads;
+            v[u] = i < n ? src(i) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * nthreads;
+            if (i < n) dst[i] = v[u];
+        }
+    }
+}
+
 // Stage bf16 x [K] into LDS as P*256 elements, zero past K.
 __device__ __forceinline__ void stage_x_bf16(uint4 *xl, const uint16_t *x, int K, int P,
                                              int tid, int nthreads) {
     const int nx4 = K / 8;
-    for (int i = tid; i < P * 32; i += nthreads) {
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (i < nx4) v = reinterpret_cast<const uint4 *>(x)[i];
-        xl[i] = v;
-    }
+    const uint4 *src = reinterpret_cast<const uint4 *>(x);
+    lds_fill16<4>(xl, P * 32, tid, nthreads, [=](int i) {
+        return i < nx4 ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    });
 }
 
 // Sum of this wave's lanes for each of the 16 rows (k-slices kg = lane >> 4).
@@ -354,9 +374,10 @@ moe_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws,
         }
         __syncthreads();  // the previous block is written out
         {
-            const float4 *src = reinterpret_cast<const float4 *>(h_ws + (size_t)s * F);
-            for (int i = tid; i < nb * MS_TPB * 64; i += MS_THREADS)
-                hl[i] = (i < F / 4) ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const uint4 *src = reinterpret_cast<const uint4 *>(h_ws + (size_t)s * F);
+            const int nh4 = F / 4;
+            lds_fill16<4>(reinterpret_cast<uint4 *>(hl), nb * MS_TPB * 64, tid, MS_THREADS,
+                          [=](int i) { return i < nh4 ? src[i] : make_uint4(0u, 0u, 0u, 0u); });
             for (int i = tid; i < nr * MS_WAVES * 16; i += MS_THREADS) part[i] = 0.f;
         }
         __syncthreads();
@@ -456,10 +477,14 @@ moe_down_fused_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ 
         const int e = ids[i];
         wl[i] = (e >= 0 && e < E) ? w[i] : 0.f;  // an invalid id contributes nothing
     }
-    for (int i = tid; i < top_k * hstride; i += MF_THREADS) {
-        const int s = i / hstride, c = i - s * hstride;
-        hl[i] = (c < F / 4) ? reinterpret_cast<const float4 *>(h_ws + (size_t)s * F)[c]
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(h_ws);
+        const int nh4 = F / 4;
+        lds_fill16<8>(reinterpret_cast<uint4 *>(hl), top_k * hstride, tid, MF_THREADS,
+                      [=](int i) {
+                          const int s = i / hstride, c = i - s * hstride;
+                          return c < nh4 ? src[(size_t)s * nh4 + c] : make_uint4(0u, 0u, 0u, 0u);
+                      });
     }
     __syncthreads();
 #pragma unroll 1

@@ -232,6 +232,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mt_rsrc(const uint8_t *mat, in
 struct MtPairs {
     int p[MOE_GROUP_ROWS_MAX];
 };
+// Entry r (0 <= r < MOE_GROUP_ROWS_MAX; r may differ between lanes), chosen
+// by selects among the wave-uniform entries (taken through readfirstlane so
+// that the choice stays in registers rather than becoming an indexed load
+// from a private array).
+static_assert(MOE_GROUP_ROWS_MAX == 4, "mt_pair selects among 4 entries");
+__device__ __forceinline__ int mt_pair(const MtPairs &pp, int r) {
+    const int p0 = __builtin_amdgcn_readfirstlane(pp.p[0]);
+    const int p1 = __builtin_amdgcn_readfirstlane(pp.p[1]);
+    const int p2 = __builtin_amdgcn_readfirstlane(pp.p[2]);
+    const int p3 = __builtin_amdgcn_readfirstlane(pp.p[3]);
+    return r == 3 ? p3 : r == 2 ? p2 : r == 1 ? p1 : p0;
+}
+constexpr int MT_SU = 8;  // staging chunks per thread in flight
+
+// Cached 16-byte buffer load (activations that other workgroups read too);
+// an offset at or past the resource's range reads zero.
+__device__ __forceinline__ u32x4_t buf_ld_x4_cached(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
 __device__ __forceinline__ MtPairs mt_pairs(const int32_t *groups, int g) {
     MtPairs r;
 #pragma unroll
@@ -249,9 +268,9 @@ constexpr int MT_WAVES_A = 8, MT_THREADS_A = 512;
 // h = silu(g) u of the unit's rows for the group's pairs from registers.
 __global__ void __launch_bounds__(MT_THREADS_A, 2)
 moe_t_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__ pu,
-                     const uint16_t *__restrict__ X, int top_k, int H, int F, int PH, int nrbF,
-                     int mc, const int32_t *__restrict__ groups, const unsigned *__restrict__ hdr,
-                     float *__restrict__ h_ws) {
+                     const uint16_t *__restrict__ X, int T_x, int top_k, int H, int F, int PH,
+                     int nrbF, int mc, const int32_t *__restrict__ groups,
+                     const unsigned *__restrict__ hdr, float *__restrict__ h_ws) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int nb = (PH + MS_TPB - 1) / MS_TPB, nbu = 2 * nb;
     const int XS = nb * MS_TPB * 256 + 8;  // row stride (bf16), 16-byte pad
@@ -282,15 +301,28 @@ moe_t_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__
         }
         __syncthreads();  // the previous block is done with x
         if (g != staged) {
-            const int per = XS / 8;  // 16-byte chunks per staged row (the pad included)
-            for (int i = tid; i < mc * per; i += MT_THREADS_A) {
-                const int r = i / per, k8 = i - r * per;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (r < c && k8 < H / 8) {
-                    const int p = ld_global(groups + (size_t)g * MT_GREC + 2 + r);
-                    v = ld_global(reinterpret_cast<const u32x4_t *>(X + (size_t)(p / top_k) * H) + k8);
+            // 16-byte chunks per staged row (the pad included); each thread
+            // issues the loads of MT_SU chunks before it writes any of them
+            // (buffer loads: a chunk past the row or the group reads zero)
+            const int per = XS / 8, n = mc * per;
+            const unsigned xbytes = (unsigned)T_x * (unsigned)H * 2u;
+            const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, xbytes);
+            for (int i0 = tid; i0 < n; i0 += MT_SU * MT_THREADS_A) {
+                u32x4_t v[MT_SU];
+#pragma unroll
+                for (int q = 0; q < MT_SU; ++q) {
+                    const int i = i0 + q * MT_THREADS_A, r = i / per, k8 = i - r * per;
+                    const bool ok = r < c && k8 < H / 8;
+                    const unsigned off =
+                        ok ? 2u * ((unsigned)(mt_pair(pp, r) / top_k) * (unsigned)H + 8u * k8)
+                           : xbytes;
+                    v[q] = buf_ld_x4_cached(rx, off);
                 }
-                reinterpret_cast<u32x4_t *>(xl)[i] = v;
+#pragma unroll
+                for (int q = 0; q < MT_SU; ++q) {
+                    const int i = i0 + q * MT_THREADS_A;
+                    if (i < n) reinterpret_cast<u32x4_t *>(xl)[i] = v[q];
+                }
             }
             staged = g;
         }
@@ -352,8 +384,8 @@ moe_t_gate_up_kernel(const uint8_t *__restrict__ pg, const uint8_t *__restrict__
 // Units u = g * nrbH + rb, nb batches each, streamed per wave as in A; h of
 // the group's pairs is staged as bf16 hi rows [0, mc) and lo rows [mc, 2 mc).
 __global__ void __launch_bounds__(MT_THREADS, 3)
-moe_t_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws, int H, int F,
-                  int PF, int nrbH, int mc, const int32_t *__restrict__ groups,
+moe_t_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws, int P, int H,
+                  int F, int PF, int nrbH, int mc, const int32_t *__restrict__ groups,
                   const unsigned *__restrict__ hdr, float *__restrict__ part_ws) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int nb = (PF + MS_TPB - 1) / MS_TPB;
@@ -384,28 +416,41 @@ moe_t_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws
         }
         __syncthreads();  // the previous block is done with h
         if (g != staged) {
-            const int per = FS / 4;  // 4-element chunks per staged row (the pad included)
-            for (int i = tid; i < mc * per; i += MT_THREADS) {
-                const int r = i / per, k4 = i - r * per;
-                f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-                if (r < c && k4 < F / 4) {
-                    const int p = ld_global(groups + (size_t)g * MT_GREC + 2 + r);
-                    v = ld_global(reinterpret_cast<const f32x4_t *>(h_ws + (size_t)p * F) + k4);
-                }
-                const float f[4] = {v[0], v[1], v[2], v[3]};
-                uint16_t hi[4], lo[4];
+            // 4-element chunks per staged row (the pad included); each thread
+            // issues the loads of MT_SU chunks before it converts any of them
+            // (buffer loads: a chunk past the row or the group reads zero)
+            const int per = FS / 4, n = mc * per;
+            const unsigned hbytes = (unsigned)P * (unsigned)F * 4u;
+            const __amdgpu_buffer_rsrc_t rh = make_rsrc(h_ws, hbytes);
+            for (int i0 = tid; i0 < n; i0 += MT_SU * MT_THREADS) {
+                f32x4_t vv[MT_SU];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    hi[q] = f32_to_bf16(f[q]);
-                    lo[q] = f32_to_bf16(f[q] - __builtin_bit_cast(float, (unsigned)hi[q] << 16));
+                for (int q = 0; q < MT_SU; ++q) {
+                    const int i = i0 + q * MT_THREADS, r = i / per, k4 = i - r * per;
+                    const bool ok = r < c && k4 < F / 4;
+                    const unsigned off =
+                        ok ? 4u * ((unsigned)mt_pair(pp, r) * (unsigned)F + 4u * k4) : hbytes;
+                    vv[q] = __builtin_bit_cast(f32x4_t, buf_ld_x4_cached(rh, off));
                 }
-                uint2 vh, vl;
-                vh.x = hi[0] | ((unsigned)hi[1] << 16);
-                vh.y = hi[2] | ((unsigned)hi[3] << 16);
-                vl.x = lo[0] | ((unsigned)lo[1] << 16);
-                vl.y = lo[2] | ((unsigned)lo[3] << 16);
-                reinterpret_cast<uint2 *>(hl + (size_t)r * FS)[k4] = vh;
-                reinterpret_cast<uint2 *>(hl + (size_t)(mc + r) * FS)[k4] = vl;
+#pragma unroll
+                for (int q = 0; q < MT_SU; ++q) {
+                    const int i = i0 + q * MT_THREADS, r = i / per, k4 = i - r * per;
+                    if (i >= n) continue;
+                    uint16_t hi[4], lo[4];
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const float f = vv[q][e4];
+                        hi[e4] = f32_to_bf16(f);
+                        lo[e4] = f32_to_bf16(f - __builtin_bit_cast(float, (unsigned)hi[e4] << 16));
+                    }
+                    uint2 vh, vl;
+                    vh.x = hi[0] | ((unsigned)hi[1] << 16);
+                    vh.y = hi[2] | ((unsigned)hi[3] << 16);
+                    vl.x = lo[0] | ((unsigned)lo[1] << 16);
+                    vl.y = lo[2] | ((unsigned)lo[3] << 16);
+                    reinterpret_cast<uint2 *>(hl + (size_t)r * FS)[k4] = vh;
+                    reinterpret_cast<uint2 *>(hl + (size_t)(mc + r) * FS)[k4] = vl;
+                }
             }
             staged = g;
         }
@@ -487,7 +532,7 @@ hipError_t launch_moe_skinny(const uint8_t *pg, const uint8_t *pu, const uint8_t
         const int gridA = (int)(unitsA < (int64_t)cus * 2 ? unitsA : (int64_t)cus * 2);
         const size_t ldsA = (size_t)mc * (nbA * MS_TPB * 256 + 8) * 2;
         hipLaunchKernelGGL(moe_t_gate_up_kernel, dim3(gridA), dim3(MT_THREADS_A), ldsA, s, pg, pu, X,
-                           top_k, (int)H, (int)F, PH, nrbF, mc, groups, hdr, h_ws);
+                           T, top_k, (int)H, (int)F, PH, nrbF, mc, groups, hdr, h_ws);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
         const int PF = (int)ceil_div(F, FP4_TILE_K), nrbH = (int)(H / RB);
@@ -495,7 +540,7 @@ hipError_t launch_moe_skinny(const uint8_t *pg, const uint8_t *pu, const uint8_t
         const int64_t unitsB = (int64_t)P * nrbH;
         const int gridB = (int)(unitsB < (int64_t)cus * 3 ? unitsB : (int64_t)cus * 3);
         const size_t ldsB = (size_t)2 * mc * (nbB * MS_TPB * 256 + 8) * 2;
-        hipLaunchKernelGGL(moe_t_down_kernel, dim3(gridB), dim3(MT_THREADS), ldsB, s, pd, h_ws,
+        hipLaunchKernelGGL(moe_t_down_kernel, dim3(gridB), dim3(MT_THREADS), ldsB, s, pd, h_ws, P,
                            (int)H, (int)F, PF, nrbH, mc, groups, hdr, part);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
