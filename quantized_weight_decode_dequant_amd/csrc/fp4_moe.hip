@@ -433,6 +433,7 @@ moe_down_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ h_ws,
 constexpr int MF_WAVES = 16;
 constexpr int MF_THREADS = MF_WAVES * 64;
 constexpr int MF_HMAX = 32768;  // fp32 values of h staged (128 KB)
+constexpr int MF_UMAX = 8;      // units whose wave sums are added together
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mf_rsrc(const uint8_t *pd, const int32_t *ids,
                                                           int E, int nrbH, int PF, int rb, int s,
@@ -452,8 +453,8 @@ moe_down_fused_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ 
     const int nb = (PF + MS_TPB - 1) / MS_TPB;       // batches per slot
     const int hstride = nb * MS_TPB * 64;             // float4 per staged slot
     float4 *hl = reinterpret_cast<float4 *>(smem);
-    float *red = reinterpret_cast<float *>(smem + (size_t)top_k * hstride * 16);  // [WAVES][16]
-    float *wl = red + MF_WAVES * 16;                                                // [top_k]
+    float *red = reinterpret_cast<float *>(smem + (size_t)top_k * hstride * 16);  // [UMAX][WAVES][16]
+    float *wl = red + MF_UMAX * MF_WAVES * 16;                                      // [top_k]
     const int tid = threadIdx.x, lane = tid & 63, kg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (blockIdx.x == 0 && tid == 0) {
@@ -467,6 +468,7 @@ moe_down_fused_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ 
     const MsCursor first = {wave / nb, wave % nb};  // a wave's first batch of every unit
     Fp4Batch A, B;
     int rb = blockIdx.x;
+    int rb0 = rb, ui = 0;  // first unit of the pending slots, and their count
     {
         const __amdgpu_buffer_rsrc_t rs = mf_rsrc(pd, ids, E, nrbH, PF, rb, first.i, wave < T);
 #pragma unroll
@@ -529,21 +531,31 @@ moe_down_fused_kernel(const uint8_t *__restrict__ pd, const float *__restrict__ 
                 if (t >= T) break;
             }
         }
+        // the wave's sums of this unit wait in the unit's own slot; a wave
+        // goes on to its next unit without waiting for the others, and the
+        // workgroup adds the slots of up to MF_UMAX units at once
         acc = reduce_kslices(acc);
-        if (lane < 16) red[wave * 16 + lane] = acc;
-        __syncthreads();
-        if (tid < 16) {
-            float v = 0.f;
+        if (lane < 16) red[(ui * MF_WAVES + wave) * 16 + lane] = acc;
+        ++ui;
+        const int rbn = rb + G;
+        if (ui == MF_UMAX || rbn >= nrbH) {
+            __syncthreads();
+            for (int r = tid; r < ui * 16; r += MF_THREADS) {
+                const int i = r >> 4, row = r & 15;
+                float v = 0.f;
 #pragma unroll
-            for (int wv = 0; wv < MF_WAVES; ++wv) v += red[wv * 16 + tid];
-            const int n = rb * RB + tid;
-            if (out_f32)
-                st_global<float>(y, n, v);
-            else
-                st_global<uint16_t>(y, n, f32_to_bf16(v));
+                for (int wv = 0; wv < MF_WAVES; ++wv) v += red[(i * MF_WAVES + wv) * 16 + row];
+                const int n = (rb0 + i * G) * RB + row;
+                if (out_f32)
+                    st_global<float>(y, n, v);
+                else
+                    st_global<uint16_t>(y, n, f32_to_bf16(v));
+            }
+            __syncthreads();  // the slots are reused by the next units
+            ui = 0;
+            rb0 = rbn;
         }
-        __syncthreads();  // red is reused by the next unit
-        rb += G;
+        rb = rbn;
         if (rb >= nrbH) break;
         if (steps & 1) A = B;  // the next unit's first batch went to B
     }
@@ -628,7 +640,8 @@ hipError_t launch_moe(const uint8_t *pg, const uint8_t *pu, const uint8_t *pd, i
         if (hstaged <= MF_HMAX) {
             // down projection and the weighted sum over slots in one launch
             const int gridF = nrbH < cus ? nrbH : cus;
-            const size_t ldsF = (size_t)hstaged * 4 + (size_t)MF_WAVES * 16 * 4 + (size_t)top_k * 4;
+            const size_t ldsF = (size_t)hstaged * 4 + (size_t)MF_UMAX * MF_WAVES * 16 * 4 +
+                                (size_t)top_k * 4;
             hipLaunchKernelGGL(moe_down_fused_kernel, dim3(gridF), dim3(MF_THREADS), ldsF, s, pd,
                                h_ws, ids, w, (int)E, (int)H, (int)F, PF, nrbH, top_k, y,
                                out_f32 ? 1 : 0, status);
