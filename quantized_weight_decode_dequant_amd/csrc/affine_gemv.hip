@@ -85,8 +85,10 @@ pack_affine_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict
                 unsigned word = 0;
                 for (int s = 0; s < per_word; ++s) {
                     const int j = wi * per_word + s;
-                    word |= (((unsigned)c[2 * j] >> o) & m) << (w * s);
-                    word |= (((unsigned)c[2 * j + 1] >> o) & m) << (16 + w * s);
+                    // 3-bit codes: bit 2 of pair j at ag3_pos(j) (affine_tile.h)
+                    const int b = (bits == 3 && q == 1) ? ag3_pos(j) : w * s;
+                    word |= (((unsigned)c[2 * j] >> o) & m) << b;
+                    word |= (((unsigned)c[2 * j + 1] >> o) & m) << (16 + b);
                 }
                 reinterpret_cast<uint32_t *>(base + off + (size_t)4 * w * l)[wi] = word;
             }
@@ -167,7 +169,7 @@ __device__ __forceinline__ unsigned ag2_pair(const AgTile<BITS, GPT> &T, int j,
     const unsigned u = s < 3 ? w : s < 6 ? w >> 6 : w >> 12;
     if constexpr (BITS == 3) {
         const unsigned w1 = T.p1[0];
-        const int sh = j - (2 * r + 2);  // plane-1 bit j goes to bit 2 r + 2
+        const int sh = ag3_pos(j) - (2 * r + 2);  // pair j's plane-1 bit goes to bit 2 r + 2
         return ((sh >= 0 ? w1 >> sh : w1 << -sh) & k.b[r]) | ag_and_or(u, k.m[r], k.g[r]);
     } else {
         return (u & k.m[r]) | k.g[r];

@@ -17,6 +17,21 @@ template <> struct AffPlanes<5> { static constexpr int NP = 2, W0 = 4, W1 = 1, O
 template <> struct AffPlanes<6> { static constexpr int NP = 2, W0 = 4, W1 = 2, O1 = 4; };
 template <> struct AffPlanes<8> { static constexpr int NP = 2, W0 = 4, W1 = 4, O1 = 4; };
 
+// 3-bit codes: the bit position, within each 16-bit half of the tile's
+// plane-1 word, of bit 2 of pair j's codes (j = 0..15).  Pair j's plane-0
+// field is read from a copy of its plane-0 word shifted by 0, 6 or 12, at
+// bits 2r..2r+1 with r = (j % 8) % 3, and its plane-1 bit belongs at bit
+// 2r + 2.  The positions are chosen so that pairs of different r share the
+// shift that brings their bits there (j = 0-2 by -2, 3-5 by -1, 8-10 by 4,
+// 11-13 by 5, 6-7 by 10, 14-15 by 11): six shifts of the plane-1 word serve
+// the 16 pairs.
+__host__ __device__ constexpr int ag3_pos(int j) {
+    return j < 6    ? 2 * (j % 3) + j / 3
+           : j < 8  ? 12 + 2 * (j - 6)
+           : j < 14 ? 6 + 2 * ((j - 8) % 3) + (j - 8) / 3
+                    : 13 + 2 * (j - 14);
+}
+
 __device__ __forceinline__ unsigned buf_ld_x1(__amdgpu_buffer_rsrc_t r, unsigned voff,
                                               unsigned soff) {
     return (unsigned)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 2);
@@ -108,7 +123,7 @@ __device__ __forceinline__ unsigned ag_bf16_pair(const AgTile<BITS, GPT> &T, int
     const unsigned a = T.p0[j / PER0] >> (PL::W0 * (j % PER0));
     if constexpr (PL::NP == 2 && BITS != 8) {
         constexpr int PER1 = 16 / PL::W1;
-        const int sh = PL::W1 * (j % PER1) - PL::O1;
+        const int sh = (BITS == 3 ? ag3_pos(j) : PL::W1 * (j % PER1)) - PL::O1;
         const unsigned w = T.p1[j / PER1];
         return ((sh >= 0 ? w >> sh : w << -sh) & k.m1) | ag_and_or(a, k.m0, k.magic);
     } else {

@@ -51,7 +51,10 @@ namespace qg {
 //   covers k = 32i .. 32i + 32, one 32-k block: the k of one 16x16x32 MFMA
 //   step, inside one group).  Pair j (codes 2j, 2j+1) sits in word
 //   j / (16 / w_p), at bit w_p (j % (16 / w_p)) (code 2j) and 16 + the same
-//   (code 2j+1), so a shift and an and-or yield both as the two halves.
+//   (code 2j+1), so a shift and an and-or yield both as the two halves; the
+//   one exception is the 1-bit plane of 3-bit codes, where pair j's bits sit
+//   at ag3_pos(j) and 16 + ag3_pos(j) (affine_tile.h), an order that lets
+//   one shift serve three pairs.
 //   [256 b, ...)  per (row r, group t of the tile): (scale | bias << 16) at
 //   256 b + 4 (r (128 / g) + t).
 // Rows past N and k past K are zero-filled (zero codes and zero scales).
